@@ -1,0 +1,431 @@
+"""Float64 CPU oracle for basis-synchronized online low-rank KV-cache compression.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it, and this module imports nothing from the product path: the two
+share no code, no tables and no constants.
+
+What is computed, and where it comes from
+-----------------------------------------
+Page cited throughout: "iS-KV -- Basis-synchronized online low-rank KV
+compression -- What does it mean?" (learnaivisually.com explainer of the iS-KV
+paper), abbreviated [iS-KV explainer].
+
+* Cache layout [iS-KV explainer, TL;DR and the window paragraph ("paint
+  shop")]: the newest tokens are kept exact; every older position is kept as a
+  short coefficient vector over a shared basis; nothing is evicted.
+* Maintenance [iS-KV explainer, Jargon "Block-incremental SVD" and the drift
+  paragraph]: each time 64 tokens leave the exact window they are folded into
+  the factorization as one block with Brand's block-incremental SVD, solved on a
+  small core matrix whose size is independent of the history length.
+* Basis synchronization [iS-KV explainer, FAQ "What is basis synchronization?"
+  and the drift paragraph]: when the basis changes, all stored coefficients are
+  rewritten for the new basis in the same step.
+* Keys are compressed before RoPE and RoPE is re-applied when a key is rebuilt
+  [iS-KV explainer, Jargon "Pre-RoPE keys"].
+* Every new query scores every earlier key [iS-KV explainer, the re-attention
+  paragraph ("Why not bin the quiet colors?")].
+* Persistent-KV bytes [iS-KV explainer, Jargon "Persistent-KV compression"].
+
+Readings taken where the page is silent (each is listed in the design doc):
+  window of W exact tokens plus up to 63 not yet folded (ring of W+64 rows,
+  fold when it is full); basis per KV head, separate for K and V, one rank r;
+  initial basis I[:, :r] with S = 0; core [[diag S, 0], [P, R_r^T]]; a
+  rank-revealing residual basis and a unit-vector completion of null
+  directions; half-split RoPE with base 10000 and fp64 angles; absolute
+  positions from 0; scale 1/sqrt(d); bf16 round-to-nearest-even at every store
+  in the "bf16" storage mode.
+
+Decode is reached exactly (up to rounding order) by the fused route the GPU
+takes, so here it is the plain definition: softmax attention over the rebuilt
+cache.  The fold is an approximation built step by step, so it follows Brand's
+update in order, with a LAPACK SVD of the core (numpy.linalg.svd).
+
+Parity unpinned: the choice of directions with zero singular value (null
+completion), the signs of singular vectors, exact ties between singular values,
+and the page's printed drift and accuracy figures (they come from model
+traces that are not available).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+EPS64 = float(np.finfo(np.float64).eps)
+BLOCK = 64
+
+
+# ----------------------------------------------------------------------------
+# Storage rounding
+# ----------------------------------------------------------------------------
+
+def bf16_round(x):
+    """Round to the nearest bfloat16 value (ties to even), returned as float64.
+
+    bfloat16 keeps the float32 exponent and 8 significant bits.  Rounding is
+    done in one step from float64 (no intermediate float32).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    # bfloat16 subnormals share float32's smallest exponent (2**-126); below
+    # it the spacing is fixed at 2**-133.
+    e_eff = np.maximum(e, -125)
+    scaled = np.ldexp(x, 8 - e_eff)           # 8 significant bits above the point
+    return np.ldexp(np.rint(scaled), e_eff - 8)   # np.rint: ties to even
+
+
+def store_round(x, storage: str):
+    """Apply the rounding of one store in the given storage mode."""
+    if storage == "bf16":
+        return bf16_round(x)
+    if storage == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if storage == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown storage mode {storage!r}")
+
+
+# ----------------------------------------------------------------------------
+# RoPE (half-split pairing), re-applied when a key is rebuilt
+# [iS-KV explainer, Jargon "Pre-RoPE keys"]
+# ----------------------------------------------------------------------------
+
+def rope_theta(d: int, base: float) -> np.ndarray:
+    """Frequencies theta_i = base**(-2i/d) for i < d/2, in float64."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / d)
+
+
+def rope(x, pos, base: float = 10000.0):
+    """Rotate feature pairs (i, i + d/2) of x by angle pos * theta_i.
+
+    x has shape (..., d); pos broadcasts against x's leading axes.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_theta(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Brand's block-incremental SVD step for one factor (K or V of one KV head)
+# [iS-KV explainer, Jargon "Block-incremental SVD"; drift paragraph]
+# ----------------------------------------------------------------------------
+
+def _residual_basis(R, B, norm_a):
+    """Orthonormal basis of the residual rows R, orthogonal to span(B).
+
+    Rank-revealing: take the thin SVD of R^T and keep the left singular
+    vectors whose singular value exceeds sqrt(eps) * ||A||_F; project them off
+    B twice and re-orthonormalize.  Returns Q of shape (d, T) with the kept
+    columns first and zero columns after them.
+    """
+    T, d = R.shape
+    Q = np.zeros((d, T))
+    if norm_a == 0.0:
+        return Q
+    w, sig, _ = np.linalg.svd(R.T, full_matrices=False)
+    keep = sig > math.sqrt(EPS64) * norm_a
+    qk = w[:, keep]
+    for _ in range(2):
+        qk = qk - B @ (B.T @ qk)
+    if qk.shape[1]:
+        qk, _ = np.linalg.qr(qk)
+        Q[:, : qk.shape[1]] = qk
+    return Q
+
+
+def _complete_null_columns(Bn, sig_r, tol):
+    """Replace columns whose singular value is <= tol by unit vectors.
+
+    In column order, each such column becomes the e_k (k = lowest index among
+    the largest) whose remainder after two Gram-Schmidt passes against the
+    columns kept so far is largest, normalized.  Keeps the basis orthonormal
+    when the core has fewer than r non-zero singular values.
+    """
+    d, r = Bn.shape
+    bad = [j for j in range(r) if not sig_r[j] > tol]
+    if not bad:
+        return Bn
+    Bn = Bn.copy()
+    cols = [Bn[:, j] for j in range(r) if sig_r[j] > tol]
+    for j in bad:
+        basis = np.stack(cols, axis=1) if cols else np.zeros((d, 0))
+        best_norm, best_vec = -1.0, None
+        for k in range(d):
+            e = np.zeros(d)
+            e[k] = 1.0
+            for _ in range(2):
+                e = e - basis @ (basis.T @ e)
+            nrm = float(np.linalg.norm(e))
+            if nrm > best_norm:
+                best_norm, best_vec = nrm, e
+        Bn[:, j] = best_vec / best_norm
+        cols.append(Bn[:, j])
+    return Bn
+
+
+def brand_fold(A, B, S):
+    """Fold one block of rows A (T x d) into the rank-r factorization (B, S).
+
+    State invariant (Brand): the stored coefficients C of the old rows satisfy
+    C = U diag(S) with U orthonormal, so the old history is U diag(S) B^T.
+
+    Steps:
+      1. projection P = A B and residual R = A - P B^T, repeated once;
+      2. residual basis Q (rank-revealing, orthogonal to B) and R_r^T = R Q;
+      3. core K = [[diag S, 0], [P, R_r^T]] of size (r+T) x (r+T); the stacked
+         history equals diag(U, I) K [B Q]^T, so K carries its singular values
+         and right singular vectors;
+      4. K = U' diag(s') V'^T by LAPACK, s' descending;
+      5. keep r: B_new = [B Q] V'[:, :r] (null columns completed), S_new = s'[:r];
+         M = B^T B_new rewrites old coefficients (basis synchronization);
+         the block's own coefficients are P M + R_r^T (Q^T B_new).
+
+    Returns (B_new, S_new, M, C_blk).
+    """
+    A = np.asarray(A, dtype=np.float64)
+    T, d = A.shape
+    r = B.shape[1]
+    P = A @ B
+    R = A - P @ B.T
+    P2 = R @ B
+    P = P + P2
+    R = R - P2 @ B.T
+    Q = _residual_basis(R, B, float(np.linalg.norm(A)))
+    RrT = R @ Q                                        # (T, T)
+    core = np.zeros((r + T, r + T))
+    core[:r, :r] = np.diag(S)
+    core[r:, :r] = P
+    core[r:, r:] = RrT
+    _, s, vt = np.linalg.svd(core)
+    Vr = vt[:r].T                                      # (r+T, r)
+    BQ = np.concatenate([B, Q], axis=1)                # (d, r+T)
+    Bn = BQ @ Vr
+    tol = BLOCK * (r + T) * EPS64 * float(s[0])
+    Bn = _complete_null_columns(Bn, s[:r], tol)
+    S_new = s[:r].copy()
+    M = B.T @ Bn
+    C_blk = P @ M + RrT @ (Q.T @ Bn)
+    return Bn, S_new, M, C_blk
+
+
+# ----------------------------------------------------------------------------
+# One factor of one KV head: ring rows, basis, singular values, coefficients
+# ----------------------------------------------------------------------------
+
+class Factor:
+    """K or V store of one (sequence, layer, KV head)."""
+
+    def __init__(self, d: int, r: int, window: int, max_tokens: int, storage: str,
+                 block: int = BLOCK):
+        if window % block:
+            raise ValueError("window must be a multiple of the block size")
+        self.d, self.r, self.window, self.block = d, r, window, block
+        self.storage = storage
+        self.slots = window + block
+        self.ring = np.zeros((self.slots, d))
+        self.B = np.eye(d, r)                 # basis before the first block
+        self.S = np.zeros(r)
+        self.C = np.zeros((max_tokens, r))
+        self.pending = None                    # M awaiting synchronization
+
+    def write(self, pos: int, x):
+        self.ring[pos % self.slots] = store_round(x, self.storage)
+
+    def block_rows(self, n_c: int):
+        s0 = n_c % self.slots
+        return self.ring[s0: s0 + self.block]
+
+    def fold(self, n_c: int):
+        Bn, Sn, M, C_blk = brand_fold(self.block_rows(n_c), self.B, self.S)
+        self.C[n_c: n_c + self.block] = store_round(C_blk, self.storage)
+        self.B, self.S, self.pending = Bn, Sn, M
+        return M
+
+    def sync(self, n_c_old: int):
+        """Rewrite the old coefficients for the current basis: C <- C M."""
+        M = self.pending
+        self.C[:n_c_old] = store_round(self.C[:n_c_old] @ M, self.storage)
+        self.pending = None
+
+    def rebuilt(self, n_c: int, length: int):
+        """Rows 0..length-1 as decode sees them: C B^T, then exact ring rows."""
+        out = np.empty((length, self.d))
+        out[:n_c] = self.C[:n_c] @ self.B.T
+        for p in range(n_c, length):
+            out[p] = self.ring[p % self.slots]
+        return out
+
+
+class Unit:
+    """One (sequence, layer, KV head): a K factor, a V factor and counters."""
+
+    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK):
+        self.K = Factor(d, r, window, max_tokens, storage, block)
+        self.V = Factor(d, r, window, max_tokens, storage, block)
+        self.length = 0          # tokens appended (L)
+        self.n_c = 0             # tokens held as coefficients (N_c)
+        self.block = block
+        self.window = window
+
+    @property
+    def ready(self) -> bool:
+        return self.length - self.n_c == self.window + self.block
+
+    def append(self, k, v):
+        if self.length - self.n_c >= self.window + self.block:
+            raise RuntimeError("ring full: fold the oldest block first")
+        self.K.write(self.length, k)
+        self.V.write(self.length, v)
+        self.length += 1
+
+    def fold(self):
+        if not self.ready:
+            raise RuntimeError("no block ready")
+        mk = self.K.fold(self.n_c)
+        mv = self.V.fold(self.n_c)
+        self.n_c += self.block
+        return mk, mv
+
+    def sync(self):
+        if self.K.pending is None:
+            raise RuntimeError("no pending update")
+        old = self.n_c - self.block
+        self.K.sync(old)
+        self.V.sync(old)
+
+    def decode(self, q, q_pos, scale, rope_base=10000.0):
+        """Softmax attention of the query rows q (g x d) over every position.
+
+        Keys: rebuilt (C_K B_K^T) or exact (ring), each rotated at its own
+        position; queries rotated at q_pos; values rebuilt likewise, never
+        rotated.
+        """
+        q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+        L = self.length
+        keys = rope(self.K.rebuilt(self.n_c, L), np.arange(L), rope_base)
+        vals = self.V.rebuilt(self.n_c, L)
+        qr = rope(q, q_pos, rope_base)
+        s = (qr @ keys.T) * scale                  # (g, L)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        return p @ vals
+
+    def history(self, which: str):
+        """Reconstructed pre-RoPE history C B^T of the compressed rows."""
+        f = self.K if which == "K" else self.V
+        return f.C[: self.n_c] @ f.B.T
+
+    def load_state(self, length, n_c, ring_k, ring_v, Bk, Sk, Ck, Bv, Sv, Cv):
+        """Install a state (used to hand an oracle-made state to other code)."""
+        self.length, self.n_c = int(length), int(n_c)
+        for f, ring, B, S, C in ((self.K, ring_k, Bk, Sk, Ck), (self.V, ring_v, Bv, Sv, Cv)):
+            f.ring[:] = ring
+            f.B = np.array(B, dtype=np.float64)
+            f.S = np.array(S, dtype=np.float64)
+            f.C[: n_c] = C[: n_c]
+            f.pending = None
+
+
+def drift(before, after):
+    """Relative change of a reconstructed history caused by one update.
+
+    Reading of [iS-KV explainer, drift paragraph]: drift is the change of the
+    stored history from one update (not the error against the uncompressed
+    cache); measured as ||H_after - H_before||_F / ||H_before||_F over the rows
+    that existed before the update.
+    """
+    before = np.asarray(before, dtype=np.float64)
+    after = np.asarray(after, dtype=np.float64)[: before.shape[0]]
+    nb = np.linalg.norm(before)
+    return float(np.linalg.norm(after - before) / nb) if nb > 0 else 0.0
+
+
+# ----------------------------------------------------------------------------
+# Whole cache: batch x layers x KV heads, with grouped query heads
+# ----------------------------------------------------------------------------
+
+class Oracle:
+    """The five verbs over every (sequence, layer, KV head), in float64.
+
+    Shapes follow the library: k, v are [batch, n, kv_heads, d] (pre-RoPE),
+    q is [batch, q_heads, d] (pre-RoPE), out is [batch, q_heads, d].  Query head
+    h reads KV head h // (q_heads // kv_heads) (grouped-query attention).
+    """
+
+    def __init__(self, batch, num_layers, kv_heads, q_heads, head_dim, rank, window,
+                 max_tokens, storage="bf16", rope_base=10000.0, softmax_scale=None,
+                 block=BLOCK):
+        if q_heads % kv_heads:
+            raise ValueError("q_heads must be a multiple of kv_heads")
+        self.batch, self.num_layers = batch, num_layers
+        self.kv_heads, self.q_heads = kv_heads, q_heads
+        self.d, self.r, self.window, self.block = head_dim, rank, window, block
+        self.storage, self.rope_base = storage, rope_base
+        self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale else float(softmax_scale)
+        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block)
+                        for _ in range(kv_heads)] for _ in range(num_layers)]
+                      for _ in range(batch)]
+
+    def unit(self, b, layer, h) -> Unit:
+        return self.units[b][layer][h]
+
+    def append(self, layer, k, v):
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        for b in range(self.batch):
+            for t in range(k.shape[1]):
+                for h in range(self.kv_heads):
+                    self.units[b][layer][h].append(k[b, t, h], v[b, t, h])
+        return self.ready(layer)
+
+    def ready(self, layer) -> bool:
+        return self.units[0][layer][0].ready
+
+    def block_update(self, layer):
+        for b in range(self.batch):
+            for h in range(self.kv_heads):
+                self.units[b][layer][h].fold()
+
+    def sync(self, layer):
+        for b in range(self.batch):
+            for h in range(self.kv_heads):
+                self.units[b][layer][h].sync()
+
+    def decode_attn(self, layer, q, q_pos):
+        q = np.asarray(q, dtype=np.float64)
+        g = self.q_heads // self.kv_heads
+        out = np.zeros((self.batch, self.q_heads, self.d))
+        for b in range(self.batch):
+            for h in range(self.kv_heads):
+                u = self.units[b][layer][h]
+                out[b, h * g:(h + 1) * g] = u.decode(q[b, h * g:(h + 1) * g], q_pos,
+                                                     self.scale, self.rope_base)
+        return out
+
+
+# ----------------------------------------------------------------------------
+# Persistent-KV byte model [iS-KV explainer, Jargon "Persistent-KV compression"]
+# ----------------------------------------------------------------------------
+
+def full_kv_bytes(tokens, layers, kv_heads, head_dim, elem_bytes):
+    """Bytes of an uncompressed K+V cache."""
+    return 2 * tokens * layers * kv_heads * head_dim * elem_bytes
+
+
+def persistent_kv_bytes(n_c, n_exact, layers, kv_heads, head_dim, rank, elem_bytes,
+                        basis_bytes=4):
+    """Bytes kept between decode steps: coefficients, bases and singular values
+    of K and V, plus the exact rows.  Model weights and temporary rebuild
+    buffers are excluded."""
+    per_head = 2 * (n_c * rank * elem_bytes + head_dim * rank * basis_bytes
+                    + rank * basis_bytes + n_exact * head_dim * elem_bytes)
+    return layers * kv_heads * per_head

@@ -1,0 +1,403 @@
+"""Pins of the float64 oracle to facts fixed outside the oracle itself.
+
+Each test compares the oracle with a closed form, an invariant, a special case
+that reduces to a textbook or library routine, a brute-force result on tiny
+inputs, or a figure printed on the page -- never with a retyping of the
+oracle's own formula.  Page cited: the iS-KV explainer ("iS-KV --
+Basis-synchronized online low-rank KV compression -- What does it mean?").
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (Oracle, Unit, bf16_round, brand_fold, drift, full_kv_bytes,
+                    persistent_kv_bytes, rope)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Independent references (library routines, different formulations)
+# ---------------------------------------------------------------------------
+
+def rope_complex(x, pos, base=10000.0):
+    """RoPE as complex multiplication: z_i = x_i + 1j*x_{i+d/2}, z_i * exp(1j*pos*f_i),
+    with the usual inverse-frequency vector 1 / base**(arange(0, d, 2)/d)."""
+    x = torch.as_tensor(np.asarray(x), dtype=torch.float64)
+    d = x.shape[-1]
+    inv = 1.0 / (base ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    ang = torch.as_tensor(np.asarray(pos), dtype=torch.float64)[..., None] * inv
+    z = torch.complex(x[..., : d // 2], x[..., d // 2:]) * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1).numpy()
+
+
+def exact_attention(q, keys, vals, q_pos, scale, base=10000.0):
+    """Uncompressed attention via torch's scaled_dot_product_attention (float64)."""
+    L = keys.shape[0]
+    kr = torch.as_tensor(rope_complex(keys, np.arange(L), base))
+    qr = torch.as_tensor(rope_complex(q, np.full(q.shape[0], q_pos), base))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qr[None], kr[None], torch.as_tensor(np.asarray(vals))[None], scale=scale)
+    return out[0].numpy()
+
+
+def subspace_dist(B1, B2):
+    """||P1 - P2||_2 for the projectors onto span(B1), span(B2)."""
+    Q1, _ = np.linalg.qr(B1)
+    Q2, _ = np.linalg.qr(B2)
+    return float(np.linalg.norm(Q1 @ Q1.T - Q2 @ Q2.T, 2))
+
+
+def lowrank(rng, L, d, k, noise=0.0):
+    X = rng.standard_normal((L, k)) @ rng.standard_normal((k, d)) / math.sqrt(k)
+    return X + noise * rng.standard_normal((L, d))
+
+
+def run_unit(X, Y, d, r, window, storage="f64", block=64, sync=True, after_fold=None):
+    u = Unit(d, r, window, X.shape[0] + block, storage, block)
+    for t in range(X.shape[0]):
+        u.append(X[t], Y[t])
+        if u.ready:
+            u.fold()
+            if sync:
+                u.sync()
+            if after_fold:
+                after_fold(u)
+    return u
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage rounding: pinned to torch's float32 -> bfloat16 conversion
+# ---------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-39, -2.5e-40]]).astype(np.float32)
+    # exact ties: values halfway between two bf16 numbers
+    ties = (np.arange(1, 512, dtype=np.float32) * 2 + 1) * np.float32(2.0 ** -8) + 1
+    x = np.concatenate([x, ties, -ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(bf16_round(x.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------------------
+# P7: RoPE invariants and the complex-multiplication form
+# ---------------------------------------------------------------------------
+
+def test_rope_matches_complex_form_and_invariants():
+    rng = np.random.default_rng(1)
+    d = 128
+    x = rng.standard_normal((50, d))
+    pos = rng.integers(0, 70000, 50)
+    np.testing.assert_allclose(rope(x, pos), rope_complex(x, pos), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(np.linalg.norm(rope(x, pos), axis=1), np.linalg.norm(x, axis=1),
+                               rtol=1e-13)
+    np.testing.assert_array_equal(rope(x, np.zeros(50)), x)
+    # scores depend only on the position difference
+    q = rng.standard_normal(d)
+    kp, qp, delta = rng.integers(0, 60000, 50), 61234, 1234
+    s0 = rope(x, kp) @ rope(q, qp)
+    s1 = rope(x, kp + delta) @ rope(q, qp + delta)
+    np.testing.assert_allclose(s1, s0, rtol=0, atol=1e-11 * np.abs(s0).max())
+
+
+# ---------------------------------------------------------------------------
+# P8: ring slots and no-fold decode = exact attention
+# ---------------------------------------------------------------------------
+
+def test_ring_slots_and_exact_attention_before_first_fold():
+    rng = np.random.default_rng(2)
+    d, r, W = 64, 8, 128
+    L = W + 63                                   # one short of the first fold
+    X, Y = rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    u = run_unit(X, Y, d, r, W)
+    assert u.n_c == 0 and not u.ready
+    for p in range(L):
+        np.testing.assert_array_equal(u.K.ring[p % (W + 64)], X[p])
+        np.testing.assert_array_equal(u.V.ring[p % (W + 64)], Y[p])
+    q = rng.standard_normal((3, d))
+    scale = 1 / math.sqrt(d)
+    np.testing.assert_allclose(u.decode(q, L - 1, scale), exact_attention(q, X, Y, L - 1, scale),
+                               rtol=0, atol=1e-12)
+
+
+def test_ring_slot_is_position_mod_window_plus_block():
+    rng = np.random.default_rng(3)
+    d, W = 16, 64
+    X = rng.standard_normal((1000, d))
+    u = run_unit(X, X, d, 4, W)
+    for p in range(u.n_c, u.length):
+        np.testing.assert_array_equal(u.K.ring[p % (W + 64)], X[p])
+    assert u.length - u.n_c < W + 64 and u.length - u.n_c >= W
+
+
+# ---------------------------------------------------------------------------
+# P1: full rank (r = d) reproduces exact attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,W,L", [(32, 64, 600), (64, 128, 700)])
+def test_full_rank_decode_is_exact_attention(d, W, L):
+    rng = np.random.default_rng(4)
+    X, Y = rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    u = run_unit(X, Y, d, d, W)
+    assert u.n_c >= 4 * 64
+    q = rng.standard_normal((4, d))
+    scale = 1 / math.sqrt(d)
+    got = u.decode(q, L, scale)
+    ref = exact_attention(q, X, Y, L, scale)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-11
+    # every stored row is rebuilt exactly
+    np.testing.assert_allclose(u.history("K"), X[: u.n_c], rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# P2: true rank <= r -> the incremental factorization is the batch SVD
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,r,k", [(128, 32, 24), (64, 64, 40), (128, 64, 64), (32, 8, 8)])
+def test_rank_le_r_matches_batch_svd(d, r, k):
+    rng = np.random.default_rng(5 + k)
+    L = 64 * 12 + 64 + 17
+    X = lowrank(rng, L, d, k)
+    Y = lowrank(rng, L, d, k)
+    u = run_unit(X, Y, d, r, 64)
+    H = X[: u.n_c]
+    rec = u.history("K")
+    assert np.linalg.norm(rec - H) / np.linalg.norm(H) < 1e-11
+    s_batch = np.linalg.svd(H, compute_uv=False)
+    np.testing.assert_allclose(u.K.S[:k], s_batch[:k], rtol=1e-12, atol=1e-12 * s_batch[0])
+    assert np.all(u.K.S[k:] <= 1e-9 * s_batch[0])
+    _, _, vt = np.linalg.svd(H, full_matrices=False)
+    assert subspace_dist(u.K.B[:, :k], vt[:k].T) < 1e-10
+    # Independent route (incremental covariance, token by token): the top-k
+    # eigenvectors of sum x^T x span the same subspace.
+    G = np.zeros((d, d))
+    for x in H:
+        G += np.outer(x, x)
+    w, V = np.linalg.eigh(G)
+    assert subspace_dist(u.K.B[:, :k], V[:, ::-1][:, :k]) < 1e-9
+
+
+def test_noisy_top_subspace_close_to_batch():
+    """Sanity (not an exact pin): with rank-24 signal + 1% noise and r = 32,
+    the gapped top-24 subspace agrees with the batch SVD's."""
+    rng = np.random.default_rng(6)
+    d, r, L = 128, 32, 64 * 30
+    X = lowrank(rng, L, d, 24, noise=0.01)
+    u = run_unit(X, X, d, r, 256)
+    _, _, vt = np.linalg.svd(X[: u.n_c], full_matrices=False)
+    assert subspace_dist(u.K.B[:, :24], vt[:24].T) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# P9: brute force on tiny inputs (d = 8, r = 2, block = 4)
+# ---------------------------------------------------------------------------
+
+def test_tiny_brute_force_block4():
+    rng = np.random.default_rng(7)
+    d, r, blk = 8, 2, 4
+    X = lowrank(rng, 4 * 9 + 8 + 3, d, 2)
+    u = run_unit(X, X, d, r, 8, block=blk)
+    H = X[: u.n_c]
+    U_, s, vt = np.linalg.svd(H)
+    np.testing.assert_allclose(u.K.S, s[:2], rtol=1e-12)
+    np.testing.assert_allclose(u.history("K"), H, rtol=0, atol=1e-12)
+    # coefficients are the batch left singular vectors times sigma (up to sign)
+    C = u.K.C[: u.n_c]
+    for j in range(2):
+        ref = U_[:, j] * s[j]
+        sgn = np.sign(C[:, j] @ ref)
+        np.testing.assert_allclose(C[:, j] * sgn, ref, rtol=0, atol=1e-11 * s[0])
+
+
+# ---------------------------------------------------------------------------
+# P3 / P4: orthonormal basis and Brand's coefficient invariant
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["noisy", "rank5", "zeros", "full_rank", "rank5_r_eq_d"])
+def test_basis_orthonormal_after_every_fold(kind):
+    rng = np.random.default_rng(8)
+    d, r = 64, 16
+    L = 64 * 8 + 64
+    if kind == "noisy":
+        X = lowrank(rng, L, d, 24, noise=0.05)
+    elif kind == "rank5":
+        X = lowrank(rng, L, d, 5)
+    elif kind == "zeros":
+        X = np.zeros((L, d))
+    elif kind == "rank5_r_eq_d":
+        # fewer non-zero singular values than r: the null completion decides
+        d = r = 32
+        X = lowrank(rng, L, d, 5)
+    else:
+        r = d
+        X = rng.standard_normal((L, d))
+    errs = []
+    run_unit(X, X, d, r, 64, after_fold=lambda u: errs.append(
+        np.linalg.norm(u.K.B.T @ u.K.B - np.eye(r), 2)))
+    assert len(errs) >= 8 and max(errs) < 1e-12
+
+
+def test_coefficient_gram_is_diag_s_squared():
+    rng = np.random.default_rng(9)
+    d, r = 128, 32
+    X = lowrank(rng, 64 * 10 + 64, d, 48, noise=0.02)
+    u = run_unit(X, X, d, r, 64)
+    C = u.K.C[: u.n_c]
+    G = C.T @ C
+    assert np.linalg.norm(G - np.diag(u.K.S ** 2)) / np.linalg.norm(G) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# P5: synchronization -- drift identities and ordering
+# ---------------------------------------------------------------------------
+
+def _drift_pair(X, d, r, W, folds_before):
+    """(synchronized drift, basis-only drift, truncated-energy drift) of the next fold."""
+    u = run_unit(X[: W + 64 * (folds_before + 1)], X[: W + 64 * (folds_before + 1)], d, r, W)
+    n_old = u.n_c
+    Ck, Bk = u.K.C[:n_old].copy(), u.K.B.copy()
+    H0 = Ck @ Bk.T
+    for t in range(u.length, u.length + 64):
+        u.append(X[t], X[t])
+    u.fold()
+    Bn = u.K.B
+    basis_only = drift(H0, Ck @ Bn.T)
+    truncated = float(np.linalg.norm(H0 - H0 @ Bn @ Bn.T) / np.linalg.norm(H0))
+    u.sync()
+    synced = drift(H0, u.K.C[:n_old] @ Bn.T)
+    return synced, basis_only, truncated
+
+
+def test_sync_drift_zero_for_rank_le_r():
+    rng = np.random.default_rng(10)
+    X = lowrank(rng, 256 + 64 * 8, 128, 20)
+    synced, basis_only, _ = _drift_pair(X, 128, 32, 256, 4)
+    assert synced < 1e-12
+    assert basis_only > 0.3
+
+
+def test_sync_drift_equals_truncated_energy():
+    rng = np.random.default_rng(11)
+    X = lowrank(rng, 256 + 64 * 8, 128, 40, noise=0.05)
+    synced, basis_only, truncated = _drift_pair(X, 128, 32, 256, 4)
+    assert abs(synced - truncated) < 1e-12
+    assert synced < 0.1 * basis_only
+
+
+# ---------------------------------------------------------------------------
+# P6: fused decode algebra ((p^T C) B^T for values, c B^T rebuilt keys)
+# ---------------------------------------------------------------------------
+
+def test_factored_value_route_equals_plain_decode():
+    rng = np.random.default_rng(12)
+    d, r, W = 64, 16, 64
+    X, Y = lowrank(rng, 900, d, 16, 0.1), lowrank(rng, 900, d, 16, 0.1)
+    u = run_unit(X, Y, d, r, W)
+    q = rng.standard_normal((2, d))
+    scale = 0.11
+    n_c, L = u.n_c, u.length
+    k_c = rope(u.K.C[:n_c] @ u.K.B.T, np.arange(n_c))
+    k_w = rope(np.stack([u.K.ring[p % (W + 64)] for p in range(n_c, L)]), np.arange(n_c, L))
+    s = np.concatenate([k_c, k_w]) @ rope(q, 1000).T * scale        # (L, g)
+    p = np.exp(s - s.max(0))
+    acc_c = p[:n_c].T @ u.V.C[:n_c]                                  # coefficient space
+    acc_w = p[n_c:].T @ np.stack([u.V.ring[t % (W + 64)] for t in range(n_c, L)])
+    fused = (acc_c @ u.V.B.T + acc_w) / p.sum(0)[:, None]
+    np.testing.assert_allclose(u.decode(q, 1000, scale), fused, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P10: grouped-query attention head map
+# ---------------------------------------------------------------------------
+
+def test_gqa_head_map_and_mha_special_case():
+    rng = np.random.default_rng(13)
+    B_, Hkv, Hq, d, r, W = 2, 2, 6, 32, 8, 64
+    o = Oracle(B_, 1, Hkv, Hq, d, r, W, 600, storage="f64")
+    k = rng.standard_normal((B_, 300, Hkv, d))
+    v = rng.standard_normal((B_, 300, Hkv, d))
+    for t in range(300):
+        if o.append(0, k[:, t:t + 1], v[:, t:t + 1]):
+            o.block_update(0)
+            o.sync(0)
+    q = rng.standard_normal((B_, Hq, d))
+    out = o.decode_attn(0, q, 299)
+    for b in range(B_):
+        for h in range(Hq):
+            u = o.unit(b, 0, h // 3)
+            np.testing.assert_allclose(out[b, h], u.decode(q[b, h:h + 1], 299, o.scale)[0],
+                                       rtol=0, atol=1e-14)
+    # H_q = H_kv: multi-head attention; before any fold it is exact attention
+    o2 = Oracle(1, 1, 3, 3, d, r, W, 200, storage="f64")
+    k2, v2 = rng.standard_normal((1, 100, 3, d)), rng.standard_normal((1, 100, 3, d))
+    o2.append(0, k2, v2)
+    q2 = rng.standard_normal((1, 3, d))
+    out2 = o2.decode_attn(0, q2, 99)
+    for h in range(3):
+        ref = exact_attention(q2[0, h:h + 1], k2[0, :, h], v2[0, :, h], 99, 1 / math.sqrt(d))
+        np.testing.assert_allclose(out2[0, h:h + 1], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Storage rounding mode: ring rows and coefficients are bf16 values
+# ---------------------------------------------------------------------------
+
+def test_bf16_mode_stores_bf16_values():
+    rng = np.random.default_rng(14)
+    X = lowrank(rng, 400, 64, 8, 0.01)
+    u = run_unit(X, X, 64, 16, 64, storage="bf16")
+    for arr in (u.K.ring, u.K.C[: u.n_c], u.V.C[: u.n_c]):
+        np.testing.assert_array_equal(bf16_round(arr), arr)
+
+
+# ---------------------------------------------------------------------------
+# Byte model, pinned to the page's figures
+# ---------------------------------------------------------------------------
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    return rows
+
+
+def test_full_kv_bytes_matches_page_figure():
+    (tokens, layers, heads, d, eb, expect, gib), = _golden("full_kv_bytes.txt")
+    got = full_kv_bytes(int(tokens), int(layers), int(heads), int(d), int(eb))
+    assert got == int(expect)
+    assert got / 2 ** 30 == float(gib)
+
+
+def test_compression_ratio_is_inverse_budget():
+    (ratio, budget, tol), = _golden("compression_ratio.txt")
+    assert abs(1.0 / float(ratio) - float(budget)) < float(tol)
+
+
+def test_persistent_bytes_full_rank_window_only():
+    # with nothing compressed, the kept bytes are the exact rows plus the
+    # (fixed) bases and singular values
+    full = full_kv_bytes(300, 2, 4, 128, 2)
+    kept = persistent_kv_bytes(0, 300, 2, 4, 128, 32, 2)
+    assert kept - full == 2 * 4 * 2 * (128 * 32 * 4 + 32 * 4)
+
+
+# ---------------------------------------------------------------------------
+# Brand step alone: the single-block special case is a truncated SVD
+# ---------------------------------------------------------------------------
+
+def test_first_fold_is_truncated_svd_of_block():
+    rng = np.random.default_rng(15)
+    d, r = 128, 32
+    A = rng.standard_normal((64, d))
+    B0, S0 = np.eye(d, r), np.zeros(r)
+    Bn, Sn, M, C_blk = brand_fold(A, B0, S0)
+    U_, s, vt = np.linalg.svd(A, full_matrices=False)
+    np.testing.assert_allclose(Sn, s[:r], rtol=1e-12)
+    assert subspace_dist(Bn, vt[:r].T) < 1e-10
+    best = (U_[:, :r] * s[:r]) @ vt[:r]                 # Eckart-Young optimum
+    np.testing.assert_allclose(C_blk @ Bn.T, best, rtol=0, atol=1e-11 * s[0])
