@@ -1,0 +1,177 @@
+/*
+ * iskv.h -- C ABI of the MI355X (gfx950) library for basis-synchronized online
+ * low-rank KV-cache compression.
+ *
+ * Source of the operations (page: "iS-KV -- Basis-synchronized online low-rank
+ * KV compression -- What does it mean?", learnaivisually.com explainer of the
+ * iS-KV paper, cited below as [iS-KV explainer]):
+ *   - recent tokens are kept exact, older tokens as coefficient vectors over a
+ *     shared basis, no position is dropped            [TL;DR; window paragraph]
+ *   - every 64 tokens that leave the exact window are folded in as one block
+ *     by Brand's block-incremental SVD on a small core matrix
+ *                                                     [Jargon "Block-incremental
+ *                                                      SVD"; drift paragraph]
+ *   - the stored coefficients are rewritten whenever the basis changes
+ *     (basis synchronization)                         [FAQ "What is basis
+ *                                                      synchronization?"]
+ *   - keys are compressed before RoPE and RoPE is re-applied on rebuild
+ *                                                     [Jargon "Pre-RoPE keys"]
+ *   - each new query scores every earlier key         [re-attention paragraph]
+ *   - persistent-KV bytes = factors + exact rows      [Jargon "Persistent-KV
+ *                                                      compression"]
+ * The page gives no interface; the verbs below follow its statement of the
+ * problem: append tokens, fold a block, synchronize, attend.
+ *
+ * Conventions
+ *   - Every pointer named dev_* or documented as "device" is a device pointer on
+ *     the GPU current when iskv_init ran; host_* pointers are host memory.
+ *   - Tensors are dense, row-major, innermost dimension last.
+ *   - All verbs except iskv_status / iskv_export_state / iskv_import_state
+ *     enqueue work on the stream given to iskv_init and return without waiting.
+ *     Caller buffers must stay valid until the stream reaches the call.
+ *   - Return codes are from host-side validation (ISKV_E*); a launch failure
+ *     returns ISKV_EDEVICE.  Device-detected numeric trouble (non-finite input
+ *     or core, Jacobi sweep cap reached) is reported by iskv_status.
+ *   - A context is not thread-safe.  Sequences of a batch advance in lockstep.
+ *   - head_dim must be 128; rank must be 16, 32, 64 or 128; window a multiple
+ *     of 64; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ */
+#ifndef ISKV_H
+#define ISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct iskv_ctx iskv_ctx; /* opaque; host heap; owned by the library */
+
+typedef enum { ISKV_F32 = 0, ISKV_BF16 = 1 } iskv_dtype;
+
+enum {
+  ISKV_OK = 0,
+  ISKV_EINVAL = -1,   /* bad argument or unsupported configuration */
+  ISKV_ESTATE = -2,   /* verb not allowed in the current state */
+  ISKV_ENOMEM = -3,   /* workspace smaller than iskv_workspace_bytes() */
+  ISKV_EDEVICE = -4,  /* HIP runtime error */
+  ISKV_ENUMERIC = -5  /* device-side numeric flag raised (see iskv_status) */
+};
+
+/* Device numeric flags reported in iskv_status_t.numeric_flags. */
+enum {
+  ISKV_FLAG_NONFINITE_CORE = 1,  /* NaN/Inf met while folding a block */
+  ISKV_FLAG_JACOBI_CAP = 2,      /* core SVD hit its sweep cap unconverged */
+  ISKV_FLAG_NONFINITE_INPUT = 4  /* NaN/Inf in appended k or v */
+};
+
+typedef struct {
+  int32_t batch;          /* sequences, advanced in lockstep */
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;    /* multiple of num_kv_heads (grouped-query attention) */
+  int32_t head_dim;       /* 128 */
+  int32_t rank;           /* r: 16, 32, 64 or 128 (<= head_dim) */
+  int32_t window;         /* W: exact tokens kept after a fold; multiple of 64 */
+  int32_t block;          /* tokens per fold; must be 64 */
+  int32_t max_tokens;     /* capacity per sequence and layer */
+  int32_t storage;        /* iskv_dtype of ring rows and coefficients */
+  float rope_base;        /* RoPE base, e.g. 10000 */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
+} iskv_config;
+
+typedef struct {
+  int64_t length;             /* tokens appended to the layer (per sequence) */
+  int64_t compressed;         /* tokens held as coefficients (N_c, multiple of 64) */
+  int32_t blocks_ready;       /* 1: ring is full, a block must be folded before the next append */
+  int32_t pending_sync;       /* 1: iskv_block_update ran and iskv_sync has not */
+  int64_t folds;              /* iskv_block_update calls that folded this layer */
+  int64_t syncs;              /* iskv_sync calls that synchronized this layer */
+  uint64_t persistent_bytes;  /* kept bytes of all layers (coefficients, bases,
+                                 singular values, exact rows) for the whole batch */
+  uint64_t full_bytes;        /* bytes of the same tokens uncompressed (K+V, storage dtype) */
+  int32_t numeric_flags;      /* OR of ISKV_FLAG_* raised since init */
+  int32_t reserved;
+} iskv_status_t;
+
+/* Device workspace bytes needed for cfg (0 if cfg is invalid). */
+size_t iskv_workspace_bytes(const iskv_config *cfg);
+
+/* Bytes of one layer's state blob for iskv_export_state / iskv_import_state
+ * (0 if cfg is invalid). Layout, all little-endian:
+ *   int64 length, int64 compressed, then for b in [0,batch), h in [0,kv_heads),
+ *   X in (K, V):  float basis[head_dim][rank], float S[rank],
+ *                 float coeff[max_tokens][rank]   (rows >= compressed are 0),
+ *                 float ring[window+64][head_dim] (slot = position % (window+64)). */
+size_t iskv_state_bytes(const iskv_config *cfg);
+
+/* Validate cfg, carve the caller's device workspace (dev_ws, ws_bytes >=
+ * iskv_workspace_bytes), and reset every layer to the empty state: basis
+ * I[:, :rank], S = 0, no tokens.  hip_stream is a hipStream_t (NULL = default
+ * stream); all later work is enqueued on it.  The workspace is owned by the
+ * caller and must outlive the context.  Synchronizes the stream once. */
+int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_stream,
+              iskv_ctx **out);
+
+/* Append n_tokens tokens of every sequence to one layer.
+ * dev_k, dev_v: [batch][n_tokens][num_kv_heads][head_dim] of dtype in_dtype,
+ * keys before RoPE.  Each row is rounded to the storage dtype (round to nearest
+ * even) and written to ring slot position % (window+64).
+ * ESTATE if n_tokens exceeds the free ring slots (window+64 - (length -
+ * compressed)) or if length would pass max_tokens.
+ * *blocks_ready (may be NULL) is set to 1 when the ring is full, i.e. the next
+ * call must be iskv_block_update. */
+int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                int in_dtype, int *blocks_ready);
+
+/* Fold the oldest 64 exact tokens of every (sequence, KV head, K|V) of the
+ * layer (layer = -1: every layer that has a full ring) into its rank-r basis
+ * by Brand's block-incremental SVD: projection, residual CholeskyQR2, core
+ * [[diag S, 0], [P, R_r^T]] of size (r+64)^2, one-sided Jacobi SVD, truncation
+ * to r.  Writes the new basis, S, the block's coefficients, and the pending
+ * synchronization matrix M = B_old^T B_new.  ESTATE if no block is ready (for
+ * layer >= 0) or a sync is pending. */
+int iskv_block_update(iskv_ctx *c, int layer);
+
+/* Basis synchronization: rewrite every older coefficient row of the layer
+ * (layer = -1: every layer with a pending update) as C <- C M.  ESTATE if no
+ * update is pending (layer >= 0).  A pending sync blocks further folds of
+ * that layer until iskv_sync or iskv_discard_sync. */
+int iskv_sync(iskv_ctx *c, int layer);
+
+/* Drop a pending synchronization without applying it: the old coefficients
+ * stay in the previous basis (the basis-only update, which drifts). ESTATE if
+ * none is pending (layer >= 0). */
+int iskv_discard_sync(iskv_ctx *c, int layer);
+
+/* Decode attention of one query per query head over every cached position of
+ * the layer: keys rebuilt from coefficients (or read exact from the ring),
+ * rotated by RoPE at their position; the query rotated at q_pos; softmax with
+ * the configured scale; values accumulated in coefficient space and mapped
+ * back by the value basis.  dev_q: float [batch][num_q_heads][head_dim], before
+ * RoPE.  dev_out: float [batch][num_q_heads][head_dim].  Query head h reads KV
+ * head h / (num_q_heads / num_kv_heads).  ESTATE if the layer is empty. */
+int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out);
+
+/* Synchronizes the stream; fills *st for one layer.  Returns ISKV_ENUMERIC if
+ * any numeric flag is set (st is still filled), else ISKV_OK. */
+int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st);
+
+/* Copy one layer's state to / from a host blob (layout: iskv_state_bytes).
+ * Both synchronize the stream.  Import rounds coefficients and ring rows to
+ * the storage dtype, clears any pending sync, and rebuilds derived operands. */
+int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes);
+int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes);
+
+/* Free the context (not the caller's workspace). Synchronizes the stream. */
+int iskv_destroy(iskv_ctx *c);
+
+/* Static string for a return code. */
+const char *iskv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISKV_H */

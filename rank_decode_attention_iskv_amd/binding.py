@@ -1,0 +1,250 @@
+"""Thin ctypes binding of libiskv (include/iskv.h).
+
+Argument marshalling only: every step of the compressed cache (append, fold,
+synchronization, decode attention) runs in the HIP kernels of libiskv.so.
+PyTorch is used for device memory (the workspace and caller tensors) and for
+the stream handle.  There is no fallback: if libiskv.so is missing the import
+fails loudly.
+
+Functions keep the C names without the ``iskv_`` prefix; ``IskvCache`` owns a
+workspace tensor and a context for convenience.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libiskv.so")
+
+F32, BF16 = 0, 1
+OK, EINVAL, ESTATE, ENOMEM, EDEVICE, ENUMERIC = 0, -1, -2, -3, -4, -5
+FLAG_NONFINITE_CORE, FLAG_JACOBI_CAP, FLAG_NONFINITE_INPUT = 1, 2, 4
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("storage", ctypes.c_int32),
+        ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class Status(ctypes.Structure):
+    _fields_ = [
+        ("length", ctypes.c_int64), ("compressed", ctypes.c_int64),
+        ("blocks_ready", ctypes.c_int32), ("pending_sync", ctypes.c_int32),
+        ("folds", ctypes.c_int64), ("syncs", ctypes.c_int64),
+        ("persistent_bytes", ctypes.c_uint64), ("full_bytes", ctypes.c_uint64),
+        ("numeric_flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+EXPORTED = (
+    "iskv_workspace_bytes", "iskv_state_bytes", "iskv_init", "iskv_append",
+    "iskv_block_update", "iskv_sync", "iskv_discard_sync", "iskv_decode_attn",
+    "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_destroy", "iskv_strerror",
+)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libiskv.so not built at {path}; run "
+                          "`python -m rank_decode_attention_iskv_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, SZ, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int64
+    cfgp = ctypes.POINTER(Config)
+    sig = {
+        "iskv_workspace_bytes": (SZ, [cfgp]),
+        "iskv_state_bytes": (SZ, [cfgp]),
+        "iskv_init": (I, [cfgp, P, SZ, P, ctypes.POINTER(P)]),
+        "iskv_append": (I, [P, I, P, P, I, I, ctypes.POINTER(I)]),
+        "iskv_block_update": (I, [P, I]),
+        "iskv_sync": (I, [P, I]),
+        "iskv_discard_sync": (I, [P, I]),
+        "iskv_decode_attn": (I, [P, I, P, I64, P]),
+        "iskv_status": (I, [P, I, ctypes.POINTER(Status)]),
+        "iskv_export_state": (I, [P, I, P, SZ]),
+        "iskv_import_state": (I, [P, I, P, SZ]),
+        "iskv_destroy": (I, [P]),
+        "iskv_strerror": (ctypes.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+class IskvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+
+
+def _check(code: int, what: str) -> int:
+    if code != OK:
+        raise IskvError(code, what)
+    return code
+
+
+def strerror(code: int) -> str:
+    return lib().iskv_strerror(code).decode()
+
+
+def make_config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window,
+                max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64) -> Config:
+    return Config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window, block,
+                  max_tokens, storage, rope_base, softmax_scale)
+
+
+def workspace_bytes(cfg: Config) -> int:
+    return lib().iskv_workspace_bytes(ctypes.byref(cfg))
+
+
+def state_bytes(cfg: Config) -> int:
+    return lib().iskv_state_bytes(ctypes.byref(cfg))
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+class IskvCache:
+    """A libiskv context plus the torch tensor that backs its workspace."""
+
+    def __init__(self, cfg: Config, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.torch = torch
+        n = workspace_bytes(cfg)
+        if n == 0:
+            raise IskvError(EINVAL, "iskv_workspace_bytes")
+        # 256-byte alignment is guaranteed by the caching allocator
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        ctx = ctypes.c_void_p()
+        _check(lib().iskv_init(ctypes.byref(cfg), ctypes.c_void_p(self.workspace.data_ptr()),
+                               n, ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(ctx)),
+               "iskv_init")
+        self.ctx = ctx
+
+    # -- verbs -------------------------------------------------------------
+    def append(self, layer: int, k, v) -> bool:
+        """k, v: device tensors [batch, n, kv_heads, head_dim], float32 or bfloat16."""
+        torch = self.torch
+        if k.dtype != v.dtype or k.shape != v.shape or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        dt = BF16 if k.dtype == torch.bfloat16 else F32
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k, v must be float32 or bfloat16")
+        ready = ctypes.c_int(0)
+        _check(lib().iskv_append(self.ctx, layer, ctypes.c_void_p(k.data_ptr()),
+                                 ctypes.c_void_p(v.data_ptr()), int(k.shape[1]), dt,
+                                 ctypes.byref(ready)), "iskv_append")
+        return bool(ready.value)
+
+    def block_update(self, layer: int = -1):
+        _check(lib().iskv_block_update(self.ctx, layer), "iskv_block_update")
+
+    def sync(self, layer: int = -1):
+        _check(lib().iskv_sync(self.ctx, layer), "iskv_sync")
+
+    def discard_sync(self, layer: int = -1):
+        _check(lib().iskv_discard_sync(self.ctx, layer), "iskv_discard_sync")
+
+    def decode_attn(self, layer: int, q, q_pos: int, out):
+        """q, out: contiguous float32 device tensors [batch, q_heads, head_dim]."""
+        torch = self.torch
+        if q.dtype != torch.float32 or out.dtype != torch.float32:
+            raise ValueError("q and out must be float32")
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        _check(lib().iskv_decode_attn(self.ctx, layer, ctypes.c_void_p(q.data_ptr()),
+                                      int(q_pos), ctypes.c_void_p(out.data_ptr())),
+               "iskv_decode_attn")
+        return out
+
+    def status(self, layer: int = 0, raise_numeric: bool = False) -> Status:
+        st = Status()
+        code = lib().iskv_status(self.ctx, layer, ctypes.byref(st))
+        if code not in (OK, ENUMERIC) or (raise_numeric and code == ENUMERIC):
+            raise IskvError(code, "iskv_status")
+        return st
+
+    def export_state(self, layer: int) -> bytearray:
+        n = state_bytes(self.cfg)
+        buf = bytearray(n)
+        c_buf = (ctypes.c_char * n).from_buffer(buf)
+        _check(lib().iskv_export_state(self.ctx, layer, c_buf, n), "iskv_export_state")
+        return buf
+
+    def import_state(self, layer: int, blob) -> None:
+        n = state_bytes(self.cfg)
+        if len(blob) < n:
+            raise ValueError("state blob too small")
+        buf = blob if isinstance(blob, bytearray) else bytearray(blob)
+        c_buf = (ctypes.c_char * len(buf)).from_buffer(buf)
+        _check(lib().iskv_import_state(self.ctx, layer, c_buf, len(buf)), "iskv_import_state")
+
+    def destroy(self):
+        if getattr(self, "ctx", None):
+            lib().iskv_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+# -- state blob helpers (layout documented at iskv_state_bytes) --------------
+
+def unpack_state(cfg: Config, blob):
+    """Split a state blob into numpy arrays per (unit, K|V)."""
+    import numpy as np
+    d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    length, n_c = np.frombuffer(bytes(blob[:16]), dtype=np.int64)
+    f = np.frombuffer(bytes(blob[16:]), dtype=np.float32)
+    units = cfg.batch * cfg.num_kv_heads
+    per = d * r + r + T * r + S * d
+    out = []
+    for u in range(units):
+        xs = []
+        for x in range(2):
+            o = (u * 2 + x) * per
+            B = f[o: o + d * r].reshape(d, r); o += d * r
+            Sv = f[o: o + r]; o += r
+            C = f[o: o + T * r].reshape(T, r); o += T * r
+            ring = f[o: o + S * d].reshape(S, d)
+            xs.append(dict(basis=B, S=Sv, coef=C, ring=ring))
+        out.append(xs)
+    return int(length), int(n_c), out
+
+
+def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
+    """Inverse of unpack_state; units[u][x] holds basis, S, coef, ring arrays."""
+    import numpy as np
+    parts = [np.array([length, n_c], dtype=np.int64).tobytes()]
+    d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    for xs in units:
+        for x in xs:
+            C = np.zeros((T, r), dtype=np.float32)
+            C[: x["coef"].shape[0]] = x["coef"][:T]
+            parts += [np.asarray(x["basis"], np.float32).reshape(d, r).tobytes(),
+                      np.asarray(x["S"], np.float32).reshape(r).tobytes(),
+                      C.tobytes(), np.asarray(x["ring"], np.float32).reshape(S, d).tobytes()]
+    return bytearray(b"".join(parts))

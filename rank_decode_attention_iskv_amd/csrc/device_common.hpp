@@ -1,0 +1,59 @@
+// Device helpers shared by the libiskv kernels: storage-type conversion and
+// RoPE angles from the precomputed tables.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "iskv_internal.hpp"
+
+namespace iskv {
+
+// bf16 is carried as its uint16 bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ float load(const float *p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Store<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t *p, size_t i) {
+    return bf16_to_f32(p[i].bits);
+  }
+  static __device__ __forceinline__ void store(bf16_t *p, size_t i, float v) {
+    p[i].bits = f32_to_bf16(v);
+  }
+};
+
+// cos, sin of pos * theta_i for frequency i < 64, from the anchor table
+// (multiples of 64 positions) and the step table (offsets 0..63), by the
+// angle-addition identity.  Both tables hold float values of float64-exact
+// angles, so the result is within a few float ulps for any position covered.
+__device__ __forceinline__ void rope_cs(const Shared &S, int64_t pos, int i, float &c, float &s) {
+  const int64_t a = pos / kRopeAnchor;
+  const int o = (int)(pos - a * kRopeAnchor);
+  const float2 A = reinterpret_cast<const float2 *>(S.rope_anchor)[a * 64 + i];
+  const float2 B = reinterpret_cast<const float2 *>(S.rope_step)[o * 64 + i];
+  c = A.x * B.x - A.y * B.y;
+  s = A.y * B.x + A.x * B.y;
+}
+
+__device__ __forceinline__ void set_flag(const Shared &S, int f) { atomicOr(S.flags, f); }
+
+}  // namespace iskv

@@ -1,0 +1,480 @@
+// libiskv host side: configuration checks, workspace carving, the per-layer
+// state machine (length, compressed count, pending synchronization), launches,
+// status, and state export/import.
+//
+// Operations follow [iS-KV explainer] ("iS-KV -- Basis-synchronized online
+// low-rank KV compression -- What does it mean?", learnaivisually.com):
+// exact recent window, 64-token blocks folded by Brand's block-incremental
+// SVD, basis synchronization of old coefficients, decode attention over every
+// position; persistent-KV bytes as in its Jargon entry.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/iskv.h"
+#include "iskv_internal.hpp"
+
+using namespace iskv;
+
+namespace {
+
+struct LayerState {
+  int64_t length = 0;
+  int64_t n_c = 0;
+  bool pending = false;
+  int64_t folds = 0;
+  int64_t syncs = 0;
+};
+
+bool valid_config(const iskv_config *c) {
+  if (!c) return false;
+  if (c->batch < 1 || c->num_layers < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1) return false;
+  if (c->num_q_heads % c->num_kv_heads) return false;
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return false;
+  if (c->head_dim != kHeadDim) return false;
+  if (c->rank != 16 && c->rank != 32 && c->rank != 64 && c->rank != 128) return false;
+  if (c->rank > c->head_dim) return false;
+  if (c->block != kBlock) return false;
+  if (c->window < kBlock || c->window % kBlock) return false;
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 24)) return false;
+  if (c->storage != ISKV_F32 && c->storage != ISKV_BF16) return false;
+  if (!(c->rope_base > 1.f) || !std::isfinite(c->rope_base)) return false;
+  if (!std::isfinite(c->softmax_scale)) return false;
+  return true;
+}
+
+Dims make_dims(const iskv_config *c) {
+  Dims D{};
+  D.batch = c->batch;
+  D.layers = c->num_layers;
+  D.kv_heads = c->num_kv_heads;
+  D.q_heads = c->num_q_heads;
+  D.group = c->num_q_heads / c->num_kv_heads;
+  D.d = c->head_dim;
+  D.r = c->rank;
+  D.window = c->window;
+  D.slots = c->window + kBlock;
+  D.max_tokens = c->max_tokens;
+  D.storage = c->storage;
+  D.elem = c->storage == ISKV_BF16 ? 2 : 4;
+  const double scale = c->softmax_scale > 0.f ? (double)c->softmax_scale
+                                              : 1.0 / std::sqrt((double)c->head_dim);
+  D.scale_log2 = (float)(scale * 1.4426950408889634);
+  D.rope_base = c->rope_base;
+  D.units = c->batch * c->num_kv_heads;
+  // enough decode records to split the history over ~2 waves of workgroups on
+  // 256 compute units, plus the window splits
+  int per_unit = (4096 + D.units - 1) / D.units;
+  if (per_unit < 16) per_unit = 16;
+  if (per_unit > 512) per_unit = 512;
+  D.max_rec = per_unit;
+  D.rope_anchors = (c->max_tokens + kBlock) / kRopeAnchor + 2;
+  return D;
+}
+
+uint16_t host_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float host_from_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+}  // namespace
+
+struct iskv_ctx {
+  iskv_config cfg;
+  Dims D;
+  GlobalLayout G;
+  Model M;
+  hipStream_t stream;
+  int device;
+  std::vector<LayerState> layers;
+};
+
+namespace {
+
+int hip_err(hipError_t e) { return e == hipSuccess ? ISKV_OK : ISKV_EDEVICE; }
+
+int check_layer(const iskv_ctx *c, int layer) {
+  return (layer >= 0 && layer < c->D.layers) ? ISKV_OK : ISKV_EINVAL;
+}
+
+void fill_sel(LayerSel &sel, const std::vector<int> &idx, size_t from) {
+  sel.n = 0;
+  for (size_t i = from; i < idx.size() && sel.n < kMaxLayerSel; ++i) sel.idx[sel.n++] = idx[i];
+}
+
+uint64_t persistent_bytes(const iskv_ctx *c) {
+  const Dims &D = c->D;
+  uint64_t tot = 0;
+  for (const LayerState &L : c->layers) {
+    const uint64_t n_e = (uint64_t)(L.length - L.n_c);
+    const uint64_t per = 2ull * ((uint64_t)L.n_c * D.r * D.elem + (uint64_t)D.d * D.r * 4 +
+                                 (uint64_t)D.r * 4 + n_e * D.d * D.elem);
+    tot += per * (uint64_t)D.units;
+  }
+  return tot;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t iskv_workspace_bytes(const iskv_config *cfg) {
+  if (!valid_config(cfg)) return 0;
+  return global_layout(make_dims(cfg)).total;
+}
+
+size_t iskv_state_bytes(const iskv_config *cfg) {
+  if (!valid_config(cfg)) return 0;
+  const Dims D = make_dims(cfg);
+  const size_t per_x = (size_t)D.d * D.r + D.r + (size_t)D.max_tokens * D.r + (size_t)D.slots * D.d;
+  return 16 + (size_t)D.units * 2 * per_x * 4;
+}
+
+int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_stream,
+              iskv_ctx **out) {
+  if (!out) return ISKV_EINVAL;
+  *out = nullptr;
+  if (!valid_config(cfg) || !dev_ws) return ISKV_EINVAL;
+  if (((uintptr_t)dev_ws) % 256) return ISKV_EINVAL;
+  iskv_ctx *c = new (std::nothrow) iskv_ctx();
+  if (!c) return ISKV_ENOMEM;
+  c->cfg = *cfg;
+  c->D = make_dims(cfg);
+  c->G = global_layout(c->D);
+  if (ws_bytes < c->G.total) {
+    delete c;
+    return ISKV_ENOMEM;
+  }
+  c->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return ISKV_EDEVICE;
+  }
+  c->layers.assign(c->D.layers, LayerState{});
+  uint8_t *base = reinterpret_cast<uint8_t *>(dev_ws);
+  Model &M = c->M;
+  M.base = base;
+  M.layers_base = c->G.layers_base;
+  M.layer_stride = c->G.layer.bytes;
+  M.lay = c->G.layer;
+  M.D = c->D;
+  M.sh.rec = reinterpret_cast<float *>(base + c->G.rec);
+  M.sh.cnt = reinterpret_cast<unsigned *>(base + c->G.cnt);
+  M.sh.flags = reinterpret_cast<int *>(base + c->G.flags);
+  M.sh.fold = reinterpret_cast<float *>(base + c->G.fold);
+  M.sh.rope_anchor = reinterpret_cast<const float *>(base + c->G.rope_anchor);
+  M.sh.rope_step = reinterpret_cast<const float *>(base + c->G.rope_step);
+
+  // RoPE tables: theta_i = base^(-2i/d), angles in double, stored as float.
+  const int na = c->D.rope_anchors;
+  std::vector<float> anchor((size_t)na * 64 * 2), step((size_t)kRopeAnchor * 64 * 2);
+  for (int i = 0; i < 64; ++i) {
+    const double th = std::pow((double)cfg->rope_base, -2.0 * i / (double)cfg->head_dim);
+    for (int a = 0; a < na; ++a) {
+      const double ang = (double)a * kRopeAnchor * th;
+      anchor[((size_t)a * 64 + i) * 2] = (float)std::cos(ang);
+      anchor[((size_t)a * 64 + i) * 2 + 1] = (float)std::sin(ang);
+    }
+    for (int o = 0; o < kRopeAnchor; ++o) {
+      const double ang = (double)o * th;
+      step[((size_t)o * 64 + i) * 2] = (float)std::cos(ang);
+      step[((size_t)o * 64 + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  hipError_t e = hipMemsetAsync(dev_ws, 0, c->G.total, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(base + c->G.rope_anchor, anchor.data(), anchor.size() * 4,
+                       hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(base + c->G.rope_step, step.data(), step.size() * 4,
+                       hipMemcpyHostToDevice, c->stream);
+  for (int l = 0; l < c->D.layers && e == hipSuccess; ++l) e = launch_reset_layer(M, l, c->stream);
+  std::vector<int> all(c->D.layers);
+  for (int l = 0; l < c->D.layers; ++l) all[l] = l;
+  for (size_t from = 0; from < all.size() && e == hipSuccess; from += kMaxLayerSel) {
+    LayerSel sel;
+    fill_sel(sel, all, from);
+    e = launch_prep_frag(M, sel, c->stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    delete c;
+    return ISKV_EDEVICE;
+  }
+  *out = c;
+  return ISKV_OK;
+}
+
+int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                int in_dtype, int *blocks_ready) {
+  if (!c || check_layer(c, layer) || !dev_k || !dev_v || n_tokens < 0) return ISKV_EINVAL;
+  if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
+  LayerState &L = c->layers[layer];
+  const int64_t used = L.length - L.n_c;
+  if (used + n_tokens > c->D.slots) return ISKV_ESTATE;
+  if (L.length + n_tokens > c->D.max_tokens) return ISKV_ESTATE;
+  hipError_t e = launch_append(c->M, layer, dev_k, dev_v, n_tokens, in_dtype, L.length, c->stream);
+  if (e != hipSuccess) return ISKV_EDEVICE;
+  L.length += n_tokens;
+  if (blocks_ready) *blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
+  return ISKV_OK;
+}
+
+int iskv_block_update(iskv_ctx *c, int layer) {
+  if (!c) return ISKV_EINVAL;
+  std::vector<int> idx;
+  if (layer >= 0) {
+    if (check_layer(c, layer)) return ISKV_EINVAL;
+    const LayerState &L = c->layers[layer];
+    if (L.pending || L.length - L.n_c != c->D.slots) return ISKV_ESTATE;
+    idx.push_back(layer);
+  } else if (layer == -1) {
+    for (int l = 0; l < c->D.layers; ++l) {
+      const LayerState &L = c->layers[l];
+      if (!L.pending && L.length - L.n_c == c->D.slots) idx.push_back(l);
+    }
+  } else {
+    return ISKV_EINVAL;
+  }
+  // group layers by their compressed count (one launch per distinct n_c)
+  std::vector<bool> done(idx.size(), false);
+  for (size_t i = 0; i < idx.size(); ++i) {
+    if (done[i]) continue;
+    const int64_t n_c = c->layers[idx[i]].n_c;
+    std::vector<int> grp;
+    for (size_t j = i; j < idx.size(); ++j)
+      if (!done[j] && c->layers[idx[j]].n_c == n_c) { grp.push_back(idx[j]); done[j] = true; }
+    for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
+      LayerSel sel;
+      fill_sel(sel, grp, from);
+      hipError_t e = launch_block_update(c->M, sel, n_c, c->stream);
+      if (e == hipSuccess) e = launch_prep_frag(c->M, sel, c->stream);
+      if (e != hipSuccess) return ISKV_EDEVICE;
+    }
+    for (int l : grp) {
+      c->layers[l].n_c += kBlock;
+      c->layers[l].pending = true;
+      c->layers[l].folds += 1;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_sync(iskv_ctx *c, int layer) {
+  if (!c) return ISKV_EINVAL;
+  std::vector<int> idx;
+  if (layer >= 0) {
+    if (check_layer(c, layer)) return ISKV_EINVAL;
+    if (!c->layers[layer].pending) return ISKV_ESTATE;
+    idx.push_back(layer);
+  } else if (layer == -1) {
+    for (int l = 0; l < c->D.layers; ++l)
+      if (c->layers[l].pending) idx.push_back(l);
+  } else {
+    return ISKV_EINVAL;
+  }
+  std::vector<bool> done(idx.size(), false);
+  for (size_t i = 0; i < idx.size(); ++i) {
+    if (done[i]) continue;
+    const int64_t n_c = c->layers[idx[i]].n_c;
+    std::vector<int> grp;
+    for (size_t j = i; j < idx.size(); ++j)
+      if (!done[j] && c->layers[idx[j]].n_c == n_c) { grp.push_back(idx[j]); done[j] = true; }
+    for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
+      LayerSel sel;
+      fill_sel(sel, grp, from);
+      if (launch_sync(c->M, sel, n_c - kBlock, c->stream) != hipSuccess) return ISKV_EDEVICE;
+    }
+    for (int l : grp) {
+      c->layers[l].pending = false;
+      c->layers[l].syncs += 1;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_discard_sync(iskv_ctx *c, int layer) {
+  if (!c) return ISKV_EINVAL;
+  if (layer >= 0) {
+    if (check_layer(c, layer)) return ISKV_EINVAL;
+    if (!c->layers[layer].pending) return ISKV_ESTATE;
+    c->layers[layer].pending = false;
+    return ISKV_OK;
+  }
+  if (layer != -1) return ISKV_EINVAL;
+  for (LayerState &L : c->layers) L.pending = false;
+  return ISKV_OK;
+}
+
+int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out) {
+  if (!c || check_layer(c, layer) || !dev_q || !dev_out) return ISKV_EINVAL;
+  if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
+  const LayerState &L = c->layers[layer];
+  if (L.length <= 0) return ISKV_ESTATE;
+  return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
+}
+
+int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
+  if (!c || !st || check_layer(c, layer)) return ISKV_EINVAL;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
+  int flags = 0;
+  if (hipMemcpy(&flags, c->M.sh.flags, 4, hipMemcpyDeviceToHost) != hipSuccess) return ISKV_EDEVICE;
+  const LayerState &L = c->layers[layer];
+  std::memset(st, 0, sizeof(*st));
+  st->length = L.length;
+  st->compressed = L.n_c;
+  st->blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
+  st->pending_sync = L.pending ? 1 : 0;
+  st->folds = L.folds;
+  st->syncs = L.syncs;
+  st->persistent_bytes = persistent_bytes(c);
+  uint64_t full = 0;
+  for (const LayerState &S : c->layers)
+    full += 2ull * (uint64_t)S.length * c->D.units * c->D.d * c->D.elem;
+  st->full_bytes = full;
+  st->numeric_flags = flags;
+  return flags ? ISKV_ENUMERIC : ISKV_OK;
+}
+
+int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
+  if (!c || check_layer(c, layer) || !host_buf) return ISKV_EINVAL;
+  if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
+  const Dims &D = c->D;
+  const LayerLayout &Ly = c->G.layer;
+  const size_t lb = Ly.bytes;
+  std::vector<uint8_t> raw(lb);
+  const uint8_t *src = c->M.base + c->G.layers_base + (size_t)layer * lb;
+  if (hipMemcpy(raw.data(), src, lb, hipMemcpyDeviceToHost) != hipSuccess) return ISKV_EDEVICE;
+  auto elem = [&](size_t off, size_t i) -> float {
+    if (D.storage == ISKV_BF16) {
+      uint16_t h;
+      std::memcpy(&h, raw.data() + off + i * 2, 2);
+      return host_from_bf16(h);
+    }
+    float f;
+    std::memcpy(&f, raw.data() + off + i * 4, 4);
+    return f;
+  };
+  uint8_t *o = reinterpret_cast<uint8_t *>(host_buf);
+  const LayerState &L = c->layers[layer];
+  std::memcpy(o, &L.length, 8);
+  std::memcpy(o + 8, &L.n_c, 8);
+  float *f = reinterpret_cast<float *>(o + 16);
+  for (int u = 0; u < D.units; ++u) {
+    for (int x = 0; x < 2; ++x) {
+      const size_t ux = (size_t)u * 2 + x;
+      std::memcpy(f, raw.data() + Ly.basis + ux * D.d * D.r * 4, (size_t)D.d * D.r * 4);
+      f += (size_t)D.d * D.r;
+      std::memcpy(f, raw.data() + Ly.sing + ux * D.r * 4, (size_t)D.r * 4);
+      f += D.r;
+      const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
+      for (size_t i = 0; i < (size_t)D.max_tokens * D.r; ++i)
+        f[i] = (i < (size_t)L.n_c * D.r) ? elem(coff, i) : 0.f;
+      f += (size_t)D.max_tokens * D.r;
+      for (int s = 0; s < D.slots; ++s)
+        for (int d = 0; d < D.d; ++d) {
+          const size_t i = (x == 0)
+              ? (size_t)u * D.slots * D.d + (size_t)s * D.d + d
+              : (size_t)u * D.slots * D.d + (size_t)d * D.slots + s;
+          f[(size_t)s * D.d + d] = elem(x == 0 ? Ly.ringk : Ly.ringv, i);
+        }
+      f += (size_t)D.slots * D.d;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes) {
+  if (!c || check_layer(c, layer) || !host_buf) return ISKV_EINVAL;
+  if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
+  const Dims &D = c->D;
+  const uint8_t *in = reinterpret_cast<const uint8_t *>(host_buf);
+  int64_t length, n_c;
+  std::memcpy(&length, in, 8);
+  std::memcpy(&n_c, in + 8, 8);
+  if (length < 0 || n_c < 0 || n_c % kBlock || n_c > length || length > D.max_tokens ||
+      length - n_c > D.slots)
+    return ISKV_EINVAL;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
+  const LayerLayout &Ly = c->G.layer;
+  const size_t lb = Ly.bytes;
+  std::vector<uint8_t> raw(lb, 0);
+  auto put = [&](size_t off, size_t i, float v) {
+    if (D.storage == ISKV_BF16) {
+      const uint16_t h = host_bf16(v);
+      std::memcpy(raw.data() + off + i * 2, &h, 2);
+    } else {
+      std::memcpy(raw.data() + off + i * 4, &v, 4);
+    }
+  };
+  const float *f = reinterpret_cast<const float *>(in + 16);
+  for (int u = 0; u < D.units; ++u) {
+    for (int x = 0; x < 2; ++x) {
+      const size_t ux = (size_t)u * 2 + x;
+      std::memcpy(raw.data() + Ly.basis + ux * D.d * D.r * 4, f, (size_t)D.d * D.r * 4);
+      f += (size_t)D.d * D.r;
+      std::memcpy(raw.data() + Ly.sing + ux * D.r * 4, f, (size_t)D.r * 4);
+      f += D.r;
+      const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
+      for (size_t i = 0; i < (size_t)n_c * D.r; ++i) put(coff, i, f[i]);
+      f += (size_t)D.max_tokens * D.r;
+      for (int s = 0; s < D.slots; ++s)
+        for (int d = 0; d < D.d; ++d) {
+          const size_t i = (x == 0)
+              ? (size_t)u * D.slots * D.d + (size_t)s * D.d + d
+              : (size_t)u * D.slots * D.d + (size_t)d * D.slots + s;
+          put(x == 0 ? Ly.ringk : Ly.ringv, i, f[(size_t)s * D.d + d]);
+        }
+      f += (size_t)D.slots * D.d;
+    }
+  }
+  uint8_t *dst = c->M.base + c->G.layers_base + (size_t)layer * lb;
+  if (hipMemcpy(dst, raw.data(), lb, hipMemcpyHostToDevice) != hipSuccess) return ISKV_EDEVICE;
+  LayerSel sel;
+  sel.n = 1;
+  sel.idx[0] = layer;
+  if (launch_prep_frag(c->M, sel, c->stream) != hipSuccess) return ISKV_EDEVICE;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
+  LayerState &L = c->layers[layer];
+  L.length = length;
+  L.n_c = n_c;
+  L.pending = false;
+  return ISKV_OK;
+}
+
+int iskv_destroy(iskv_ctx *c) {
+  if (!c) return ISKV_EINVAL;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  delete c;
+  return hip_err(e);
+}
+
+const char *iskv_strerror(int code) {
+  switch (code) {
+    case ISKV_OK: return "ok";
+    case ISKV_EINVAL: return "invalid argument or unsupported configuration";
+    case ISKV_ESTATE: return "operation not allowed in the current cache state";
+    case ISKV_ENOMEM: return "workspace too small";
+    case ISKV_EDEVICE: return "HIP runtime error";
+    case ISKV_ENUMERIC: return "device numeric flag raised";
+  }
+  return "unknown error";
+}
+
+}  // extern "C"

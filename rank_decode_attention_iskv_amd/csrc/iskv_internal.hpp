@@ -1,0 +1,163 @@
+// Internal layout and kernel-launch interface of libiskv (not part of the ABI).
+//
+// Device workspace, per layer (u = sequence * kv_heads + kv_head, x = 0 for K,
+// 1 for V):
+//   basis  float [U][2][d][r]        row f, column c (orthonormal columns)
+//   sing   float [U][2][r]           singular values S
+//   msync  float [U][2][r][r]        pending synchronization matrix M = B_old^T B_new
+//   frag   bytes [U][2][4*d*r]       basis in the decode kernel's MFMA operand order
+//   coef   T     [U][2][max_tokens][r]  coefficient rows (row = token)
+//   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
+//   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
+// plus, shared by all layers:
+//   rec    float [U][max_rec][G][REC_STRIDE]  split-K partial records of decode
+//   cnt    uint  [U]                          arrival counters (self-resetting)
+//   flags  int                                numeric flags (ISKV_FLAG_*)
+//   fold   float [L][U][2][FOLD_SCRATCH(r)]   block-update scratch (Q^T, P, B_new)
+//   rope   float                              RoPE tables (see rope_tables below)
+// with T = float or bf16 (uint16 bit pattern) per the storage dtype.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace iskv {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 64;
+constexpr int kRecStride = 2 + kHeadDim + 2;   // m, l, acc[128], pad
+constexpr int kRopeAnchor = 64;                 // positions per anchor of the RoPE table
+
+struct Dims {
+  int batch, layers, kv_heads, q_heads, group, d, r, window, slots, max_tokens;
+  int storage;            // 0 f32, 1 bf16
+  int elem;               // bytes per stored element
+  float scale_log2;       // softmax scale * log2(e)
+  float rope_base;
+  int units;              // batch * kv_heads
+  int max_rec;            // decode records per unit
+  int rope_anchors;       // anchors in the RoPE table
+};
+
+// Pointers of one layer.
+struct LayerPtrs {
+  float *basis, *sing, *msync;
+  uint8_t *frag;
+  uint8_t *coef, *ringk, *ringv;
+};
+
+struct Shared {
+  float *rec;
+  unsigned *cnt;
+  int *flags;
+  float *fold;            // base of the fold scratch (all layers)
+  const float *rope_anchor;   // [anchors][64 freq][2] cos, sin of (a * 64) * theta_i
+  const float *rope_step;     // [64 offsets][64 freq][2] cos, sin of o * theta_i
+};
+
+inline __host__ __device__ size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+inline __host__ __device__ size_t fold_scratch_floats(int r) {
+  // Q rows (64 x d), P (64 x r), R_r^T (64 x 64), B_new (d x r)
+  size_t n = (size_t)kBlock * kHeadDim + (size_t)kBlock * r + (size_t)kBlock * kBlock +
+             (size_t)kHeadDim * r;
+  return (n + 63) / 64 * 64;
+}
+
+struct LayerLayout {
+  size_t basis, sing, msync, frag, coef, ringk, ringv, bytes;
+};
+
+inline LayerLayout layer_layout(const Dims &D) {
+  LayerLayout L{};
+  size_t o = 0;
+  const size_t U2 = (size_t)D.units * 2;
+  L.basis = o; o = align_up(o + U2 * D.d * D.r * 4);
+  L.sing = o;  o = align_up(o + U2 * D.r * 4);
+  L.msync = o; o = align_up(o + U2 * D.r * D.r * 4);
+  L.frag = o;  o = align_up(o + U2 * 4 * (size_t)D.d * D.r);
+  L.coef = o;  o = align_up(o + U2 * (size_t)D.max_tokens * D.r * D.elem);
+  L.ringk = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
+  L.ringv = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
+  L.bytes = o;
+  return L;
+}
+
+struct GlobalLayout {
+  LayerLayout layer;
+  size_t layers_base, rec, cnt, flags, fold, rope_anchor, rope_step, total;
+};
+
+inline GlobalLayout global_layout(const Dims &D) {
+  GlobalLayout G{};
+  G.layer = layer_layout(D);
+  size_t o = 0;
+  G.layers_base = o; o = align_up(o + G.layer.bytes * D.layers);
+  G.rec = o;   o = align_up(o + (size_t)D.units * D.max_rec * D.group * kRecStride * 4);
+  G.cnt = o;   o = align_up(o + (size_t)D.units * 4);
+  G.flags = o; o = align_up(o + 4);
+  G.fold = o;  o = align_up(o + (size_t)D.layers * D.units * 2 * fold_scratch_floats(D.r) * 4);
+  G.rope_anchor = o; o = align_up(o + (size_t)D.rope_anchors * 64 * 2 * 4);
+  G.rope_step = o;   o = align_up(o + (size_t)kRopeAnchor * 64 * 2 * 4);
+  G.total = o;
+  return G;
+}
+
+// Whole-workspace view handed to kernels by value.
+struct Model {
+  uint8_t *base;          // workspace base
+  size_t layers_base;     // offset of layer 0
+  size_t layer_stride;    // bytes per layer
+  LayerLayout lay;        // offsets inside a layer
+  Shared sh;
+  Dims D;
+};
+
+constexpr int kMaxLayerSel = 64;
+struct LayerSel {
+  int n;
+  int idx[kMaxLayerSel];
+};
+
+__host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
+  uint8_t *b = M.base + M.layers_base + (size_t)l * M.layer_stride;
+  LayerPtrs P;
+  P.basis = (float *)(b + M.lay.basis);
+  P.sing = (float *)(b + M.lay.sing);
+  P.msync = (float *)(b + M.lay.msync);
+  P.frag = b + M.lay.frag;
+  P.coef = b + M.lay.coef;
+  P.ringk = b + M.lay.ringk;
+  P.ringv = b + M.lay.ringv;
+  return P;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files). Each returns hipSuccess or the
+// launch error.
+// ---------------------------------------------------------------------------
+
+// Reset one layer: basis = I[:, :r], S = 0, M = 0, coefficients and rings 0.
+hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s);
+
+// Write n tokens at positions pos0.. into the rings (in_dtype 0 f32, 1 bf16).
+hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
+                         int in_dtype, int64_t pos0, hipStream_t s);
+
+// Fold the block at positions n_c..n_c+63 of every unit (K and V) of the
+// selected layers.
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s);
+
+// C[0:n_old] <- C[0:n_old] * M for every unit and K|V of the selected layers.
+hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, hipStream_t s);
+
+// Rebuild the decode operand copy of the basis from the fp32 basis.
+hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s);
+
+// Decode attention for one layer.
+hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
+                         int64_t length, int64_t n_c, hipStream_t s);
+
+}  // namespace iskv

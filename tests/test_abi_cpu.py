@@ -1,0 +1,81 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, and validates configurations without touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_decode_attention_iskv_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "iskv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(iskv_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = binding.load_library()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTED)
+
+
+def base_cfg(**kw):
+    d = dict(batch=2, num_layers=3, num_kv_heads=8, num_q_heads=32, head_dim=128, rank=32,
+             window=256, max_tokens=4096, storage=binding.BF16)
+    d.update(kw)
+    return binding.make_config(**d)
+
+
+def test_workspace_bytes_valid_and_monotone():
+    small = binding.workspace_bytes(base_cfg())
+    big = binding.workspace_bytes(base_cfg(max_tokens=8192))
+    assert small > 0 and big > small
+    # coefficients dominate: two factors x units x tokens x rank x 2 bytes per layer
+    assert big - small >= 3 * 2 * 16 * 4096 * 32 * 2
+    assert binding.workspace_bytes(base_cfg(storage=binding.F32)) > small
+
+
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=64), dict(rank=48), dict(rank=256), dict(window=100), dict(window=0),
+    dict(block=32), dict(num_q_heads=12), dict(num_q_heads=96), dict(storage=7),
+    dict(batch=0), dict(max_tokens=0), dict(rope_base=0.5),
+])
+def test_invalid_configs_rejected(kw):
+    assert binding.workspace_bytes(base_cfg(**kw)) == 0
+    assert binding.state_bytes(base_cfg(**kw)) == 0
+
+
+def test_state_bytes_layout():
+    cfg = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000)
+    d, r, T, S = 128, 32, 1000, 256 + 64
+    assert binding.state_bytes(cfg) == 16 + 2 * 2 * (d * r + r + T * r + S * d) * 4
+
+
+def test_init_rejects_bad_arguments_without_device_work():
+    lib = binding.load_library()
+    ctx = ctypes.c_void_p()
+    bad = base_cfg(rank=48)
+    assert lib.iskv_init(ctypes.byref(bad), ctypes.c_void_p(256), 1 << 30, None,
+                         ctypes.byref(ctx)) == binding.EINVAL
+    good = base_cfg()
+    # misaligned workspace pointer
+    assert lib.iskv_init(ctypes.byref(good), ctypes.c_void_p(8), 1 << 40, None,
+                         ctypes.byref(ctx)) == binding.EINVAL
+    # null context for every verb
+    assert lib.iskv_block_update(None, 0) == binding.EINVAL
+    assert lib.iskv_sync(None, 0) == binding.EINVAL
+    assert lib.iskv_destroy(None) == binding.EINVAL
+
+
+def test_strerror_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert binding.strerror(code)
+    assert binding.strerror(99) == "unknown error"
