@@ -1,0 +1,344 @@
+"""Throughput of the compressed-KV decode path on one MI355X.
+
+Workload (default): one GQA attention layer with 8 KV / 32 query heads,
+head_dim 128, rank 32, 32K-token context, exact window 256, bf16 storage with
+fp32 accumulation, batch 1; a block update + sync every 64 decode steps; keys
+and values are a rank-32 Gaussian signal plus 1% noise (synthetic, seeded).
+
+A step is one decode step of that layer: append one token (k, v), decode
+attention of 32 query heads over the whole mixed cache, and -- whenever the
+ring holds window + 64 tokens -- a block update (Brand fold of 64 tokens for
+all 8 heads, K and V) followed by the coefficient sync.  The bench holds
+several independent instances of the layer and runs the steps round-robin
+over them, so every step reads its cache from HBM rather than from the 256 MB
+Infinity Cache (one instance is ~35 MB).
+
+Prints one JSON line (see --help).  Only one GPU: --gpus N > 1 exits.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attn tokens/s + block updates/s; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4096, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=512, help="untimed decode steps")
+    ap.add_argument("--instances", type=int, default=16,
+                    help="independent copies of the layer, stepped round-robin")
+    ap.add_argument("--context", type=int, default=32768, help="tokens in the cache when timing starts")
+    ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--window", type=int, default=256)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=1002)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# synthetic inputs (GPU-side generation, before the timed region)
+# ---------------------------------------------------------------------------
+
+class Generator:
+    """x_t = G z_t + 0.01 e_t per (instance, KV head, K|V); G fixed, 128 x 32."""
+
+    def __init__(self, torch, n_inst, batch, kv_heads, d, signal_rank, seed):
+        self.torch = torch
+        self.g = torch.Generator(device="cuda")
+        self.g.manual_seed(seed)
+        self.mix = torch.randn(n_inst, batch, kv_heads, 2, signal_rank, d, device="cuda",
+                               generator=self.g) / math.sqrt(signal_rank)
+        self.shape = (batch, kv_heads, d, signal_rank)
+
+    def tokens(self, inst, n):
+        torch = self.torch
+        b, h, d, k = self.shape
+        z = torch.randn(b, h, 2, n, k, device="cuda", generator=self.g)
+        x = torch.matmul(z, self.mix[inst]) + 0.01 * torch.randn(b, h, 2, n, d, device="cuda",
+                                                                generator=self.g)
+        x = x.permute(2, 0, 3, 1, 4).contiguous()          # [2, b, n, h, d]
+        return x[0], x[1]
+
+    def queries(self, count, q_heads, d):
+        return self.torch.randn(count, self.shape[0], q_heads, d, device="cuda", generator=self.g)
+
+
+def decode_bytes(batch, kv_heads, q_heads, d, r, n_c, n_e, elem=2):
+    """Algorithmic bytes of one decode call: coefficients of K and V, exact
+    window rows of K and V, the two fp32 bases, the fp32 query and output."""
+    per_unit = n_c * r * 2 * elem + n_e * d * 2 * elem + 2 * d * r * 4
+    return batch * kv_heads * per_unit + batch * q_heads * d * 4 * 2
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "rank_decode_attention_iskv_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_hash):
+    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "decode_attn_config2_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.strip().split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host cores, bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries=4):
+    import numpy as np
+
+    import workloads
+    from oracle import Unit
+
+    cores = len(os.sched_getaffinity(0))
+    w = workloads.with_(workloads.WORKLOADS[2], window=window, rank=rank, context=context)
+    u = Unit(w.head_dim, rank, window, context + 64, "bf16")
+    t0 = time.perf_counter()
+    fold_t = 0.0
+    folds = 0
+    pos = 0
+    while pos < context:
+        n = min(64, context - pos)
+        k, v = workloads.tokens(w, 0, pos, n)
+        for i in range(n):
+            u.append(k[0, i, 0], v[0, i, 0])
+        pos += n
+        if u.ready:
+            f0 = time.perf_counter()
+            u.fold()
+            u.sync()
+            fold_t += time.perf_counter() - f0
+            folds += 1
+    build_t = time.perf_counter() - t0
+    g = q_heads // kv_heads
+    d0 = time.perf_counter()
+    for s in range(decode_queries):
+        q = workloads.query(w, 0, s)[0, :g]
+        u.decode(q, u.length - 1, 1.0 / math.sqrt(w.head_dim))
+    dec_t = (time.perf_counter() - d0) / decode_queries
+    # one decode step of the layer: kv_heads units decode; every 64 steps each
+    # unit folds + syncs at the current history length (the sample's last
+    # folds are the most expensive; use the average over the sample)
+    fold_avg = fold_t / max(folds, 1)
+    step_s = kv_heads * (dec_t + fold_avg / 64.0)
+    return {
+        "value": 1.0 / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"one KV head (K and V) of the layer built to {context} tokens by the oracle "
+                   f"({folds} folds + syncs, {build_t:.1f} s), then {decode_queries} decode calls of "
+                   f"{g} query heads ({dec_t * 1e3:.1f} ms each); per step = {kv_heads} heads x "
+                   f"(decode + average fold+sync / 64)"),
+        "oracle_decode_ms_per_head": dec_t * 1e3,
+        "oracle_fold_sync_ms_avg": fold_avg * 1e3,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
+              "not part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from rank_decode_attention_iskv_amd import binding
+
+    torch.cuda.set_device(0)
+    H, HQ, D, R, W, B = 8, 32, 128, args.rank, args.window, args.batch
+    I = args.instances
+    total_steps = args.warmup + args.steps
+    per_inst_steps = (total_steps + I - 1) // I
+    max_tokens = args.context + per_inst_steps + 64
+    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16)
+    cache = binding.IskvCache(cfg)
+    stream = torch.cuda.current_stream()
+    gen = Generator(torch, I, B, H, D, 32, args.seed)
+
+    # ---- prefill every instance to `context` tokens (fold + sync as the ring fills)
+    t_pre = time.perf_counter()
+    length, n_c = 0, 0
+    while length < args.context:
+        n = min(64, args.context - length, (W + 64) - (length - n_c))
+        ready = False
+        for inst in range(I):
+            k, v = gen.tokens(inst, n)
+            ready = cache.append(inst, k, v)
+        length += n
+        if ready:
+            cache.block_update(-1)
+            cache.sync(-1)
+            n_c += 64
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t_pre
+
+    # ---- inputs of the timed steps, resident before timing
+    k_all, v_all = [], []
+    for inst in range(I):
+        k, v = gen.tokens(inst, per_inst_steps)
+        k_all.append(k)
+        v_all.append(v)
+    q_all = gen.queries(total_steps, HQ, D)
+    out = torch.empty(B, HQ, D, device="cuda")
+    torch.cuda.synchronize()
+
+    lengths = [cache.status(i).length for i in range(I)]
+    comp = [cache.status(i).compressed for i in range(I)]
+    used = [0] * I
+    ev = []                      # (start, end, bytes) per timed decode launch
+    fold_ev, sync_ev = [], []
+    bytes_total = 0
+    folds = 0
+
+    def step(s, timed):
+        nonlocal bytes_total, folds
+        inst = s % I
+        j = used[inst]
+        used[inst] += 1
+        ready = cache.append(inst, k_all[inst][:, j:j + 1], v_all[inst][:, j:j + 1])
+        lengths[inst] += 1
+        L, n_c = lengths[inst], comp[inst]
+        q = q_all[s]
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cache.decode_attn(inst, q, L - 1, out)
+            e1.record(stream)
+            nb = decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
+            ev.append((e0, e1, nb))
+            bytes_total += nb
+        else:
+            cache.decode_attn(inst, q, L - 1, out)
+        if ready:
+            if timed:
+                f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                f0.record(stream)
+                cache.block_update(inst)
+                f1.record(stream)
+                cache.sync(inst)
+                f2.record(stream)
+                fold_ev.append((f0, f1))
+                sync_ev.append((f1, f2))
+                folds += 1
+            else:
+                cache.block_update(inst)
+                cache.sync(inst)
+            comp[inst] += 64
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.warmup, total_steps):
+        step(s, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+
+    dec_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    bytes_avg = bytes_total / len(ev)
+    achieved = bytes_avg / (dec_avg_ms * 1e-3) / 1e9
+    fold_ms = [a.elapsed_time(b) for a, b in fold_ev]
+    sync_ms = [a.elapsed_time(b) for a, b in sync_ev]
+    units_per_fold = B * H * 2
+    st = cache.status(0)
+    flags = max(cache.status(i).numeric_flags for i in range(I))
+    finite = bool(torch.isfinite(out).all().item())
+    value = args.steps / (total_ms * 1e-3)
+    kh = kernel_source_hash()
+    traffic = committed_traffic(kh)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"one GQA layer: {H} KV / {HQ} q heads, head_dim {D}, rank {R}, "
+                         f"{args.context}-token context (grows by 1 per step), window {W}, "
+                         f"bf16 storage, fp32 accumulate, batch {B}, block update + sync every "
+                         f"64 steps; K/V rank-32 signal + 1% noise"),
+            "instances_rotated": I,
+            "global_batch": B,
+            "seq_len": args.context,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_attn",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_avg,
+            "avg_launch_us": dec_avg_ms * 1e3,
+        },
+        "decode_attn_tokens_per_s_kernel_only": 1e3 / dec_avg_ms,
+        "block_updates_per_s": (units_per_fold * len(fold_ms) / (sum(fold_ms) * 1e-3)) if fold_ms else None,
+        "block_updates_per_s_with_sync": (units_per_fold * len(fold_ms) /
+                                          ((sum(fold_ms) + sum(sync_ms)) * 1e-3)) if fold_ms else None,
+        "fold_avg_us": (sum(fold_ms) / len(fold_ms) * 1e3) if fold_ms else None,
+        "sync_avg_us": (sum(sync_ms) / len(sync_ms) * 1e3) if sync_ms else None,
+        "timed_folds": folds,
+        "prefill_s": t_pre,
+        "wall_s_timed": wall,
+        "numeric_flags": flags,
+        "output_finite": finite,
+        "kernel_sources_sha256_16": kh,
+        "persistent_kv_bytes_per_instance": st.persistent_bytes // I,
+        "full_kv_bytes_per_instance": st.full_bytes // I,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.context, W, R, H, HQ)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

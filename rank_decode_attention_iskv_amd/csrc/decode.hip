@@ -10,10 +10,34 @@
 //
 // Split-K: each workgroup attends over one token range of one (sequence, KV
 // head) for all query heads of its group and writes a partial record
-// (running max m, sum l, accumulator); the last workgroup to arrive for that
-// (sequence, KV head) merges the records by log-sum-exp and writes the output.
+// (running max m, sum l, accumulator); a second, small kernel merges the
+// records of each (sequence, KV head) by log-sum-exp and writes the output
+// (the kernel boundary makes every record visible across the XCDs' L2s, so
+// no device-wide fences are needed inside the decode kernel).
+//
+// Per wave and tile of 16 tokens (all on MFMA except RoPE and the softmax):
+//   stream  the coefficient tiles of K and V are copied HBM -> LDS by direct
+//           DMA loads (no registers), kept several tiles ahead in a per-wave
+//           LDS ring;
+//   keys    K^T (128 x 16) = B_K (128 x r) C_K^T (r x 16): the fp32 basis
+//           enters as bf16 hi + lo (two products), bf16 coefficients exactly
+//           (fp32 storage: fp32 MFMA).  Lane l holds features 16*mb + 4*(l/16)
+//           + i, mb = 0..7, of token l%16: 16 RoPE pairs (f, f + 64), rotated
+//           in registers at the token's position;
+//   scores  S (16 tokens x 16 heads) = K~ Q~^T with both sides split bf16
+//           hi/lo (hi*hi + hi*lo + lo*hi, relative error ~1e-5); lane l gets
+//           head l%16 and tokens 4*(l/16)..+3, the A-operand layout of the
+//           value product; query heads beyond the group are zero;
+//   softmax running max per head in log2 units, rescaled lazily (only when
+//           the max grows by more than 8, so p <= 2^8);
+//   values  acc (16 heads x r) += P (16 x 16 tokens) C_V (16 tokens x r) with P
+//           split bf16 hi/lo, C_V read transposed from the LDS ring.  Window
+//           tiles read V^T straight from the transposed ring (acc over 128
+//           features).
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 
@@ -25,260 +49,688 @@ namespace iskv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4_ __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uint4_ __attribute__((ext_vector_type(4)));
+typedef unsigned uint2_ __attribute__((ext_vector_type(2)));
+
+constexpr float kRescale = 8.f;
 
 struct SplitPlan {
   int n_comp;        // splits over compressed tokens
   int comp_len;      // tokens per compressed split (multiple of 64)
   int n_win;         // splits over window tokens
-  int win_len;       // tokens per window split
+  int win_len;       // tokens per window split (multiple of 16)
 };
 
-// Merge the split records of unit u and write out[b][h_kv*G + h][:].
-// Called by every thread of the last-arriving workgroup.
-template <int R>
-__device__ void merge_records(const Model &M, int layer, int u, int n_rec, int n_comp,
-                              float *out, float *lds) {
-  const Dims &D = M.D;
-  const int G = D.group, tid = threadIdx.x;
-  const float *rec = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
-  float *sMx = lds;                       // [G]
-  float *sL = sMx + 16;                   // [G]
-  float *sC = sL + 16;                    // [G][R]
-  float *sW = sC + 16 * R;                // [G][128]
-  if (tid < G) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n_rec; ++s) mx = fmaxf(mx, rec[((size_t)s * G + tid) * kRecStride]);
-    float l = 0.f;
-    for (int s = 0; s < n_rec; ++s) {
-      const float *r = rec + ((size_t)s * G + tid) * kRecStride;
-      l += r[1] * exp2f(r[0] - mx);
-    }
-    sMx[tid] = mx;
-    sL[tid] = l;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * R; e += blockDim.x) {
-    const int h = e / R, c = e % R;
-    float a = 0.f;
-    for (int s = 0; s < n_comp; ++s) {
-      const float *r = rec + ((size_t)s * G + h) * kRecStride;
-      a += r[2 + c] * exp2f(r[0] - sMx[h]);
-    }
-    sC[h * R + c] = a;
-  }
-  for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
-    const int h = e / kHeadDim, f = e % kHeadDim;
-    float a = 0.f;
-    for (int s = n_comp; s < n_rec; ++s) {
-      const float *r = rec + ((size_t)s * G + h) * kRecStride;
-      a += r[2 + f] * exp2f(r[0] - sMx[h]);
-    }
-    sW[h * kHeadDim + f] = a;
-  }
-  __syncthreads();
-  LayerPtrs P = layer_ptrs(M, layer);
-  const float *Bv = P.basis + ((size_t)u * 2 + 1) * kHeadDim * R;
-  const int b = u / D.kv_heads, hk = u % D.kv_heads;
-  for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
-    const int h = e / kHeadDim, f = e % kHeadDim;
-    float a = sW[h * kHeadDim + f];
-    if (n_comp > 0)
-      for (int c = 0; c < R; ++c) a += Bv[f * R + c] * sC[h * R + c];
-    out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a / sL[h];
-  }
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// (a, b) -> packed bf16 high parts (round to nearest even) and low parts.
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
+  const bf16x2 h = __builtin_convertvector((floatx2){a, b}, bf16x2);
+  const unsigned hb = __builtin_bit_cast(unsigned, h);
+  const float ha = __uint_as_float(hb << 16), hh = __uint_as_float(hb & 0xffff0000u);
+  const bf16x2 l = __builtin_convertvector((floatx2){a - ha, b - hh}, bf16x2);
+  hi = hb;
+  lo = __builtin_bit_cast(unsigned, l);
 }
 
-// Arrival counter; returns true in every thread of the last workgroup.
-__device__ bool arrive_last(const Model &M, int u, int total, int *s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old = atomicAdd(&M.sh.cnt[u], 1u);
-    const bool last = (old == (unsigned)total - 1);
-    if (last) M.sh.cnt[u] = 0;       // self-reset for the next call
-    *s_flag = last;
-  }
-  __syncthreads();
-  const bool last = *s_flag;
-  if (last) __threadfence();
-  return last;
+__device__ __forceinline__ floatx4 mfma32(uint4_ a, uint4_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(uint2_ a, uint2_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_, a),
+                                                   __builtin_bit_cast(short4_, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// reductions over the four lane rows (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// feature held by lane row rho in slot j of K-block kb of the score product
+__device__ __forceinline__ int score_feature(int kb, int j, int rho) {
+  return 16 * (2 * kb + (j >> 2)) + 4 * rho + (j & 3);
+}
+
+// 16-byte direct load global -> LDS for this lane (LDS-DMA; the wave-uniform
+// LDS base receives lane l's bytes at offset 16*l).  The builtin exists only
+// for the device target, so the host pass sees an empty body.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+#endif
+}
+
+// s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // ---------------------------------------------------------------------------
-// Reference-style decode: one token per thread, fp32 VALU throughout.
-// grid (splits, units); LDS: q (G x 128), B_K (128 x (R+1)), scores (G x 256).
+// Online softmax over one 16-token tile for the lane's head (l%16) and tokens
+// 4*(l/16)..+3.  Rescales the value accumulators (lane layout: heads
+// 4*(l/16)+i) when the running max of any head grows by more than kRescale.
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void softmax_tile(floatx4 sc, int valid_mask, float &m, float &l,
+                                             floatx4 (&acc)[NB], int rho, float (&p)[4]) {
+  float s[4] = {sc[0], sc[1], sc[2], sc[3]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) if (!((valid_mask >> i) & 1)) s[i] = -INFINITY;
+  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  tmax = row_max(tmax);
+  const bool need = tmax > m + kRescale;
+  if (__any(need)) {
+    const float mnew = need ? tmax : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // m = -inf -> 0
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __shfl(alpha, 4 * rho + i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb][i] *= a;
+    }
+    m = mnew;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(s[i] - m);
+    l += p[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tunables per (rank, storage): workgroups per CU and the per-wave LDS ring.
+// ---------------------------------------------------------------------------
+template <int R, typename T> struct Cfg {
+  static constexpr bool BF = std::is_same<T, bf16_t>::value;
+  static constexpr int kElem = BF ? 2 : 4;
+  static constexpr int kMatBytes = 16 * R * kElem;           // one 16-token tile of C_K or C_V
+  static constexpr int kDma = kMatBytes >= 1024 ? kMatBytes / 1024 : 1;   // dwordx4 DMAs per matrix
+  static constexpr int kRingBytes = 16384;                    // per wave
+  static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
+  static constexpr int kOcc = (BF && R <= 32) ? 2 : 1;
+  static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
+  static constexpr int kDynBytes = (4 * kRingBytes > kAccBytes) ? 4 * kRingBytes : kAccBytes;
+};
+
+// ---------------------------------------------------------------------------
+// The MFMA decode kernel.  grid (splits, units), 256 threads.
 // ---------------------------------------------------------------------------
 template <int R, typename T>
-__global__ __launch_bounds__(kThreads) void decode_simple_kernel(Model M, int layer,
-                                                                 const float *q, int64_t q_pos,
-                                                                 float *out, int64_t length,
-                                                                 int64_t n_c, SplitPlan plan) {
-  extern __shared__ float lds[];
-  __shared__ float sm[16], sl[16], salpha[16];
-  __shared__ int s_flag;
+__global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kernel(
+    Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
+    int64_t n_c, SplitPlan plan) {
+  using C = Cfg<R, T>;
+  constexpr bool BF = C::BF;
+  constexpr int NBV = R / 16;                            // value N-blocks (compressed)
+  constexpr int DEPTH = C::kDepth;
+  constexpr int LPT = 2 * C::kDma;                       // DMA loads per tile
+  extern __shared__ __align__(16) uint8_t s_dyn[];       // per-wave rings, then results
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float2 s_step[64];          // cos, sin of 16 * theta_i (tile advance)
+  __shared__ float s_q[16][kHeadDim];    // rotated, scaled query rows of the group
+  float (*s_acc)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(s_dyn);
+
   const Dims &D = M.D;
-  const int G = D.group, tid = threadIdx.x;
+  const int G = D.group;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, rho = lane >> 4;
   const int split = blockIdx.x, u = blockIdx.y;
   const int b = u / D.kv_heads, hk = u % D.kv_heads;
   const bool comp = split < plan.n_comp;
-  int64_t t_begin, t_end;
+
+  int64_t r_begin, r_end;
   if (comp) {
-    t_begin = (int64_t)split * plan.comp_len;
-    t_end = t_begin + plan.comp_len < n_c ? t_begin + plan.comp_len : n_c;
+    r_begin = (int64_t)split * plan.comp_len;
+    r_end = r_begin + plan.comp_len < n_c ? r_begin + plan.comp_len : n_c;
   } else {
-    t_begin = n_c + (int64_t)(split - plan.n_comp) * plan.win_len;
-    t_end = t_begin + plan.win_len < length ? t_begin + plan.win_len : length;
+    r_begin = n_c + (int64_t)(split - plan.n_comp) * plan.win_len;
+    r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
-  constexpr int BP = R + 1;
-  float *sq = lds;                          // [16][128]
-  float *sB = sq + 16 * kHeadDim;           // [128][BP]
-  float *ssc = sB + kHeadDim * BP;          // [16][256]
-  float *sacc = ssc + 16 * kThreads;        // [16][128]
+  const int ntiles = (int)((r_end - r_begin + 15) / 16);
+  const int tpw = (ntiles + 3) / 4;
+  const int tile_lo = wave * tpw < ntiles ? wave * tpw : ntiles;
+  const int tile_hi = (wave + 1) * tpw < ntiles ? (wave + 1) * tpw : ntiles;
+  const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
+  const int nt = tile_hi - tile_lo;
 
   LayerPtrs P = layer_ptrs(M, layer);
-  // query rows of the group, rotated at q_pos, scaled by scale*log2(e)
-  for (int e = tid; e < G * 64; e += kThreads) {
-    const int h = e / 64, i = e % 64;
-    const float *qr = q + ((size_t)b * D.q_heads + hk * G + h) * kHeadDim;
-    float c, s;
-    rope_cs(M.sh, q_pos, i, c, s);
-    const float x0 = qr[i], x1 = qr[i + 64];
-    sq[h * kHeadDim + i] = (x0 * c - x1 * s) * D.scale_log2;
-    sq[h * kHeadDim + i + 64] = (x1 * c + x0 * s) * D.scale_log2;
-  }
-  const float *Bk = P.basis + ((size_t)u * 2 + 0) * kHeadDim * R;
-  if (comp)
-    for (int e = tid; e < kHeadDim * R; e += kThreads) sB[(e / R) * BP + e % R] = Bk[e];
-  const int accw = comp ? R : kHeadDim;
-  for (int e = tid; e < G * kHeadDim; e += kThreads) sacc[e] = 0.f;
-  if (tid < 16) { sm[tid] = -INFINITY; sl[tid] = 0.f; }
-  __syncthreads();
 
-  const T *Ck = reinterpret_cast<const T *>(P.coef) + ((size_t)u * 2 + 0) * D.max_tokens * R;
-  const T *Cv = reinterpret_cast<const T *>(P.coef) + ((size_t)u * 2 + 1) * D.max_tokens * R;
-  const T *rk = reinterpret_cast<const T *>(P.ringk) + (size_t)u * D.slots * kHeadDim;
-  const T *rv = reinterpret_cast<const T *>(P.ringv) + (size_t)u * D.slots * kHeadDim;
-
-  for (int64_t base = t_begin; base < t_end; base += kThreads) {
-    const int64_t t = base + tid;
-    const bool valid = t < t_end;
-    float s[16];
-    for (int h = 0; h < 16; ++h) s[h] = 0.f;
-    if (valid) {
-      float cf[R];
-      if (comp) {
+  // ---- RoPE angle state of the lane's token for its 16 frequencies
+  floatx2 cs[16];
+  auto anchor = [&](int64_t t) {
 #pragma unroll
-        for (int c = 0; c < R; ++c) cf[c] = Store<T>::load(Ck, (size_t)t * R + c);
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float c, s;
+        rope_cs(M.sh, t, 16 * mb + 4 * rho + i, c, s);
+        cs[mb * 4 + i] = floatx2{c, s};
       }
-      const int slot = (int)(t % D.slots);
-      for (int i = 0; i < 64; ++i) {
-        float k0, k1;
-        if (comp) {
-          k0 = 0.f; k1 = 0.f;
+  };
+
+  // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS
+  // (one (head, frequency) pair per thread), then split bf16 hi/lo into the
+  // B-operand layout of the score product
+  uint4_ qhi[4], qlo[4];
+  auto prepare_query = [&]() {
+    for (int e = threadIdx.x; e < 16 * 64; e += kThreads) {
+      const int h = e >> 6, i = e & 63;
+      float x0 = 0.f, x1 = 0.f, c = 1.f, s = 0.f;
+      if (h < G) {
+        const float *qr = q + ((size_t)b * D.q_heads + hk * G + h) * kHeadDim;
+        x0 = qr[i];
+        x1 = qr[i + 64];
+        rope_cs(M.sh, q_pos, i, c, s);
+      }
+      s_q[h][i] = fmaf(x0, c, -x1 * s) * D.scale_log2;
+      s_q[h][i + 64] = fmaf(x1, c, x0 * s) * D.scale_log2;
+    }
+    if (threadIdx.x < 64)
+      s_step[threadIdx.x] = reinterpret_cast<const float2 *>(M.sh.rope_step)[16 * 64 + threadIdx.x];
+    __syncthreads();
 #pragma unroll
-          for (int c = 0; c < R; ++c) {
-            k0 += sB[i * BP + c] * cf[c];
-            k1 += sB[(i + 64) * BP + c] * cf[c];
+    for (int kb = 0; kb < 4; ++kb) {
+      unsigned h[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        split2(s_q[n16][score_feature(kb, 2 * j, rho)], s_q[n16][score_feature(kb, 2 * j + 1, rho)],
+               h[j], lo[j]);
+      qhi[kb] = uint4_{h[0], h[1], h[2], h[3]};
+      qlo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
+    }
+  };
+
+  // rotate the key tile by the angle state (then advance it 16 positions),
+  // then the score product
+  auto rope_scores = [&](floatx4 (&ka)[8]) -> floatx4 {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = cs[mb * 4 + i].x, s = cs[mb * 4 + i].y;
+        const float x0 = ka[mb][i], x1 = ka[mb + 4][i];
+        ka[mb][i] = fmaf(x0, c, -x1 * s);
+        ka[mb + 4][i] = fmaf(x1, c, x0 * s);
+        const float2 st = s_step[16 * mb + 4 * rho + i];
+        cs[mb * 4 + i] = floatx2{fmaf(c, st.x, -s * st.y), fmaf(s, st.x, c * st.y)};
+      }
+    floatx4 sc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      unsigned h[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        split2(ka[2 * kb][2 * j], ka[2 * kb][2 * j + 1], h[j], lo[j]);
+        split2(ka[2 * kb + 1][2 * j], ka[2 * kb + 1][2 * j + 1], h[2 + j], lo[2 + j]);
+      }
+      const uint4_ kh = {h[0], h[1], h[2], h[3]}, kl = {lo[0], lo[1], lo[2], lo[3]};
+      sc = mfma32(kh, qhi[kb], sc);
+      sc = mfma32(kh, qlo[kb], sc);
+      sc = mfma32(kl, qhi[kb], sc);
+    }
+    return sc;
+  };
+
+  float m = -INFINITY, l = 0.f;
+  const int64_t w_end = r_end;
+
+  if (comp) {
+    // ================= compressed tokens =================
+    floatx4 vacc[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) vacc[nb] = zero4();
+    // per-wave LDS ring of DEPTH slots, each [C_K tile | C_V tile]
+    uint8_t *ring = s_dyn + wave * C::kRingBytes;
+    const uint8_t *gk = P.coef + (((size_t)u * 2 + 0) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
+    const uint8_t *gv = P.coef + (((size_t)u * 2 + 1) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
+    // one tile: kDma dwordx4 DMAs per matrix; lane l moves 16 bytes of chunk
+    // d*64 + l of the tile (lanes past the tile size idle)
+    auto issue = [&](int it) {
+      uint8_t *slot = ring + (it % DEPTH) * 2 * C::kMatBytes;
+#pragma unroll
+      for (int d = 0; d < C::kDma; ++d) {
+        const int off = (d * 64 + lane) * 16;
+        if (off < C::kMatBytes) {
+          dma16(gk + (size_t)it * C::kMatBytes + off, slot + d * 1024);
+          dma16(gv + (size_t)it * C::kMatBytes + off, slot + C::kMatBytes + d * 1024);
+        }
+      }
+    };
+    // operands issued before the query barrier: the first DEPTH-1 tiles, the
+    // basis fragments and the first angle state
+#pragma unroll
+    for (int j = 0; j < DEPTH - 1; ++j)
+      if (j < nt) issue(j);
+    const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
+    uint4_ F[8][R / 16];
+    if (nt > 0) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int ch = 0; ch < R / 16; ++ch)
+          F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + ch) * 64 + lane) * 16);
+      anchor(w_begin + n16);
+    }
+    prepare_query();
+    for (int it = 0; it < nt; ++it) {
+      if (it + DEPTH - 1 < nt) {
+        issue(it + DEPTH - 1);
+        wait_vmcnt<(DEPTH - 1) * LPT>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      const uint8_t *slot = ring + (it % DEPTH) * 2 * C::kMatBytes;
+      const T *tk = reinterpret_cast<const T *>(slot);
+      const T *tv = reinterpret_cast<const T *>(slot + C::kMatBytes);
+      // keys: rebuild from the basis fragments and this lane's coefficients
+      floatx4 ka[8];
+      if constexpr (BF) {
+        const T *row = tk + n16 * R + rho * (R / 4);
+        if constexpr (R == 16) {
+          const uint2_ bop = *reinterpret_cast<const uint2_ *>(row);
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb) {
+            floatx4 a = mfma16(uint2_{F[mb][0].x, F[mb][0].y}, bop, zero4());
+            ka[mb] = mfma16(uint2_{F[mb][0].z, F[mb][0].w}, bop, a);
           }
         } else {
-          k0 = Store<T>::load(rk, (size_t)slot * kHeadDim + i);
-          k1 = Store<T>::load(rk, (size_t)slot * kHeadDim + i + 64);
+          uint4_ bop[R / 32];
+#pragma unroll
+          for (int kb = 0; kb < R / 32; ++kb) bop[kb] = reinterpret_cast<const uint4_ *>(row)[kb];
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb) {
+            floatx4 a = zero4();
+#pragma unroll
+            for (int kb = 0; kb < R / 32; ++kb) {
+              a = mfma32(F[mb][2 * kb], bop[kb], a);
+              a = mfma32(F[mb][2 * kb + 1], bop[kb], a);
+            }
+            ka[mb] = a;
+          }
         }
-        float cs, sn;
-        rope_cs(M.sh, t, i, cs, sn);
-        const float r0 = k0 * cs - k1 * sn, r1 = k1 * cs + k0 * sn;
-        for (int h = 0; h < G; ++h)
-          s[h] += sq[h * kHeadDim + i] * r0 + sq[h * kHeadDim + i + 64] * r1;
-      }
-    }
-    for (int h = 0; h < G; ++h) ssc[h * kThreads + tid] = valid ? s[h] : -INFINITY;
-    __syncthreads();
-    // online softmax update, one wave per head
-    const int w = tid >> 6, ln = tid & 63;
-    for (int h = w; h < G; h += kThreads / 64) {
-      float mx = -INFINITY;
-      for (int j = ln; j < kThreads; j += 64) mx = fmaxf(mx, ssc[h * kThreads + j]);
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float mnew = fmaxf(sm[h], mx);
-      float sum = 0.f;
-      for (int j = ln; j < kThreads; j += 64) {
-        const float p = exp2f(ssc[h * kThreads + j] - mnew);
-        ssc[h * kThreads + j] = p;
-        sum += p;
-      }
-      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-      if (ln == 0) {
-        const float al = exp2f(sm[h] - mnew);
-        salpha[h] = al;
-        sl[h] = sl[h] * al + sum;
-        sm[h] = mnew;
-      }
-    }
-    __syncthreads();
-    const int n = (int)((t_end - base) < kThreads ? (t_end - base) : kThreads);
-    for (int e = tid; e < G * accw; e += kThreads) {
-      const int h = e / accw, x = e % accw;
-      float a = sacc[h * kHeadDim + x] * salpha[h];
-      if (comp) {
-        for (int j = 0; j < n; ++j) a += ssc[h * kThreads + j] * Store<T>::load(Cv, (size_t)(base + j) * R + x);
       } else {
-        for (int j = 0; j < n; ++j)
-          a += ssc[h * kThreads + j] *
-               Store<T>::load(rv, (size_t)x * D.slots + (size_t)((base + j) % D.slots));
+        const float *row = reinterpret_cast<const float *>(tk) + n16 * R + rho * (R / 4);
+        float cf[R / 4];
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) cf[c] = row[c];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          floatx4 a = zero4();
+#pragma unroll
+          for (int c = 0; c < R / 4; ++c) a = mfma4(__uint_as_float(F[mb][c / 4][c % 4]), cf[c], a);
+          ka[mb] = a;
+        }
       }
-      sacc[h * kHeadDim + x] = a;
+      const floatx4 sc = rope_scores(ka);
+      if ((it & 31) == 31) anchor(w_begin + 16 * (int64_t)(it + 1) + n16);   // bound the recurrence
+      float p[4];
+      softmax_tile<NBV>(sc, 0xf, m, l, vacc, rho, p);
+      // values: C_V tokens 4*rho..+3 of coefficient 16*nb + n16, transposed reads
+      if constexpr (BF) {
+        unsigned h0, l0, h1, l1;
+        split2(p[0], p[1], h0, l0);
+        split2(p[2], p[3], h1, l1);
+        const uint16_t *tl = reinterpret_cast<const uint16_t *>(tv);
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) {
+          const int c = 16 * nb + n16;
+          const unsigned x0 = tl[(4 * rho + 0) * R + c], x1 = tl[(4 * rho + 1) * R + c];
+          const unsigned x2 = tl[(4 * rho + 2) * R + c], x3 = tl[(4 * rho + 3) * R + c];
+          const uint2_ v = {x0 | (x1 << 16), x2 | (x3 << 16)};
+          vacc[nb] = mfma16(uint2_{h0, h1}, v, vacc[nb]);
+          vacc[nb] = mfma16(uint2_{l0, l1}, v, vacc[nb]);
+        }
+      } else {
+        const float *tf = reinterpret_cast<const float *>(tv);
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
+      }
+    }
+    // per-wave results: acc[head 4*rho+i][coef 16*nb + n16] (over the rings)
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[wave][4 * rho + i][16 * nb + n16] = vacc[nb][i];
+  } else {
+    // ================= exact window tokens =================
+    floatx4 wacc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) wacc[nb] = zero4();
+    if (nt > 0) anchor(w_begin + n16);
+    prepare_query();
+    if (nt > 0) {
+      const T *RK = reinterpret_cast<const T *>(P.ringk) + (size_t)u * D.slots * kHeadDim;
+      const T *RV = reinterpret_cast<const T *>(P.ringv) + (size_t)u * D.slots * kHeadDim;
+      for (int it = 0; it < nt; ++it) {
+        const int64_t t0 = w_begin + 16 * (int64_t)it;
+        const int slot = (int)((t0 + n16) % D.slots);
+        const int slot0 = (int)(t0 % D.slots);          // tiles never wrap (16 | slots)
+        floatx4 ka[8];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          const T *src = RK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho;
+          if constexpr (BF) {
+            const uint2_ v = *reinterpret_cast<const uint2_ *>(src);
+            ka[mb] = floatx4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+          } else {
+            ka[mb] = *reinterpret_cast<const floatx4 *>(src);
+          }
+        }
+        const floatx4 sc = rope_scores(ka);
+        int vm = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vm |= (t0 + 4 * rho + i < w_end) ? (1 << i) : 0;
+        float p[4];
+        softmax_tile<8>(sc, vm, m, l, wacc, rho, p);
+        if constexpr (BF) {
+          unsigned h0, l0, h1, l1;
+          split2(p[0], p[1], h0, l0);
+          split2(p[2], p[3], h1, l1);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const uint2_ v = *reinterpret_cast<const uint2_ *>(
+                RV + (size_t)(16 * nb + n16) * D.slots + slot0 + 4 * rho);
+            wacc[nb] = mfma16(uint2_{h0, h1}, v, wacc[nb]);
+            wacc[nb] = mfma16(uint2_{l0, l1}, v, wacc[nb]);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(
+                RV + (size_t)(16 * nb + n16) * D.slots + slot0 + 4 * rho);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wacc[nb] = mfma4(p[i], v[i], wacc[nb]);
+          }
+        }
+        if ((it & 31) == 31) anchor(t0 + 16 + n16);
+      }
     }
     __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[wave][4 * rho + i][16 * nb + n16] = wacc[nb][i];
   }
-  // partial record
-  float *rec = M.sh.rec + ((size_t)u * D.max_rec + split) * G * kRecStride;
-  for (int e = tid; e < G * (2 + kHeadDim); e += kThreads) {
-    const int h = e / (2 + kHeadDim), x = e % (2 + kHeadDim);
-    float v;
-    if (x == 0) v = sm[h];
-    else if (x == 1) v = sl[h];
-    else v = sacc[h * kHeadDim + x - 2];
-    rec[(size_t)h * kRecStride + x] = v;
+  const float lt = row_sum(l);
+  if (rho == 0) {
+    s_m[wave][n16] = m;
+    s_l[wave][n16] = lt;
   }
-  const int total = plan.n_comp + plan.n_win;
-  if (!arrive_last(M, u, total, &s_flag)) return;
-  merge_records<R>(M, layer, u, total, plan.n_comp, out, lds);
+  __syncthreads();
+
+  // ---- combine the four waves into this split's record
+  const int width = comp ? R : kHeadDim;
+  const size_t rec0 = ((size_t)u * D.max_rec + split) * G;
+  for (int e = threadIdx.x; e < G * (2 + width); e += kThreads) {
+    const int h = e / (2 + width), x = e % (2 + width);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_m[w][h]);
+    if (x == 0) {
+      M.sh.recml[(rec0 + h) * 2] = mx;
+      continue;
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
+      v += wt * (x == 1 ? s_l[w][h] : s_acc[w][h][x - 2]);
+    }
+    if (x == 1) M.sh.recml[(rec0 + h) * 2 + 1] = v;
+    else M.sh.rec[(rec0 + h) * kRecStride + x - 2] = v;
+  }
 }
 
-template <int R, typename T>
-hipError_t launch_simple(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                         int64_t length, int64_t n_c, hipStream_t s) {
+// ---------------------------------------------------------------------------
+// Merge of the split records of one unit (sequence, KV head) per workgroup:
+// log-sum-exp weights w_s = 2^(m_s - max m), L = sum w_s l_s,
+// acc_C = sum over compressed splits of w_s acc_s (r wide), acc_W likewise over
+// window splits (128 wide); out = (B_V acc_C + acc_W) / L for each query head.
+// Latency-bound: every global load (record accumulators, m/l pairs, the value
+// basis) is issued before any of them is used.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int layer, float *out,
+                                                                SplitPlan plan) {
+  extern __shared__ floatx4 s_bv[];       // value basis, [128][R/4] float4
+  __shared__ float s_w[4096];             // weight per (record, head)
+  __shared__ float s_part[16][16];
+  __shared__ float s_mx[16], s_L[16];
+  __shared__ floatx4 s_red[kThreads];
+  __shared__ float s_acc[16][R + kHeadDim];
   const Dims &D = M.D;
+  const int G = D.group, tid = threadIdx.x, u = blockIdx.x;
+  const int n_rec = plan.n_comp + plan.n_win;
+  const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
+  const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
+  LayerPtrs P = layer_ptrs(M, layer);
+  const floatx4 *Bv = reinterpret_cast<const floatx4 *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
+
+  // ---- issue: value basis -> LDS, m/l pairs, record accumulators
+  for (int e = tid; e < kHeadDim * R / 4; e += kThreads) s_bv[e] = Bv[e];
+  float mlm[16], mll[16];
+  int nml = 0;
+  for (int e = tid; e < n_rec * G && nml < 16; e += kThreads, ++nml) {
+    mlm[nml] = ml[2 * e];
+    mll[nml] = ml[2 * e + 1];
+  }
+  // record items: (kind, float4 column, record group); thread -> fixed column
+  // and group, records strided by the group count
+  const int cols_c = G * R / 4, cols_w = G * kHeadDim / 4;
+  constexpr int NVC = 12, NVW = 4;          // prefetched float4 per thread (compressed, window)
+  floatx4 vc[NVC], vw[NVW];
+  struct Item { int col, grp, groups; };
+  auto item_of = [&](int kind, int c0) -> Item {
+    const int cols = kind == 0 ? cols_c : cols_w;
+    const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
+    return Item{c0 + tid % nc, tid / nc, kThreads / nc};
+  };
+  // the first column chunk of each kind is prefetched (all columns when
+  // G * width / 4 <= 256)
+  const Item ic = item_of(0, 0), iw = item_of(1, 0);
+  {
+    const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
+#pragma unroll
+    for (int k = 0; k < NVC; ++k) {
+      const int s = ic.grp + k * ic.groups;
+      if (ic.grp < ic.groups && s < plan.n_comp)
+        vc[k] = *reinterpret_cast<const floatx4 *>(acc + ((size_t)s * G + hc) * kRecStride + xc);
+    }
+    const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
+#pragma unroll
+    for (int k = 0; k < NVW; ++k) {
+      const int s = iw.grp + k * iw.groups;
+      if (iw.grp < iw.groups && s < plan.n_win)
+        vw[k] = *reinterpret_cast<const floatx4 *>(acc + ((size_t)(plan.n_comp + s) * G + hw) * kRecStride + xw);
+    }
+  }
+
+  // ---- weights
+  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = mlm[k];
+  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads) s_w[e] = ml[2 * e];
+  __syncthreads();
+  {
+    const int h = tid & 15, part = tid >> 4;
+    float mx = -INFINITY;
+    if (h < G)
+      for (int s = part; s < n_rec; s += 16) mx = fmaxf(mx, s_w[s * G + h]);
+    s_part[part][h] = mx;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mx = -INFINITY;
+    for (int p = 0; p < 16; ++p) mx = fmaxf(mx, s_part[p][tid]);
+    s_mx[tid] = mx;
+  }
+  __syncthreads();
+  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]);
+  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads)
+    s_w[e] = __builtin_amdgcn_exp2f(s_w[e] - s_mx[e % G]);
+  {
+    // L: sum of w * l, partials per (part, head)
+    float l = 0.f;
+    for (int k = 0, e = tid; k < nml; ++k, e += kThreads)
+      l += __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]) * mll[k];
+    s_red[tid] = floatx4{l, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  if (tid < G) {
+    float l = 0.f;
+    for (int t = tid; t < kThreads && t < n_rec * G; t += G) l += s_red[t][0];
+    for (int e = 16 * kThreads + tid; e < n_rec * G; e += G)
+      l += s_w[e] * ml[2 * e + 1];
+    s_L[tid] = l;
+  }
+  __syncthreads();
+
+  // ---- weighted sums over the records of each kind, float4 columns
+  for (int kind = 0; kind < 2; ++kind) {
+    const int width = kind == 0 ? R : kHeadDim;
+    const int s0 = kind == 0 ? 0 : plan.n_comp;
+    const int n = kind == 0 ? plan.n_comp : plan.n_win;
+    if (n == 0) {
+      for (int e = tid; e < G * width; e += kThreads) s_acc[e / width][(kind ? R : 0) + e % width] = 0.f;
+      continue;
+    }
+    const int cols = kind == 0 ? cols_c : cols_w;
+    for (int c0 = 0; c0 < cols; c0 += kThreads) {
+      const Item I = item_of(kind, c0);
+      (void)I;
+      const int h = (I.col * 4) / width, x = (I.col * 4) % width;
+      floatx4 a = zero4();
+      if (I.grp < I.groups) {
+        int s = I.grp;
+        if (c0 == 0) {                       // prefetched part
+          if (kind == 0) {
+#pragma unroll
+            for (int k = 0; k < NVC; ++k, s += I.groups)
+              if (s < n) a += s_w[(s0 + s) * G + h] * vc[k];
+          } else {
+#pragma unroll
+            for (int k = 0; k < NVW; ++k, s += I.groups)
+              if (s < n) a += s_w[(s0 + s) * G + h] * vw[k];
+          }
+        }
+        for (; s < n; s += I.groups)
+          a += s_w[(s0 + s) * G + h] *
+               *reinterpret_cast<const floatx4 *>(acc + ((size_t)(s0 + s) * G + h) * kRecStride + x);
+      }
+      s_red[tid] = a;
+      __syncthreads();
+      const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
+      if (tid < nc) {
+        floatx4 t = s_red[tid];
+        for (int g = 1; g < kThreads / nc; ++g) t += s_red[g * nc + tid];
+        const int cc = c0 + tid, hh = (cc * 4) / width, xx = (cc * 4) % width;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_acc[hh][(kind ? R : 0) + xx + j] = t[j];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- out = (B_V acc_C + acc_W) / L
+  const int b = u / D.kv_heads, hk = u % D.kv_heads;
+  for (int e = tid; e < G * kHeadDim; e += kThreads) {
+    const int h = e / kHeadDim, f = e % kHeadDim;
+    float a = s_acc[h][R + f];
+    if (plan.n_comp > 0) {
+#pragma unroll
+      for (int c4 = 0; c4 < R / 4; ++c4) {
+        const floatx4 bv = s_bv[f * (R / 4) + c4];
+        a += bv[0] * s_acc[h][4 * c4] + bv[1] * s_acc[h][4 * c4 + 1] +
+             bv[2] * s_acc[h][4 * c4 + 2] + bv[3] * s_acc[h][4 * c4 + 3];
+      }
+    }
+    out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a / s_L[h];
+  }
+}
+
+int target_workgroups() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = std::getenv("ISKV_DECODE_WORKGROUPS");
+    v = e ? std::atoi(e) : 0;
+    if (v <= 0) v = 1024;
+  }
+  return v;
+}
+
+SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
   SplitPlan plan{};
   const int64_t n_e = length - n_c;
+  const int target = target_workgroups();
   if (n_e > 0) {
+    // about 4 tiles per wave for the window
     int64_t nw = (n_e + 255) / 256;
     if (nw > D.max_rec / 2) nw = D.max_rec / 2;
     plan.n_win = (int)nw;
-    plan.win_len = (int)((n_e + nw - 1) / nw);
+    plan.win_len = (int)(((n_e + nw - 1) / nw + 15) / 16 * 16);
+    plan.n_win = (int)((n_e + plan.win_len - 1) / plan.win_len);
   }
-  const int target = 1024;
-  const int want = (target + D.units - 1) / D.units;
   if (n_c > 0) {
-    int64_t nc = (n_c + 255) / 256;
+    int64_t want = (target + D.units - 1) / D.units - plan.n_win;
+    if (want < 1) want = 1;
+    int64_t nc = (n_c + 127) / 128;                  // at least 2 tiles per wave
     if (nc > want) nc = want;
     if (nc > D.max_rec - plan.n_win) nc = D.max_rec - plan.n_win;
     if (nc < 1) nc = 1;
     plan.comp_len = (int)(((n_c + nc - 1) / nc + 63) / 64 * 64);
     plan.n_comp = (int)((n_c + plan.comp_len - 1) / plan.comp_len);
   }
-  const size_t bytes = (size_t)(16 * kHeadDim + kHeadDim * (R + 1) + 16 * kThreads + 16 * kHeadDim) * 4;
+  return plan;
+}
+
+template <int R, typename T>
+hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
+                       int64_t length, int64_t n_c, hipStream_t s) {
+  const SplitPlan plan = make_plan(M.D, length, n_c);
+  dim3 grid(plan.n_comp + plan.n_win, M.D.units);
+  constexpr int dyn = Cfg<R, T>::kDynBytes;
+  static bool dattr = false;
+  hipError_t e;
+  if (!dattr) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<R, T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+    if (e != hipSuccess) return e;
+    dattr = true;
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<R, T>), grid, dim3(kThreads), dyn, s, M, layer, q, q_pos,
+                     out, length, n_c, plan);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   static bool attr = false;
+  const size_t bv_bytes = (size_t)kHeadDim * R * 4;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_simple_kernel<R, T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_merge_kernel<R>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bv_bytes);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid(plan.n_comp + plan.n_win, D.units);
-  hipLaunchKernelGGL((decode_simple_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, layer, q,
-                     q_pos, out, length, n_c, plan);
+  hipLaunchKernelGGL((decode_merge_kernel<R>), dim3(M.D.units), dim3(kThreads), bv_bytes, s, M,
+                     layer, out, plan);
   return hipGetLastError();
 }
 
@@ -286,10 +738,10 @@ template <typename T>
 hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                            int64_t length, int64_t n_c, hipStream_t s) {
   switch (M.D.r) {
-    case 16: return launch_simple<16, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 32: return launch_simple<32, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 64: return launch_simple<64, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 128: return launch_simple<128, T>(M, layer, q, q_pos, out, length, n_c, s);
+    case 16: return launch_mfma<16, T>(M, layer, q, q_pos, out, length, n_c, s);
+    case 32: return launch_mfma<32, T>(M, layer, q, q_pos, out, length, n_c, s);
+    case 64: return launch_mfma<64, T>(M, layer, q, q_pos, out, length, n_c, s);
+    case 128: return launch_mfma<128, T>(M, layer, q, q_pos, out, length, n_c, s);
   }
   return hipErrorInvalidValue;
 }

@@ -16,7 +16,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/iskv.h"
+#include "iskv.h"
 #include "iskv_internal.hpp"
 
 using namespace iskv;
@@ -68,11 +68,12 @@ Dims make_dims(const iskv_config *c) {
   D.scale_log2 = (float)(scale * 1.4426950408889634);
   D.rope_base = c->rope_base;
   D.units = c->batch * c->num_kv_heads;
-  // enough decode records to split the history over ~2 waves of workgroups on
-  // 256 compute units, plus the window splits
+  // decode split records per unit: enough to spread the history over a few
+  // waves of workgroups on 256 compute units, plus the window splits; the
+  // merge keeps every (record, head) max and sum of a unit in LDS (<= 4096)
   int per_unit = (4096 + D.units - 1) / D.units;
   if (per_unit < 16) per_unit = 16;
-  if (per_unit > 512) per_unit = 512;
+  if (per_unit * D.group > 4096) per_unit = 4096 / D.group;
   D.max_rec = per_unit;
   D.rope_anchors = (c->max_tokens + kBlock) / kRopeAnchor + 2;
   return D;
@@ -174,6 +175,7 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   M.lay = c->G.layer;
   M.D = c->D;
   M.sh.rec = reinterpret_cast<float *>(base + c->G.rec);
+  M.sh.recml = reinterpret_cast<float *>(base + c->G.recml);
   M.sh.cnt = reinterpret_cast<unsigned *>(base + c->G.cnt);
   M.sh.flags = reinterpret_cast<int *>(base + c->G.flags);
   M.sh.fold = reinterpret_cast<float *>(base + c->G.fold);

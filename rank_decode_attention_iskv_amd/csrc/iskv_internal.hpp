@@ -10,8 +10,9 @@
 //   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
 //   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
 // plus, shared by all layers:
-//   rec    float [U][max_rec][G][REC_STRIDE]  split-K partial records of decode
-//   cnt    uint  [U]                          arrival counters (self-resetting)
+//   rec    float [U][max_rec][G][128]         split-K partial accumulators of decode
+//   recml  float [U][max_rec][G][2]           split-K running max m and sum l
+//   cnt    uint  [U]                          (reserved)
 //   flags  int                                numeric flags (ISKV_FLAG_*)
 //   fold   float [L][U][2][FOLD_SCRATCH(r)]   block-update scratch (Q^T, P, B_new)
 //   rope   float                              RoPE tables (see rope_tables below)
@@ -27,7 +28,7 @@ namespace iskv {
 
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 64;
-constexpr int kRecStride = 2 + kHeadDim + 2;   // m, l, acc[128], pad
+constexpr int kRecStride = kHeadDim;           // accumulator floats per (record, head)
 constexpr int kRopeAnchor = 64;                 // positions per anchor of the RoPE table
 
 struct Dims {
@@ -50,6 +51,7 @@ struct LayerPtrs {
 
 struct Shared {
   float *rec;
+  float *recml;
   unsigned *cnt;
   int *flags;
   float *fold;            // base of the fold scratch (all layers)
@@ -87,7 +89,7 @@ inline LayerLayout layer_layout(const Dims &D) {
 
 struct GlobalLayout {
   LayerLayout layer;
-  size_t layers_base, rec, cnt, flags, fold, rope_anchor, rope_step, total;
+  size_t layers_base, rec, recml, cnt, flags, fold, rope_anchor, rope_step, total;
 };
 
 inline GlobalLayout global_layout(const Dims &D) {
@@ -96,6 +98,7 @@ inline GlobalLayout global_layout(const Dims &D) {
   size_t o = 0;
   G.layers_base = o; o = align_up(o + G.layer.bytes * D.layers);
   G.rec = o;   o = align_up(o + (size_t)D.units * D.max_rec * D.group * kRecStride * 4);
+  G.recml = o; o = align_up(o + (size_t)D.units * D.max_rec * D.group * 2 * 4);
   G.cnt = o;   o = align_up(o + (size_t)D.units * 4);
   G.flags = o; o = align_up(o + 4);
   G.fold = o;  o = align_up(o + (size_t)D.layers * D.units * 2 * fold_scratch_floats(D.r) * 4);
