@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libiskv.so")
 
-SOURCES = ["iskv.cpp", "maintain.hip", "decode.hip"]
+SOURCES = ["iskv.cpp", "maintain.hip", "fold.hip", "decode.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

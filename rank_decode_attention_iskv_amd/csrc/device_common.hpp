@@ -56,4 +56,37 @@ __device__ __forceinline__ void rope_cs(const Shared &S, int64_t pos, int i, flo
 
 __device__ __forceinline__ void set_flag(const Shared &S, int f) { atomicOr(S.flags, f); }
 
+// MFMA operand types and wrappers (gfx950).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4_ __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uint4_ __attribute__((ext_vector_type(4)));
+typedef unsigned uint2_ __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// (a, b) -> packed bf16 high parts (round to nearest even) and low parts.
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
+  const bf16x2 h = __builtin_convertvector((floatx2){a, b}, bf16x2);
+  const unsigned hb = __builtin_bit_cast(unsigned, h);
+  const float ha = __uint_as_float(hb << 16), hh = __uint_as_float(hb & 0xffff0000u);
+  const bf16x2 l = __builtin_convertvector((floatx2){a - ha, b - hh}, bf16x2);
+  hi = hb;
+  lo = __builtin_bit_cast(unsigned, l);
+}
+
+__device__ __forceinline__ floatx4 mfma32(uint4_ a, uint4_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(uint2_ a, uint2_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_, a),
+                                                   __builtin_bit_cast(short4_, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 }  // namespace iskv

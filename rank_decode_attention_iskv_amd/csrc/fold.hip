@@ -1,0 +1,785 @@
+// Brand block-incremental SVD fold for gfx950 -- one workgroup per (selected
+// layer, unit, K|V), every operand resident in LDS.
+//
+// Page: "iS-KV -- Basis-synchronized online low-rank KV compression -- What does
+// it mean?" (learnaivisually.com), Jargon "Block-incremental SVD" and the drift
+// paragraph: the 64 tokens that leave the exact window are folded into the
+// rank-r basis as one block, on a small core whose size does not depend on the
+// history length.
+//
+// With the old history H = U diag(S) B^T (U orthonormal; the stored
+// coefficients are U diag(S)) and a new block A (64 x d):
+//   P = A B, Res = A - P B^T (projected twice);
+//   Res = L Q with Q (64 x d) orthonormal rows, orthogonal to B (CholeskyQR2,
+//     with a pivot guard that drops directions at the rounding level);
+//   [H; A] = diag(U, I) K [B Q^T]^T,  K = [[diag S, 0], [P, A Q^T]]  ((r+64)^2);
+//   K = U' diag(s') V'^T;  B_new = [B Q^T] V'[:, :r];  S_new = s'[:r];
+//   old coefficients map by M = B^T B_new; the block's are A B_new.
+// The SVD of K is a one-sided (Hestenes) Jacobi on the rows of K: rows are
+// rotated pairwise (round-robin ordering, 8 lanes per pair) until mutually
+// orthogonal, after which row j = s'_j v'_j^T.
+#include <cfloat>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "iskv_internal.hpp"
+
+namespace iskv {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kMaxSweeps = 40;
+constexpr float kJacobiTol = 1.0e-6f;     // rotate while |y_p . y_q| > tol |y_p||y_q|
+// A residual direction is dropped when its squared norm is below
+// kGuard * ||A||_F^2 (so kept directions have condition number < ~1/sqrt(kGuard)).
+constexpr float kGuard = 1.0e-7f;
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// LDS plan in floats.  Row strides are padded by 4 floats: rows stay 16-byte
+// aligned and consecutive rows start in different LDS banks.
+template <int R>
+struct FoldLayout {
+  static constexpr int D = kHeadDim, TB = kBlock;
+  static constexpr bool kRes = R < D;           // a residual space exists
+  static constexpr int N = R + TB;              // core rows
+  static constexpr int NC = kRes ? N : R;       // core columns
+  static constexpr int LA = D + 4, LB = R + 4, LG = TB + 4, LC = NC + 4;
+  static constexpr int oB = 0;                               // B (d x r), r < d only
+  static constexpr int oQ = oB + (kRes ? D * LB : 0);        // Res -> Q; later B_new
+  static constexpr int oA = oQ + cmax(TB * LA, D * LB);      // A
+  static constexpr int oP = oA + TB * LA;                    // P
+  static constexpr int oG = oP + TB * LB;                    // Gram / L / A Q^T
+  static constexpr int end12 = oG + (kRes ? TB * LG : 0);
+  static constexpr int oCore = kRes ? oA : 0;                // core over A, P, G
+  static constexpr int endCore = oCore + N * LC;
+  static constexpr int oNrm = cmax(end12, endCore);
+  static constexpr int oSig = oNrm + N;
+  static constexpr int oPerm = oSig + N;
+  static constexpr int oAct = oPerm + N;
+  static constexpr int oInv = oAct + R;
+  static constexpr int oRem = oInv + cmax(TB, R);
+  static constexpr int oVec = oRem + D;
+  static constexpr int oDot = oVec + D;
+  static constexpr int floats = oDot + R;
+  static constexpr size_t bytes = (size_t)floats * 4;
+  static_assert(oQ % 4 == 0 && oA % 4 == 0 && oP % 4 == 0 && oG % 4 == 0 && oCore % 4 == 0,
+                "16-byte aligned regions");
+};
+
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void st4(float *p, const float4 &v) { *reinterpret_cast<float4 *>(p) = v; }
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Sum over aligned groups of GS = 4 or 8 lanes (identical result in every
+// lane of the group): DPP quad permutations, then the half-row mirror.
+template <int GS>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(GS == 4 || GS == 8, "group size");
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (GS == 8)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// A zero the compiler cannot see through.  Added to an LDS pointer before a
+// fully unrolled loop, it keeps the base in one register with small
+// immediate offsets, instead of one materialized absolute address per access
+// (LDS offsets above 64 KiB do not fit the instruction's offset field).
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// C(m, n) = sum_k A(m, k) B(k, n) over 16-byte-aligned operands, 4 x 4
+// outputs per thread tile, handed to out(m, n, value).
+//   A(m, k) = A[m * lda + k] (AT = false)  or  A[k * lda + m] (AT = true)
+//   B(k, n) = B[k * ldb + n] (BT = false)  or  B[n * ldb + k] (BT = true)
+// With BT the tile's four n are strided by N/4, so the lanes of a wave read
+// rows that start in different banks.
+// ---------------------------------------------------------------------------
+template <int M, int N, int K, bool AT, bool BT, typename Out>
+__device__ __forceinline__ void gemm4(const float *A, int lda, const float *B, int ldb, Out out) {
+  static_assert(M % 4 == 0 && N % 4 == 0 && K % 4 == 0, "tile multiples");
+  constexpr int TN = N / 4, TILES = (M / 4) * TN;
+  for (int tile = threadIdx.x; tile < TILES; tile += kThreads) {
+    const int m0 = (tile / TN) * 4, tn = tile % TN;
+    int nn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nn[j] = BT ? tn + j * TN : tn * 4 + j;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      float a[4][4], b[4][4];     // a[m][k], b[k][n]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (!AT) {
+          const float4 v = ld4(A + (m0 + i) * lda + k0);
+          a[i][0] = v.x; a[i][1] = v.y; a[i][2] = v.z; a[i][3] = v.w;
+        } else {
+          const float4 v = ld4(A + (k0 + i) * lda + m0);
+          a[0][i] = v.x; a[1][i] = v.y; a[2][i] = v.z; a[3][i] = v.w;
+        }
+        if constexpr (!BT) {
+          const float4 v = ld4(B + (k0 + i) * ldb + nn[0]);
+          b[i][0] = v.x; b[i][1] = v.y; b[i][2] = v.z; b[i][3] = v.w;
+        } else {
+          const float4 v = ld4(B + nn[i] * ldb + k0);
+          b[0][i] = v.x; b[1][i] = v.y; b[2][i] = v.z; b[3][i] = v.w;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i][kk], b[kk][j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out(m0 + i, nn[j], acc[i][j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The 64 x d block leaving the window, from the ring, as float rows in LDS
+// (row stride LA).  Keys are stored [slot][d], values [d][slot].  Returns this
+// thread's share of ||A||_F^2.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float (&v)[8]) {
+  const float4 a = ld4(p), b = ld4(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t *p, float (&v)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+
+template <typename T, int LA>
+__device__ float load_block(const T *ring, int X, int s0, int slots, float *sA) {
+  constexpr int D = kHeadDim, TB = kBlock;
+  float asq = 0.f;
+  if (X == 0) {
+    for (int i = threadIdx.x; i < TB * D / 8; i += kThreads) {
+      const int t = i / (D / 8), f0 = (i % (D / 8)) * 8;
+      float v[8];
+      load8<T>(ring + (size_t)(s0 + t) * D + f0, v);
+      st4(sA + t * LA + f0, make_float4(v[0], v[1], v[2], v[3]));
+      st4(sA + t * LA + f0 + 4, make_float4(v[4], v[5], v[6], v[7]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asq = fmaf(v[j], v[j], asq);
+    }
+  } else {
+    for (int i = threadIdx.x; i < TB * D / 8; i += kThreads) {
+      const int f = i / (TB / 8), t0 = (i % (TB / 8)) * 8;
+      float v[8];
+      load8<T>(ring + (size_t)f * slots + s0 + t0, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sA[(t0 + j) * LA + f] = v[j];
+        asq = fmaf(v[j], v[j], asq);
+      }
+    }
+  }
+  return asq;
+}
+
+// ---------------------------------------------------------------------------
+// Lower Cholesky factor of the n x n matrix G (row stride ldg, lower part
+// read), in place, by the whole workgroup, in blocks of 8 columns: every
+// thread factors the 8 x 8 diagonal block in registers (the same values in
+// all threads, no exchange), one thread per row below solves its 8 panel
+// entries, then the trailing matrix takes the rank-8 update.  Two barriers
+// per block.  A pivot <= tau drops its column (L_:j = 0), exactly as in the
+// unblocked right-looking order.  L ends in the lower part of G (upper part
+// zeroed), 1/L_jj (0 where dropped) in invd.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_rcp(float x) {
+  float r = __builtin_amdgcn_rcpf(x);
+  return r * fmaf(-x, r, 2.f);               // one Newton step
+}
+
+template <int n>
+__device__ __forceinline__ void chol_lds(float *G, int ldg, float tau, float *invd) {
+  constexpr int BS = 8, TPR = kThreads / n, KMAX = (n + TPR - 1) / TPR;
+  static_assert(n % BS == 0 && kThreads % n == 0, "block shape");
+  const int tid = threadIdx.x;
+  const int ri = tid / TPR, rc = tid % TPR;     // trailing-update row and lane
+  for (int J = 0; J < n; J += BS) {
+    // diagonal block (lower part), right-looking in registers
+    float l[BS][BS], inv[BS];
+#pragma unroll
+    for (int a = 0; a < BS; ++a)
+#pragma unroll
+      for (int c = 0; c <= a; ++c) l[a][c] = G[(J + a) * ldg + J + c];
+#pragma unroll
+    for (int c = 0; c < BS; ++c) {
+      const float piv = l[c][c];
+      const float ljj = piv > tau ? __builtin_amdgcn_sqrtf(piv) : 0.f;
+      inv[c] = ljj > 0.f ? fast_rcp(ljj) : 0.f;
+      l[c][c] = ljj;
+#pragma unroll
+      for (int a = c + 1; a < BS; ++a) l[a][c] *= inv[c];
+#pragma unroll
+      for (int a = c + 1; a < BS; ++a)
+#pragma unroll
+        for (int b = c + 1; b <= a; ++b) l[a][b] = fmaf(-l[a][c], l[b][c], l[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < BS; ++a) {               // static indices keep l in registers
+      if (tid == a) {
+#pragma unroll
+        for (int c = 0; c <= a; ++c) G[(J + a) * ldg + J + c] = l[a][c];
+        invd[J + a] = inv[a];
+      }
+    }
+    // panel: rows below the block, L_iJ = G_iJ L_JJ^{-T}
+    for (int i = J + BS + tid; i < n; i += kThreads) {
+      const float4 g0 = ld4(G + i * ldg + J), g1 = ld4(G + i * ldg + J + 4);
+      float x[BS] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int c = 0; c < BS; ++c) {
+        float acc = x[c];
+#pragma unroll
+        for (int k = 0; k < c; ++k) acc = fmaf(-x[k], l[c][k], acc);
+        x[c] = acc * inv[c];
+      }
+      st4(G + i * ldg + J, make_float4(x[0], x[1], x[2], x[3]));
+      st4(G + i * ldg + J + 4, make_float4(x[4], x[5], x[6], x[7]));
+    }
+    __syncthreads();
+    // trailing update G_ik -= L_iJ . L_kJ  (J + 8 <= k <= i): reads first
+    if (ri >= J + BS) {
+      const float4 a0 = ld4(G + ri * ldg + J), a1 = ld4(G + ri * ldg + J + 4);
+      constexpr int CH = KMAX < 8 ? KMAX : 8;     // reads batched per chunk
+#pragma unroll
+      for (int u0 = 0; u0 < KMAX; u0 += CH) {
+        float4 k0[CH], k1[CH];
+        float gi[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const int k = J + BS + rc + (u0 + u) * TPR;
+          const bool ok = k <= ri;
+          k0[u] = ok ? ld4(G + k * ldg + J) : make_float4(0.f, 0.f, 0.f, 0.f);
+          k1[u] = ok ? ld4(G + k * ldg + J + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+          gi[u] = ok ? G[ri * ldg + k] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const int k = J + BS + rc + (u0 + u) * TPR;
+          float v = gi[u];
+          v = fmaf(-a0.x, k0[u].x, v); v = fmaf(-a0.y, k0[u].y, v);
+          v = fmaf(-a0.z, k0[u].z, v); v = fmaf(-a0.w, k0[u].w, v);
+          v = fmaf(-a1.x, k1[u].x, v); v = fmaf(-a1.y, k1[u].y, v);
+          v = fmaf(-a1.z, k1[u].z, v); v = fmaf(-a1.w, k1[u].w, v);
+          if (k <= ri) G[ri * ldg + k] = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < n * n; e += kThreads) {
+    const int r = e / n, k = e % n;
+    if (k > r) G[r * ldg + k] = 0.f;
+  }
+  __syncthreads();
+}
+
+// x <- L^{-1} x for a vector held in registers (L lower triangular, row
+// stride ldl, invd = 1/diag or 0).  Four partial sums shorten the chains.
+template <int n>
+__device__ __forceinline__ void fwd_solve(float (&x)[n], const float *L0, int ldl,
+                                          const float *invd0) {
+  const int z = opaque_zero();
+  const float *L = L0 + z, *invd = invd0 + z;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 + 4 <= i; k0 += 4) {
+      const float4 l = ld4(L + i * ldl + k0);
+      s[0] = fmaf(l.x, x[k0], s[0]);
+      s[1] = fmaf(l.y, x[k0 + 1], s[1]);
+      s[2] = fmaf(l.z, x[k0 + 2], s[2]);
+      s[3] = fmaf(l.w, x[k0 + 3], s[3]);
+    }
+#pragma unroll
+    for (int k = i & ~3; k < i; ++k) s[k & 3] = fmaf(L[i * ldl + k], x[k], s[k & 3]);
+    x[i] = (x[i] - ((s[0] + s[1]) + (s[2] + s[3]))) * invd[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-sided Jacobi on the N rows (length NC, stride LC) of `core`.  A pair
+// (x, y) is rotated while |x.y| > tol |x||y|; the three dot products are
+// recomputed for every pair (norms carried over from earlier rotations would
+// drift by more than the off-diagonal being removed when two norms are
+// close).  Rows whose squared norm is below (64 eps)^2 times the largest are
+// at the rounding level of the core and are left alone.  Returns the number
+// of sweeps that rotated (kMaxSweeps if it did not converge).
+// ---------------------------------------------------------------------------
+template <int N, int NC, int LC>
+__device__ int jacobi_rows(float *core, int *flag, int *maxbits) {
+  constexpr int GS = NC % 32 == 0 ? 8 : 4;      // lanes per pair
+  constexpr int NP = N / 2, CPT = NC / (4 * GS);
+  static_assert(NC % (4 * GS) == 0 && N % 2 == 0, "row shape");
+  constexpr float kNegl = (64.f * FLT_EPSILON) * (64.f * FLT_EPSILON);
+  const int tid = threadIdx.x, li = tid & (GS - 1);
+  int sweep = 0;
+  for (; sweep < kMaxSweeps; ++sweep) {
+    if (tid == 0) { *flag = 0; *maxbits = 0; }
+    __syncthreads();
+    for (int j = tid; j < N; j += kThreads) {
+      const float *row = core + j * LC;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll 4
+      for (int i = 0; i < NC; i += 4) {
+        const float4 v = ld4(row + i);
+        s0 = fmaf(v.x, v.x, s0); s1 = fmaf(v.y, v.y, s1);
+        s0 = fmaf(v.z, v.z, s0); s1 = fmaf(v.w, v.w, s1);
+      }
+      atomicMax(maxbits, __float_as_int(s0 + s1));
+    }
+    __syncthreads();
+    const float negl = kNegl * __int_as_float(*maxbits);
+    for (int k = 0; k < N - 1; ++k) {
+      for (int g = tid / GS; g < NP; g += kThreads / GS) {
+        int p, q;
+        if (g == 0) { p = k; q = N - 1; }
+        else { p = (k + g) % (N - 1); q = (k - g + N - 1) % (N - 1); }
+        float *rp = core + p * LC + 4 * li, *rq = core + q * LC + 4 * li;
+        float4 x[CPT], y[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          x[i] = ld4(rp + 4 * GS * i);
+          y[i] = ld4(rq + 4 * GS * i);
+        }
+        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          a0 = fmaf(x[i].x, x[i].x, a0); a1 = fmaf(x[i].y, x[i].y, a1);
+          a0 = fmaf(x[i].z, x[i].z, a0); a1 = fmaf(x[i].w, x[i].w, a1);
+          b0 = fmaf(y[i].x, y[i].x, b0); b1 = fmaf(y[i].y, y[i].y, b1);
+          b0 = fmaf(y[i].z, y[i].z, b0); b1 = fmaf(y[i].w, y[i].w, b1);
+          c0 = fmaf(x[i].x, y[i].x, c0); c1 = fmaf(x[i].y, y[i].y, c1);
+          c0 = fmaf(x[i].z, y[i].z, c0); c1 = fmaf(x[i].w, y[i].w, c1);
+        }
+        const float a = group_sum<GS>(a0 + a1), b = group_sum<GS>(b0 + b1), c = group_sum<GS>(c0 + c1);
+        if (c != 0.f && a > negl && b > negl &&
+            fabsf(c) > kJacobiTol * (__builtin_amdgcn_sqrtf(a) * __builtin_amdgcn_sqrtf(b))) {
+          // tan of the angle that zeroes the pair's inner product (the
+          // smaller root), then cos by rsqrt refined with one Newton step
+          const float zeta = (b - a) * __builtin_amdgcn_rcpf(2.f * c);
+          const float az = fabsf(zeta);
+          const float t = copysignf(az > 1.0e18f ? 0.5f * __builtin_amdgcn_rcpf(az)
+                                                 : __builtin_amdgcn_rcpf(
+                                                       az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.f))),
+                                    zeta);
+          const float s2 = fmaf(t, t, 1.f);
+          float cs = __builtin_amdgcn_rsqf(s2);
+          cs = cs * fmaf(-0.5f * s2 * cs, cs, 1.5f);
+          const float sn = cs * t;
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            const float4 u = x[i], v = y[i];
+            st4(rp + 4 * GS * i, make_float4(cs * u.x - sn * v.x, cs * u.y - sn * v.y,
+                                         cs * u.z - sn * v.z, cs * u.w - sn * v.w));
+            st4(rq + 4 * GS * i, make_float4(sn * u.x + cs * v.x, sn * u.y + cs * v.y,
+                                         sn * u.z + cs * v.z, sn * u.w + cs * v.w));
+          }
+          if (li == 0) *flag = 1;
+        }
+      }
+      __syncthreads();
+    }
+    const int rotated = *flag;
+    __syncthreads();
+    if (!rotated) break;
+  }
+  return sweep;
+}
+
+template <int R, typename T>
+__global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSel sel,
+                                                                int64_t n_c) {
+  using Ly = FoldLayout<R>;
+  constexpr int D = kHeadDim, TB = kBlock, N = Ly::N, NC = Ly::NC;
+  constexpr int LA = Ly::LA, LB = Ly::LB, LG = Ly::LG, LC = Ly::LC;
+  constexpr bool kRes = Ly::kRes;
+  extern __shared__ float4 lds4[];
+  float *lds = reinterpret_cast<float *>(lds4);
+  __shared__ float red[kThreads / 64];
+  __shared__ int s_int[4];
+  __shared__ float s_f[4];
+  const Dims &Dm = M.D;
+  const int layer = sel.idx[blockIdx.y];
+  const int ux = blockIdx.x, u = ux >> 1, X = ux & 1;
+  const int tid = threadIdx.x;
+  LayerPtrs P = layer_ptrs(M, layer);
+  float *basis = P.basis + (size_t)ux * D * R;
+  float *sing = P.sing + (size_t)ux * R;
+  float *msync = P.msync + (size_t)ux * R * R;
+  T *coef = reinterpret_cast<T *>(P.coef) + (size_t)ux * Dm.max_tokens * R;
+  const T *ring = reinterpret_cast<const T *>(X == 0 ? P.ringk : P.ringv) +
+                  (size_t)u * Dm.slots * D;
+  const int s0 = (int)(n_c % Dm.slots);
+
+  float *sB = lds + Ly::oB, *sQ = lds + Ly::oQ, *sA = lds + Ly::oA, *sP = lds + Ly::oP;
+  float *sG = lds + Ly::oG, *core = lds + Ly::oCore;
+  float *sig = lds + Ly::oSig, *invd = lds + Ly::oInv;
+  int *perm = reinterpret_cast<int *>(lds + Ly::oPerm);
+  int *act = reinterpret_cast<int *>(lds + Ly::oAct);
+  float *sBn = sQ;                  // B_new (d x LB) once Q is consumed
+  const float *Bsrc;
+  int ldB;
+  if constexpr (kRes) { Bsrc = sB; ldB = LB; } else { Bsrc = basis; ldB = R; }
+
+  // ---------------- phase 1: load, projection (twice) ----------------
+  const float asq = load_block<T, LA>(ring, X, s0, Dm.slots, sA);
+  if constexpr (kRes) {
+    for (int i = tid; i < D * R / 4; i += kThreads) {
+      const int f = (4 * i) / R, c = (4 * i) % R;
+      st4(sB + f * LB + c, ld4(basis + 4 * i));
+    }
+  }
+  const float normA2 = block_sum(asq, red);     // barriers inside
+  gemm4<TB, R, D, false, false>(sA, LA, Bsrc, ldB,
+                                [&](int t, int c, float v) { sP[t * LB + c] = v; });
+  __syncthreads();
+  if constexpr (kRes) {
+    // Res = A - P B^T
+    gemm4<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
+      sQ[t * LA + f] = sA[t * LA + f] - v;
+    });
+    __syncthreads();
+    // second projection: T = Res B (in the G region), Res -= T B^T, P += T
+    gemm4<TB, R, D, false, false>(sQ, LA, sB, LB,
+                                  [&](int t, int c, float v) { sG[t * LB + c] = v; });
+    __syncthreads();
+    gemm4<TB, D, R, false, true>(sG, LB, sB, LB,
+                                 [&](int t, int f, float v) { sQ[t * LA + f] -= v; });
+    for (int i = tid; i < TB * R; i += kThreads) {
+      const int t = i / R, c = i % R;
+      sP[t * LB + c] += sG[t * LB + c];
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: Q by CholeskyQR2 ----------------
+    // pass 0 drops directions with sigma^2 <= kGuard ||A||^2 (float noise of
+    // the projection); pass 1 sees ~unit rows and drops those that lost
+    // their norm.
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      gemm4<TB, TB, D, false, true>(sQ, LA, sQ, LA,
+                                    [&](int a, int b, float v) { sG[a * LG + b] = v; });
+      __syncthreads();
+      chol_lds<TB>(sG, LG, pass == 0 ? kGuard * normA2 : 0.25f, invd);
+      if (tid < D) {
+        float x[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) x[t] = sQ[t * LA + tid];
+        fwd_solve<TB>(x, sG, LG, invd);
+#pragma unroll
+        for (int t = 0; t < TB; ++t) sQ[t * LA + tid] = x[t];
+      }
+      __syncthreads();
+    }
+    // re-orthogonalize Q against B
+    gemm4<TB, R, D, false, false>(sQ, LA, sB, LB,
+                                  [&](int t, int c, float v) { sG[t * LB + c] = v; });
+    __syncthreads();
+    gemm4<TB, D, R, false, true>(sG, LB, sB, LB,
+                                 [&](int t, int f, float v) { sQ[t * LA + f] -= v; });
+    __syncthreads();
+    // A Q^T (64 x 64) into the G region
+    gemm4<TB, TB, D, false, true>(sA, LA, sQ, LA,
+                                  [&](int t, int j, float v) { sG[t * LG + j] = v; });
+    __syncthreads();
+  }
+
+  // ---------------- phase 3: core ----------------
+  {
+    constexpr int PER = TB * NC / kThreads;
+    static_assert(TB * NC % kThreads == 0, "core rows per thread");
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + j * kThreads, t = e / NC, c = e % NC;
+      if constexpr (kRes) v[j] = c < R ? sP[t * LB + c] : sG[t * LG + (c - R)];
+      else v[j] = sP[t * LB + c];
+    }
+    __syncthreads();
+    int bad = !isfinite(normA2);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + j * kThreads, t = e / NC, c = e % NC;
+      bad |= !isfinite(v[j]);
+      core[(R + t) * LC + c] = v[j];
+    }
+    for (int e = tid; e < R * NC; e += kThreads) {
+      const int i = e / NC, c = e % NC;
+      const float x = (c == i) ? sing[i] : 0.f;
+      bad |= !isfinite(x);
+      core[i * LC + c] = x;
+    }
+    if (bad) set_flag(M.sh, 1);
+    __syncthreads();
+  }
+
+  // ---------------- phase 4: one-sided Jacobi ----------------
+  {
+    const int sweeps = jacobi_rows<N, NC, LC>(core, &s_int[0], &s_int[2]);
+    if (sweeps >= kMaxSweeps && tid == 0) set_flag(M.sh, 2);
+  }
+
+  // ---------------- phase 5: singular values, descending order -------------
+  for (int j = tid; j < N; j += kThreads) {
+    const float *row = core + j * LC;
+    float s0a = 0.f, s1a = 0.f;
+    for (int i = 0; i < NC; i += 4) {
+      const float4 w = ld4(row + i);
+      s0a = fmaf(w.x, w.x, s0a); s1a = fmaf(w.y, w.y, s1a);
+      s0a = fmaf(w.z, w.z, s0a); s1a = fmaf(w.w, w.w, s1a);
+    }
+    sig[j] = sqrtf(s0a + s1a);
+  }
+  __syncthreads();
+  for (int j = tid; j < N; j += kThreads) {
+    const float sj = sig[j];
+    int rank = 0;
+    for (int i = 0; i < N; ++i) rank += (sig[i] > sj) || (sig[i] == sj && i < j);
+    perm[rank] = j;
+  }
+  __syncthreads();
+
+  // ---------------- phase 6: B_new = [B Q^T] V'[:, :r] ----------------
+  const float sig0 = sig[perm[0]];
+  const float tol_null = 64.f * N * FLT_EPSILON * sig0;
+  if (!isfinite(sig0) && tid == 0) set_flag(M.sh, 1);
+  {
+    constexpr int TK = R / 4, TILES = (D / 4) * TK, TPT = (TILES + kThreads - 1) / kThreads;
+    float acc[TPT][4][4];
+#pragma unroll
+    for (int tt = 0; tt < TPT; ++tt) {
+      const int tile = tid + tt * kThreads;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[tt][i][j] = 0.f;
+      if (tile < TILES) {
+        const int f0 = (tile / TK) * 4, k0 = (tile % TK) * 4;
+        const float *zr[4];
+        float zs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = perm[k0 + j];
+          zr[j] = core + row * LC;
+          zs[j] = sig[row] > tol_null ? 1.f / sig[row] : 0.f;
+        }
+#pragma unroll 2
+        for (int c0 = 0; c0 < R; c0 += 4) {
+          float xb[4][4], z[4][4];     // xb[f][c], z[k][c]
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 w = ld4(Bsrc + (f0 + i) * ldB + c0);
+            xb[i][0] = w.x; xb[i][1] = w.y; xb[i][2] = w.z; xb[i][3] = w.w;
+            const float4 y = ld4(zr[i] + c0);
+            z[i][0] = y.x; z[i][1] = y.y; z[i][2] = y.z; z[i][3] = y.w;
+          }
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[tt][i][j] = fmaf(xb[i][cc], z[j][cc], acc[tt][i][j]);
+        }
+        if constexpr (kRes) {
+#pragma unroll 2
+          for (int j0 = 0; j0 < TB; j0 += 4) {
+            float xq[4][4], z[4][4];   // xq[j][f] = Q[j0 + j][f0 + f], z[k][j]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 w = ld4(sQ + (j0 + i) * LA + f0);
+              xq[i][0] = w.x; xq[i][1] = w.y; xq[i][2] = w.z; xq[i][3] = w.w;
+              const float4 y = ld4(zr[i] + R + j0);
+              z[i][0] = y.x; z[i][1] = y.y; z[i][2] = y.z; z[i][3] = y.w;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[tt][i][j] = fmaf(xq[jj][i], z[j][jj], acc[tt][i][j]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[tt][i][j] *= zs[j];
+      }
+    }
+    __syncthreads();              // Q and the core are no longer read
+#pragma unroll
+    for (int tt = 0; tt < TPT; ++tt) {
+      const int tile = tid + tt * kThreads;
+      if (tile < TILES) {
+        const int f0 = (tile / TK) * 4, k0 = (tile % TK) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st4(sBn + (f0 + i) * LB + k0,
+              make_float4(acc[tt][i][0], acc[tt][i][1], acc[tt][i][2], acc[tt][i][3]));
+      }
+    }
+  }
+  // null completion: each column whose singular value is ~0 becomes the unit
+  // vector with the largest remainder against the columns kept so far, made
+  // orthogonal to them by two Gram-Schmidt passes.
+  float *rem = lds + Ly::oRem, *vec = lds + Ly::oVec, *dot = lds + Ly::oDot;
+  for (int k = tid; k < R; k += kThreads) act[k] = sig[perm[k]] > tol_null;
+  __syncthreads();
+  for (int k = 0; k < R; ++k) {
+    if (act[k]) continue;                      // uniform: act is shared
+    for (int e = tid; e < D; e += kThreads) {
+      float s = 0.f;
+      for (int c = 0; c < R; ++c) s += act[c] ? sBn[e * LB + c] * sBn[e * LB + c] : 0.f;
+      rem[e] = 1.f - s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int best = 0;
+      for (int e = 1; e < D; ++e)
+        if (rem[e] > rem[best]) best = e;
+      s_int[1] = best;
+    }
+    __syncthreads();
+    for (int e = tid; e < D; e += kThreads) vec[e] = (e == s_int[1]) ? 1.f : 0.f;
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int c = tid; c < R; c += kThreads) {
+        float s = 0.f;
+        if (act[c])
+          for (int f = 0; f < D; ++f) s += sBn[f * LB + c] * vec[f];
+        dot[c] = s;
+      }
+      __syncthreads();
+      for (int f = tid; f < D; f += kThreads) {
+        float s = vec[f];
+        for (int c = 0; c < R; ++c) s -= sBn[f * LB + c] * dot[c];
+        vec[f] = s;
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      float s = 0.f;
+      for (int f = 0; f < D; ++f) s += vec[f] * vec[f];
+      s_f[1] = sqrtf(s);
+    }
+    __syncthreads();
+    for (int f = tid; f < D; f += kThreads) sBn[f * LB + k] = vec[f] / s_f[1];
+    __syncthreads();
+    if (tid == 0) act[k] = 1;
+    __syncthreads();
+  }
+  __syncthreads();
+
+  // Re-orthonormalize B_new (one CholeskyQR pass on its columns): the Jacobi
+  // stopping tolerance leaves the columns orthogonal only to ~1e-6, which
+  // would otherwise accumulate fold after fold.
+  {
+    float *sGb = lds + Ly::oA;     // R x LB, over the dead A / core region
+    gemm4<R, R, D, true, false>(sBn, LB, sBn, LB,
+                                [&](int a, int b, float v) { sGb[a * LB + b] = v; });
+    __syncthreads();
+    chol_lds<R>(sGb, LB, 0.25f, invd);
+    if (tid < D) {
+      float x[R];
+#pragma unroll
+      for (int c = 0; c < R; ++c) x[c] = sBn[tid * LB + c];
+      fwd_solve<R>(x, sGb, LB, invd);
+#pragma unroll
+      for (int c = 0; c < R; ++c) sBn[tid * LB + c] = x[c];
+    }
+    __syncthreads();
+  }
+
+  // ---------------- phase 7: M, block coefficients, new basis --------------
+  gemm4<R, R, D, true, false>(Bsrc, ldB, sBn, LB,
+                              [&](int c, int k, float v) { msync[c * R + k] = v; });
+  // the block again (the core region over A is free now)
+  (void)load_block<T, LA>(ring, X, s0, Dm.slots, sA);
+  __syncthreads();
+  gemm4<TB, R, D, false, false>(sA, LA, sBn, LB, [&](int t, int k, float v) {
+    Store<T>::store(coef, (size_t)(n_c + t) * R + k, v);
+  });
+  __syncthreads();                 // M (which reads the old basis) is done
+  for (int i = tid; i < D * R / 4; i += kThreads) {
+    const int f = (4 * i) / R, c = (4 * i) % R;
+    st4(basis + 4 * i, ld4(sBn + f * LB + c));
+  }
+  if (tid < R) sing[tid] = sig[perm[tid]];
+}
+
+template <int R, typename T>
+hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
+  static bool attr = false;
+  const size_t bytes = FoldLayout<R>::bytes;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&block_update_kernel<R, T>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid(M.D.units * 2, sel.n);
+  hipLaunchKernelGGL((block_update_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, sel, n_c);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
+  switch (M.D.r) {
+    case 16: return launch_fold_t<16, T>(M, sel, n_c, s);
+    case 32: return launch_fold_t<32, T>(M, sel, n_c, s);
+    case 64: return launch_fold_t<64, T>(M, sel, n_c, s);
+    case 128: return launch_fold_t<128, T>(M, sel, n_c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
+  return M.D.storage == 1 ? dispatch_fold<bf16_t>(M, sel, n_c, s)
+                          : dispatch_fold<float>(M, sel, n_c, s);
+}
+
+}  // namespace iskv

@@ -178,7 +178,6 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   M.sh.recml = reinterpret_cast<float *>(base + c->G.recml);
   M.sh.cnt = reinterpret_cast<unsigned *>(base + c->G.cnt);
   M.sh.flags = reinterpret_cast<int *>(base + c->G.flags);
-  M.sh.fold = reinterpret_cast<float *>(base + c->G.fold);
   M.sh.rope_anchor = reinterpret_cast<const float *>(base + c->G.rope_anchor);
   M.sh.rope_step = reinterpret_cast<const float *>(base + c->G.rope_step);
 

@@ -14,7 +14,6 @@
 //   recml  float [U][max_rec][G][2]           split-K running max m and sum l
 //   cnt    uint  [U]                          (reserved)
 //   flags  int                                numeric flags (ISKV_FLAG_*)
-//   fold   float [L][U][2][FOLD_SCRATCH(r)]   block-update scratch (Q^T, P, B_new)
 //   rope   float                              RoPE tables (see rope_tables below)
 // with T = float or bf16 (uint16 bit pattern) per the storage dtype.
 #pragma once
@@ -54,19 +53,11 @@ struct Shared {
   float *recml;
   unsigned *cnt;
   int *flags;
-  float *fold;            // base of the fold scratch (all layers)
   const float *rope_anchor;   // [anchors][64 freq][2] cos, sin of (a * 64) * theta_i
   const float *rope_step;     // [64 offsets][64 freq][2] cos, sin of o * theta_i
 };
 
 inline __host__ __device__ size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
-
-inline __host__ __device__ size_t fold_scratch_floats(int r) {
-  // Q rows (64 x d), P (64 x r), R_r^T (64 x 64), B_new (d x r)
-  size_t n = (size_t)kBlock * kHeadDim + (size_t)kBlock * r + (size_t)kBlock * kBlock +
-             (size_t)kHeadDim * r;
-  return (n + 63) / 64 * 64;
-}
 
 struct LayerLayout {
   size_t basis, sing, msync, frag, coef, ringk, ringv, bytes;
@@ -89,7 +80,7 @@ inline LayerLayout layer_layout(const Dims &D) {
 
 struct GlobalLayout {
   LayerLayout layer;
-  size_t layers_base, rec, recml, cnt, flags, fold, rope_anchor, rope_step, total;
+  size_t layers_base, rec, recml, cnt, flags, rope_anchor, rope_step, total;
 };
 
 inline GlobalLayout global_layout(const Dims &D) {
@@ -101,7 +92,6 @@ inline GlobalLayout global_layout(const Dims &D) {
   G.recml = o; o = align_up(o + (size_t)D.units * D.max_rec * D.group * 2 * 4);
   G.cnt = o;   o = align_up(o + (size_t)D.units * 4);
   G.flags = o; o = align_up(o + 4);
-  G.fold = o;  o = align_up(o + (size_t)D.layers * D.units * 2 * fold_scratch_floats(D.r) * 4);
   G.rope_anchor = o; o = align_up(o + (size_t)D.rope_anchors * 64 * 2 * 4);
   G.rope_step = o;   o = align_up(o + (size_t)kRopeAnchor * 64 * 2 * 4);
   G.total = o;
