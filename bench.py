@@ -46,7 +46,25 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only stream a 256 MiB float32 tensor through an elementwise kernel "
+                         "(x * 1 -> y) five times: the reference for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain streaming kernel of known traffic: reads and writes 256 MiB per
+    dispatch.  HBM byte counters read on it give the scale factor between the
+    counter and real bytes."""
+    import torch
+    n = 64 << 20
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "torch.mul(x, 1.0, out=y), float32", "dispatches": 5,
+                      "bytes_read_per_dispatch": 4 * n, "bytes_written_per_dispatch": 4 * n}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -96,7 +114,7 @@ def kernel_source_hash():
 def committed_traffic(kernel_hash):
     """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "decode_attn_config2_counters.txt")
+    path = os.path.join(ROOT, "profiles", "decode_attn_r32_ctx32k_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -118,14 +136,21 @@ def committed_traffic(kernel_hash):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries=4):
-    import numpy as np
+    from threadpoolctl import threadpool_limits
 
+    # the oracle is plain numpy; its BLAS calls are held to one thread so the
+    # figure is per core and reproducible
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries)
+
+
+def _cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries, sample_heads=3):
     import workloads
     from oracle import Unit
 
-    cores = len(os.sched_getaffinity(0))
+    cores = 1
     w = workloads.with_(workloads.WORKLOADS[2], window=window, rank=rank, context=context)
-    u = Unit(w.head_dim, rank, window, context + 64, "bf16")
+    units = [Unit(w.head_dim, rank, window, context + 64, "bf16") for _ in range(sample_heads)]
     t0 = time.perf_counter()
     fold_t = 0.0
     folds = 0
@@ -133,33 +158,36 @@ def cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries=4):
     while pos < context:
         n = min(64, context - pos)
         k, v = workloads.tokens(w, 0, pos, n)
-        for i in range(n):
-            u.append(k[0, i, 0], v[0, i, 0])
+        for h, u in enumerate(units):
+            for i in range(n):
+                u.append(k[0, i, h], v[0, i, h])
         pos += n
-        if u.ready:
-            f0 = time.perf_counter()
-            u.fold()
-            u.sync()
-            fold_t += time.perf_counter() - f0
-            folds += 1
+        for u in units:
+            if u.ready:
+                f0 = time.perf_counter()
+                u.fold()
+                u.sync()
+                fold_t += time.perf_counter() - f0
+                folds += 1
     build_t = time.perf_counter() - t0
     g = q_heads // kv_heads
     d0 = time.perf_counter()
     for s in range(decode_queries):
-        q = workloads.query(w, 0, s)[0, :g]
-        u.decode(q, u.length - 1, 1.0 / math.sqrt(w.head_dim))
-    dec_t = (time.perf_counter() - d0) / decode_queries
+        q = workloads.query(w, 0, s)[0]
+        for h, u in enumerate(units):
+            u.decode(q[h * g:(h + 1) * g], u.length - 1, 1.0 / math.sqrt(w.head_dim))
+    dec_t = (time.perf_counter() - d0) / (decode_queries * sample_heads)
     # one decode step of the layer: kv_heads units decode; every 64 steps each
-    # unit folds + syncs at the current history length (the sample's last
-    # folds are the most expensive; use the average over the sample)
+    # unit folds + syncs at the current history length (averaged over the
+    # sample's whole growth to `context`)
     fold_avg = fold_t / max(folds, 1)
     step_s = kv_heads * (dec_t + fold_avg / 64.0)
     return {
         "value": 1.0 / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"one KV head (K and V) of the layer built to {context} tokens by the oracle "
-                   f"({folds} folds + syncs, {build_t:.1f} s), then {decode_queries} decode calls of "
-                   f"{g} query heads ({dec_t * 1e3:.1f} ms each); per step = {kv_heads} heads x "
-                   f"(decode + average fold+sync / 64)"),
+        "sample": (f"{sample_heads} KV heads (K and V each) of the layer built to {context} tokens by the "
+                   f"float64 oracle ({folds} folds + syncs, {build_t:.1f} s), then {decode_queries} decode "
+                   f"calls of {g} query heads per KV head ({dec_t * 1e3:.1f} ms each); one step = "
+                   f"{kv_heads} KV heads x (decode + average fold+sync / 64); BLAS held to one thread"),
         "oracle_decode_ms_per_head": dec_t * 1e3,
         "oracle_fold_sync_ms_avg": fold_avg * 1e3,
     }
@@ -171,6 +199,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
               "not part of this build", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     from rank_decode_attention_iskv_amd import binding
