@@ -151,7 +151,9 @@ int iskv_discard_sync(iskv_ctx *c, int layer);
  * the configured scale; values accumulated in coefficient space and mapped
  * back by the value basis.  dev_q: float [batch][num_q_heads][head_dim], before
  * RoPE.  dev_out: float [batch][num_q_heads][head_dim].  Query head h reads KV
- * head h / (num_q_heads / num_kv_heads).  ESTATE if the layer is empty. */
+ * head h / (num_q_heads / num_kv_heads).  q_pos must lie in [0, max_tokens + 128)
+ * (the range of the RoPE tables built at init), else EINVAL.  ESTATE if the
+ * layer is empty. */
 int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out);
 
 /* Synchronizes the stream; fills *st for one layer.  Returns ISKV_ENUMERIC if

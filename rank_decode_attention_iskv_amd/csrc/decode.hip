@@ -59,6 +59,22 @@ struct SplitPlan {
   int win_len;       // tokens per window split (multiple of 16)
 };
 
+// A float store performed at agent scope (coherent across the XCDs' L2s).
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads performed at agent scope: they read what other XCDs stored with
+// store_agent, whatever this XCD's L2 holds.
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ floatx4 load4_agent(const float *p) {
+  return floatx4{load_agent(p), load_agent(p + 1), load_agent(p + 2), load_agent(p + 3)};
+}
+
 // reductions over the four lane rows (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -123,6 +139,196 @@ __device__ __forceinline__ void softmax_tile(floatx4 sc, int valid_mask, float &
 }
 
 // ---------------------------------------------------------------------------
+// Merge of the split records of one unit (sequence, KV head), run by the last
+// split workgroup of the unit to finish:
+// log-sum-exp weights w_s = 2^(m_s - max m), L = sum w_s l_s,
+// acc_C = sum over compressed splits of w_s acc_s (r wide), acc_W likewise over
+// window splits (128 wide); out = (B_V acc_C + acc_W) / L for each query head.
+// Latency-bound: every global load (record accumulators, m/l pairs, the value
+// basis) is issued before any of them is used.
+// ---------------------------------------------------------------------------
+template <int R> struct MergeLds {
+  static constexpr int oBv = 0;                            // value basis [128][R/4] float4
+  static constexpr int oW = oBv + kHeadDim * R * 4;        // weight per (record, head) [4096]
+  static constexpr int oPart = oW + 4096 * 4;              // [16][16]
+  static constexpr int oMx = oPart + 16 * 16 * 4;          // [16]
+  static constexpr int oL = oMx + 16 * 4;                  // [16]
+  static constexpr int oRed = oL + 16 * 4;                 // [256] float4
+  static constexpr int oAcc = oRed + kThreads * 16;        // [16][R + 128]
+  static constexpr int bytes = oAcc + 16 * (R + kHeadDim) * 4;
+};
+
+template <int R>
+__device__ void merge_unit(const Model &M, int layer, float *out, const SplitPlan &plan, int u,
+                           uint8_t *lds) {
+  using ML = MergeLds<R>;
+  floatx4 *s_bv = reinterpret_cast<floatx4 *>(lds + ML::oBv);
+  float *s_w = reinterpret_cast<float *>(lds + ML::oW);
+  float (*s_part)[16] = reinterpret_cast<float (*)[16]>(lds + ML::oPart);
+  float *s_mx = reinterpret_cast<float *>(lds + ML::oMx);
+  float *s_L = reinterpret_cast<float *>(lds + ML::oL);
+  floatx4 *s_red = reinterpret_cast<floatx4 *>(lds + ML::oRed);
+  float (*s_acc)[R + kHeadDim] = reinterpret_cast<float (*)[R + kHeadDim]>(lds + ML::oAcc);
+  const Dims &D = M.D;
+  const int G = D.group, tid = threadIdx.x;
+  const int n_rec = plan.n_comp + plan.n_win;
+  const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
+  const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
+  LayerPtrs P = layer_ptrs(M, layer);
+  const floatx4 *Bv = reinterpret_cast<const floatx4 *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
+
+  // ---- issue: value basis -> LDS, m/l pairs, record accumulators
+  for (int e = tid; e < kHeadDim * R / 4; e += kThreads) s_bv[e] = Bv[e];
+  float mlm[16], mll[16];
+  int nml = 0;
+  for (int e = tid; e < n_rec * G && nml < 16; e += kThreads, ++nml) {
+    mlm[nml] = load_agent(ml + 2 * e);
+    mll[nml] = load_agent(ml + 2 * e + 1);
+  }
+  // record items: (kind, float4 column, record group); thread -> fixed column
+  // and group, records strided by the group count
+  const int cols_c = G * R / 4, cols_w = G * kHeadDim / 4;
+  constexpr int NVC = 12, NVW = 4;          // prefetched float4 per thread (compressed, window)
+  floatx4 vc[NVC], vw[NVW];
+  struct Item { int col, grp, groups; };
+  auto item_of = [&](int kind, int c0) -> Item {
+    const int cols = kind == 0 ? cols_c : cols_w;
+    const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
+    return Item{c0 + tid % nc, tid / nc, kThreads / nc};
+  };
+  // the first column chunk of each kind is prefetched (all columns when
+  // G * width / 4 <= 256)
+  const Item ic = item_of(0, 0), iw = item_of(1, 0);
+  {
+    const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
+#pragma unroll
+    for (int k = 0; k < NVC; ++k) {
+      const int s = ic.grp + k * ic.groups;
+      if (ic.grp < ic.groups && s < plan.n_comp)
+        vc[k] = load4_agent(acc + ((size_t)s * G + hc) * kRecStride + xc);
+    }
+    const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
+#pragma unroll
+    for (int k = 0; k < NVW; ++k) {
+      const int s = iw.grp + k * iw.groups;
+      if (iw.grp < iw.groups && s < plan.n_win)
+        vw[k] = load4_agent(acc + ((size_t)(plan.n_comp + s) * G + hw) * kRecStride + xw);
+    }
+  }
+
+  // ---- weights
+  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = mlm[k];
+  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads) s_w[e] = load_agent(ml + 2 * e);
+  __syncthreads();
+  {
+    const int h = tid & 15, part = tid >> 4;
+    float mx = -INFINITY;
+    if (h < G)
+      for (int s = part; s < n_rec; s += 16) mx = fmaxf(mx, s_w[s * G + h]);
+    s_part[part][h] = mx;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mx = -INFINITY;
+    for (int p = 0; p < 16; ++p) mx = fmaxf(mx, s_part[p][tid]);
+    s_mx[tid] = mx;
+  }
+  __syncthreads();
+  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]);
+  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads)
+    s_w[e] = __builtin_amdgcn_exp2f(s_w[e] - s_mx[e % G]);
+  {
+    // L: sum of w * l, partials per (part, head)
+    float l = 0.f;
+    for (int k = 0, e = tid; k < nml; ++k, e += kThreads)
+      l += __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]) * mll[k];
+    s_red[tid] = floatx4{l, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  if (tid < G) {
+    float l = 0.f;
+    for (int t = tid; t < kThreads && t < n_rec * G; t += G) l += s_red[t][0];
+    for (int e = 16 * kThreads + tid; e < n_rec * G; e += G)
+      l += s_w[e] * load_agent(ml + 2 * e + 1);
+    s_L[tid] = l;
+  }
+  __syncthreads();
+
+  // ---- weighted sums over the records of each kind, float4 columns
+  for (int kind = 0; kind < 2; ++kind) {
+    const int width = kind == 0 ? R : kHeadDim;
+    const int s0 = kind == 0 ? 0 : plan.n_comp;
+    const int n = kind == 0 ? plan.n_comp : plan.n_win;
+    if (n == 0) {
+      for (int e = tid; e < G * width; e += kThreads) s_acc[e / width][(kind ? R : 0) + e % width] = 0.f;
+      continue;
+    }
+    const int cols = kind == 0 ? cols_c : cols_w;
+    for (int c0 = 0; c0 < cols; c0 += kThreads) {
+      const Item I = item_of(kind, c0);
+      (void)I;
+      const int h = (I.col * 4) / width, x = (I.col * 4) % width;
+      floatx4 a = zero4();
+      if (I.grp < I.groups) {
+        int s = I.grp;
+        if (c0 == 0) {                       // prefetched part
+          if (kind == 0) {
+#pragma unroll
+            for (int k = 0; k < NVC; ++k, s += I.groups)
+              if (s < n) a += s_w[(s0 + s) * G + h] * vc[k];
+          } else {
+#pragma unroll
+            for (int k = 0; k < NVW; ++k, s += I.groups)
+              if (s < n) a += s_w[(s0 + s) * G + h] * vw[k];
+          }
+        }
+        // the rest in chunks of 8 records, every load of a chunk issued first
+        for (; s < n; s += 8 * I.groups) {
+          floatx4 v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int sk = s + k * I.groups;
+            v[k] = sk < n ? load4_agent(acc + ((size_t)(s0 + sk) * G + h) * kRecStride + x) : zero4();
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int sk = s + k * I.groups;
+            if (sk < n) a += s_w[(s0 + sk) * G + h] * v[k];
+          }
+        }
+      }
+      s_red[tid] = a;
+      __syncthreads();
+      const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
+      if (tid < nc) {
+        floatx4 t = s_red[tid];
+        for (int g = 1; g < kThreads / nc; ++g) t += s_red[g * nc + tid];
+        const int cc = c0 + tid, hh = (cc * 4) / width, xx = (cc * 4) % width;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_acc[hh][(kind ? R : 0) + xx + j] = t[j];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- out = (B_V acc_C + acc_W) / L
+  const int b = u / D.kv_heads, hk = u % D.kv_heads;
+  for (int e = tid; e < G * kHeadDim; e += kThreads) {
+    const int h = e / kHeadDim, f = e % kHeadDim;
+    float a = s_acc[h][R + f];
+    if (plan.n_comp > 0) {
+#pragma unroll
+      for (int c4 = 0; c4 < R / 4; ++c4) {
+        const floatx4 bv = s_bv[f * (R / 4) + c4];
+        a += bv[0] * s_acc[h][4 * c4] + bv[1] * s_acc[h][4 * c4 + 1] +
+             bv[2] * s_acc[h][4 * c4 + 2] + bv[3] * s_acc[h][4 * c4 + 3];
+      }
+    }
+    out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a / s_L[h];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tunables per (rank, storage): workgroups per CU and the per-wave LDS ring.
 // ---------------------------------------------------------------------------
 template <int R, typename T> struct Cfg {
@@ -134,7 +340,8 @@ template <int R, typename T> struct Cfg {
   static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
   static constexpr int kOcc = (BF && R <= 32) ? 2 : 1;
   static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
-  static constexpr int kDynBytes = (4 * kRingBytes > kAccBytes) ? 4 * kRingBytes : kAccBytes;
+  static constexpr int kLoopBytes = (4 * kRingBytes > kAccBytes) ? 4 * kRingBytes : kAccBytes;
+  static constexpr int kDynBytes = kLoopBytes > MergeLds<R>::bytes ? kLoopBytes : MergeLds<R>::bytes;
 };
 
 // ---------------------------------------------------------------------------
@@ -143,7 +350,7 @@ template <int R, typename T> struct Cfg {
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
-    int64_t n_c, SplitPlan plan) {
+    int64_t n_c, SplitPlan plan, int fused) {
   using C = Cfg<R, T>;
   constexpr bool BF = C::BF;
   constexpr int NBV = R / 16;                            // value N-blocks (compressed)
@@ -457,7 +664,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
 #pragma unroll
     for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_m[w][h]);
     if (x == 0) {
-      M.sh.recml[(rec0 + h) * 2] = mx;
+      store_agent(M.sh.recml + (rec0 + h) * 2, mx);
       continue;
     }
     float v = 0.f;
@@ -466,190 +673,61 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
       v += wt * (x == 1 ? s_l[w][h] : s_acc[w][h][x - 2]);
     }
-    if (x == 1) M.sh.recml[(rec0 + h) * 2 + 1] = v;
-    else M.sh.rec[(rec0 + h) * kRecStride + x - 2] = v;
+    if (x == 1) store_agent(M.sh.recml + (rec0 + h) * 2 + 1, v);
+    else store_agent(M.sh.rec + (rec0 + h) * kRecStride + x - 2, v);
   }
+
+  // ---- fused: the last split workgroup of this unit to finish merges all
+  // records (used when the whole grid is resident at once, so no merge holds
+  // a CU that later workgroups wait for).  Records are written with
+  // agent-scope stores (through to the coherence point shared by every XCD)
+  // and complete before the count is raised; the merging workgroup reads them
+  // with agent-scope loads.  No workgroup waits on another.
+  if (!fused) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    const unsigned done =
+        __hip_atomic_fetch_add(M.sh.cnt + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (done + 1 == gridDim.x) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_unit<R>(M, layer, out, plan, u, s_dyn);
+  if (threadIdx.x == 0) __hip_atomic_store(M.sh.cnt + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// Merge of the split records of one unit (sequence, KV head) per workgroup:
-// log-sum-exp weights w_s = 2^(m_s - max m), L = sum w_s l_s,
-// acc_C = sum over compressed splits of w_s acc_s (r wide), acc_W likewise over
-// window splits (128 wide); out = (B_V acc_C + acc_W) / L for each query head.
-// Latency-bound: every global load (record accumulators, m/l pairs, the value
-// basis) is issued before any of them is used.
-// ---------------------------------------------------------------------------
+// Unfused: one workgroup per unit merges after the split kernel.
 template <int R>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int layer, float *out,
                                                                 SplitPlan plan) {
-  extern __shared__ floatx4 s_bv[];       // value basis, [128][R/4] float4
-  __shared__ float s_w[4096];             // weight per (record, head)
-  __shared__ float s_part[16][16];
-  __shared__ float s_mx[16], s_L[16];
-  __shared__ floatx4 s_red[kThreads];
-  __shared__ float s_acc[16][R + kHeadDim];
-  const Dims &D = M.D;
-  const int G = D.group, tid = threadIdx.x, u = blockIdx.x;
-  const int n_rec = plan.n_comp + plan.n_win;
-  const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
-  const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
-  LayerPtrs P = layer_ptrs(M, layer);
-  const floatx4 *Bv = reinterpret_cast<const floatx4 *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
-
-  // ---- issue: value basis -> LDS, m/l pairs, record accumulators
-  for (int e = tid; e < kHeadDim * R / 4; e += kThreads) s_bv[e] = Bv[e];
-  float mlm[16], mll[16];
-  int nml = 0;
-  for (int e = tid; e < n_rec * G && nml < 16; e += kThreads, ++nml) {
-    mlm[nml] = ml[2 * e];
-    mll[nml] = ml[2 * e + 1];
-  }
-  // record items: (kind, float4 column, record group); thread -> fixed column
-  // and group, records strided by the group count
-  const int cols_c = G * R / 4, cols_w = G * kHeadDim / 4;
-  constexpr int NVC = 12, NVW = 4;          // prefetched float4 per thread (compressed, window)
-  floatx4 vc[NVC], vw[NVW];
-  struct Item { int col, grp, groups; };
-  auto item_of = [&](int kind, int c0) -> Item {
-    const int cols = kind == 0 ? cols_c : cols_w;
-    const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
-    return Item{c0 + tid % nc, tid / nc, kThreads / nc};
-  };
-  // the first column chunk of each kind is prefetched (all columns when
-  // G * width / 4 <= 256)
-  const Item ic = item_of(0, 0), iw = item_of(1, 0);
-  {
-    const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
-#pragma unroll
-    for (int k = 0; k < NVC; ++k) {
-      const int s = ic.grp + k * ic.groups;
-      if (ic.grp < ic.groups && s < plan.n_comp)
-        vc[k] = *reinterpret_cast<const floatx4 *>(acc + ((size_t)s * G + hc) * kRecStride + xc);
-    }
-    const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
-#pragma unroll
-    for (int k = 0; k < NVW; ++k) {
-      const int s = iw.grp + k * iw.groups;
-      if (iw.grp < iw.groups && s < plan.n_win)
-        vw[k] = *reinterpret_cast<const floatx4 *>(acc + ((size_t)(plan.n_comp + s) * G + hw) * kRecStride + xw);
-    }
-  }
-
-  // ---- weights
-  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = mlm[k];
-  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads) s_w[e] = ml[2 * e];
-  __syncthreads();
-  {
-    const int h = tid & 15, part = tid >> 4;
-    float mx = -INFINITY;
-    if (h < G)
-      for (int s = part; s < n_rec; s += 16) mx = fmaxf(mx, s_w[s * G + h]);
-    s_part[part][h] = mx;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float mx = -INFINITY;
-    for (int p = 0; p < 16; ++p) mx = fmaxf(mx, s_part[p][tid]);
-    s_mx[tid] = mx;
-  }
-  __syncthreads();
-  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]);
-  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads)
-    s_w[e] = __builtin_amdgcn_exp2f(s_w[e] - s_mx[e % G]);
-  {
-    // L: sum of w * l, partials per (part, head)
-    float l = 0.f;
-    for (int k = 0, e = tid; k < nml; ++k, e += kThreads)
-      l += __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]) * mll[k];
-    s_red[tid] = floatx4{l, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = 0.f;
-    for (int t = tid; t < kThreads && t < n_rec * G; t += G) l += s_red[t][0];
-    for (int e = 16 * kThreads + tid; e < n_rec * G; e += G)
-      l += s_w[e] * ml[2 * e + 1];
-    s_L[tid] = l;
-  }
-  __syncthreads();
-
-  // ---- weighted sums over the records of each kind, float4 columns
-  for (int kind = 0; kind < 2; ++kind) {
-    const int width = kind == 0 ? R : kHeadDim;
-    const int s0 = kind == 0 ? 0 : plan.n_comp;
-    const int n = kind == 0 ? plan.n_comp : plan.n_win;
-    if (n == 0) {
-      for (int e = tid; e < G * width; e += kThreads) s_acc[e / width][(kind ? R : 0) + e % width] = 0.f;
-      continue;
-    }
-    const int cols = kind == 0 ? cols_c : cols_w;
-    for (int c0 = 0; c0 < cols; c0 += kThreads) {
-      const Item I = item_of(kind, c0);
-      (void)I;
-      const int h = (I.col * 4) / width, x = (I.col * 4) % width;
-      floatx4 a = zero4();
-      if (I.grp < I.groups) {
-        int s = I.grp;
-        if (c0 == 0) {                       // prefetched part
-          if (kind == 0) {
-#pragma unroll
-            for (int k = 0; k < NVC; ++k, s += I.groups)
-              if (s < n) a += s_w[(s0 + s) * G + h] * vc[k];
-          } else {
-#pragma unroll
-            for (int k = 0; k < NVW; ++k, s += I.groups)
-              if (s < n) a += s_w[(s0 + s) * G + h] * vw[k];
-          }
-        }
-        for (; s < n; s += I.groups)
-          a += s_w[(s0 + s) * G + h] *
-               *reinterpret_cast<const floatx4 *>(acc + ((size_t)(s0 + s) * G + h) * kRecStride + x);
-      }
-      s_red[tid] = a;
-      __syncthreads();
-      const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
-      if (tid < nc) {
-        floatx4 t = s_red[tid];
-        for (int g = 1; g < kThreads / nc; ++g) t += s_red[g * nc + tid];
-        const int cc = c0 + tid, hh = (cc * 4) / width, xx = (cc * 4) % width;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s_acc[hh][(kind ? R : 0) + xx + j] = t[j];
-      }
-      __syncthreads();
-    }
-  }
-
-  // ---- out = (B_V acc_C + acc_W) / L
-  const int b = u / D.kv_heads, hk = u % D.kv_heads;
-  for (int e = tid; e < G * kHeadDim; e += kThreads) {
-    const int h = e / kHeadDim, f = e % kHeadDim;
-    float a = s_acc[h][R + f];
-    if (plan.n_comp > 0) {
-#pragma unroll
-      for (int c4 = 0; c4 < R / 4; ++c4) {
-        const floatx4 bv = s_bv[f * (R / 4) + c4];
-        a += bv[0] * s_acc[h][4 * c4] + bv[1] * s_acc[h][4 * c4 + 1] +
-             bv[2] * s_acc[h][4 * c4 + 2] + bv[3] * s_acc[h][4 * c4 + 3];
-      }
-    }
-    out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a / s_L[h];
-  }
+  extern __shared__ __align__(16) uint8_t s_mrg[];
+  merge_unit<R>(M, layer, out, plan, blockIdx.x, s_mrg);
 }
 
-int target_workgroups() {
+// Workgroups per decode call: about 16 tiles of 16 tokens per wave (enough to
+// amortize the per-workgroup set-up and keep the merge short), between 256
+// (one per CU) and 4096.  ISKV_DECODE_WORKGROUPS overrides it.
+int target_workgroups(const Dims &D, int64_t length) {
   static int v = -1;
   if (v < 0) {
     const char *e = std::getenv("ISKV_DECODE_WORKGROUPS");
     v = e ? std::atoi(e) : 0;
-    if (v <= 0) v = 1024;
+    if (v < 0) v = 0;
   }
-  return v;
+  if (v > 0) return v;
+  const int64_t tiles = (int64_t)D.units * ((length + 15) / 16);
+  int64_t t = (tiles + 63) / 64;
+  if (t < 256) t = 256;
+  if (t > 4096) t = 4096;
+  return (int)t;
 }
 
 SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
   SplitPlan plan{};
   const int64_t n_e = length - n_c;
-  const int target = target_workgroups();
+  const int target = target_workgroups(D, length);
   if (n_e > 0) {
     // about 4 tiles per wave for the window
     int64_t nw = (n_e + 255) / 256;
@@ -685,20 +763,23 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
     if (e != hipSuccess) return e;
     dattr = true;
   }
+  // fuse the merge when every workgroup is resident at once
+  const int64_t slots = 256LL * Cfg<R, T>::kOcc;
+  const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<R, T>), grid, dim3(kThreads), dyn, s, M, layer, q, q_pos,
-                     out, length, n_c, plan);
+                     out, length, n_c, plan, fused);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  static bool attr = false;
-  const size_t bv_bytes = (size_t)kHeadDim * R * 4;
-  if (!attr) {
+  if (e != hipSuccess || fused) return e;
+  constexpr int mbytes = MergeLds<R>::bytes;
+  static bool mattr = false;
+  if (!mattr) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_merge_kernel<R>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bv_bytes);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
     if (e != hipSuccess) return e;
-    attr = true;
+    mattr = true;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<R>), dim3(M.D.units), dim3(kThreads), bv_bytes, s, M,
-                     layer, out, plan);
+  hipLaunchKernelGGL((decode_merge_kernel<R>), dim3(M.D.units), dim3(kThreads), mbytes, s, M, layer,
+                     out, plan);
   return hipGetLastError();
 }
 

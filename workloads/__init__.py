@@ -164,3 +164,43 @@ def query(w: Workload, layer: int, step: int) -> np.ndarray:
         for hq in range(w.q_heads):
             q[:, hq] += w.hot_beta * hot_direction(w, layer, hq // g)
     return q
+
+
+def _bf16_grid(x: np.ndarray) -> np.ndarray:
+    """float32 values with the low 16 mantissa bits cleared, so that they are
+    exactly representable in bfloat16 (truncation: a way to draw values on the
+    bf16 grid, not a model of any store)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: int = 7):
+    """A random cache state of the workload's shapes, for decode-only checks at
+    full size without running the folds that would build it: per (sequence,
+    KV head) and K|V, an orthonormal d x r basis (QR of a Gaussian matrix),
+    singular values, coefficient rows [0, n_c) and ring rows for the exact
+    positions [n_c, length) at slot p mod (window + 64).  With bf16 storage the
+    coefficients and ring rows are drawn on the bf16 grid.
+
+    Returns a list over units (b * kv_heads + h) of [K, V] dicts with keys
+    basis, S, coef (max_tokens x r), ring ((window + 64) x d)."""
+    d, r, slots = w.head_dim, w.rank, w.window + 64
+    assert n_c % 64 == 0 and w.window <= length - n_c <= w.window + 63
+    units = []
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            xs = []
+            for x in range(2):
+                rng = _rng(w, 9001, seed, b, h, x)          # 9001: state stream tag
+                B, _ = np.linalg.qr(rng.standard_normal((d, r)))
+                S = np.sort(rng.uniform(1.0, 50.0, r))[::-1].astype(np.float32)
+                C = np.zeros((max_tokens, r), np.float32)
+                C[:n_c] = rng.standard_normal((n_c, r)).astype(np.float32) * (2.0 / np.sqrt(r))
+                ring = np.zeros((slots, d), np.float32)
+                for p in range(n_c, length):
+                    ring[p % slots] = rng.standard_normal(d).astype(np.float32) * 0.25
+                if w.storage == "bf16":
+                    C, ring = _bf16_grid(C), _bf16_grid(ring)
+                xs.append(dict(basis=B.astype(np.float32), S=S, coef=C, ring=ring))
+            units.append(xs)
+    return units
