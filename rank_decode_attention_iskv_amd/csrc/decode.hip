@@ -76,14 +76,27 @@ __device__ __forceinline__ floatx4 load4_agent(const float *p) {
 }
 
 // reductions over the four lane rows (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// v_permlane16_swap / v_permlane32_swap with both operands = v return the
+// pair (v[l], v[l ^ 16]) (resp. ^ 32) in some order in every lane, without
+// the LDS round trip of a lane shuffle.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-__device__ __forceinline__ float row_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float row_max(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float row_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 // feature held by lane row rho in slot j of K-block kb of the score product
 __device__ __forceinline__ int score_feature(int kb, int j, int rho) {
@@ -336,8 +349,10 @@ template <int R, typename T> struct Cfg {
   static constexpr int kElem = BF ? 2 : 4;
   static constexpr int kMatBytes = 16 * R * kElem;           // one 16-token tile of C_K or C_V
   static constexpr int kDma = kMatBytes >= 1024 ? kMatBytes / 1024 : 1;   // dwordx4 DMAs per matrix
-  static constexpr int kRingBytes = 16384;                    // per wave
+  // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring
+  static constexpr int kRingBytes = kMatBytes >= 4096 ? 32768 : 16384;
   static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
+  static_assert(kDepth >= 2, "ring depth");
   static constexpr int kOcc = (BF && R <= 32) ? 2 : 1;
   static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
   static constexpr int kLoopBytes = (4 * kRingBytes > kAccBytes) ? 4 * kRingBytes : kAccBytes;
@@ -383,12 +398,12 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
   const int tile_lo = wave * tpw < ntiles ? wave * tpw : ntiles;
   const int tile_hi = (wave + 1) * tpw < ntiles ? (wave + 1) * tpw : ntiles;
   const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
-  const int nt = tile_hi - tile_lo;
+  const int nt = __builtin_amdgcn_readfirstlane(tile_hi - tile_lo);   // wave-uniform
 
   LayerPtrs P = layer_ptrs(M, layer);
 
   // ---- RoPE angle state of the lane's token for its 16 frequencies
-  floatx2 cs[16];
+  float cs_c[16], cs_s[16];          // separate arrays: no 64-bit register pairs
   auto anchor = [&](int64_t t) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -396,7 +411,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       for (int i = 0; i < 4; ++i) {
         float c, s;
         rope_cs(M.sh, t, 16 * mb + 4 * rho + i, c, s);
-        cs[mb * 4 + i] = floatx2{c, s};
+        cs_c[mb * 4 + i] = c;
+        cs_s[mb * 4 + i] = s;
       }
   };
 
@@ -439,14 +455,15 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float c = cs[mb * 4 + i].x, s = cs[mb * 4 + i].y;
+        const float c = cs_c[mb * 4 + i], s = cs_s[mb * 4 + i];
         const float x0 = ka[mb][i], x1 = ka[mb + 4][i];
         ka[mb][i] = fmaf(x0, c, -x1 * s);
         ka[mb + 4][i] = fmaf(x1, c, x0 * s);
         const float2 st = s_step[16 * mb + 4 * rho + i];
-        cs[mb * 4 + i] = floatx2{fmaf(c, st.x, -s * st.y), fmaf(s, st.x, c * st.y)};
+        cs_c[mb * 4 + i] = fmaf(c, st.x, -s * st.y);
+        cs_s[mb * 4 + i] = fmaf(s, st.x, c * st.y);
       }
-    floatx4 sc = zero4();
+    floatx4 sc[2] = {zero4(), zero4()};          // two chains of dependent MFMAs
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       unsigned h[4], lo[4];
@@ -456,11 +473,12 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         split2(ka[2 * kb + 1][2 * j], ka[2 * kb + 1][2 * j + 1], h[2 + j], lo[2 + j]);
       }
       const uint4_ kh = {h[0], h[1], h[2], h[3]}, kl = {lo[0], lo[1], lo[2], lo[3]};
-      sc = mfma32(kh, qhi[kb], sc);
-      sc = mfma32(kh, qlo[kb], sc);
-      sc = mfma32(kl, qhi[kb], sc);
+      floatx4 &a = sc[kb & 1];
+      a = mfma32(kh, qhi[kb], a);
+      a = mfma32(kh, qlo[kb], a);
+      a = mfma32(kl, qhi[kb], a);
     }
-    return sc;
+    return sc[0] + sc[1];
   };
 
   float m = -INFINITY, l = 0.f;
@@ -504,7 +522,12 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       anchor(w_begin + n16);
     }
     prepare_query();
-    for (int it = 0; it < nt; ++it) {
+    // chunks of 32 tiles: the angle state is re-anchored from the table at
+    // each chunk start (bounding the recurrence) outside the inner loop
+    for (int c0 = 0; c0 < nt; c0 += 32) {
+    if (c0 > 0) anchor(w_begin + 16 * (int64_t)c0 + n16);
+    const int c1 = nt < c0 + 32 ? nt : c0 + 32;
+    for (int it = c0; it < c1; ++it) {
       if (it + DEPTH - 1 < nt) {
         issue(it + DEPTH - 1);
         wait_vmcnt<(DEPTH - 1) * LPT>();
@@ -554,7 +577,6 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         }
       }
       const floatx4 sc = rope_scores(ka);
-      if ((it & 31) == 31) anchor(w_begin + 16 * (int64_t)(it + 1) + n16);   // bound the recurrence
       float p[4];
       softmax_tile<NBV>(sc, 0xf, m, l, vacc, rho, p);
       // values: C_V tokens 4*rho..+3 of coefficient 16*nb + n16, transposed reads
@@ -580,6 +602,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
           for (int i = 0; i < 4; ++i)
             vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
       }
+    }
     }
     // per-wave results: acc[head 4*rho+i][coef 16*nb + n16] (over the rings)
     __syncthreads();
