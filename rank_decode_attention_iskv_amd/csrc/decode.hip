@@ -349,13 +349,18 @@ template <int R, typename T> struct Cfg {
   static constexpr int kElem = BF ? 2 : 4;
   static constexpr int kMatBytes = 16 * R * kElem;           // one 16-token tile of C_K or C_V
   static constexpr int kDma = kMatBytes >= 1024 ? kMatBytes / 1024 : 1;   // dwordx4 DMAs per matrix
+  // bf16 r = 64: the low bf16 parts of the key-basis fragments live in LDS
+  // (16 KiB per workgroup) instead of registers, so two workgroups fit per CU
+  static constexpr bool kLoLds = BF && R == 64;
+  static constexpr int kFloBytes = kLoLds ? 8 * (R / 32) * 1024 : 0;
   // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring
-  static constexpr int kRingBytes = kMatBytes >= 4096 ? 32768 : 16384;
+  static constexpr int kRingBytes = kLoLds ? 12288 : (kMatBytes >= 4096 ? 32768 : 16384);
   static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
   static_assert(kDepth >= 2, "ring depth");
-  static constexpr int kOcc = (BF && R <= 32) ? 2 : 1;
+  static constexpr int kOcc = (BF && R <= 64) ? 2 : 1;
   static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
-  static constexpr int kLoopBytes = (4 * kRingBytes > kAccBytes) ? 4 * kRingBytes : kAccBytes;
+  static constexpr int kLoopBytes = (kFloBytes + 4 * kRingBytes > kAccBytes) ? kFloBytes + 4 * kRingBytes
+                                                                            : kAccBytes;
   static constexpr int kDynBytes = kLoopBytes > MergeLds<R>::bytes ? kLoopBytes : MergeLds<R>::bytes;
 };
 
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
 #pragma unroll
     for (int nb = 0; nb < NBV; ++nb) vacc[nb] = zero4();
     // per-wave LDS ring of DEPTH slots, each [C_K tile | C_V tile]
-    uint8_t *ring = s_dyn + wave * C::kRingBytes;
+    uint8_t *ring = s_dyn + C::kFloBytes + wave * C::kRingBytes;
     const uint8_t *gk = P.coef + (((size_t)u * 2 + 0) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
     const uint8_t *gv = P.coef + (((size_t)u * 2 + 1) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
     // one tile: kDma dwordx4 DMAs per matrix; lane l moves 16 bytes of chunk
@@ -506,19 +511,33 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         }
       }
     };
-    // operands issued before the query barrier: the first DEPTH-1 tiles, the
-    // basis fragments and the first angle state
+    // operands issued before the query barrier: the LDS-resident basis
+    // fragments (r = 64), the first DEPTH-1 tiles, the register-resident basis
+    // fragments and the first angle state.  Every wave's LDS fragment copies
+    // have completed before its query loads do, hence before the barrier in
+    // prepare_query, after which all waves read them.
+    const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
+    constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
+    if constexpr (C::kLoLds) {
+      // low-part chunks (mb, 2 kb + 1) -> LDS [mb][kb][64 lanes][16 B]; a quarter per wave
+#pragma unroll
+      for (int j = 0; j < 8 * (R / 32) / 4; ++j) {
+        const int c = wave * (8 * (R / 32) / 4) + j, mb = c / (R / 32), kb = c % (R / 32);
+        dma16(FB + ((size_t)(mb * (R / 16) + 2 * kb + 1) * 64 + lane) * 16, s_dyn + c * 1024);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; ++j)
       if (j < nt) issue(j);
-    const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
-    uint4_ F[8][R / 16];
+    uint4_ F[8][FCH];
     if (nt > 0) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int ch = 0; ch < R / 16; ++ch)
-          F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + ch) * 64 + lane) * 16);
+        for (int ch = 0; ch < FCH; ++ch) {
+          const int gch = C::kLoLds ? 2 * ch : ch;          // high parts only when the lows are in LDS
+          F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + gch) * 64 + lane) * 16);
+        }
       anchor(w_begin + n16);
     }
     prepare_query();
@@ -557,8 +576,15 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
             floatx4 a = zero4();
 #pragma unroll
             for (int kb = 0; kb < R / 32; ++kb) {
-              a = mfma32(F[mb][2 * kb], bop[kb], a);
-              a = mfma32(F[mb][2 * kb + 1], bop[kb], a);
+              if constexpr (C::kLoLds) {
+                const uint4_ lo = *reinterpret_cast<const uint4_ *>(
+                    s_dyn + ((mb * (R / 32) + kb) * 64 + lane) * 16);
+                a = mfma32(F[mb][kb], bop[kb], a);
+                a = mfma32(lo, bop[kb], a);
+              } else {
+                a = mfma32(F[mb][2 * kb], bop[kb], a);
+                a = mfma32(F[mb][2 * kb + 1], bop[kb], a);
+              }
             }
             ka[mb] = a;
           }
