@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--async-maintenance", action="store_true",
+                    help="run block updates and syncs on a second stream (each layer "
+                         "instance's later work waits for its own); default: the decode stream")
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only stream a 256 MiB float32 tensor through an elementwise kernel "
@@ -235,11 +238,13 @@ def main():
     t_pre = time.perf_counter() - t_pre
 
     # ---- inputs of the timed steps, resident before timing
+    # per instance [step][batch][1][kv_heads][d], so each step's token is one
+    # contiguous [batch, 1, kv_heads, d] block
     k_all, v_all = [], []
     for inst in range(I):
-        k, v = gen.tokens(inst, per_inst_steps)
-        k_all.append(k)
-        v_all.append(v)
+        k, v = gen.tokens(inst, per_inst_steps)            # [B, n, H, D]
+        k_all.append(k.permute(1, 0, 2, 3).contiguous())
+        v_all.append(v.permute(1, 0, 2, 3).contiguous())
     q_all = gen.queries(total_steps, HQ, D)
     out = torch.empty(B, HQ, D, device="cuda")
     torch.cuda.synchronize()
@@ -248,31 +253,56 @@ def main():
     comp = [cache.status(i).compressed for i in range(I)]
     used = [0] * I
     ev = []                      # (start, end, bytes) per timed decode launch
+    mstream = None
     fold_ev, sync_ev = [], []
     bytes_total = 0
     folds = 0
 
-    def step(s, timed):
-        nonlocal bytes_total, folds
+    # The step loop calls the C ABI directly with precomputed device pointers
+    # and pre-created events: the per-step host work must stay well below the
+    # GPU time of a step, or the timeline measures the Python loop.
+    import ctypes
+    L_ = binding.lib()
+    ctx = cache.ctx
+    tok_bytes = B * H * D * 4
+    k_base = [t.data_ptr() for t in k_all]
+    v_base = [t.data_ptr() for t in v_all]
+    q_base, q_bytes = q_all.data_ptr(), B * HQ * D * 4
+    out_p = ctypes.c_void_p(out.data_ptr())
+    ready_c = ctypes.c_int(0)
+    ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+
+    def step(s, timed, warm=False):
+        nonlocal bytes_total, folds, mstream
         inst = s % I
         j = used[inst]
         used[inst] += 1
-        ready = cache.append(inst, k_all[inst][:, j:j + 1], v_all[inst][:, j:j + 1])
+        code = L_.iskv_append(ctx, inst, ctypes.c_void_p(k_base[inst] + j * tok_bytes),
+                              ctypes.c_void_p(v_base[inst] + j * tok_bytes), 1, binding.F32,
+                              ctypes.byref(ready_c))
+        if code != 0:
+            raise binding.IskvError(code, "iskv_append")
+        ready = bool(ready_c.value)
         lengths[inst] += 1
         L, n_c = lengths[inst], comp[inst]
-        q = q_all[s]
-        if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        qp = ctypes.c_void_p(q_base + s * q_bytes)
+        if timed and not warm:
+            e0, e1 = ev_pool[len(ev)]
+            if mstream is not None:
+                L_.iskv_join_maintenance(ctx, inst)   # a wait for this instance's fold stays outside e0..e1
             e0.record(stream)
-            cache.decode_attn(inst, q, L - 1, out)
+            code = L_.iskv_decode_attn(ctx, inst, qp, L - 1, out_p)
             e1.record(stream)
             nb = decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
             ev.append((e0, e1, nb))
             bytes_total += nb
         else:
-            cache.decode_attn(inst, q, L - 1, out)
+            code = L_.iskv_decode_attn(ctx, inst, qp, L - 1, out_p)
+        if code != 0:
+            raise binding.IskvError(code, "iskv_decode_attn")
         if ready:
-            if timed:
+            if warm or (timed and (not args.async_maintenance)):
                 f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                 f0.record(stream)
                 cache.block_update(inst)
@@ -281,21 +311,28 @@ def main():
                 f2.record(stream)
                 fold_ev.append((f0, f1))
                 sync_ev.append((f1, f2))
-                folds += 1
+                folds += 0 if warm else 1
             else:
+                folds += 0 if warm else 1
                 cache.block_update(inst)
                 cache.sync(inst)
             comp[inst] += 64
 
+    # warm-up on one stream, with the fold and sync kernels timed by events
     for s in range(args.warmup):
-        step(s, False)
+        step(s, True, warm=True)
     torch.cuda.synchronize()
+    if args.async_maintenance:
+        mstream = torch.cuda.Stream()
+        cache.set_maintenance_stream(mstream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.warmup, total_steps):
         step(s, True)
+    if mstream is not None:
+        cache.join_maintenance()          # the timed region ends after every fold and sync
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -337,6 +374,8 @@ def main():
             "global_batch": B,
             "seq_len": args.context,
             "parallelism": "single GPU",
+            "maintenance": "same stream" if (not args.async_maintenance) else
+                           "second stream (each instance waits for its own fold + sync)",
         },
         "roofline": {
             "bound": "hbm",

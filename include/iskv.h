@@ -166,7 +166,28 @@ int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st);
 int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes);
 int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes);
 
-/* Free the context (not the caller's workspace). Synchronizes the stream. */
+/* Maintenance off the decode path ([ASKV report, Design requirements]:
+ * maintenance must not block token generation).  With a non-NULL hip_stream
+ * (a hipStream_t on the same device, distinct from the init stream),
+ * iskv_block_update and iskv_sync enqueue their kernels there instead: each
+ * call is ordered after everything already enqueued on the init stream, and
+ * later init-stream work that touches the same layer (append, decode,
+ * export/import) waits for that layer's maintenance; other layers' work does
+ * not.  Results are identical to the single-stream order.  NULL (or the init
+ * stream) returns to single-stream operation.  Pending maintenance is joined
+ * into the init stream before the switch.  The caller keeps ownership of the
+ * stream, which must outlive the context or the next switch. */
+int iskv_set_maintenance_stream(iskv_ctx *c, void *hip_stream);
+
+/* Make the init stream wait for the pending maintenance of `layer` (-1: all
+ * layers).  Enqueued, does not block the host: init-stream work issued after
+ * it is ordered after every block update and sync of that layer issued so
+ * far.  (Verbs that touch a layer do this themselves; the call lets a caller
+ * place the wait, e.g. outside a timed interval.)  EINVAL for a bad layer. */
+int iskv_join_maintenance(iskv_ctx *c, int layer);
+
+/* Free the context (not the caller's workspace).  Joins pending maintenance,
+ * then synchronizes the init stream. */
 int iskv_destroy(iskv_ctx *c);
 
 /* Static string for a return code. */

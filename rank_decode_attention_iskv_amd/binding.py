@@ -46,7 +46,8 @@ class Status(ctypes.Structure):
 EXPORTED = (
     "iskv_workspace_bytes", "iskv_state_bytes", "iskv_init", "iskv_append",
     "iskv_block_update", "iskv_sync", "iskv_discard_sync", "iskv_decode_attn",
-    "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_destroy", "iskv_strerror",
+    "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_set_maintenance_stream",
+    "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
 )
 
 
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_status": (I, [P, I, ctypes.POINTER(Status)]),
         "iskv_export_state": (I, [P, I, P, SZ]),
         "iskv_import_state": (I, [P, I, P, SZ]),
+        "iskv_set_maintenance_stream": (I, [P, P]),
+        "iskv_join_maintenance": (I, [P, I]),
         "iskv_destroy": (I, [P]),
         "iskv_strerror": (ctypes.c_char_p, [I]),
     }
@@ -198,6 +201,16 @@ class IskvCache:
         buf = blob if isinstance(blob, bytearray) else bytearray(blob)
         c_buf = (ctypes.c_char * len(buf)).from_buffer(buf)
         _check(lib().iskv_import_state(self.ctx, layer, c_buf, len(buf)), "iskv_import_state")
+
+    def set_maintenance_stream(self, stream) -> None:
+        """Run block updates and syncs on `stream` (a torch.cuda.Stream), off the
+        init stream; None returns to single-stream operation."""
+        self.mstream = stream                     # kept alive with the cache
+        ptr = ctypes.c_void_p(stream.cuda_stream if stream is not None else 0)
+        _check(lib().iskv_set_maintenance_stream(self.ctx, ptr), "iskv_set_maintenance_stream")
+
+    def join_maintenance(self, layer: int = -1) -> None:
+        _check(lib().iskv_join_maintenance(self.ctx, layer), "iskv_join_maintenance")
 
     def destroy(self):
         if getattr(self, "ctx", None):

@@ -103,6 +103,13 @@ struct iskv_ctx {
   hipStream_t stream;
   int device;
   std::vector<LayerState> layers;
+  // optional maintenance stream: block update + sync of a layer run there,
+  // after the main stream's earlier work, and the main stream's later work on
+  // that layer waits for them (per-layer events)
+  hipStream_t mstream = nullptr;
+  hipEvent_t ev_main = nullptr;
+  std::vector<hipEvent_t> ev_done;
+  std::vector<char> maint_pending;
 };
 
 namespace {
@@ -111,6 +118,37 @@ int hip_err(hipError_t e) { return e == hipSuccess ? ISKV_OK : ISKV_EDEVICE; }
 
 int check_layer(const iskv_ctx *c, int layer) {
   return (layer >= 0 && layer < c->D.layers) ? ISKV_OK : ISKV_EINVAL;
+}
+
+// Main-stream work on `layer` from here on waits for its pending maintenance.
+hipError_t join_layer(iskv_ctx *c, int layer) {
+  if (!c->mstream || !c->maint_pending[layer]) return hipSuccess;
+  c->maint_pending[layer] = 0;
+  return hipStreamWaitEvent(c->stream, c->ev_done[layer], 0);
+}
+
+hipError_t join_all(iskv_ctx *c) {
+  for (int l = 0; l < c->D.layers; ++l) {
+    hipError_t e = join_layer(c, l);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The stream maintenance work goes to, ordered after the main stream's work
+// enqueued so far.
+hipStream_t maint_stream(iskv_ctx *c, hipError_t *err) {
+  *err = hipSuccess;
+  if (!c->mstream) return c->stream;
+  *err = hipEventRecord(c->ev_main, c->stream);
+  if (*err == hipSuccess) *err = hipStreamWaitEvent(c->mstream, c->ev_main, 0);
+  return c->mstream;
+}
+
+hipError_t maint_done(iskv_ctx *c, int layer) {
+  if (!c->mstream) return hipSuccess;
+  c->maint_pending[layer] = 1;
+  return hipEventRecord(c->ev_done[layer], c->mstream);
 }
 
 void fill_sel(LayerSel &sel, const std::vector<int> &idx, size_t from) {
@@ -229,6 +267,7 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
   const int64_t used = L.length - L.n_c;
   if (used + n_tokens > c->D.slots) return ISKV_ESTATE;
   if (L.length + n_tokens > c->D.max_tokens) return ISKV_ESTATE;
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   hipError_t e = launch_append(c->M, layer, dev_k, dev_v, n_tokens, in_dtype, L.length, c->stream);
   if (e != hipSuccess) return ISKV_EDEVICE;
   L.length += n_tokens;
@@ -252,6 +291,10 @@ int iskv_block_update(iskv_ctx *c, int layer) {
   } else {
     return ISKV_EINVAL;
   }
+  if (idx.empty()) return ISKV_OK;
+  hipError_t se;
+  hipStream_t s = maint_stream(c, &se);
+  if (se != hipSuccess) return ISKV_EDEVICE;
   // group layers by their compressed count (one launch per distinct n_c)
   std::vector<bool> done(idx.size(), false);
   for (size_t i = 0; i < idx.size(); ++i) {
@@ -263,14 +306,15 @@ int iskv_block_update(iskv_ctx *c, int layer) {
     for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
       LayerSel sel;
       fill_sel(sel, grp, from);
-      hipError_t e = launch_block_update(c->M, sel, n_c, c->stream);
-      if (e == hipSuccess) e = launch_prep_frag(c->M, sel, c->stream);
+      hipError_t e = launch_block_update(c->M, sel, n_c, s);
+      if (e == hipSuccess) e = launch_prep_frag(c->M, sel, s);
       if (e != hipSuccess) return ISKV_EDEVICE;
     }
     for (int l : grp) {
       c->layers[l].n_c += kBlock;
       c->layers[l].pending = true;
       c->layers[l].folds += 1;
+      if (maint_done(c, l) != hipSuccess) return ISKV_EDEVICE;
     }
   }
   return ISKV_OK;
@@ -289,6 +333,10 @@ int iskv_sync(iskv_ctx *c, int layer) {
   } else {
     return ISKV_EINVAL;
   }
+  if (idx.empty()) return ISKV_OK;
+  hipError_t se;
+  hipStream_t s = maint_stream(c, &se);
+  if (se != hipSuccess) return ISKV_EDEVICE;
   std::vector<bool> done(idx.size(), false);
   for (size_t i = 0; i < idx.size(); ++i) {
     if (done[i]) continue;
@@ -299,11 +347,12 @@ int iskv_sync(iskv_ctx *c, int layer) {
     for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
       LayerSel sel;
       fill_sel(sel, grp, from);
-      if (launch_sync(c->M, sel, n_c - kBlock, c->stream) != hipSuccess) return ISKV_EDEVICE;
+      if (launch_sync(c->M, sel, n_c - kBlock, s) != hipSuccess) return ISKV_EDEVICE;
     }
     for (int l : grp) {
       c->layers[l].pending = false;
       c->layers[l].syncs += 1;
+      if (maint_done(c, l) != hipSuccess) return ISKV_EDEVICE;
     }
   }
   return ISKV_OK;
@@ -327,11 +376,13 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
   if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
   const LayerState &L = c->layers[layer];
   if (L.length <= 0) return ISKV_ESTATE;
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
 }
 
 int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
   if (!c || !st || check_layer(c, layer)) return ISKV_EINVAL;
+  if (join_all(c) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   int flags = 0;
   if (hipMemcpy(&flags, c->M.sh.flags, 4, hipMemcpyDeviceToHost) != hipSuccess) return ISKV_EDEVICE;
@@ -355,6 +406,7 @@ int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
 int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   if (!c || check_layer(c, layer) || !host_buf) return ISKV_EINVAL;
   if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   const Dims &D = c->D;
   const LayerLayout &Ly = c->G.layer;
@@ -412,6 +464,7 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   if (length < 0 || n_c < 0 || n_c % kBlock || n_c > length || length > D.max_tokens ||
       length - n_c > D.slots)
     return ISKV_EINVAL;
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   const LayerLayout &Ly = c->G.layer;
   const size_t lb = Ly.bytes;
@@ -459,9 +512,37 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   return ISKV_OK;
 }
 
+int iskv_set_maintenance_stream(iskv_ctx *c, void *hip_stream) {
+  if (!c) return ISKV_EINVAL;
+  hipStream_t ms = reinterpret_cast<hipStream_t>(hip_stream);
+  if (ms == c->stream) ms = nullptr;
+  // pending maintenance of the old stream is joined into the main stream first
+  if (join_all(c) != hipSuccess) return ISKV_EDEVICE;
+  if (ms && !c->ev_main) {
+    if (hipEventCreateWithFlags(&c->ev_main, hipEventDisableTiming) != hipSuccess) return ISKV_EDEVICE;
+    c->ev_done.assign(c->D.layers, nullptr);
+    for (hipEvent_t &e : c->ev_done)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return ISKV_EDEVICE;
+    c->maint_pending.assign(c->D.layers, 0);
+  }
+  c->mstream = ms;
+  return ISKV_OK;
+}
+
+int iskv_join_maintenance(iskv_ctx *c, int layer) {
+  if (!c) return ISKV_EINVAL;
+  if (layer == -1) return hip_err(join_all(c));
+  if (check_layer(c, layer)) return ISKV_EINVAL;
+  return hip_err(join_layer(c, layer));
+}
+
 int iskv_destroy(iskv_ctx *c) {
   if (!c) return ISKV_EINVAL;
-  hipError_t e = hipStreamSynchronize(c->stream);
+  hipError_t e = join_all(c);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (c->ev_main) hipEventDestroy(c->ev_main);
+  for (hipEvent_t ev : c->ev_done)
+    if (ev) hipEventDestroy(ev);
   delete c;
   return hip_err(e);
 }

@@ -281,3 +281,33 @@ def test_state_machine_errors():
     with pytest.raises(IskvError) as e:
         p.gpu.append(0, k[:, :1], k[:, :1])
     assert e.value.code == ESTATE
+
+
+def test_maintenance_stream_matches_single_stream():
+    """Block updates and syncs on a second stream (off the decode stream) give
+    bit-identical decode outputs and states: every layer's later work waits
+    for its own maintenance, other layers' work proceeds meanwhile."""
+    import torch
+    w = small(2, kv_heads=2, q_heads=8, window=128)
+    runs = []
+    for use_stream in (False, True):
+        p = Pair(w, max_tokens=64 * 16 + 256, oracle=False, layers=3)
+        if use_stream:
+            p.gpu.set_maintenance_stream(torch.cuda.Stream())
+        outs = []
+        for rnd in range(12):
+            for layer in (0, 1, 2):
+                p.feed(layer, 64 + 7 * layer)
+                q = q32(workloads.query(w, layer, rnd))
+                outs.append(p.decode(layer, q, p.length[layer] - 1))
+        p.gpu.join_maintenance()
+        runs.append((outs, [p.state(l) for l in (0, 1, 2)]))
+        assert p.gpu.status(0).folds > 0
+    for a, b in zip(runs[0][0], runs[1][0]):
+        np.testing.assert_array_equal(a, b)
+    for (la, na, ua), (lb, nb, ub) in zip(runs[0][1], runs[1][1]):
+        assert (la, na) == (lb, nb)
+        for xa, xb in zip(ua, ub):
+            for fa, fb in zip(xa, xb):
+                for key in ("basis", "S", "coef", "ring"):
+                    np.testing.assert_array_equal(fa[key], fb[key])
