@@ -34,7 +34,7 @@
  *     or core, Jacobi sweep cap reached) is reported by iskv_status.
  *   - A context is not thread-safe.  Sequences of a batch advance in lockstep.
  *   - head_dim must be 128; rank must be 16, 32, 64 or 128; window a multiple
- *     of 64; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ *     of 64; num_q_heads a multiple of num_kv_heads, at most 16 times it.
  */
 #ifndef ISKV_H
 #define ISKV_H

@@ -79,13 +79,15 @@ __device__ __forceinline__ floatx4 load4_agent(const float *p) {
 // v_permlane16_swap / v_permlane32_swap with both operands = v return the
 // pair (v[l], v[l ^ 16]) (resp. ^ 32) in some order in every lane, without
 // the LDS round trip of a lane shuffle.
+// max(a, b) as the median of (a, b, +inf): no operand canonicalization
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 __device__ __forceinline__ float xor16_max(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return max2(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xor32_max(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return max2(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -171,11 +173,29 @@ template <int R> struct MergeLds {
   static constexpr int bytes = oAcc + 16 * (R + kHeadDim) * 4;
 };
 
+// record loads at agent scope (sc1), 16 bytes, through a buffer descriptor
+// whose range covers the unit's records (reads past it return zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t agent_rsrc(const float *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ floatx4 load4_rec(__amdgpu_buffer_rsrc_t r, int float_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, 16);
+}
+__device__ __forceinline__ float2 load2_agent(const float *p) {
+  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32))};
+}
+
+// Merge of one unit's split records (log-sum-exp combination; compressed
+// records hold p^T C_V, which the value basis maps to head space).  Every
+// global read is issued before the first wait: the value basis by DMA into
+// LDS, the (m, l) pairs and the first record columns into registers.
 template <int R>
 __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPlan &plan, int u,
                            uint8_t *lds) {
   using ML = MergeLds<R>;
-  floatx4 *s_bv = reinterpret_cast<floatx4 *>(lds + ML::oBv);
+  const floatx4 *s_bv = reinterpret_cast<const floatx4 *>(lds + ML::oBv);
   float *s_w = reinterpret_cast<float *>(lds + ML::oW);
   float (*s_part)[16] = reinterpret_cast<float (*)[16]>(lds + ML::oPart);
   float *s_mx = reinterpret_cast<float *>(lds + ML::oMx);
@@ -183,20 +203,29 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   floatx4 *s_red = reinterpret_cast<floatx4 *>(lds + ML::oRed);
   float (*s_acc)[R + kHeadDim] = reinterpret_cast<float (*)[R + kHeadDim]>(lds + ML::oAcc);
   const Dims &D = M.D;
-  const int G = D.group, tid = threadIdx.x;
-  const int n_rec = plan.n_comp + plan.n_win;
+  const int G = D.group, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n_rec = plan.n_comp + plan.n_win, NE = n_rec * G;
   const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
   const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
+  const __amdgpu_buffer_rsrc_t rr = agent_rsrc(acc, NE * kRecStride * 4);
   LayerPtrs P = layer_ptrs(M, layer);
-  const floatx4 *Bv = reinterpret_cast<const floatx4 *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
+  const uint8_t *Bv = reinterpret_cast<const uint8_t *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
 
-  // ---- issue: value basis -> LDS, m/l pairs, record accumulators
-  for (int e = tid; e < kHeadDim * R / 4; e += kThreads) s_bv[e] = Bv[e];
-  float mlm[16], mll[16];
-  int nml = 0;
-  for (int e = tid; e < n_rec * G && nml < 16; e += kThreads, ++nml) {
-    mlm[nml] = load_agent(ml + 2 * e);
-    mll[nml] = load_agent(ml + 2 * e + 1);
+  // ---- issue: value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA)
+#pragma unroll
+  for (int j = 0; j < (R / 2 + 3) / 4; ++j) {
+    const int c = wave + 4 * j;
+    if (c < R / 2) dma16(Bv + c * 1024 + lane * 16, lds + ML::oBv + c * 1024);
+  }
+  // (m, l) pairs: thread (head mh, part mp) holds records s = mp + 16 k, k < KML
+  constexpr int KML = 4;
+  const int mh = tid & 15, mp = tid >> 4;
+  const bool mok = mh < G;
+  float2 mlp[KML];
+#pragma unroll
+  for (int k = 0; k < KML; ++k) {
+    const int s = mp + 16 * k;
+    mlp[k] = mok && s < n_rec ? load2_agent(ml + 2 * (s * G + mh)) : float2{-INFINITY, 0.f};
   }
   // record items: (kind, float4 column, record group); thread -> fixed column
   // and group, records strided by the group count
@@ -210,59 +239,72 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
     return Item{c0 + tid % nc, tid / nc, kThreads / nc};
   };
   // the first column chunk of each kind is prefetched (all columns when
-  // G * width / 4 <= 256)
+  // G * width / 4 <= 256); loads past the records read zero
   const Item ic = item_of(0, 0), iw = item_of(1, 0);
   {
     const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
+    const bool okc = ic.grp < ic.groups;
 #pragma unroll
     for (int k = 0; k < NVC; ++k) {
       const int s = ic.grp + k * ic.groups;
-      if (ic.grp < ic.groups && s < plan.n_comp)
-        vc[k] = load4_agent(acc + ((size_t)s * G + hc) * kRecStride + xc);
+      vc[k] = okc && s < plan.n_comp ? load4_rec(rr, (s * G + hc) * kRecStride + xc) : zero4();
     }
     const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
+    const bool okw = iw.grp < iw.groups;
 #pragma unroll
     for (int k = 0; k < NVW; ++k) {
       const int s = iw.grp + k * iw.groups;
-      if (iw.grp < iw.groups && s < plan.n_win)
-        vw[k] = load4_agent(acc + ((size_t)(plan.n_comp + s) * G + hw) * kRecStride + xw);
+      vw[k] = okw && s < plan.n_win ? load4_rec(rr, ((plan.n_comp + s) * G + hw) * kRecStride + xw)
+                                    : zero4();
     }
   }
 
-  // ---- weights
-  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = mlm[k];
-  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads) s_w[e] = load_agent(ml + 2 * e);
+  // ---- weights w = exp2(m - max_h), L_h = sum w l; records past the
+  // prefetched ones (more than 16 KML) are read here
+  wait_vmcnt<0>();
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KML; ++k) mx = fmaxf(mx, mlp[k].x);
+  if (mok)
+    for (int s = mp + 16 * KML; s < n_rec; s += 16) {
+      const float m = load_agent(ml + 2 * (s * G + mh));
+      s_w[s * G + mh] = m;
+      mx = fmaxf(mx, m);
+    }
+  s_part[mp][mh] = mx;
+  __syncthreads();               // also: the value basis DMA is complete
+  if (tid < G) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) m = fmaxf(m, s_part[p][tid]);
+    s_mx[tid] = m;
+  }
   __syncthreads();
   {
-    const int h = tid & 15, part = tid >> 4;
-    float mx = -INFINITY;
-    if (h < G)
-      for (int s = part; s < n_rec; s += 16) mx = fmaxf(mx, s_w[s * G + h]);
-    s_part[part][h] = mx;
+    const float mh_max = mok ? s_mx[mh] : 0.f;
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < KML; ++k) {
+      const int s = mp + 16 * k;
+      if (mok && s < n_rec) {
+        const float w = __builtin_amdgcn_exp2f(mlp[k].x - mh_max);
+        s_w[s * G + mh] = w;
+        l += w * mlp[k].y;
+      }
+    }
+    if (mok)
+      for (int s = mp + 16 * KML; s < n_rec; s += 16) {
+        const float w = __builtin_amdgcn_exp2f(s_w[s * G + mh] - mh_max);
+        s_w[s * G + mh] = w;
+        l += w * load_agent(ml + 2 * (s * G + mh) + 1);
+      }
+    s_part[mp][mh] = l;
   }
   __syncthreads();
   if (tid < G) {
-    float mx = -INFINITY;
-    for (int p = 0; p < 16; ++p) mx = fmaxf(mx, s_part[p][tid]);
-    s_mx[tid] = mx;
-  }
-  __syncthreads();
-  for (int k = 0, e = tid; k < nml; ++k, e += kThreads) s_w[e] = __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]);
-  for (int e = tid + 16 * kThreads; e < n_rec * G; e += kThreads)
-    s_w[e] = __builtin_amdgcn_exp2f(s_w[e] - s_mx[e % G]);
-  {
-    // L: sum of w * l, partials per (part, head)
     float l = 0.f;
-    for (int k = 0, e = tid; k < nml; ++k, e += kThreads)
-      l += __builtin_amdgcn_exp2f(mlm[k] - s_mx[e % G]) * mll[k];
-    s_red[tid] = floatx4{l, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = 0.f;
-    for (int t = tid; t < kThreads && t < n_rec * G; t += G) l += s_red[t][0];
-    for (int e = 16 * kThreads + tid; e < n_rec * G; e += G)
-      l += s_w[e] * load_agent(ml + 2 * e + 1);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) l += s_part[p][tid];
     s_L[tid] = l;
   }
   __syncthreads();
@@ -279,7 +321,6 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
     const int cols = kind == 0 ? cols_c : cols_w;
     for (int c0 = 0; c0 < cols; c0 += kThreads) {
       const Item I = item_of(kind, c0);
-      (void)I;
       const int h = (I.col * 4) / width, x = (I.col * 4) % width;
       floatx4 a = zero4();
       if (I.grp < I.groups) {
@@ -301,7 +342,7 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int sk = s + k * I.groups;
-            v[k] = sk < n ? load4_agent(acc + ((size_t)(s0 + sk) * G + h) * kRecStride + x) : zero4();
+            v[k] = sk < n ? load4_rec(rr, ((s0 + sk) * G + h) * kRecStride + x) : zero4();
           }
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
@@ -358,6 +399,9 @@ template <int R, typename T> struct Cfg {
   static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
   static_assert(kDepth >= 2, "ring depth");
   static constexpr int kOcc = (BF && R <= 64) ? 2 : 1;
+  // compressed tiles in pairs (two register sets for the angle state); wider
+  // ranks lack the registers for it
+  static constexpr bool kPair = R <= 32;
   static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
   static constexpr int kLoopBytes = (kFloBytes + 4 * kRingBytes > kAccBytes) ? kFloBytes + 4 * kRingBytes
                                                                             : kAccBytes;
@@ -407,39 +451,58 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
 
   LayerPtrs P = layer_ptrs(M, layer);
 
-  // ---- RoPE angle state of the lane's token for its 16 frequencies
+  const SplitK sk = split_consts();
+
+  // ---- RoPE angle state of the lane's token for its 16 frequencies; the
+  // table loads (anchor_issue) and the products (anchor_finish) are apart so
+  // the prologue issues every load before its first wait
   float cs_c[16], cs_s[16];          // separate arrays: no 64-bit register pairs
-  auto anchor = [&](int64_t t) {
+  float2 an_A[16], an_B[16];
+  auto anchor_issue = [&](int64_t t) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float c, s;
-        rope_cs(M.sh, t, 16 * mb + 4 * rho + i, c, s);
-        cs_c[mb * 4 + i] = c;
-        cs_s[mb * 4 + i] = s;
-      }
+      for (int i = 0; i < 4; ++i) rope_load(M.sh, t, 16 * mb + 4 * rho + i, an_A[mb * 4 + i], an_B[mb * 4 + i]);
+  };
+  auto anchor_finish = [&]() {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rope_combine(an_A[j], an_B[j], cs_c[j], cs_s[j]);
+  };
+  auto anchor = [&](int64_t t) {
+    anchor_issue(t);
+    anchor_finish();
   };
 
-  // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS
-  // (one (head, frequency) pair per thread), then split bf16 hi/lo into the
-  // B-operand layout of the score product
-  uint4_ qhi[4], qlo[4];
-  auto prepare_query = [&]() {
-    for (int e = threadIdx.x; e < 16 * 64; e += kThreads) {
-      const int h = e >> 6, i = e & 63;
-      float x0 = 0.f, x1 = 0.f, c = 1.f, s = 0.f;
-      if (h < G) {
-        const float *qr = q + ((size_t)b * D.q_heads + hk * G + h) * kHeadDim;
-        x0 = qr[i];
-        x1 = qr[i + 64];
-        rope_cs(M.sh, q_pos, i, c, s);
-      }
-      s_q[h][i] = fmaf(x0, c, -x1 * s) * D.scale_log2;
-      s_q[h][i + 64] = fmaf(x1, c, x0 * s) * D.scale_log2;
+  // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS:
+  // thread (frequency qi, heads qh0 + 4k) loads (query_issue), then rotates
+  // and stores them, after which the rows are split bf16 hi/lo into the
+  // B-operand layout of the score product (query_finish, one barrier)
+  const int qi = threadIdx.x & 63, qh0 = threadIdx.x >> 6;
+  float qx0[4], qx1[4];
+  float2 qA, qB, qstep;
+  auto query_issue = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = qh0 + 4 * k < G ? qh0 + 4 * k : G - 1;      // rows past the group: not used
+      const float *qr = q + ((size_t)b * D.q_heads + hk * G + h) * kHeadDim;
+      qx0[k] = qr[qi];
+      qx1[k] = qr[qi + 64];
     }
-    if (threadIdx.x < 64)
-      s_step[threadIdx.x] = reinterpret_cast<const float2 *>(M.sh.rope_step)[16 * 64 + threadIdx.x];
+    rope_load(M.sh, q_pos, qi, qA, qB);
+    qstep = reinterpret_cast<const float2 *>(M.sh.rope_step)[16 * 64 + qi];
+  };
+  uint4_ qhi[4], qlo[4];
+  auto query_finish = [&]() {
+    float c, s;
+    rope_combine(qA, qB, c, s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = qh0 + 4 * k;
+      const float x0 = h < G ? qx0[k] : 0.f, x1 = h < G ? qx1[k] : 0.f;
+      s_q[h][qi] = fmaf(x0, c, -x1 * s) * D.scale_log2;
+      s_q[h][qi + 64] = fmaf(x1, c, x0 * s) * D.scale_log2;
+    }
+    if (threadIdx.x < 64) s_step[threadIdx.x] = qstep;
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -474,8 +537,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       unsigned h[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        split2(ka[2 * kb][2 * j], ka[2 * kb][2 * j + 1], h[j], lo[j]);
-        split2(ka[2 * kb + 1][2 * j], ka[2 * kb + 1][2 * j + 1], h[2 + j], lo[2 + j]);
+        split2(ka[2 * kb][2 * j], ka[2 * kb][2 * j + 1], h[j], lo[j], sk);
+        split2(ka[2 * kb + 1][2 * j], ka[2 * kb + 1][2 * j + 1], h[2 + j], lo[2 + j], sk);
       }
       const uint4_ kh = {h[0], h[1], h[2], h[3]}, kl = {lo[0], lo[1], lo[2], lo[3]};
       floatx4 &a = sc[kb & 1];
@@ -511,11 +574,12 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         }
       }
     };
-    // operands issued before the query barrier: the LDS-resident basis
-    // fragments (r = 64), the first DEPTH-1 tiles, the register-resident basis
-    // fragments and the first angle state.  Every wave's LDS fragment copies
-    // have completed before its query loads do, hence before the barrier in
-    // prepare_query, after which all waves read them.
+    // every prologue load is issued before the first wait: the query, the
+    // LDS-resident basis fragments (r = 64), the first DEPTH-1 tiles, the
+    // register-resident basis fragments and the first angle state.  Every
+    // wave's LDS fragment copies have completed before the barrier in
+    // query_finish, after which all waves read them.
+    query_issue();
     const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
     constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
     if constexpr (C::kLoLds) {
@@ -538,15 +602,14 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
           const int gch = C::kLoLds ? 2 * ch : ch;          // high parts only when the lows are in LDS
           F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + gch) * 64 + lane) * 16);
         }
-      anchor(w_begin + n16);
+      anchor_issue(w_begin + n16);
     }
-    prepare_query();
-    // chunks of 32 tiles: the angle state is re-anchored from the table at
-    // each chunk start (bounding the recurrence) outside the inner loop
-    for (int c0 = 0; c0 < nt; c0 += 32) {
-    if (c0 > 0) anchor(w_begin + 16 * (int64_t)c0 + n16);
-    const int c1 = nt < c0 + 32 ? nt : c0 + 32;
-    for (int it = c0; it < c1; ++it) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (nt > 0) anchor_finish();
+    query_finish();
+    // one 16-token tile: wait for its ring slot, rebuild the keys, scores,
+    // online softmax, values
+    auto comp_tile = [&](int it) {
       if (it + DEPTH - 1 < nt) {
         issue(it + DEPTH - 1);
         wait_vmcnt<(DEPTH - 1) * LPT>();
@@ -608,8 +671,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       // values: C_V tokens 4*rho..+3 of coefficient 16*nb + n16, transposed reads
       if constexpr (BF) {
         unsigned h0, l0, h1, l1;
-        split2(p[0], p[1], h0, l0);
-        split2(p[2], p[3], h1, l1);
+        split2(p[0], p[1], h0, l0, sk);
+        split2(p[2], p[3], h1, l1, sk);
         const uint16_t *tl = reinterpret_cast<const uint16_t *>(tv);
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) {
@@ -628,7 +691,21 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
           for (int i = 0; i < 4; ++i)
             vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
       }
-    }
+    };
+    // chunks of 32 tiles: the angle state is re-anchored from the table at
+    // each chunk start (bounding the recurrence) outside the inner loop.
+    // Paired tiles let the angle state alternate between two register sets
+    // instead of being copied back after every tile.
+    for (int c0 = 0; c0 < nt; c0 += 32) {
+      if (c0 > 0) anchor(w_begin + 16 * (int64_t)c0 + n16);
+      const int c1 = nt < c0 + 32 ? nt : c0 + 32;
+      int it = c0;
+      if constexpr (C::kPair)
+        for (; it + 1 < c1; it += 2) {
+          comp_tile(it);
+          comp_tile(it + 1);
+        }
+      for (; it < c1; ++it) comp_tile(it);
     }
     // per-wave results: acc[head 4*rho+i][coef 16*nb + n16] (over the rings)
     __syncthreads();
@@ -641,8 +718,11 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     floatx4 wacc[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) wacc[nb] = zero4();
-    if (nt > 0) anchor(w_begin + n16);
-    prepare_query();
+    query_issue();
+    if (nt > 0) anchor_issue(w_begin + n16);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nt > 0) anchor_finish();
+    query_finish();
     if (nt > 0) {
       const T *RK = reinterpret_cast<const T *>(P.ringk) + (size_t)u * D.slots * kHeadDim;
       const T *RV = reinterpret_cast<const T *>(P.ringv) + (size_t)u * D.slots * kHeadDim;
@@ -670,8 +750,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         softmax_tile<8>(sc, vm, m, l, wacc, rho, p);
         if constexpr (BF) {
           unsigned h0, l0, h1, l1;
-          split2(p[0], p[1], h0, l0);
-          split2(p[2], p[3], h1, l1);
+          split2(p[0], p[1], h0, l0, sk);
+          split2(p[2], p[3], h1, l1, sk);
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
             const uint2_ v = *reinterpret_cast<const uint2_ *>(

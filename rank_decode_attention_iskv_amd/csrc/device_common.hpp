@@ -45,13 +45,22 @@ template <> struct Store<bf16_t> {
 // (multiples of 64 positions) and the step table (offsets 0..63), by the
 // angle-addition identity.  Both tables hold float values of float64-exact
 // angles, so the result is within a few float ulps for any position covered.
-__device__ __forceinline__ void rope_cs(const Shared &S, int64_t pos, int i, float &c, float &s) {
+// the two table entries whose product is the rotation of position pos for
+// frequency i, and that product
+__device__ __forceinline__ void rope_load(const Shared &S, int64_t pos, int i, float2 &A, float2 &B) {
   const int64_t a = pos / kRopeAnchor;
   const int o = (int)(pos - a * kRopeAnchor);
-  const float2 A = reinterpret_cast<const float2 *>(S.rope_anchor)[a * 64 + i];
-  const float2 B = reinterpret_cast<const float2 *>(S.rope_step)[o * 64 + i];
+  A = reinterpret_cast<const float2 *>(S.rope_anchor)[a * 64 + i];
+  B = reinterpret_cast<const float2 *>(S.rope_step)[o * 64 + i];
+}
+__device__ __forceinline__ void rope_combine(float2 A, float2 B, float &c, float &s) {
   c = A.x * B.x - A.y * B.y;
   s = A.y * B.x + A.x * B.y;
+}
+__device__ __forceinline__ void rope_cs(const Shared &S, int64_t pos, int i, float &c, float &s) {
+  float2 A, B;
+  rope_load(S, pos, i, A, B);
+  rope_combine(A, B, c, s);
 }
 
 __device__ __forceinline__ void set_flag(const Shared &S, int f) { atomicOr(S.flags, f); }
@@ -74,6 +83,28 @@ __device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned 
   const float ha = __uint_as_float(hb << 16), hh = __uint_as_float(hb & 0xffff0000u);
   const bf16x2 l = __builtin_convertvector((floatx2){a - ha, b - hh}, bf16x2);
   hi = hb;
+  lo = __builtin_bit_cast(unsigned, l);
+}
+
+// The same split with each residual x - hi(x) from one v_dot2c_f32_bf16: the
+// packed high parts dotted with bf16 (-1, 0) or (0, -1) and accumulated onto
+// x (exact: the products and the sum are exact in fp32).  The two constant
+// operands sit in scalar registers (SplitK, made once per kernel): written
+// as immediates, these packed bf16 pairs are not encoded as intended.
+struct SplitK {
+  unsigned m0, m1;       // bf16 (-1, 0) and (0, -1), element 0 in the low half
+};
+__device__ __forceinline__ SplitK split_consts() {
+  unsigned m0 = 0x0000BF80u, m1 = 0xBF800000u;
+  asm volatile("" : "+s"(m0), "+s"(m1));
+  return SplitK{m0, m1};
+}
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo, SplitK k) {
+  const bf16x2 h = __builtin_convertvector((floatx2){a, b}, bf16x2);
+  const float la = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k.m0), a, false);
+  const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k.m1), b, false);
+  const bf16x2 l = __builtin_convertvector((floatx2){la, lb}, bf16x2);
+  hi = __builtin_bit_cast(unsigned, h);
   lo = __builtin_bit_cast(unsigned, l);
 }
 

@@ -36,7 +36,7 @@ bool valid_config(const iskv_config *c) {
   if (c->batch < 1 || c->num_layers < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1) return false;
   if (c->num_q_heads % c->num_kv_heads) return false;
   const int g = c->num_q_heads / c->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return false;
+  if (g < 1 || g > 16) return false;           // query heads of a group fill <= 16 MFMA columns
   if (c->head_dim != kHeadDim) return false;
   if (c->rank != 16 && c->rank != 32 && c->rank != 64 && c->rank != 128) return false;
   if (c->rank > c->head_dim) return false;

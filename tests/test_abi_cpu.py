@@ -45,7 +45,7 @@ def test_workspace_bytes_valid_and_monotone():
 
 @pytest.mark.parametrize("kw", [
     dict(head_dim=64), dict(rank=48), dict(rank=256), dict(window=100), dict(window=0),
-    dict(block=32), dict(num_q_heads=12), dict(num_q_heads=96), dict(storage=7),
+    dict(block=32), dict(num_q_heads=12), dict(num_q_heads=136), dict(storage=7),
     dict(batch=0), dict(max_tokens=0), dict(rope_base=0.5),
 ])
 def test_invalid_configs_rejected(kw):
