@@ -162,14 +162,39 @@ __device__ __forceinline__ void softmax_tile(floatx4 sc, int valid_mask, float &
 // Latency-bound: every global load (record accumulators, m/l pairs, the value
 // basis) is issued before any of them is used.
 // ---------------------------------------------------------------------------
+// XOR swizzle of the 16-byte chunks of value-basis row f in LDS
+template <int R> __device__ __forceinline__ int bv_swz(int f) { return f & ((R / 4 < 8 ? R / 4 : 8) - 1); }
+
+// sum over aligned groups of gp lanes (gp a wave-uniform power of two <= 64):
+// DPP swaps of lane pairs 1 and 2 apart, the half-row and row mirrors, then
+// the 16- and 32-lane swaps; every lane ends with its group's sum
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int x = __float_as_int(v), y;
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;    // quad_perm 1,0,3,2
+    case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;    // quad_perm 2,3,0,1
+    case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
+    default: y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break;  // row_mirror
+  }
+  return v + __int_as_float(y);
+}
+__device__ __forceinline__ float lane_group_sum(float v, int gp) {
+  if (gp >= 2) v = dpp_add(v, 0);
+  if (gp >= 4) v = dpp_add(v, 1);
+  if (gp >= 8) v = dpp_add(v, 2);
+  if (gp >= 16) v = dpp_add(v, 3);
+  if (gp >= 32) v = xor16_sum(v);
+  if (gp >= 64) v = xor32_sum(v);
+  return v;
+}
+
 template <int R> struct MergeLds {
   static constexpr int oBv = 0;                            // value basis [128][R/4] float4
   static constexpr int oW = oBv + kHeadDim * R * 4;        // weight per (record, head) [4096]
   static constexpr int oPart = oW + 4096 * 4;              // [16][16]
   static constexpr int oMx = oPart + 16 * 16 * 4;          // [16]
   static constexpr int oL = oMx + 16 * 4;                  // [16]
-  static constexpr int oRed = oL + 16 * 4;                 // [256] float4
-  static constexpr int oAcc = oRed + kThreads * 16;        // [16][R + 128]
+  static constexpr int oAcc = oL + 16 * 4;                 // [16][R + 128]
   static constexpr int bytes = oAcc + 16 * (R + kHeadDim) * 4;
 };
 
@@ -200,7 +225,6 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   float (*s_part)[16] = reinterpret_cast<float (*)[16]>(lds + ML::oPart);
   float *s_mx = reinterpret_cast<float *>(lds + ML::oMx);
   float *s_L = reinterpret_cast<float *>(lds + ML::oL);
-  floatx4 *s_red = reinterpret_cast<floatx4 *>(lds + ML::oRed);
   float (*s_acc)[R + kHeadDim] = reinterpret_cast<float (*)[R + kHeadDim]>(lds + ML::oAcc);
   const Dims &D = M.D;
   const int G = D.group, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -211,11 +235,16 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   LayerPtrs P = layer_ptrs(M, layer);
   const uint8_t *Bv = reinterpret_cast<const uint8_t *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
 
-  // ---- issue: value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA)
+  // ---- issue: value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA).
+  // 16-byte chunk c4 of row f lands at chunk c4 ^ bv_swz(f) of the row, so
+  // the output phase (lane = row) reads without bank conflicts.
 #pragma unroll
   for (int j = 0; j < (R / 2 + 3) / 4; ++j) {
     const int c = wave + 4 * j;
-    if (c < R / 2) dma16(Bv + c * 1024 + lane * 16, lds + ML::oBv + c * 1024);
+    if (c < R / 2) {
+      const int pos = c * 64 + lane, f = pos / (R / 4), c4 = (pos % (R / 4)) ^ bv_swz<R>(f);
+      dma16(Bv + (f * (R / 4) + c4) * 16, lds + ML::oBv + c * 1024);
+    }
   }
   // (m, l) pairs: thread (head mh, part mp) holds records s = mp + 16 k, k < KML
   constexpr int KML = 4;
@@ -232,25 +261,29 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   const int cols_c = G * R / 4, cols_w = G * kHeadDim / 4;
   constexpr int NVC = 12, NVW = 4;          // prefetched float4 per thread (compressed, window)
   floatx4 vc[NVC], vw[NVW];
-  struct Item { int col, grp, groups; };
+  // a column's record groups are gp adjacent lanes (gp a power of two, at
+  // most 64, so a group never spans two waves): lane shuffles sum them
+  struct Item { int col, grp, groups; bool ok; };
   auto item_of = [&](int kind, int c0) -> Item {
     const int cols = kind == 0 ? cols_c : cols_w;
     const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
-    return Item{c0 + tid % nc, tid / nc, kThreads / nc};
+    int gp = 1;
+    while (gp < 64 && 2 * gp * nc <= kThreads) gp *= 2;
+    return Item{c0 + tid / gp, tid % gp, gp, tid / gp < nc};
   };
   // the first column chunk of each kind is prefetched (all columns when
   // G * width / 4 <= 256); loads past the records read zero
   const Item ic = item_of(0, 0), iw = item_of(1, 0);
   {
     const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
-    const bool okc = ic.grp < ic.groups;
+    const bool okc = ic.ok;
 #pragma unroll
     for (int k = 0; k < NVC; ++k) {
       const int s = ic.grp + k * ic.groups;
       vc[k] = okc && s < plan.n_comp ? load4_rec(rr, (s * G + hc) * kRecStride + xc) : zero4();
     }
     const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
-    const bool okw = iw.grp < iw.groups;
+    const bool okw = iw.ok;
 #pragma unroll
     for (int k = 0; k < NVW; ++k) {
       const int s = iw.grp + k * iw.groups;
@@ -323,47 +356,52 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
       const Item I = item_of(kind, c0);
       const int h = (I.col * 4) / width, x = (I.col * 4) % width;
       floatx4 a = zero4();
-      if (I.grp < I.groups) {
+      if (I.ok) {
+        // weights are read for clamped record indices (all reads issued
+        // together); records past n hold zeros, so their terms vanish
+        auto wt = [&](int sk) { return s_w[(s0 + (sk < n ? sk : n - 1)) * G + h]; };
         int s = I.grp;
         if (c0 == 0) {                       // prefetched part
           if (kind == 0) {
+            float w[NVC];
 #pragma unroll
-            for (int k = 0; k < NVC; ++k, s += I.groups)
-              if (s < n) a += s_w[(s0 + s) * G + h] * vc[k];
+            for (int k = 0; k < NVC; ++k) w[k] = wt(s + k * I.groups);
+#pragma unroll
+            for (int k = 0; k < NVC; ++k) a += w[k] * vc[k];
+            s += NVC * I.groups;
           } else {
+            float w[NVW];
 #pragma unroll
-            for (int k = 0; k < NVW; ++k, s += I.groups)
-              if (s < n) a += s_w[(s0 + s) * G + h] * vw[k];
+            for (int k = 0; k < NVW; ++k) w[k] = wt(s + k * I.groups);
+#pragma unroll
+            for (int k = 0; k < NVW; ++k) a += w[k] * vw[k];
+            s += NVW * I.groups;
           }
         }
         // the rest in chunks of 8 records, every load of a chunk issued first
         for (; s < n; s += 8 * I.groups) {
           floatx4 v[8];
+          float w[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int sk = s + k * I.groups;
             v[k] = sk < n ? load4_rec(rr, ((s0 + sk) * G + h) * kRecStride + x) : zero4();
           }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int sk = s + k * I.groups;
-            if (sk < n) a += s_w[(s0 + sk) * G + h] * v[k];
-          }
+          for (int k = 0; k < 8; ++k) w[k] = wt(s + k * I.groups);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) a += w[k] * v[k];
         }
       }
-      s_red[tid] = a;
-      __syncthreads();
-      const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
-      if (tid < nc) {
-        floatx4 t = s_red[tid];
-        for (int g = 1; g < kThreads / nc; ++g) t += s_red[g * nc + tid];
-        const int cc = c0 + tid, hh = (cc * 4) / width, xx = (cc * 4) % width;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_acc[hh][(kind ? R : 0) + xx + j] = t[j];
+      for (int j = 0; j < 4; ++j) a[j] = lane_group_sum(a[j], I.groups);
+      if (I.ok && I.grp == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_acc[h][(kind ? R : 0) + x + j] = a[j];
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
 
   // ---- out = (B_V acc_C + acc_W) / L
   const int b = u / D.kv_heads, hk = u % D.kv_heads;
@@ -373,7 +411,7 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
     if (plan.n_comp > 0) {
 #pragma unroll
       for (int c4 = 0; c4 < R / 4; ++c4) {
-        const floatx4 bv = s_bv[f * (R / 4) + c4];
+        const floatx4 bv = s_bv[f * (R / 4) + (c4 ^ bv_swz<R>(f))];
         a += bv[0] * s_acc[h][4 * c4] + bv[1] * s_acc[h][4 * c4 + 1] +
              bv[2] * s_acc[h][4 * c4 + 2] + bv[3] * s_acc[h][4 * c4 + 3];
       }
@@ -563,23 +601,26 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     const uint8_t *gv = P.coef + (((size_t)u * 2 + 1) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
     // one tile: kDma dwordx4 DMAs per matrix; lane l moves 16 bytes of chunk
     // d*64 + l of the tile (lanes past the tile size idle)
-    auto issue = [&](int it) {
+    // tile `src` into ring slot `it` % DEPTH
+    auto issue_from = [&](int it, int src) {
       uint8_t *slot = ring + (it % DEPTH) * 2 * C::kMatBytes;
 #pragma unroll
       for (int d = 0; d < C::kDma; ++d) {
         const int off = (d * 64 + lane) * 16;
         if (off < C::kMatBytes) {
-          dma16(gk + (size_t)it * C::kMatBytes + off, slot + d * 1024);
-          dma16(gv + (size_t)it * C::kMatBytes + off, slot + C::kMatBytes + d * 1024);
+          dma16(gk + (size_t)src * C::kMatBytes + off, slot + d * 1024);
+          dma16(gv + (size_t)src * C::kMatBytes + off, slot + C::kMatBytes + d * 1024);
         }
       }
     };
-    // every prologue load is issued before the first wait: the query, the
-    // LDS-resident basis fragments (r = 64), the first DEPTH-1 tiles, the
-    // register-resident basis fragments and the first angle state.  Every
-    // wave's LDS fragment copies have completed before the barrier in
-    // query_finish, after which all waves read them.
-    query_issue();
+    auto issue = [&](int it) { issue_from(it, it); };
+    // prologue: the LDS-resident basis fragments (r = 64), the query, the
+    // register-resident basis fragments and the first angle state are issued
+    // first, then the first DEPTH-1 ring tiles; one wait then covers all but
+    // the ring tiles, so the first tile is consumed as soon as it lands.
+    // Every wave's LDS fragment copies are older than its query loads, so
+    // they have completed before the barrier in query_finish, after which
+    // all waves read them.
     const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
     constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
     if constexpr (C::kLoLds) {
@@ -590,9 +631,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         dma16(FB + ((size_t)(mb * (R / 16) + 2 * kb + 1) * 64 + lane) * 16, s_dyn + c * 1024);
       }
     }
-#pragma unroll
-    for (int j = 0; j < DEPTH - 1; ++j)
-      if (j < nt) issue(j);
+    query_issue();
     uint4_ F[8][FCH];
     if (nt > 0) {
 #pragma unroll
@@ -603,9 +642,14 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
           F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + gch) * 64 + lane) * 16);
         }
       anchor_issue(w_begin + n16);
+      // always DEPTH-1 tiles, so the wait below has a fixed count: a range
+      // shorter than that re-reads its last tile into slots it never uses
+#pragma unroll
+      for (int j = 0; j < DEPTH - 1; ++j) issue_from(j, j < nt ? j : nt - 1);
+      wait_vmcnt<(DEPTH - 1) * LPT>();
+      __builtin_amdgcn_sched_barrier(0);
+      anchor_finish();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (nt > 0) anchor_finish();
     query_finish();
     // one 16-token tile: wait for its ring slot, rebuild the keys, scores,
     // online softmax, values
