@@ -880,8 +880,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int lay
 }
 
 // Workgroups per decode call: about 16 tiles of 16 tokens per wave (enough to
-// amortize the per-workgroup set-up and keep the merge short), between 256
-// (one per CU) and 4096.  ISKV_DECODE_WORKGROUPS overrides it.
+// amortize the per-workgroup set-up and keep the merge short), between one
+// and 16 per CU, rounded down to a whole number per CU.
+// ISKV_DECODE_WORKGROUPS overrides it.
 int target_workgroups(const Dims &D, int64_t length) {
   static int v = -1;
   if (v < 0) {
@@ -891,10 +892,13 @@ int target_workgroups(const Dims &D, int64_t length) {
   }
   if (v > 0) return v;
   const int64_t tiles = (int64_t)D.units * ((length + 15) / 16);
+  const int64_t cus = D.cus;
   int64_t t = (tiles + 63) / 64;
-  if (t < 256) t = 256;
-  if (t > 4096) t = 4096;
-  return (int)t;
+  if (t < cus) t = cus;
+  if (t > 16 * cus) t = 16 * cus;
+  // a grid just past one workgroup per CU would put a second one on a few
+  // CUs and make them the tail of the launch
+  return (int)(t / cus * cus);
 }
 
 SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
@@ -910,7 +914,7 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
     plan.n_win = (int)((n_e + plan.win_len - 1) / plan.win_len);
   }
   if (n_c > 0) {
-    int64_t want = (target + D.units - 1) / D.units - plan.n_win;
+    int64_t want = target / D.units - plan.n_win;
     if (want < 1) want = 1;
     int64_t nc = (n_c + 127) / 128;                  // at least 2 tiles per wave
     if (nc > want) nc = want;
@@ -937,7 +941,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
     dattr = true;
   }
   // fuse the merge when every workgroup is resident at once
-  const int64_t slots = 256LL * Cfg<R, T>::kOcc;
+  const int64_t slots = (int64_t)M.D.cus * Cfg<R, T>::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<R, T>), grid, dim3(kThreads), dyn, s, M, layer, q, q_pos,
                      out, length, n_c, plan, fused);

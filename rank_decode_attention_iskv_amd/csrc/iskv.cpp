@@ -200,7 +200,9 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
     return ISKV_ENOMEM;
   }
   c->stream = reinterpret_cast<hipStream_t>(hip_stream);
-  if (hipGetDevice(&c->device) != hipSuccess) {
+  if (hipGetDevice(&c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&c->D.cus, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess ||
+      c->D.cus < 1) {
     delete c;
     return ISKV_EDEVICE;
   }

@@ -39,6 +39,7 @@ struct Dims {
   int units;              // batch * kv_heads
   int max_rec;            // decode records per unit
   int rope_anchors;       // anchors in the RoPE table
+  int cus;                // compute units of the device (decode grid sizing)
 };
 
 // Pointers of one layer.
