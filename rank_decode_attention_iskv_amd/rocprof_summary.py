@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 result databases (SQLite) as short text.
 
-    python -m rank_decode_attention_iskv_amd.rocprof_summary trace RUN_results.db [--match S ...]
-        per-kernel dispatch count and duration statistics (us)
+    python -m rank_decode_attention_iskv_amd.rocprof_summary trace RUN_results.db [--match S ...] [--last N]
+        per-kernel dispatch count and duration statistics (us); with --last N,
+        over the last N dispatches of each kernel only
     python -m rank_decode_attention_iskv_amd.rocprof_summary pmc RUN_results.db [--match S ...]
         per-kernel average of every collected counter per dispatch
 
@@ -35,14 +36,16 @@ def _cols(cur, table):
     return {r[1]: i for i, r in enumerate(cur.execute(f"pragma table_info({table})"))}
 
 
-def trace(db: str, match: list[str]) -> str:
+def trace(db: str, match: list[str], last: int = 0) -> str:
     cur = sqlite3.connect(db).cursor()
     t = _table(cur, "kernels")
     ci = _cols(cur, t)
     name_c = "kernel_name" if "kernel_name" in ci else "name"
     stats = defaultdict(list)
-    for r in cur.execute(f"select * from {t}"):
+    for r in sorted(cur.execute(f"select * from {t}"), key=lambda r: r[ci["start"]]):
         stats[r[ci[name_c]]].append((r[ci["end"]] - r[ci["start"]]) / 1000.0)
+    if last > 0:
+        stats = {k: v[-last:] for k, v in stats.items()}
     lines = [f"{'dispatches':>10} {'avg_us':>10} {'median_us':>10} {'min_us':>9} {'max_us':>9} {'total_ms':>9}  kernel"]
     for n, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         s = _short(n)
@@ -84,8 +87,9 @@ def main():
     ap.add_argument("mode", choices=["trace", "pmc"])
     ap.add_argument("db")
     ap.add_argument("--match", nargs="*", default=[])
+    ap.add_argument("--last", type=int, default=0)
     a = ap.parse_args()
-    print(trace(a.db, a.match) if a.mode == "trace" else pmc(a.db, a.match))
+    print(trace(a.db, a.match, a.last) if a.mode == "trace" else pmc(a.db, a.match))
 
 
 if __name__ == "__main__":
