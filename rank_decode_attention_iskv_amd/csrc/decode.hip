@@ -168,34 +168,41 @@ template <int R> __device__ __forceinline__ int bv_swz(int f) { return f & ((R /
 // sum over aligned groups of gp lanes (gp a wave-uniform power of two <= 64):
 // DPP swaps of lane pairs 1 and 2 apart, the half-row and row mirrors, then
 // the 16- and 32-lane swaps; every lane ends with its group's sum
-__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
-  int x = __float_as_int(v), y;
+__device__ __forceinline__ float dpp_mov(float v, int ctrl_sel) {
+  const int x = __float_as_int(v);
+  int y;
   switch (ctrl_sel) {
     case 0: y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;    // quad_perm 1,0,3,2
     case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;    // quad_perm 2,3,0,1
     case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
     default: y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break;  // row_mirror
   }
-  return v + __int_as_float(y);
+  return __int_as_float(y);
 }
 __device__ __forceinline__ float lane_group_sum(float v, int gp) {
-  if (gp >= 2) v = dpp_add(v, 0);
-  if (gp >= 4) v = dpp_add(v, 1);
-  if (gp >= 8) v = dpp_add(v, 2);
-  if (gp >= 16) v = dpp_add(v, 3);
+  if (gp >= 2) v += dpp_mov(v, 0);
+  if (gp >= 4) v += dpp_mov(v, 1);
+  if (gp >= 8) v += dpp_mov(v, 2);
+  if (gp >= 16) v += dpp_mov(v, 3);
   if (gp >= 32) v = xor16_sum(v);
   if (gp >= 64) v = xor32_sum(v);
   return v;
 }
+__device__ __forceinline__ float lane_group_max(float v, int gp) {
+  if (gp >= 2) v = max2(v, dpp_mov(v, 0));
+  if (gp >= 4) v = max2(v, dpp_mov(v, 1));
+  if (gp >= 8) v = max2(v, dpp_mov(v, 2));
+  if (gp >= 16) v = max2(v, dpp_mov(v, 3));
+  if (gp >= 32) v = xor16_max(v);
+  if (gp >= 64) v = xor32_max(v);
+  return v;
+}
 
 template <int R> struct MergeLds {
-  static constexpr int oBv = 0;                            // value basis [128][R/4] float4
-  static constexpr int oW = oBv + kHeadDim * R * 4;        // weight per (record, head) [4096]
-  static constexpr int oPart = oW + 4096 * 4;              // [16][16]
-  static constexpr int oMx = oPart + 16 * 16 * 4;          // [16]
-  static constexpr int oL = oMx + 16 * 4;                  // [16]
-  static constexpr int oAcc = oL + 16 * 4;                 // [16][R + 128]
-  static constexpr int bytes = oAcc + 16 * (R + kHeadDim) * 4;
+  static constexpr int oBv = 0;                              // value basis [128][R/4] float4, swizzled
+  static constexpr int oWt = oBv + kHeadDim * R * 4;         // per wave: weights of 64 records
+  static constexpr int oAcc = oWt + 4 * 64 * 4;              // per wave: acc_C [R], acc_W [128]
+  static constexpr int bytes = oAcc + 4 * (R + kHeadDim) * 4;
 };
 
 // record loads at agent scope (sc1), 16 bytes, through a buffer descriptor
@@ -213,31 +220,34 @@ __device__ __forceinline__ float2 load2_agent(const float *p) {
 }
 
 // Merge of one unit's split records (log-sum-exp combination; compressed
-// records hold p^T C_V, which the value basis maps to head space).  Every
-// global read is issued before the first wait: the value basis by DMA into
-// LDS, the (m, l) pairs and the first record columns into registers.
+// records hold p^T C_V, which the value basis maps to head space).  Each wave
+// merges whole query heads on its own (heads wave, wave + 4, ...): maxima and
+// sums are lane reductions, the weights of a batch of records go through a
+// per-wave LDS slot, so the only workgroup barrier is the one that publishes
+// the value basis.  The wave's first head has its (m, l) pairs and first
+// record batches in flight together with the value basis DMA.
 template <int R>
 __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPlan &plan, int u,
                            uint8_t *lds) {
   using ML = MergeLds<R>;
+  constexpr int CC = R / 4, GC = 64 / CC;              // compressed: float4 columns, lanes per column
+  constexpr int NBC = 8 * GC < 64 ? 8 * GC : 64;       // compressed records per batch (8 loads a lane)
+  constexpr int NBW = 16;                              // window records per batch (32 columns x 2 lanes)
   const floatx4 *s_bv = reinterpret_cast<const floatx4 *>(lds + ML::oBv);
-  float *s_w = reinterpret_cast<float *>(lds + ML::oW);
-  float (*s_part)[16] = reinterpret_cast<float (*)[16]>(lds + ML::oPart);
-  float *s_mx = reinterpret_cast<float *>(lds + ML::oMx);
-  float *s_L = reinterpret_cast<float *>(lds + ML::oL);
-  float (*s_acc)[R + kHeadDim] = reinterpret_cast<float (*)[R + kHeadDim]>(lds + ML::oAcc);
   const Dims &D = M.D;
   const int G = D.group, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n_rec = plan.n_comp + plan.n_win, NE = n_rec * G;
+  const int n_comp = plan.n_comp, n_win = plan.n_win, n_rec = n_comp + n_win;
+  float *wt = reinterpret_cast<float *>(lds + ML::oWt) + wave * 64;
+  float *sacc = reinterpret_cast<float *>(lds + ML::oAcc) + wave * (R + kHeadDim);
   const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
   const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
-  const __amdgpu_buffer_rsrc_t rr = agent_rsrc(acc, NE * kRecStride * 4);
+  const __amdgpu_buffer_rsrc_t rr = agent_rsrc(acc, n_rec * G * kRecStride * 4);
   LayerPtrs P = layer_ptrs(M, layer);
   const uint8_t *Bv = reinterpret_cast<const uint8_t *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
 
-  // ---- issue: value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA).
-  // 16-byte chunk c4 of row f lands at chunk c4 ^ bv_swz(f) of the row, so
-  // the output phase (lane = row) reads without bank conflicts.
+  // ---- value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA).  16-byte
+  // chunk c4 of row f lands at chunk c4 ^ bv_swz(f) of the row, so the output
+  // phase (lane = row) reads without bank conflicts.
 #pragma unroll
   for (int j = 0; j < (R / 2 + 3) / 4; ++j) {
     const int c = wave + 4 * j;
@@ -246,177 +256,111 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
       dma16(Bv + (f * (R / 4) + c4) * 16, lds + ML::oBv + c * 1024);
     }
   }
-  // (m, l) pairs: thread (head mh, part mp) holds records s = mp + 16 k, k < KML
-  constexpr int KML = 4;
-  const int mh = tid & 15, mp = tid >> 4;
-  const bool mok = mh < G;
-  float2 mlp[KML];
+
+  // lane roles: compressed column cc, record group cg (records s = cg mod GC);
+  // window column wc, group wg (records s = wg mod 2)
+  const int cc = lane / GC, cg = lane % GC, wc = lane >> 1, wg = lane & 1;
+  float2 mlp0, mlp1;                    // (m, l) of records lane and 64 + lane
+  floatx4 vc[8], vw[8];                 // first compressed / window batch
+  auto fetch = [&](int h) {
+    mlp0 = lane < n_rec ? load2_agent(ml + 2 * (lane * G + h)) : float2{-INFINITY, 0.f};
+    mlp1 = 64 + lane < n_rec ? load2_agent(ml + 2 * ((64 + lane) * G + h)) : float2{-INFINITY, 0.f};
 #pragma unroll
-  for (int k = 0; k < KML; ++k) {
-    const int s = mp + 16 * k;
-    mlp[k] = mok && s < n_rec ? load2_agent(ml + 2 * (s * G + mh)) : float2{-INFINITY, 0.f};
-  }
-  // record items: (kind, float4 column, record group); thread -> fixed column
-  // and group, records strided by the group count
-  const int cols_c = G * R / 4, cols_w = G * kHeadDim / 4;
-  constexpr int NVC = 12, NVW = 4;          // prefetched float4 per thread (compressed, window)
-  floatx4 vc[NVC], vw[NVW];
-  // a column's record groups are gp adjacent lanes (gp a power of two, at
-  // most 64, so a group never spans two waves): lane shuffles sum them
-  struct Item { int col, grp, groups; bool ok; };
-  auto item_of = [&](int kind, int c0) -> Item {
-    const int cols = kind == 0 ? cols_c : cols_w;
-    const int nc = cols - c0 < kThreads ? cols - c0 : kThreads;
-    int gp = 1;
-    while (gp < 64 && 2 * gp * nc <= kThreads) gp *= 2;
-    return Item{c0 + tid / gp, tid % gp, gp, tid / gp < nc};
+    for (int k = 0; k < 8; ++k) {
+      const int s = cg + GC * k;
+      vc[k] = s < NBC && s < n_comp ? load4_rec(rr, (s * G + h) * kRecStride + 4 * cc) : zero4();
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = wg + 2 * k;
+      vw[k] = s < NBW && s < n_win ? load4_rec(rr, ((n_comp + s) * G + h) * kRecStride + 4 * wc) : zero4();
+    }
   };
-  // the first column chunk of each kind is prefetched (all columns when
-  // G * width / 4 <= 256); loads past the records read zero
-  const Item ic = item_of(0, 0), iw = item_of(1, 0);
-  {
-    const int hc = (ic.col * 4) / R, xc = (ic.col * 4) % R;
-    const bool okc = ic.ok;
-#pragma unroll
-    for (int k = 0; k < NVC; ++k) {
-      const int s = ic.grp + k * ic.groups;
-      vc[k] = okc && s < plan.n_comp ? load4_rec(rr, (s * G + hc) * kRecStride + xc) : zero4();
-    }
-    const int hw = (iw.col * 4) / kHeadDim, xw = (iw.col * 4) % kHeadDim;
-    const bool okw = iw.ok;
-#pragma unroll
-    for (int k = 0; k < NVW; ++k) {
-      const int s = iw.grp + k * iw.groups;
-      vw[k] = okw && s < plan.n_win ? load4_rec(rr, ((plan.n_comp + s) * G + hw) * kRecStride + xw)
-                                    : zero4();
-    }
-  }
-
-  // ---- weights w = exp2(m - max_h), L_h = sum w l; records past the
-  // prefetched ones (more than 16 KML) are read here
+  if (wave < G) fetch(wave);
   wait_vmcnt<0>();
-  float mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < KML; ++k) mx = fmaxf(mx, mlp[k].x);
-  if (mok)
-    for (int s = mp + 16 * KML; s < n_rec; s += 16) {
-      const float m = load_agent(ml + 2 * (s * G + mh));
-      s_w[s * G + mh] = m;
-      mx = fmaxf(mx, m);
-    }
-  s_part[mp][mh] = mx;
-  __syncthreads();               // also: the value basis DMA is complete
-  if (tid < G) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) m = fmaxf(m, s_part[p][tid]);
-    s_mx[tid] = m;
-  }
-  __syncthreads();
-  {
-    const float mh_max = mok ? s_mx[mh] : 0.f;
-    float l = 0.f;
-#pragma unroll
-    for (int k = 0; k < KML; ++k) {
-      const int s = mp + 16 * k;
-      if (mok && s < n_rec) {
-        const float w = __builtin_amdgcn_exp2f(mlp[k].x - mh_max);
-        s_w[s * G + mh] = w;
-        l += w * mlp[k].y;
-      }
-    }
-    if (mok)
-      for (int s = mp + 16 * KML; s < n_rec; s += 16) {
-        const float w = __builtin_amdgcn_exp2f(s_w[s * G + mh] - mh_max);
-        s_w[s * G + mh] = w;
-        l += w * load_agent(ml + 2 * (s * G + mh) + 1);
-      }
-    s_part[mp][mh] = l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = 0.f;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) l += s_part[p][tid];
-    s_L[tid] = l;
-  }
-  __syncthreads();
+  __syncthreads();                      // the value basis is in LDS
 
-  // ---- weighted sums over the records of each kind, float4 columns
-  for (int kind = 0; kind < 2; ++kind) {
-    const int width = kind == 0 ? R : kHeadDim;
-    const int s0 = kind == 0 ? 0 : plan.n_comp;
-    const int n = kind == 0 ? plan.n_comp : plan.n_win;
-    if (n == 0) {
-      for (int e = tid; e < G * width; e += kThreads) s_acc[e / width][(kind ? R : 0) + e % width] = 0.f;
-      continue;
+  const int b = u / D.kv_heads, hk = u % D.kv_heads;
+  for (int h = wave; h < G; h += 4) {
+    if (h != wave) fetch(h);
+    // max and sum over all records: registers for the first 128, reads past
+    float mx = max2(mlp0.x, mlp1.x);
+    for (int s = 128 + lane; s < n_rec; s += 64) mx = max2(mx, load_agent(ml + 2 * (s * G + h)));
+    mx = lane_group_max(mx, 64);
+    float l = __builtin_amdgcn_exp2f(mlp0.x - mx) * mlp0.y + __builtin_amdgcn_exp2f(mlp1.x - mx) * mlp1.y;
+    for (int s = 128 + lane; s < n_rec; s += 64) {
+      const float2 p = load2_agent(ml + 2 * (s * G + h));
+      l += __builtin_amdgcn_exp2f(p.x - mx) * p.y;
     }
-    const int cols = kind == 0 ? cols_c : cols_w;
-    for (int c0 = 0; c0 < cols; c0 += kThreads) {
-      const Item I = item_of(kind, c0);
-      const int h = (I.col * 4) / width, x = (I.col * 4) % width;
+    l = lane_group_sum(l, 64);
+    // weights of records b0 .. b0 + 63 -> wt (lane i: record b0 + i)
+    auto weights = [&](int b0) {
+      const int s = b0 + lane;
+      const float m0 = __shfl(mlp0.x, s & 63), m1 = __shfl(mlp1.x, s & 63);
+      float m = s < 64 ? m0 : m1;
+      if (s >= 128 && s < n_rec) m = load_agent(ml + 2 * (s * G + h));
+      wt[lane] = s < n_rec ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
+    };
+    // compressed records: acc_C = sum w_s acc_s
+    {
       floatx4 a = zero4();
-      if (I.ok) {
-        // weights are read for clamped record indices (all reads issued
-        // together); records past n hold zeros, so their terms vanish
-        auto wt = [&](int sk) { return s_w[(s0 + (sk < n ? sk : n - 1)) * G + h]; };
-        int s = I.grp;
-        if (c0 == 0) {                       // prefetched part
-          if (kind == 0) {
-            float w[NVC];
-#pragma unroll
-            for (int k = 0; k < NVC; ++k) w[k] = wt(s + k * I.groups);
-#pragma unroll
-            for (int k = 0; k < NVC; ++k) a += w[k] * vc[k];
-            s += NVC * I.groups;
-          } else {
-            float w[NVW];
-#pragma unroll
-            for (int k = 0; k < NVW; ++k) w[k] = wt(s + k * I.groups);
-#pragma unroll
-            for (int k = 0; k < NVW; ++k) a += w[k] * vw[k];
-            s += NVW * I.groups;
-          }
-        }
-        // the rest in chunks of 8 records, every load of a chunk issued first
-        for (; s < n; s += 8 * I.groups) {
-          floatx4 v[8];
-          float w[8];
+      for (int b0 = 0; b0 < n_comp; b0 += NBC) {
+        weights(b0);
+        if (b0 > 0) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const int sk = s + k * I.groups;
-            v[k] = sk < n ? load4_rec(rr, ((s0 + sk) * G + h) * kRecStride + x) : zero4();
+            const int s = b0 + cg + GC * k;
+            vc[k] = cg + GC * k < NBC && s < n_comp ? load4_rec(rr, (s * G + h) * kRecStride + 4 * cc) : zero4();
           }
+        }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) w[k] = wt(s + k * I.groups);
+        for (int k = 0; k < 8; ++k) a += wt[(cg + GC * k) & 63] * vc[k];
+      }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) a += w[k] * v[k];
+      for (int j = 0; j < 4; ++j) a[j] = lane_group_sum(a[j], GC);
+      if (cg == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[4 * cc + j] = a[j];
+      }
+    }
+    // window records: acc_W = sum w_s acc_s
+    {
+      floatx4 a = zero4();
+      for (int b0 = n_comp; b0 < n_rec; b0 += NBW) {
+        weights(b0);
+        if (b0 > n_comp) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int s = b0 + wg + 2 * k;
+            vw[k] = s < n_rec ? load4_rec(rr, (s * G + h) * kRecStride + 4 * wc) : zero4();
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a += wt[wg + 2 * k] * vw[k];
+      }
+      a[0] = lane_group_sum(a[0], 2); a[1] = lane_group_sum(a[1], 2);
+      a[2] = lane_group_sum(a[2], 2); a[3] = lane_group_sum(a[3], 2);
+      if (wg == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[R + 4 * wc + j] = a[j];
+      }
+    }
+    // out = (B_V acc_C + acc_W) / L; lane -> features lane, lane + 64
+    const float inv_l = 1.f / l;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = lane + 64 * i;
+      float a = sacc[R + f];
+      if (n_comp > 0) {
+#pragma unroll
+        for (int c4 = 0; c4 < R / 4; ++c4) {
+          const floatx4 bv = s_bv[f * (R / 4) + (c4 ^ bv_swz<R>(f))];
+          a += bv[0] * sacc[4 * c4] + bv[1] * sacc[4 * c4 + 1] + bv[2] * sacc[4 * c4 + 2] +
+               bv[3] * sacc[4 * c4 + 3];
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = lane_group_sum(a[j], I.groups);
-      if (I.ok && I.grp == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s_acc[h][(kind ? R : 0) + x + j] = a[j];
-      }
+      out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a * inv_l;
     }
-  }
-  __syncthreads();
-
-  // ---- out = (B_V acc_C + acc_W) / L
-  const int b = u / D.kv_heads, hk = u % D.kv_heads;
-  for (int e = tid; e < G * kHeadDim; e += kThreads) {
-    const int h = e / kHeadDim, f = e % kHeadDim;
-    float a = s_acc[h][R + f];
-    if (plan.n_comp > 0) {
-#pragma unroll
-      for (int c4 = 0; c4 < R / 4; ++c4) {
-        const floatx4 bv = s_bv[f * (R / 4) + (c4 ^ bv_swz<R>(f))];
-        a += bv[0] * s_acc[h][4 * c4] + bv[1] * s_acc[h][4 * c4 + 1] +
-             bv[2] * s_acc[h][4 * c4 + 2] + bv[3] * s_acc[h][4 * c4 + 3];
-      }
-    }
-    out[((size_t)b * D.q_heads + hk * G + h) * kHeadDim + f] = a / s_L[h];
   }
 }
 
