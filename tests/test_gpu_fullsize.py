@@ -89,12 +89,12 @@ def test_decode_window_bounds_and_ranks(rank, n_extra):
     assert max(errs) < ATOL_OUT, errs
 
 
-@pytest.mark.parametrize("kv_heads,q_heads,batch", [(2, 12, 1), (1, 3, 1), (4, 12, 16)])
+@pytest.mark.parametrize("kv_heads,q_heads,batch", [(2, 12, 1), (1, 3, 1), (4, 12, 16), (8, 8, 1)])
 def test_decode_many_splits_odd_group(kv_heads, q_heads, batch):
-    """Groups of 6 and 3 query heads (not dividing the 256 threads of the
-    merge).  Batch 1 merges in-kernel over more than 64 split records per unit
-    (past the records the merge prefetches); batch 16 (64 units) uses the
-    merge kernel.  r = 32, window 256, bf16, 16K context."""
+    """Groups of 6, 3 and 1 query heads.  Batch 1 merges in-kernel, over more
+    than 128 split records per unit for the single KV head (past the records
+    the merge keeps in registers); batch 16 (64 units) uses the merge kernel.
+    r = 32, window 256, bf16, 16K context."""
     w = workloads.with_(workloads.WORKLOADS[2], batch=batch, kv_heads=kv_heads, q_heads=q_heads)
     n_c = 16384
     length = n_c + w.window + 7
