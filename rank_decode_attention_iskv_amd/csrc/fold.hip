@@ -33,6 +33,10 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kMaxSweeps = 40;
 constexpr float kJacobiTol = 1.0e-6f;     // rotate while |y_p . y_q| > tol |y_p||y_q|
+// Stop after a sweep whose largest |y_p . y_q| / (|y_p||y_q|) (before its
+// rotations) was below this: the cyclic sweep leaves O(that^2) behind, which is
+// at the fp32 floor of the inner products, so a further sweep only chases noise.
+constexpr float kJacobiQuad = 1.0e-3f;
 // A residual direction is dropped when its squared norm is below
 // kGuard * ||A||_F^2 (so kept directions have condition number < ~1/sqrt(kGuard)).
 constexpr float kGuard = 1.0e-7f;
@@ -340,14 +344,6 @@ __device__ __forceinline__ void fwd_solve(float (&x)[n], const float *L0, int ld
 }
 
 // ---------------------------------------------------------------------------
-// One-sided Jacobi on the N rows (length NC, stride LC) of `core`.  A pair
-// (x, y) is rotated while |x.y| > tol |x||y|; the three dot products are
-// recomputed for every pair (norms carried over from earlier rotations would
-// drift by more than the off-diagonal being removed when two norms are
-// close).  Rows whose squared norm is below (64 eps)^2 times the largest are
-// at the rounding level of the core and are left alone.  Returns the number
-// of sweeps that rotated (kMaxSweeps if it did not converge).
-// ---------------------------------------------------------------------------
 // Householder QR of the core (N x NC, N >= NC, rows in LDS): the core is
 // replaced by R (upper triangular, NC nonzero rows; rows past NC become zero).
 // R has the core's singular values and right singular vectors, and the
@@ -438,8 +434,19 @@ __device__ __forceinline__ void qr_rows(float *core, float *vbuf0, float *vbuf1)
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// One-sided Jacobi on the N rows (length NC, stride LC) of `core`.  A pair
+// (x, y) is rotated while |x.y| > tol |x||y|; the three dot products are
+// recomputed for every pair (norms carried over from earlier rotations would
+// drift by more than the off-diagonal being removed when two norms are
+// close).  Rows whose squared norm is below (64 eps)^2 times the largest are
+// at the rounding level of the core and are left alone.  The sweeps stop when
+// one rotates nothing, or when its largest pair measure was below
+// kJacobiQuad.  Returns the number of rotating sweeps, or kMaxSweeps + 1 if
+// it did not converge within kMaxSweeps.
+// ---------------------------------------------------------------------------
 template <int N, int NC, int LC>
-__device__ int jacobi_rows(float *core, int *flag, int *maxbits) {
+__device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
   constexpr int GS = NC % 32 == 0 ? 8 : 4;      // lanes per pair
   constexpr int NP = N / 2, CPT = NC / (4 * GS);
   static_assert(NC % (4 * GS) == 0 && N % 2 == 0, "row shape");
@@ -447,7 +454,8 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits) {
   const int tid = threadIdx.x, li = tid & (GS - 1);
   int sweep = 0;
   for (; sweep < kMaxSweeps; ++sweep) {
-    if (tid == 0) { *flag = 0; *maxbits = 0; }
+    if (tid == 0) { *flag = 0; *maxbits = 0; *maxrel = 0; }
+    float rel = 0.f;                     // this thread's largest pair measure in the sweep
     __syncthreads();
     for (int j = tid; j < N; j += kThreads) {
       const float *row = core + j * LC;
@@ -485,8 +493,10 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits) {
           c0 = fmaf(x[i].z, y[i].z, c0); c1 = fmaf(x[i].w, y[i].w, c1);
         }
         const float a = group_sum<GS>(a0 + a1), b = group_sum<GS>(b0 + b1), c = group_sum<GS>(c0 + c1);
-        if (c != 0.f && a > negl && b > negl &&
-            fabsf(c) > kJacobiTol * (__builtin_amdgcn_sqrtf(a) * __builtin_amdgcn_sqrtf(b))) {
+        const float sab = __builtin_amdgcn_sqrtf(a) * __builtin_amdgcn_sqrtf(b);
+        const bool live = c != 0.f && a > negl && b > negl;
+        if (live) rel = fmaxf(rel, fabsf(c) * __builtin_amdgcn_rcpf(sab));
+        if (live && fabsf(c) > kJacobiTol * sab) {
           // tan of the angle that zeroes the pair's inner product (the
           // smaller root), then cos by rsqrt refined with one Newton step
           const float zeta = (b - a) * __builtin_amdgcn_rcpf(2.f * c);
@@ -512,11 +522,15 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits) {
       }
       __syncthreads();
     }
-    const int rotated = *flag;
+    atomicMax(maxrel, __float_as_int(rel));      // non-negative: int order = float order
     __syncthreads();
-    if (!rotated) break;
+    const int rotated = *flag;
+    const float worst = __int_as_float(*maxrel);
+    __syncthreads();
+    if (!rotated) return sweep;
+    if (worst < kJacobiQuad) return sweep + 1;
   }
-  return sweep;
+  return kMaxSweeps + 1;
 }
 
 template <int R, typename T>
@@ -649,8 +663,8 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   // ---------------- phase 4: QR of the core, one-sided Jacobi on R ----------
   {
     qr_rows<N, NC, LC>(core, sig, reinterpret_cast<float *>(perm));
-    const int sweeps = jacobi_rows<NC, NC, LC>(core, &s_int[0], &s_int[2]);
-    if (sweeps >= kMaxSweeps && tid == 0) set_flag(M.sh, 2);
+    const int sweeps = jacobi_rows<NC, NC, LC>(core, &s_int[0], &s_int[2], &s_int[3]);
+    if (sweeps > kMaxSweeps && tid == 0) set_flag(M.sh, 2);
   }
 
   // ---------------- phase 5: singular values, descending order -------------
