@@ -436,17 +436,18 @@ __device__ __forceinline__ void qr_rows(float *core, float *vbuf0, float *vbuf1)
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // One-sided Jacobi on the N rows (length NC, stride LC) of `core`.  A pair
-// (x, y) is rotated while |x.y| > tol |x||y|; the three dot products are
-// recomputed for every pair (norms carried over from earlier rotations would
-// drift by more than the off-diagonal being removed when two norms are
-// close).  Rows whose squared norm is below (64 eps)^2 times the largest are
-// at the rounding level of the core and are left alone.  The sweeps stop when
-// one rotates nothing, or when its largest pair measure was below
-// kJacobiQuad.  Returns the number of rotating sweeps, or kMaxSweeps + 1 if
+// (x, y) is rotated while |x.y| > tol |x||y|.  The squared row norms are
+// computed at the start of each sweep and carried through its rotations
+// (|x'|^2 = |x|^2 - t x.y, |y'|^2 = |y|^2 + t x.y), so a pair only forms x.y;
+// carried over more than one sweep they drifted and stalled convergence on
+// clusters of near-equal singular values.  Rows whose squared norm is below
+// (64 eps)^2 times the largest are at the rounding level of the core and are
+// left alone.  The sweeps stop when one rotates nothing, or when its largest
+// pair measure was below kJacobiQuad.  Returns the number of rotating sweeps, or kMaxSweeps + 1 if
 // it did not converge within kMaxSweeps.
 // ---------------------------------------------------------------------------
 template <int N, int NC, int LC>
-__device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
+__device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int *bigflag) {
   constexpr int GS = NC % 32 == 0 ? 8 : 4;      // lanes per pair
   constexpr int NP = N / 2, CPT = NC / (4 * GS);
   static_assert(NC % (4 * GS) == 0 && N % 2 == 0, "row shape");
@@ -454,8 +455,8 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
   const int tid = threadIdx.x, li = tid & (GS - 1);
   int sweep = 0;
   for (; sweep < kMaxSweeps; ++sweep) {
-    if (tid == 0) { *flag = 0; *maxbits = 0; *maxrel = 0; }
-    float rel = 0.f;                     // this thread's largest pair measure in the sweep
+    if (tid == 0) { *flag = 0; *maxbits = 0; *bigflag = 0; }
+    int big = 0;                         // a pair measure of this thread reached kJacobiQuad
     __syncthreads();
     for (int j = tid; j < N; j += kThreads) {
       const float *row = core + j * LC;
@@ -466,10 +467,12 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
         s0 = fmaf(v.x, v.x, s0); s1 = fmaf(v.y, v.y, s1);
         s0 = fmaf(v.z, v.z, s0); s1 = fmaf(v.w, v.w, s1);
       }
+      nrm[j] = s0 + s1;
       atomicMax(maxbits, __float_as_int(s0 + s1));
     }
     __syncthreads();
     const float negl = kNegl * __int_as_float(*maxbits);
+    const float inv_max = __int_as_float(*maxbits) > 0.f ? 1.f / __int_as_float(*maxbits) : 0.f;
     for (int k = 0; k < N - 1; ++k) {
       for (int g = tid / GS; g < NP; g += kThreads / GS) {
         int p, q;
@@ -482,21 +485,19 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
           x[i] = ld4(rp + 4 * GS * i);
           y[i] = ld4(rq + 4 * GS * i);
         }
-        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+        float c0 = 0.f, c1 = 0.f;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-          a0 = fmaf(x[i].x, x[i].x, a0); a1 = fmaf(x[i].y, x[i].y, a1);
-          a0 = fmaf(x[i].z, x[i].z, a0); a1 = fmaf(x[i].w, x[i].w, a1);
-          b0 = fmaf(y[i].x, y[i].x, b0); b1 = fmaf(y[i].y, y[i].y, b1);
-          b0 = fmaf(y[i].z, y[i].z, b0); b1 = fmaf(y[i].w, y[i].w, b1);
           c0 = fmaf(x[i].x, y[i].x, c0); c1 = fmaf(x[i].y, y[i].y, c1);
           c0 = fmaf(x[i].z, y[i].z, c0); c1 = fmaf(x[i].w, y[i].w, c1);
         }
-        const float a = group_sum<GS>(a0 + a1), b = group_sum<GS>(b0 + b1), c = group_sum<GS>(c0 + c1);
-        const float sab = __builtin_amdgcn_sqrtf(a) * __builtin_amdgcn_sqrtf(b);
+        const float a = nrm[p], b = nrm[q], c = group_sum<GS>(c0 + c1);
+        // the pair measure |c| / sqrt(a b) compared through squares (a, b > 0),
+        // on values scaled by the largest squared row norm (no overflow)
+        const float cs_ = c * inv_max, c2 = cs_ * cs_, ab = (a * inv_max) * (b * inv_max);
         const bool live = c != 0.f && a > negl && b > negl;
-        if (live) rel = fmaxf(rel, fabsf(c) * __builtin_amdgcn_rcpf(sab));
-        if (live && fabsf(c) > kJacobiTol * sab) {
+        if (live && c2 > (kJacobiQuad * kJacobiQuad) * ab) big = 1;
+        if (live && c2 > (kJacobiTol * kJacobiTol) * ab) {
           // tan of the angle that zeroes the pair's inner product (the
           // smaller root), then cos by rsqrt refined with one Newton step
           const float zeta = (b - a) * __builtin_amdgcn_rcpf(2.f * c);
@@ -517,18 +518,21 @@ __device__ int jacobi_rows(float *core, int *flag, int *maxbits, int *maxrel) {
             st4(rq + 4 * GS * i, make_float4(sn * u.x + cs * v.x, sn * u.y + cs * v.y,
                                          sn * u.z + cs * v.z, sn * u.w + cs * v.w));
           }
-          if (li == 0) *flag = 1;
+          if (li == 0) {
+            *flag = 1;
+            nrm[p] = fmaf(-t, c, a);          // |x'|^2 = a - t c, |y'|^2 = b + t c
+            nrm[q] = fmaf(t, c, b);
+          }
         }
       }
       __syncthreads();
     }
-    atomicMax(maxrel, __float_as_int(rel));      // non-negative: int order = float order
+    if (big) *bigflag = 1;
     __syncthreads();
-    const int rotated = *flag;
-    const float worst = __int_as_float(*maxrel);
+    const int rotated = *flag, any_big = *bigflag;
     __syncthreads();
     if (!rotated) return sweep;
-    if (worst < kJacobiQuad) return sweep + 1;
+    if (!any_big) return sweep + 1;
   }
   return kMaxSweeps + 1;
 }
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   // ---------------- phase 4: QR of the core, one-sided Jacobi on R ----------
   {
     qr_rows<N, NC, LC>(core, sig, reinterpret_cast<float *>(perm));
-    const int sweeps = jacobi_rows<NC, NC, LC>(core, &s_int[0], &s_int[2], &s_int[3]);
+    const int sweeps = jacobi_rows<NC, NC, LC>(core, lds + Ly::oNrm, &s_int[0], &s_int[2], &s_int[3]);
     if (sweeps > kMaxSweeps && tid == 0) set_flag(M.sh, 2);
   }
 
