@@ -5,10 +5,11 @@ head_dim 128, rank 32, 32K-token context, exact window 256, bf16 storage with
 fp32 accumulation, batch 1; a block update + sync every 64 decode steps; keys
 and values are a rank-32 Gaussian signal plus 1% noise (synthetic, seeded).
 
-A step is one decode step of that layer: append one token (k, v), decode
-attention of 32 query heads over the whole mixed cache, and -- whenever the
-ring holds window + 64 tokens -- a block update (Brand fold of 64 tokens for
-all 8 heads, K and V) followed by the coefficient sync.  The bench holds
+A step is one decode step of that layer: append one token (k, v) and decode
+attention of 32 query heads over the whole mixed cache (one launch,
+iskv_append_decode), and -- whenever the ring holds window + 64 tokens -- a
+block update (Brand fold of 64 tokens for all 8 heads, K and V) followed by
+the coefficient sync.  The bench holds
 several independent instances of the layer and runs the steps round-robin
 over them, so every step reads its cache from HBM rather than from the 256 MB
 Infinity Cache (one instance is ~35 MB).
@@ -278,29 +279,29 @@ def main():
         inst = s % I
         j = used[inst]
         used[inst] += 1
-        code = L_.iskv_append(ctx, inst, ctypes.c_void_p(k_base[inst] + j * tok_bytes),
-                              ctypes.c_void_p(v_base[inst] + j * tok_bytes), 1, binding.F32,
-                              ctypes.byref(ready_c))
-        if code != 0:
-            raise binding.IskvError(code, "iskv_append")
-        ready = bool(ready_c.value)
         lengths[inst] += 1
         L, n_c = lengths[inst], comp[inst]
+        kp = ctypes.c_void_p(k_base[inst] + j * tok_bytes)
+        vp = ctypes.c_void_p(v_base[inst] + j * tok_bytes)
         qp = ctypes.c_void_p(q_base + s * q_bytes)
+        # append + decode attention of the step in one launch (iskv_append_decode)
         if timed and not warm:
             e0, e1 = ev_pool[len(ev)]
             if mstream is not None:
                 L_.iskv_join_maintenance(ctx, inst)   # a wait for this instance's fold stays outside e0..e1
             e0.record(stream)
-            code = L_.iskv_decode_attn(ctx, inst, qp, L - 1, out_p)
+            code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
+                                         ctypes.byref(ready_c))
             e1.record(stream)
             nb = decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
             ev.append((e0, e1, nb))
             bytes_total += nb
         else:
-            code = L_.iskv_decode_attn(ctx, inst, qp, L - 1, out_p)
+            code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
+                                         ctypes.byref(ready_c))
         if code != 0:
-            raise binding.IskvError(code, "iskv_decode_attn")
+            raise binding.IskvError(code, "iskv_append_decode")
+        ready = bool(ready_c.value)
         if ready:
             if warm or (timed and (not args.async_maintenance)):
                 f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -392,6 +393,7 @@ def main():
             "global_batch": B,
             "seq_len": args.context,
             "parallelism": "single GPU",
+            "step_calls": "iskv_append_decode; every 64 steps per instance iskv_block_update + iskv_sync",
             "maintenance": "same stream" if (not args.async_maintenance) else
                            "second stream (each instance waits for its own fold + sync)",
         },

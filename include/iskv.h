@@ -156,6 +156,16 @@ int iskv_discard_sync(iskv_ctx *c, int layer);
  * layer is empty. */
 int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out);
 
+/* One decode step in one launch: iskv_append of a single token (dev_k, dev_v:
+ * [batch][1][num_kv_heads][head_dim], in_dtype ISKV_F32 or ISKV_BF16)
+ * followed by iskv_decode_attn, with the same results, ring contents, error
+ * codes and *blocks_ready as the two calls (the workgroup that attends over
+ * the newest position writes its ring rows first).  Saves one launch per
+ * step of an append-then-attend loop [iS-KV explainer, the window paragraph:
+ * each new token enters the exact window and is attended to at once]. */
+int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int in_dtype,
+                       const float *dev_q, int64_t q_pos, float *dev_out, int *blocks_ready);
+
 /* Synchronizes the stream; fills *st for one layer.  Returns ISKV_ENUMERIC if
  * any numeric flag is set (st is still filled), else ISKV_OK. */
 int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st);

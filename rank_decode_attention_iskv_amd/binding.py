@@ -46,7 +46,7 @@ class Status(ctypes.Structure):
 EXPORTED = (
     "iskv_workspace_bytes", "iskv_state_bytes", "iskv_init", "iskv_append",
     "iskv_block_update", "iskv_sync", "iskv_discard_sync", "iskv_decode_attn",
-    "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_set_maintenance_stream",
+    "iskv_append_decode", "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_set_maintenance_stream",
     "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
 )
 
@@ -67,6 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_sync": (I, [P, I]),
         "iskv_discard_sync": (I, [P, I]),
         "iskv_decode_attn": (I, [P, I, P, I64, P]),
+        "iskv_append_decode": (I, [P, I, P, P, I, P, I64, P, ctypes.POINTER(I)]),
         "iskv_status": (I, [P, I, ctypes.POINTER(Status)]),
         "iskv_export_state": (I, [P, I, P, SZ]),
         "iskv_import_state": (I, [P, I, P, SZ]),
@@ -179,6 +180,30 @@ class IskvCache:
                                       int(q_pos), ctypes.c_void_p(out.data_ptr())),
                "iskv_decode_attn")
         return out
+
+    def append_decode(self, layer: int, k, v, q, q_pos: int, out) -> bool:
+        """append(layer, k, v) of one token (k, v [batch, 1, kv_heads, head_dim])
+        then decode_attn(layer, q, q_pos, out), in one launch.  Returns
+        blocks_ready."""
+        torch = self.torch
+        if k.dtype != v.dtype or k.shape != v.shape or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        if k.dim() != 4 or k.shape[1] != 1:
+            raise ValueError("k, v must be [batch, 1, kv_heads, head_dim]")
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k, v must be float32 or bfloat16")
+        if q.dtype != torch.float32 or out.dtype != torch.float32:
+            raise ValueError("q and out must be float32")
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        dt = BF16 if k.dtype == torch.bfloat16 else F32
+        ready = ctypes.c_int(0)
+        _check(lib().iskv_append_decode(self.ctx, layer, ctypes.c_void_p(k.data_ptr()),
+                                        ctypes.c_void_p(v.data_ptr()), dt,
+                                        ctypes.c_void_p(q.data_ptr()), int(q_pos),
+                                        ctypes.c_void_p(out.data_ptr()), ctypes.byref(ready)),
+               "iskv_append_decode")
+        return bool(ready.value)
 
     def status(self, layer: int = 0, raise_numeric: bool = False) -> Status:
         st = Status()

@@ -396,7 +396,7 @@ template <int R, typename T> struct Cfg {
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
-    int64_t n_c, SplitPlan plan, int fused) {
+    int64_t n_c, SplitPlan plan, int fused, FusedAppend app) {
   using C = Cfg<R, T>;
   constexpr bool BF = C::BF;
   constexpr int NBV = R / 16;                            // value N-blocks (compressed)
@@ -703,6 +703,19 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       for (int i = 0; i < 4; ++i) s_acc[wave][4 * rho + i][16 * nb + n16] = vacc[nb][i];
   } else {
     // ================= exact window tokens =================
+    if (app.k != nullptr && split == (int)gridDim.x - 1) {
+      // fused append: this split ends at the newest position; write its ring
+      // rows (rounded to the storage type) before the barrier in query_finish,
+      // after which this workgroup reads them
+      const int e = threadIdx.x & (kHeadDim - 1), x = threadIdx.x >> 7;   // K for x = 0, V for x = 1
+      const size_t src = ((size_t)b * D.kv_heads + hk) * kHeadDim + e;
+      const float val = app.in_dtype == 1 ? bf16_to_f32(reinterpret_cast<const bf16_t *>(x ? app.v : app.k)[src].bits)
+                                          : reinterpret_cast<const float *>(x ? app.v : app.k)[src];
+      if (!isfinite(val)) set_flag(M.sh, 4);
+      const int slot = (int)((length - 1) % D.slots);
+      T *ring = reinterpret_cast<T *>(x ? P.ringv : P.ringk) + (size_t)u * D.slots * kHeadDim;
+      Store<T>::store(ring, x ? (size_t)e * D.slots + slot : (size_t)slot * kHeadDim + e, val);
+    }
     floatx4 wacc[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) wacc[nb] = zero4();
@@ -872,7 +885,7 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
 
 template <int R, typename T>
 hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                       int64_t length, int64_t n_c, hipStream_t s) {
+                       int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
   const SplitPlan plan = make_plan(M.D, length, n_c);
   dim3 grid(plan.n_comp + plan.n_win, M.D.units);
   constexpr int dyn = Cfg<R, T>::kDynBytes;
@@ -888,7 +901,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   const int64_t slots = (int64_t)M.D.cus * Cfg<R, T>::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<R, T>), grid, dim3(kThreads), dyn, s, M, layer, q, q_pos,
-                     out, length, n_c, plan, fused);
+                     out, length, n_c, plan, fused, app);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   constexpr int mbytes = MergeLds<R>::bytes;
@@ -906,12 +919,12 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
 
 template <typename T>
 hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                           int64_t length, int64_t n_c, hipStream_t s) {
+                           int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
   switch (M.D.r) {
-    case 16: return launch_mfma<16, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 32: return launch_mfma<32, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 64: return launch_mfma<64, T>(M, layer, q, q_pos, out, length, n_c, s);
-    case 128: return launch_mfma<128, T>(M, layer, q, q_pos, out, length, n_c, s);
+    case 16: return launch_mfma<16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 32: return launch_mfma<32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 64: return launch_mfma<64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 128: return launch_mfma<128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
   }
   return hipErrorInvalidValue;
 }
@@ -919,9 +932,9 @@ hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_
 }  // namespace
 
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                         int64_t length, int64_t n_c, hipStream_t s) {
-  return M.D.storage == 1 ? dispatch_decode<bf16_t>(M, layer, q, q_pos, out, length, n_c, s)
-                          : dispatch_decode<float>(M, layer, q, q_pos, out, length, n_c, s);
+                         int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
+  return M.D.storage == 1 ? dispatch_decode<bf16_t>(M, layer, q, q_pos, out, length, n_c, s, app)
+                          : dispatch_decode<float>(M, layer, q, q_pos, out, length, n_c, s, app);
 }
 
 }  // namespace iskv

@@ -382,6 +382,23 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
   return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
 }
 
+int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int in_dtype,
+                       const float *dev_q, int64_t q_pos, float *dev_out, int *blocks_ready) {
+  if (!c || check_layer(c, layer) || !dev_k || !dev_v || !dev_q || !dev_out) return ISKV_EINVAL;
+  if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
+  if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
+  LayerState &L = c->layers[layer];
+  if (L.length - L.n_c + 1 > c->D.slots) return ISKV_ESTATE;
+  if (L.length + 1 > c->D.max_tokens) return ISKV_ESTATE;
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
+  const FusedAppend app{dev_k, dev_v, in_dtype};
+  hipError_t e = launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length + 1, L.n_c, c->stream, app);
+  if (e != hipSuccess) return ISKV_EDEVICE;
+  L.length += 1;
+  if (blocks_ready) *blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
+  return ISKV_OK;
+}
+
 int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
   if (!c || !st || check_layer(c, layer)) return ISKV_EINVAL;
   if (join_all(c) != hipSuccess) return ISKV_EDEVICE;

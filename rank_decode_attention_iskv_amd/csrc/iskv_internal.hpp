@@ -150,8 +150,17 @@ hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, hipSt
 // Rebuild the decode operand copy of the basis from the fp32 basis.
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s);
 
-// Decode attention for one layer.
+// A token appended by the decode launch itself (k, v: [batch][1][kv_heads][d],
+// in_dtype 0 f32, 1 bf16; k == nullptr: none).  The workgroup whose window
+// split ends at the newest position writes its ring rows before reading them.
+struct FusedAppend {
+  const void *k, *v;
+  int in_dtype;
+};
+
+// Decode attention for one layer.  With a fused append, `length` already
+// counts the appended token.
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                         int64_t length, int64_t n_c, hipStream_t s);
+                         int64_t length, int64_t n_c, hipStream_t s, FusedAppend app = FusedAppend{});
 
 }  // namespace iskv

@@ -311,3 +311,48 @@ def test_maintenance_stream_matches_single_stream():
             for fa, fb in zip(xa, xb):
                 for key in ("basis", "S", "coef", "ring"):
                     np.testing.assert_array_equal(fa[key], fb[key])
+
+
+@pytest.mark.parametrize("storage,in_bf16", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_append_decode_matches_append_then_decode(storage, in_bf16):
+    """iskv_append_decode (one launch) gives bit-identical outputs, ready flags
+    and states to iskv_append followed by iskv_decode_attn, token by token
+    over three folds; on a full ring it fails like iskv_append."""
+    import torch
+    from rank_decode_attention_iskv_amd import binding
+    w = small(2, kv_heads=2, q_heads=8, window=128, storage=storage)
+    a = Pair(w, max_tokens=64 * 12, oracle=False)
+    b = Pair(w, max_tokens=64 * 12, oracle=False)
+    a.feed(0, 128 + 40)
+    b.feed(0, 128 + 40)
+    dt = torch.bfloat16 if in_bf16 else torch.float32
+    folds = 0
+    for step in range(200):
+        pos = a.length[0]
+        k, v = workloads.tokens(w, 0, pos, 1)
+        kt = torch.from_numpy(k.astype(np.float32)).cuda().to(dt).contiguous()
+        vt = torch.from_numpy(v.astype(np.float32)).cuda().to(dt).contiguous()
+        qt = torch.from_numpy(q32(workloads.query(w, 0, step)).astype(np.float32)).cuda()
+        oa, ob = torch.empty_like(qt), torch.empty_like(qt)
+        ra = a.gpu.append(0, kt, vt)
+        a.gpu.decode_attn(0, qt, pos, oa)
+        rb = b.gpu.append_decode(0, kt, vt, qt, pos, ob)
+        a.length[0] += 1
+        b.length[0] += 1
+        torch.cuda.synchronize()
+        assert ra == rb
+        assert torch.equal(oa, ob), step
+        if ra:
+            with pytest.raises(binding.IskvError):
+                b.gpu.append_decode(0, kt, vt, qt, pos + 1, ob)
+            for p in (a, b):
+                p.gpu.block_update(0)
+                p.gpu.sync(0)
+            folds += 1
+    assert folds >= 3
+    (la, na, ua), (lb, nb, ub) = a.state(0), b.state(0)
+    assert (la, na) == (lb, nb)
+    for xa, xb in zip(ua, ub):
+        for fa, fb in zip(xa, xb):
+            for key in ("basis", "S", "coef", "ring"):
+                np.testing.assert_array_equal(fa[key], fb[key])
