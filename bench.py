@@ -272,7 +272,7 @@ def main():
     out_p = ctypes.c_void_p(out.data_ptr())
     ready_c = ctypes.c_int(0)
     ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(args.warmup)]
 
     def step(s, timed, warm=False):
         nonlocal bytes_total, folds, mstream
@@ -284,21 +284,19 @@ def main():
         kp = ctypes.c_void_p(k_base[inst] + j * tok_bytes)
         vp = ctypes.c_void_p(v_base[inst] + j * tok_bytes)
         qp = ctypes.c_void_p(q_base + s * q_bytes)
-        # append + decode attention of the step in one launch (iskv_append_decode)
-        if timed and not warm:
+        # append + decode attention of the step in one launch (iskv_append_decode);
+        # warm-up steps carry an event pair around it, timed steps carry none
+        if warm:
             e0, e1 = ev_pool[len(ev)]
-            if mstream is not None:
-                L_.iskv_join_maintenance(ctx, inst)   # a wait for this instance's fold stays outside e0..e1
             e0.record(stream)
             code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
                                          ctypes.byref(ready_c))
             e1.record(stream)
-            nb = decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
-            ev.append((e0, e1, nb))
-            bytes_total += nb
+            ev.append((e0, e1, decode_bytes(B, H, HQ, D, R, n_c, L - n_c)))
         else:
             code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
                                          ctypes.byref(ready_c))
+            bytes_total += decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
         if code != 0:
             raise binding.IskvError(code, "iskv_append_decode")
         ready = bool(ready_c.value)
@@ -339,8 +337,8 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
 
-    dec_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_ms = [a.elapsed_time(b) for a, b, _ in ev]          # warm-up steps only
+    dec_avg_ms = sum(dec_ms) / len(dec_ms) if dec_ms else None
 
     # ---- roofline of the decode kernel: one event pair around back-to-back
     # decode calls over the instances at their final lengths (the per-step
@@ -408,9 +406,9 @@ def main():
             "algorithmic_bytes_per_launch": bytes_avg,
             "avg_launch_us": rl_avg_ms * 1e3,
             "launches_timed": rl_calls,
-            "avg_launch_us_in_step": dec_avg_ms * 1e3,
+            "avg_launch_us_in_step": dec_avg_ms * 1e3 if dec_avg_ms else None,
         },
-        "decode_attn_tokens_per_s_kernel_only": 1e3 / dec_avg_ms,
+        "decode_attn_calls_per_s_kernel_only": 1e3 / rl_avg_ms,
         "block_updates_per_s": (units_per_fold * len(fold_ms) / (sum(fold_ms) * 1e-3)) if fold_ms else None,
         "block_updates_per_s_with_sync": (units_per_fold * len(fold_ms) /
                                           ((sum(fold_ms) + sum(sync_ms)) * 1e-3)) if fold_ms else None,
