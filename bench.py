@@ -71,6 +71,36 @@ def copy_calibration():
                       "bytes_read_per_dispatch": 4 * n, "bytes_written_per_dispatch": 4 * n}), flush=True)
 
 
+def stream_bandwidth():
+    """HBM bandwidth this GPU actually reaches on trivial streaming kernels
+    (1 GiB float32): a read-only reduction (x.sum()) and a copy (y <- x, read
+    + write bytes).  The best of ten dispatches each, timed by events on the
+    current stream, outside the timed region; a second reference for the
+    roofline next to the nominal 8 TB/s."""
+    import torch
+    n = 256 << 20
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), device="cuda")
+
+    def best(fn, nbytes):
+        fn()
+        times = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return nbytes / (min(times) * 1e-3) / 1e9
+
+    read = best(lambda: torch.sum(src, dim=0, out=acc), 4 * n)
+    copy = best(lambda: dst.copy_(src), 8 * n)
+    del src, dst
+    return read, copy
+
+
 # ---------------------------------------------------------------------------
 # synthetic inputs (GPU-side generation, before the timed region)
 # ---------------------------------------------------------------------------
@@ -368,6 +398,7 @@ def main():
     value = args.steps / (total_ms * 1e-3)
     kh = kernel_source_hash()
     traffic = committed_traffic(kh)
+    bw_read, bw_copy = stream_bandwidth()
 
     res = {
         "metric": METRIC,
@@ -407,6 +438,9 @@ def main():
             "avg_launch_us": rl_avg_ms * 1e3,
             "launches_timed": rl_calls,
             "avg_launch_us_in_step": dec_avg_ms * 1e3 if dec_avg_ms else None,
+            "measured_stream_read_GBs": bw_read,
+            "measured_stream_copy_GBs": bw_copy,
+            "frac_of_measured_read": achieved / bw_read,
         },
         "decode_attn_calls_per_s_kernel_only": 1e3 / rl_avg_ms,
         "block_updates_per_s": (units_per_fold * len(fold_ms) / (sum(fold_ms) * 1e-3)) if fold_ms else None,

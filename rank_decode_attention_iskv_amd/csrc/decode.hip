@@ -120,6 +120,13 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier that publishes LDS writes only: waits for this wave's
+// LDS operations, not for its vector-memory loads in flight (the memory
+// clobber keeps the compiler from moving memory accesses across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Online softmax over one 16-token tile for the lane's head (l%16) and tokens
 // 4*(l/16)..+3.  Rescales the value accumulators (lane layout: heads
@@ -198,11 +205,11 @@ __device__ __forceinline__ float lane_group_max(float v, int gp) {
   return v;
 }
 
-template <int R> struct MergeLds {
+template <int R, int NW> struct MergeLds {
   static constexpr int oBv = 0;                              // value basis [128][R/4] float4, swizzled
   static constexpr int oWt = oBv + kHeadDim * R * 4;         // per wave: weights of 64 records
-  static constexpr int oAcc = oWt + 4 * 64 * 4;              // per wave: acc_C [R], acc_W [128]
-  static constexpr int bytes = oAcc + 4 * (R + kHeadDim) * 4;
+  static constexpr int oAcc = oWt + NW * 64 * 4;             // per wave: acc_C [R], acc_W [128]
+  static constexpr int bytes = oAcc + NW * (R + kHeadDim) * 4;
 };
 
 // record loads at agent scope (sc1), 16 bytes, through a buffer descriptor
@@ -220,16 +227,17 @@ __device__ __forceinline__ float2 load2_agent(const float *p) {
 }
 
 // Merge of one unit's split records (log-sum-exp combination; compressed
-// records hold p^T C_V, which the value basis maps to head space).  Each wave
-// merges whole query heads on its own (heads wave, wave + 4, ...): maxima and
+// records hold p^T C_V, which the value basis maps to head space), by a
+// workgroup of NW waves.  Each wave merges whole query heads on its own
+// (heads wave, wave + NW, ...): maxima and
 // sums are lane reductions, the weights of a batch of records go through a
 // per-wave LDS slot, so the only workgroup barrier is the one that publishes
 // the value basis.  The wave's first head has its (m, l) pairs and first
 // record batches in flight together with the value basis DMA.
-template <int R>
+template <int R, int NW>
 __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPlan &plan, int u,
                            uint8_t *lds) {
-  using ML = MergeLds<R>;
+  using ML = MergeLds<R, NW>;
   constexpr int CC = R / 4, GC = 64 / CC;              // compressed: float4 columns, lanes per column
   constexpr int NBC = 8 * GC < 64 ? 8 * GC : 64;       // compressed records per batch (8 loads a lane)
   constexpr int NBW = 16;                              // window records per batch (32 columns x 2 lanes)
@@ -249,8 +257,8 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   // chunk c4 of row f lands at chunk c4 ^ bv_swz(f) of the row, so the output
   // phase (lane = row) reads without bank conflicts.
 #pragma unroll
-  for (int j = 0; j < (R / 2 + 3) / 4; ++j) {
-    const int c = wave + 4 * j;
+  for (int j = 0; j < (R / 2 + NW - 1) / NW; ++j) {
+    const int c = wave + NW * j;
     if (c < R / 2) {
       const int pos = c * 64 + lane, f = pos / (R / 4), c4 = (pos % (R / 4)) ^ bv_swz<R>(f);
       dma16(Bv + (f * (R / 4) + c4) * 16, lds + ML::oBv + c * 1024);
@@ -281,7 +289,7 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   __syncthreads();                      // the value basis is in LDS
 
   const int b = u / D.kv_heads, hk = u % D.kv_heads;
-  for (int h = wave; h < G; h += 4) {
+  for (int h = wave; h < G; h += NW) {
     if (h != wave) fetch(h);
     // max and sum over all records: registers for the first 128, reads past
     float mx = max2(mlp0.x, mlp1.x);
@@ -365,47 +373,72 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
 }
 
 // ---------------------------------------------------------------------------
-// Tunables per (rank, storage): workgroups per CU and the per-wave LDS ring.
+// Tunables per (rank, storage, waves per workgroup): occupancy, the LDS
+// layout and the per-wave ring.
 // ---------------------------------------------------------------------------
-template <int R, typename T> struct Cfg {
+template <int R, typename T, int NW> struct Cfg {
   static constexpr bool BF = std::is_same<T, bf16_t>::value;
   static constexpr int kElem = BF ? 2 : 4;
   static constexpr int kMatBytes = 16 * R * kElem;           // one 16-token tile of C_K or C_V
   static constexpr int kDma = kMatBytes >= 1024 ? kMatBytes / 1024 : 1;   // dwordx4 DMAs per matrix
-  // bf16 r = 64: the low bf16 parts of the key-basis fragments live in LDS
-  // (16 KiB per workgroup) instead of registers, so two workgroups fit per CU
+  // Eight-wave workgroups (bf16, r <= 64; one per CU, two waves per SIMD)
+  // share their prologue: the key-basis fragments and the RoPE rotations of
+  // offsets 0..15 reach LDS once per workgroup by DMA, and each wave's base
+  // angle takes one coalesced load per lane (lane = frequency).  Four-wave
+  // workgroups load both per wave.
+  static_assert(NW == 4 || (NW == 8 && BF && R <= 64), "wave count");
+  static constexpr bool kShared = NW == 8;
+  // bf16 r = 64: the low bf16 parts of the key-basis fragments are read from
+  // LDS in the loop instead of registers (which two waves per SIMD lack)
   static constexpr bool kLoLds = BF && R == 64;
-  static constexpr int kFloBytes = kLoLds ? 8 * (R / 32) * 1024 : 0;
-  // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring
-  static constexpr int kRingBytes = kLoLds ? 12288 : (kMatBytes >= 4096 ? 32768 : 16384);
+  // shared prologue data sits in static LDS arrays (fragments, step rows,
+  // per-wave base angles): reads of them are then known not to alias the
+  // ring DMAs in flight, so the compiler adds no wait for those.  Dynamic
+  // LDS: [low-part fragments (four waves, r = 64) | per-wave rings]
+  static constexpr int kFragBytes = kShared ? 8 * (R / 16) * 1024 : 16;
+  static constexpr int kRingOff = (!kShared && kLoLds) ? 8 * (R / 32) * 1024 : 0;
+  // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring.
+  // Eight-wave workgroups keep four r <= 32 tiles per wave (eight waves per
+  // CU hold enough bytes in flight, and a shorter ring is issued sooner)
+  static constexpr int kRingBytes = kShared ? (R == 64 ? 12288 : 8192)
+                                    : kLoLds ? 12288 : (kMatBytes >= 4096 ? 32768 : 16384);
   static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
   static_assert(kDepth >= 2, "ring depth");
-  static constexpr int kOcc = (BF && R <= 64) ? 2 : 1;
+  static constexpr int kWaves = NW;
+  static constexpr int kThr = 64 * NW;
+  static constexpr int kOcc = (BF && R <= 64 && NW == 4) ? 2 : 1;
   // compressed tiles in pairs (two register sets for the angle state); wider
   // ranks lack the registers for it
   static constexpr bool kPair = R <= 32;
-  static constexpr int kAccBytes = 4 * 16 * kHeadDim * 4;    // per-wave results, after the loop
-  static constexpr int kLoopBytes = (kFloBytes + 4 * kRingBytes > kAccBytes) ? kFloBytes + 4 * kRingBytes
-                                                                            : kAccBytes;
-  static constexpr int kDynBytes = kLoopBytes > MergeLds<R>::bytes ? kLoopBytes : MergeLds<R>::bytes;
+  static constexpr int kAccBytes = kWaves * 16 * kHeadDim * 4;    // per-wave results, after the loop
+  static constexpr int kLoopBytes = (kRingOff + NW * kRingBytes > kAccBytes)
+                                        ? kRingOff + NW * kRingBytes : kAccBytes;
+  static constexpr int kMrgBytes = MergeLds<R, kWaves>::bytes;
+  static constexpr int kDynBytes = kLoopBytes > kMrgBytes ? kLoopBytes : kMrgBytes;
 };
 
 // ---------------------------------------------------------------------------
-// The MFMA decode kernel.  grid (splits, units), 256 threads.
+// The MFMA decode kernel.  grid (splits, units), 64 * kWaves threads.
 // ---------------------------------------------------------------------------
-template <int R, typename T>
-__global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kernel(
+template <int R, typename T, int NW>
+__global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
     int64_t n_c, SplitPlan plan, int fused, FusedAppend app) {
-  using C = Cfg<R, T>;
+  using C = Cfg<R, T, NW>;
   constexpr bool BF = C::BF;
   constexpr int NBV = R / 16;                            // value N-blocks (compressed)
   constexpr int DEPTH = C::kDepth;
   constexpr int LPT = 2 * C::kDma;                       // DMA loads per tile
+  constexpr int QK = 16 / NW;
   extern __shared__ __align__(16) uint8_t s_dyn[];       // per-wave rings, then results
-  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ float2 s_step[64];          // cos, sin of 16 * theta_i (tile advance)
   __shared__ float s_q[16][kHeadDim];    // rotated, scaled query rows of the group
+  __shared__ __align__(16) uint8_t s_frag[C::kFragBytes];          // key-basis fragments (shared prologue)
+  // cos, sin of o * theta_f for offsets o < 16, as [f][o] with row stride 17
+  // (the lanes of one read take 16 offsets and 4 frequencies: no bank conflict)
+  __shared__ float2 s_st16[C::kShared ? 64 * 17 : 1];
+  __shared__ float2 s_base[C::kShared ? NW * 64 : 1];              // per wave: cos, sin of w_begin * theta_f
   float (*s_acc)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(s_dyn);
 
   const Dims &D = M.D;
@@ -425,7 +458,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
   const int ntiles = (int)((r_end - r_begin + 15) / 16);
-  const int tpw = (ntiles + 3) / 4;
+  const int tpw = (ntiles + NW - 1) / NW;
   const int tile_lo = wave * tpw < ntiles ? wave * tpw : ntiles;
   const int tile_hi = (wave + 1) * tpw < ntiles ? (wave + 1) * tpw : ntiles;
   const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
@@ -456,16 +489,16 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
   };
 
   // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS:
-  // thread (frequency qi, heads qh0 + 4k) loads (query_issue), then rotates
+  // thread (frequency qi, heads qh0 + NW k) loads (query_issue), then rotates
   // and stores them, after which the rows are split bf16 hi/lo into the
   // B-operand layout of the score product (query_finish, one barrier)
   const int qi = threadIdx.x & 63, qh0 = threadIdx.x >> 6;
-  float qx0[4], qx1[4];
+  float qx0[QK], qx1[QK];
   float2 qA, qB, qstep;
   auto query_issue = [&]() {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = qh0 + 4 * k < G ? qh0 + 4 * k : G - 1;      // rows past the group: not used
+    for (int k = 0; k < QK; ++k) {
+      const int h = qh0 + NW * k < G ? qh0 + NW * k : G - 1;    // rows past the group: not used
       const float *qr = q + ((size_t)b * D.q_heads + hk * G + h) * kHeadDim;
       qx0[k] = qr[qi];
       qx1[k] = qr[qi + 64];
@@ -474,18 +507,21 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     qstep = reinterpret_cast<const float2 *>(M.sh.rope_step)[16 * 64 + qi];
   };
   uint4_ qhi[4], qlo[4];
-  auto query_finish = [&]() {
+  // lds_only: the barrier publishes LDS writes only (no wait for the ring
+  // tiles in flight, which a full workgroup fence would drain)
+  auto query_finish = [&](bool lds_only) {
     float c, s;
     rope_combine(qA, qB, c, s);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = qh0 + 4 * k;
+    for (int k = 0; k < QK; ++k) {
+      const int h = qh0 + NW * k;
       const float x0 = h < G ? qx0[k] : 0.f, x1 = h < G ? qx1[k] : 0.f;
       s_q[h][qi] = fmaf(x0, c, -x1 * s) * D.scale_log2;
       s_q[h][qi + 64] = fmaf(x1, c, x0 * s) * D.scale_log2;
     }
     if (threadIdx.x < 64) s_step[threadIdx.x] = qstep;
-    __syncthreads();
+    if (lds_only) lds_barrier();
+    else __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       unsigned h[4], lo[4];
@@ -540,7 +576,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
 #pragma unroll
     for (int nb = 0; nb < NBV; ++nb) vacc[nb] = zero4();
     // per-wave LDS ring of DEPTH slots, each [C_K tile | C_V tile]
-    uint8_t *ring = s_dyn + C::kFloBytes + wave * C::kRingBytes;
+    uint8_t *ring = s_dyn + C::kRingOff + wave * C::kRingBytes;
     const uint8_t *gk = P.coef + (((size_t)u * 2 + 0) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
     const uint8_t *gv = P.coef + (((size_t)u * 2 + 1) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
     // one tile: kDma dwordx4 DMAs per matrix; lane l moves 16 bytes of chunk
@@ -558,16 +594,31 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       }
     };
     auto issue = [&](int it) { issue_from(it, it); };
-    // prologue: the LDS-resident basis fragments (r = 64), the query, the
-    // register-resident basis fragments and the first angle state are issued
-    // first, then the first DEPTH-1 ring tiles; one wait then covers all but
-    // the ring tiles, so the first tile is consumed as soon as it lands.
-    // Every wave's LDS fragment copies are older than its query loads, so
-    // they have completed before the barrier in query_finish, after which
-    // all waves read them.
+    // prologue: the LDS copies (basis fragments, step rows), the query, the
+    // register-resident basis fragments and the first angle state are loaded
+    // and consumed before the first DEPTH-1 ring tiles are issued.  (The
+    // compiler waits for every outstanding load, LDS DMAs included, before
+    // the first use of a value loaded ahead of an LDS DMA, so any use after
+    // the ring issue would wait for the whole ring.)  Every wave's LDS copies
+    // are older than its query loads, so they have completed before the
+    // barrier in query_finish, after which all waves read them.
     const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
     constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
-    if constexpr (C::kLoLds) {
+    // LDS address of the low-part chunk (mb, kb) of the key-basis fragments
+    auto lo_chunk = [&](int mb, int kb) -> const uint8_t * {
+      if constexpr (C::kShared) return s_frag + ((mb * (R / 16) + 2 * kb + 1) * 64 + lane) * 16;
+      return s_dyn + ((mb * (R / 32) + kb) * 64 + lane) * 16;
+    };
+    if constexpr (C::kShared) {
+      // every fragment chunk (same layout as in HBM) and step rows 0..15
+      constexpr int NCH = 8 * (R / 16);
+      static_assert(NCH % NW == 0, "fragment chunks per wave");
+#pragma unroll
+      for (int j = 0; j < NCH / NW; ++j) {
+        const int c = wave + NW * j;
+        dma16(FB + ((size_t)c * 64 + lane) * 16, s_frag + c * 1024);
+      }
+    } else if constexpr (C::kLoLds) {
       // low-part chunks (mb, 2 kb + 1) -> LDS [mb][kb][64 lanes][16 B]; a quarter per wave
 #pragma unroll
       for (int j = 0; j < 8 * (R / 32) / 4; ++j) {
@@ -577,7 +628,13 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     }
     query_issue();
     uint4_ F[8][FCH];
-    if (nt > 0) {
+    float2 bA, bB, stv[2];
+    if constexpr (C::kShared) {
+      rope_load(M.sh, w_begin, lane, bA, bB);       // base angle of the range, frequency = lane
+#pragma unroll
+      for (int k = 0; k < 2; ++k)                   // step rows 0..15, entry threadIdx.x + 512 k
+        stv[k] = reinterpret_cast<const float2 *>(M.sh.rope_step)[threadIdx.x + 512 * k];
+    } else {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -586,18 +643,68 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
           F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + gch) * 64 + lane) * 16);
         }
       anchor_issue(w_begin + n16);
-      // always DEPTH-1 tiles, so the wait below has a fixed count: a range
-      // shorter than that re-reads its last tile into slots it never uses
+    }
+    wait_vmcnt<0>();
+    if constexpr (C::kShared) {
+      float c, sn;
+      rope_combine(bA, bB, c, sn);
+      s_base[wave * 64 + lane] = float2{c, sn};
 #pragma unroll
-      for (int j = 0; j < DEPTH - 1; ++j) issue_from(j, j < nt ? j : nt - 1);
-      wait_vmcnt<(DEPTH - 1) * LPT>();
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 2; ++k) {
+        const int e = threadIdx.x + 512 * k;
+        s_st16[(e & 63) * 17 + (e >> 6)] = stv[k];
+      }
+    } else {
       anchor_finish();
     }
-    query_finish();
+    __builtin_amdgcn_sched_barrier(0);
+    // the first ring tile only: each DMA passes the CU's address path at
+    // ~1 KiB per 16 clocks, so a deep prologue issue would hold every wave
+    // (and the set-up after it) for microseconds; tiles 1 .. DEPTH-2 follow
+    // the barrier.  Always all of them, so the waits in the loop have fixed
+    // counts (a range shorter than that re-reads its last tile into slots it
+    // never uses).
+    if (nt > 0) issue_from(0, 0);
+    query_finish(true);
+    if (nt > 0) {
+#pragma unroll
+      for (int j = 1; j < DEPTH - 1; ++j) issue_from(j, j < nt ? j : nt - 1);
+    }
+    if constexpr (C::kShared) {
+      if (nt > 0) {
+        // register fragments from LDS; the lane's angle state = base angle of
+        // its frequency x rotation by its token offset n16
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int ch = 0; ch < FCH; ++ch) {
+            const int gch = C::kLoLds ? 2 * ch : ch;
+            F[mb][ch] = *reinterpret_cast<const uint4_ *>(s_frag + ((mb * (R / 16) + gch) * 64 + lane) * 16);
+          }
+        const float2 *base = s_base + wave * 64;
+        const float2 *st16 = s_st16 + n16;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = 16 * mb + 4 * rho + i;
+            rope_combine(base[f], st16[17 * f], cs_c[mb * 4 + i], cs_s[mb * 4 + i]);
+          }
+      }
+    }
     // one 16-token tile: wait for its ring slot, rebuild the keys, scores,
     // online softmax, values
+    // Two waves share each SIMD in eight-wave workgroups, and issue goes to
+    // the older one first; the wave with less of its range done takes the
+    // higher priority (four levels by quarters of the range), so both
+    // finish together instead of one running alone at the end.
+    const int q1 = (nt + 3) / 4, q2 = (nt + 1) / 2, q3 = (3 * nt + 3) / 4;
     auto comp_tile = [&](int it) {
+      if constexpr (NW == 8) {
+        if (it == q1) __builtin_amdgcn_s_setprio(2);
+        else if (it == q2) __builtin_amdgcn_s_setprio(1);
+        else if (it == q3) __builtin_amdgcn_s_setprio(0);
+      }
       if (it + DEPTH - 1 < nt) {
         issue(it + DEPTH - 1);
         wait_vmcnt<(DEPTH - 1) * LPT>();
@@ -628,8 +735,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
 #pragma unroll
             for (int kb = 0; kb < R / 32; ++kb) {
               if constexpr (C::kLoLds) {
-                const uint4_ lo = *reinterpret_cast<const uint4_ *>(
-                    s_dyn + ((mb * (R / 32) + kb) * 64 + lane) * 16);
+                const uint4_ lo = *reinterpret_cast<const uint4_ *>(lo_chunk(mb, kb));
                 a = mfma32(F[mb][kb], bop[kb], a);
                 a = mfma32(lo, bop[kb], a);
               } else {
@@ -680,6 +786,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
             vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
       }
     };
+    if constexpr (NW == 8) __builtin_amdgcn_s_setprio(3);
     // chunks of 32 tiles: the angle state is re-anchored from the table at
     // each chunk start (bounding the recurrence) outside the inner loop.
     // Paired tiles let the angle state alternate between two register sets
@@ -695,6 +802,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
         }
       for (; it < c1; ++it) comp_tile(it);
     }
+    if constexpr (NW == 8) __builtin_amdgcn_s_setprio(0);
     // per-wave results: acc[head 4*rho+i][coef 16*nb + n16] (over the rings)
     __syncthreads();
 #pragma unroll
@@ -703,7 +811,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
       for (int i = 0; i < 4; ++i) s_acc[wave][4 * rho + i][16 * nb + n16] = vacc[nb][i];
   } else {
     // ================= exact window tokens =================
-    if (app.k != nullptr && split == (int)gridDim.x - 1) {
+    if (app.k != nullptr && split == (int)gridDim.x - 1 && threadIdx.x < 2 * kHeadDim) {
       // fused append: this split ends at the newest position; write its ring
       // rows (rounded to the storage type) before the barrier in query_finish,
       // after which this workgroup reads them
@@ -723,7 +831,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
     if (nt > 0) anchor_issue(w_begin + n16);
     __builtin_amdgcn_sched_barrier(0);
     if (nt > 0) anchor_finish();
-    query_finish();
+    query_finish(false);
     if (nt > 0) {
       const T *RK = reinterpret_cast<const T *>(P.ringk) + (size_t)u * D.slots * kHeadDim;
       const T *RV = reinterpret_cast<const T *>(P.ringv) + (size_t)u * D.slots * kHeadDim;
@@ -788,18 +896,18 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
   // ---- combine the four waves into this split's record
   const int width = comp ? R : kHeadDim;
   const size_t rec0 = ((size_t)u * D.max_rec + split) * G;
-  for (int e = threadIdx.x; e < G * (2 + width); e += kThreads) {
+  for (int e = threadIdx.x; e < G * (2 + width); e += C::kThr) {
     const int h = e / (2 + width), x = e % (2 + width);
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
     if (x == 0) {
       store_agent(M.sh.recml + (rec0 + h) * 2, mx);
       continue;
     }
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
       v += wt * (x == 1 ? s_l[w][h] : s_acc[w][h][x - 2]);
     }
@@ -824,7 +932,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<R, T>::kOcc)) void decode_mfma_kerne
   }
   __syncthreads();
   if (!s_last) return;
-  merge_unit<R>(M, layer, out, plan, u, s_dyn);
+  merge_unit<R, NW>(M, layer, out, plan, u, s_dyn);
   if (threadIdx.x == 0) __hip_atomic_store(M.sh.cnt + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -833,14 +941,14 @@ template <int R>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int layer, float *out,
                                                                 SplitPlan plan) {
   extern __shared__ __align__(16) uint8_t s_mrg[];
-  merge_unit<R>(M, layer, out, plan, blockIdx.x, s_mrg);
+  merge_unit<R, 4>(M, layer, out, plan, blockIdx.x, s_mrg);
 }
 
-// Workgroups per decode call: about 16 tiles of 16 tokens per wave (enough to
-// amortize the per-workgroup set-up and keep the merge short), between one
-// and 16 per CU, rounded down to a whole number per CU.
-// ISKV_DECODE_WORKGROUPS overrides it.
-int target_workgroups(const Dims &D, int64_t length) {
+// Workgroups (of `waves` waves) per decode call: about 16 tiles of 16 tokens
+// per wave (enough to amortize the per-workgroup set-up and keep the merge
+// short), between one per CU and 64 waves per CU, rounded down to a whole
+// number per CU.  ISKV_DECODE_WORKGROUPS overrides it.
+int target_workgroups(const Dims &D, int64_t length, int waves) {
   static int v = -1;
   if (v < 0) {
     const char *e = std::getenv("ISKV_DECODE_WORKGROUPS");
@@ -850,18 +958,18 @@ int target_workgroups(const Dims &D, int64_t length) {
   if (v > 0) return v;
   const int64_t tiles = (int64_t)D.units * ((length + 15) / 16);
   const int64_t cus = D.cus;
-  int64_t t = (tiles + 63) / 64;
+  int64_t t = (tiles + 16 * waves - 1) / (16 * waves);
   if (t < cus) t = cus;
-  if (t > 16 * cus) t = 16 * cus;
+  if (t > 64 / waves * cus) t = 64 / waves * cus;
   // a grid just past one workgroup per CU would put a second one on a few
   // CUs and make them the tail of the launch
   return (int)(t / cus * cus);
 }
 
-SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
+SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
   SplitPlan plan{};
   const int64_t n_e = length - n_c;
-  const int target = target_workgroups(D, length);
+  const int target = target_workgroups(D, length, waves);
   if (n_e > 0) {
     // about 4 tiles per wave for the window
     int64_t nw = (n_e + 255) / 256;
@@ -873,7 +981,7 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
   if (n_c > 0) {
     int64_t want = target / D.units - plan.n_win;
     if (want < 1) want = 1;
-    int64_t nc = (n_c + 127) / 128;                  // at least 2 tiles per wave
+    int64_t nc = (n_c + 32 * waves - 1) / (32 * waves);   // at least 2 tiles per wave
     if (nc > want) nc = want;
     if (nc > D.max_rec - plan.n_win) nc = D.max_rec - plan.n_win;
     if (nc < 1) nc = 1;
@@ -883,28 +991,29 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c) {
   return plan;
 }
 
-template <int R, typename T>
+template <int R, typename T, int NW>
 hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                       int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
-  const SplitPlan plan = make_plan(M.D, length, n_c);
+                       int64_t length, int64_t n_c, const SplitPlan &plan, hipStream_t s,
+                       FusedAppend app) {
+  using C = Cfg<R, T, NW>;
   dim3 grid(plan.n_comp + plan.n_win, M.D.units);
-  constexpr int dyn = Cfg<R, T>::kDynBytes;
+  constexpr int dyn = C::kDynBytes;
   static bool dattr = false;
   hipError_t e;
   if (!dattr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<R, T>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<R, T, NW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
     if (e != hipSuccess) return e;
     dattr = true;
   }
   // fuse the merge when every workgroup is resident at once
-  const int64_t slots = (int64_t)M.D.cus * Cfg<R, T>::kOcc;
+  const int64_t slots = (int64_t)M.D.cus * C::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
-  hipLaunchKernelGGL((decode_mfma_kernel<R, T>), grid, dim3(kThreads), dyn, s, M, layer, q, q_pos,
+  hipLaunchKernelGGL((decode_mfma_kernel<R, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
                      out, length, n_c, plan, fused, app);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
-  constexpr int mbytes = MergeLds<R>::bytes;
+  constexpr int mbytes = MergeLds<R, 4>::bytes;
   static bool mattr = false;
   if (!mattr) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_merge_kernel<R>),
@@ -917,14 +1026,29 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   return hipGetLastError();
 }
 
+// bf16, r <= 64: eight-wave workgroups when their grid fits one per CU (a
+// single launch wave, where two waves per SIMD and an even share per CU set
+// the time); four-wave workgroups, two per CU, for larger grids, where one
+// workgroup's set-up and merge overlap the other's loop.
+template <int R, typename T>
+hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
+                       int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
+  if constexpr (std::is_same<T, bf16_t>::value && R <= 64) {
+    const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
+    if ((int64_t)(p8.n_comp + p8.n_win) * M.D.units <= M.D.cus)
+      return launch_mfma<R, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app);
+  }
+  return launch_mfma<R, T, 4>(M, layer, q, q_pos, out, length, n_c, make_plan(M.D, length, n_c, 4), s, app);
+}
+
 template <typename T>
 hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                            int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
   switch (M.D.r) {
-    case 16: return launch_mfma<16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 32: return launch_mfma<32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 64: return launch_mfma<64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 128: return launch_mfma<128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 16: return launch_rank<16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 32: return launch_rank<32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 64: return launch_rank<64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    case 128: return launch_rank<128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
   }
   return hipErrorInvalidValue;
 }

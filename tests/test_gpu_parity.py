@@ -356,3 +356,52 @@ def test_append_decode_matches_append_then_decode(storage, in_bf16):
         for fa, fb in zip(xa, xb):
             for key in ("basis", "S", "coef", "ring"):
                 np.testing.assert_array_equal(fa[key], fb[key])
+
+
+def test_multilayer_hot_keys_window_1024():
+    """Hot-key workload shape (high-norm keys aligned with later queries,
+    window 1024, r=32, bf16) over three layers held at different lengths:
+    decode on imported oracle state per layer, then one block update + sync
+    on the middle layer, which must leave the other layers' outputs unchanged
+    and match the oracle on the updated one."""
+    from oracle import Oracle
+    w = small(4, kv_heads=2, q_heads=8, num_layers=3)
+    lengths = [w.window + 64 * 3 + 17, w.window + 64 * 2 + 64, w.window - 300]
+    max_tokens = max(lengths) + 128
+    o = Oracle(w.batch, 3, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window, max_tokens,
+               storage=w.storage)
+    for layer, L in enumerate(lengths):
+        pos = 0
+        while pos < L:
+            u0 = o.unit(0, layer, 0)
+            n = min(64, L - pos, w.window + 64 - (u0.length - u0.n_c))
+            k, v = workloads.tokens(w, layer, pos, n)
+            ready = o.append(layer, k.astype(np.float32).astype(np.float64),
+                             v.astype(np.float32).astype(np.float64))
+            pos += n
+            if ready and pos < L:
+                o.block_update(layer)
+                o.sync(layer)
+    p = Pair(w, max_tokens=max_tokens, oracle=False, layers=3)
+    p.ora = o
+    for layer in range(3):
+        p.gpu.import_state(layer, p.oracle_blob(layer))
+    assert p.gpu.status(1).blocks_ready == 1
+
+    def check(layer, step):
+        L = o.unit(0, layer, 0).length
+        q = q32(workloads.query(w, layer, step))
+        got = p.decode(layer, q, L - 1)
+        ref = o.decode_attn(layer, q, L - 1)
+        assert rel_err_per_head(got, ref) < ATOL_OUT, (layer, step, rel_err_per_head(got, ref))
+        return got
+
+    before = [check(layer, 0) for layer in range(3)]
+    p.gpu.block_update(1)
+    p.gpu.sync(1)
+    o.block_update(1)
+    o.sync(1)
+    for layer in (0, 2):
+        np.testing.assert_array_equal(check(layer, 0), before[layer])
+    check(1, 1)
+    assert p.gpu.status(1).compressed == o.unit(0, 1, 0).n_c
