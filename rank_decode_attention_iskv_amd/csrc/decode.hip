@@ -439,6 +439,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
   // (the lanes of one read take 16 offsets and 4 frequencies: no bank conflict)
   __shared__ float2 s_st16[C::kShared ? 64 * 17 : 1];
   __shared__ float2 s_base[C::kShared ? NW * 64 : 1];              // per wave: cos, sin of w_begin * theta_f
+  __shared__ int s_prog[NW];                                       // per wave: tile index in the loop
   float (*s_acc)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(s_dyn);
 
   const Dims &D = M.D;
@@ -458,9 +459,11 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
     r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
   const int ntiles = (int)((r_end - r_begin + 15) / 16);
-  const int tpw = (ntiles + NW - 1) / NW;
-  const int tile_lo = wave * tpw < ntiles ? wave * tpw : ntiles;
-  const int tile_hi = (wave + 1) * tpw < ntiles ? (wave + 1) * tpw : ntiles;
+  // even split: the first ntiles % NW waves take one tile more (waves w and
+  // w + NW/2 share a SIMD, so every SIMD gets the same count within one)
+  const int tb = ntiles / NW, tx = ntiles % NW;
+  const int tile_lo = wave * tb + (wave < tx ? wave : tx);
+  const int tile_hi = tile_lo + tb + (wave < tx ? 1 : 0);
   const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
   const int nt = __builtin_amdgcn_readfirstlane(tile_hi - tile_lo);   // wave-uniform
 
@@ -649,6 +652,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
       float c, sn;
       rope_combine(bA, bB, c, sn);
       s_base[wave * 64 + lane] = float2{c, sn};
+      if (lane == 0) s_prog[wave] = 0;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int e = threadIdx.x + 512 * k;
@@ -694,16 +698,18 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
     }
     // one 16-token tile: wait for its ring slot, rebuild the keys, scores,
     // online softmax, values
-    // Two waves share each SIMD in eight-wave workgroups, and issue goes to
-    // the older one first; the wave with less of its range done takes the
-    // higher priority (four levels by quarters of the range), so both
-    // finish together instead of one running alone at the end.
-    const int q1 = (nt + 3) / 4, q2 = (nt + 1) / 2, q3 = (3 * nt + 3) / 4;
+    // Two waves share each SIMD in eight-wave workgroups (waves w and w ^ 4),
+    // and issue goes to the older one first; each wave posts its tile index
+    // in LDS and lowers its priority while it is ahead of the other, so both
+    // finish together instead of one running alone at the end.  (Reads of
+    // the other's index race with its writes; a stale value only delays the
+    // switch by a tile.)
     auto comp_tile = [&](int it) {
       if constexpr (NW == 8) {
-        if (it == q1) __builtin_amdgcn_s_setprio(2);
-        else if (it == q2) __builtin_amdgcn_s_setprio(1);
-        else if (it == q3) __builtin_amdgcn_s_setprio(0);
+        const int other = __builtin_amdgcn_readfirstlane(s_prog[wave ^ 4]);
+        if (lane == 0) s_prog[wave] = it;
+        if (it > other) __builtin_amdgcn_s_setprio(0);
+        else __builtin_amdgcn_s_setprio(2);
       }
       if (it + DEPTH - 1 < nt) {
         issue(it + DEPTH - 1);
@@ -786,7 +792,6 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
             vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
       }
     };
-    if constexpr (NW == 8) __builtin_amdgcn_s_setprio(3);
     // chunks of 32 tiles: the angle state is re-anchored from the table at
     // each chunk start (bounding the recurrence) outside the inner loop.
     // Paired tiles let the angle state alternate between two register sets
