@@ -27,6 +27,11 @@ paper), abbreviated [iS-KV explainer].
 * Every new query scores every earlier key [iS-KV explainer, the re-attention
   paragraph ("Why not bin the quiet colors?")].
 * Persistent-KV bytes [iS-KV explainer, Jargon "Persistent-KV compression"].
+* Protected prompt positions stay exact [iS-KV explainer, the window
+  paragraph ("paint shop"); the Jargon entry "Persistent-KV compression"
+  counts them among the kept bytes].  Which positions, and how many, is not
+  stated; the reading here is a leading prefix of P positions (P a multiple
+  of 64, default 0) that is never folded: compression starts at position P.
 
 Readings taken where the page is silent (each is listed in the design doc):
   window of W exact tokens plus up to 63 not yet folded (ring of W+64 rows,
@@ -224,12 +229,16 @@ class Factor:
     """K or V store of one (sequence, layer, KV head)."""
 
     def __init__(self, d: int, r: int, window: int, max_tokens: int, storage: str,
-                 block: int = BLOCK):
+                 block: int = BLOCK, prefix: int = 0):
         if window % block:
             raise ValueError("window must be a multiple of the block size")
+        if prefix % block or prefix < 0:
+            raise ValueError("the protected prefix must be a multiple of the block size")
         self.d, self.r, self.window, self.block = d, r, window, block
         self.storage = storage
         self.slots = window + block
+        self.P = prefix
+        self.prefix = np.zeros((prefix, d))   # exact rows of positions 0..P-1
         self.ring = np.zeros((self.slots, d))
         self.B = np.eye(d, r)                 # basis before the first block
         self.S = np.zeros(r)
@@ -237,7 +246,10 @@ class Factor:
         self.pending = None                    # M awaiting synchronization
 
     def write(self, pos: int, x):
-        self.ring[pos % self.slots] = store_round(x, self.storage)
+        if pos < self.P:
+            self.prefix[pos] = store_round(x, self.storage)
+        else:
+            self.ring[pos % self.slots] = store_round(x, self.storage)
 
     def block_rows(self, n_c: int):
         s0 = n_c % self.slots
@@ -250,15 +262,21 @@ class Factor:
         return M
 
     def sync(self, n_c_old: int):
-        """Rewrite the old coefficients for the current basis: C <- C M."""
+        """Rewrite the old coefficients (positions P..n_c_old-1) for the
+        current basis: C <- C M."""
         M = self.pending
-        self.C[:n_c_old] = store_round(self.C[:n_c_old] @ M, self.storage)
+        P = self.P
+        self.C[P:n_c_old] = store_round(self.C[P:n_c_old] @ M, self.storage)
         self.pending = None
 
     def rebuilt(self, n_c: int, length: int):
-        """Rows 0..length-1 as decode sees them: C B^T, then exact ring rows."""
+        """Rows 0..length-1 as decode sees them: the exact protected prefix,
+        C B^T of the compressed positions P..n_c-1, then exact ring rows."""
         out = np.empty((length, self.d))
-        out[:n_c] = self.C[:n_c] @ self.B.T
+        P = min(self.P, length)
+        n_c = max(min(n_c, length), P)
+        out[:P] = self.prefix[:P]
+        out[P:n_c] = self.C[P:n_c] @ self.B.T
         for p in range(n_c, length):
             out[p] = self.ring[p % self.slots]
         return out
@@ -267,20 +285,26 @@ class Factor:
 class Unit:
     """One (sequence, layer, KV head): a K factor, a V factor and counters."""
 
-    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK):
-        self.K = Factor(d, r, window, max_tokens, storage, block)
-        self.V = Factor(d, r, window, max_tokens, storage, block)
+    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK, prefix=0):
+        self.K = Factor(d, r, window, max_tokens, storage, block, prefix)
+        self.V = Factor(d, r, window, max_tokens, storage, block, prefix)
         self.length = 0          # tokens appended (L)
-        self.n_c = 0             # tokens held as coefficients (N_c)
+        self.P = prefix          # protected exact prefix
+        self.n_c = prefix        # end of the compressed positions P..n_c-1
         self.block = block
         self.window = window
+
+    @property
+    def compressed(self) -> int:
+        """Tokens held as coefficients (N_c)."""
+        return self.n_c - self.P
 
     @property
     def ready(self) -> bool:
         return self.length - self.n_c == self.window + self.block
 
     def append(self, k, v):
-        if self.length - self.n_c >= self.window + self.block:
+        if self.length >= self.P and self.length - self.n_c >= self.window + self.block:
             raise RuntimeError("ring full: fold the oldest block first")
         self.K.write(self.length, k)
         self.V.write(self.length, v)
@@ -320,18 +344,24 @@ class Unit:
         return p @ vals
 
     def history(self, which: str):
-        """Reconstructed pre-RoPE history C B^T of the compressed rows."""
+        """Reconstructed pre-RoPE history C B^T of the compressed rows
+        (positions P..n_c-1)."""
         f = self.K if which == "K" else self.V
-        return f.C[: self.n_c] @ f.B.T
+        return f.C[self.P: self.n_c] @ f.B.T
 
-    def load_state(self, length, n_c, ring_k, ring_v, Bk, Sk, Ck, Bv, Sv, Cv):
-        """Install a state (used to hand an oracle-made state to other code)."""
+    def load_state(self, length, n_c, ring_k, ring_v, Bk, Sk, Ck, Bv, Sv, Cv,
+                   prefix_k=None, prefix_v=None):
+        """Install a state (used to hand an oracle-made state to other code);
+        n_c is the end position of the compressed rows."""
         self.length, self.n_c = int(length), int(n_c)
-        for f, ring, B, S, C in ((self.K, ring_k, Bk, Sk, Ck), (self.V, ring_v, Bv, Sv, Cv)):
+        for f, ring, B, S, C, pre in ((self.K, ring_k, Bk, Sk, Ck, prefix_k),
+                                      (self.V, ring_v, Bv, Sv, Cv, prefix_v)):
             f.ring[:] = ring
             f.B = np.array(B, dtype=np.float64)
             f.S = np.array(S, dtype=np.float64)
             f.C[: n_c] = C[: n_c]
+            if f.P:
+                f.prefix[:] = pre
             f.pending = None
 
 
@@ -363,7 +393,7 @@ class Oracle:
 
     def __init__(self, batch, num_layers, kv_heads, q_heads, head_dim, rank, window,
                  max_tokens, storage="bf16", rope_base=10000.0, softmax_scale=None,
-                 block=BLOCK):
+                 block=BLOCK, prefix=0):
         if q_heads % kv_heads:
             raise ValueError("q_heads must be a multiple of kv_heads")
         self.batch, self.num_layers = batch, num_layers
@@ -371,7 +401,8 @@ class Oracle:
         self.d, self.r, self.window, self.block = head_dim, rank, window, block
         self.storage, self.rope_base = storage, rope_base
         self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale else float(softmax_scale)
-        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block)
+        self.prefix = prefix
+        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix)
                         for _ in range(kv_heads)] for _ in range(num_layers)]
                       for _ in range(batch)]
 

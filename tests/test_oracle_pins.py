@@ -401,3 +401,68 @@ def test_first_fold_is_truncated_svd_of_block():
     assert subspace_dist(Bn, vt[:r].T) < 1e-10
     best = (U_[:, :r] * s[:r]) @ vt[:r]                 # Eckart-Young optimum
     np.testing.assert_allclose(C_blk @ Bn.T, best, rtol=0, atol=1e-11 * s[0])
+
+
+# ---------------------------------------------------------------------------
+# Protected prompt prefix: positions 0..P-1 stay exact and are never folded
+# [iS-KV explainer, the window paragraph ("paint shop"): protected prompt
+# positions stay exact; reading: a leading prefix of P positions]
+# ---------------------------------------------------------------------------
+
+def test_protected_prefix_exact_and_lossless_composition():
+    """Full-rank random rows in the prefix, rank-12 noise-free rows after it,
+    r = 16: the prefix must stay exact (compressing it would lose its full
+    rank), the compressed part is lossless (rank <= r), so decode equals
+    uncompressed attention over every position (torch SDPA, complex-form
+    RoPE).  Compressing from position 0 instead of P, or a shifted position
+    anywhere, fails this."""
+    rng = np.random.default_rng(31)
+    d, r, W, P = 64, 16, 64, 128
+    L = P + 64 * 6 + 20
+    X = np.vstack([rng.standard_normal((P, d)), lowrank(rng, L - P, d, 12)])
+    Y = np.vstack([rng.standard_normal((P, d)), lowrank(rng, L - P, d, 12)])
+    o = Oracle(1, 1, 1, 2, d, r, W, L + 64, storage="f64", prefix=P)
+    u = o.unit(0, 0, 0)
+    folds = 0
+    for t in range(L):
+        o.append(0, X[None, t:t + 1, None], Y[None, t:t + 1, None])
+        if o.ready(0):
+            o.block_update(0)
+            o.sync(0)
+            folds += 1
+    assert folds >= 4 and u.compressed == 64 * folds and u.n_c == P + 64 * folds
+    assert u.length - u.n_c >= W
+    np.testing.assert_array_equal(u.K.prefix, X[:P])           # never touched by folds
+    np.testing.assert_array_equal(u.V.prefix, Y[:P])
+    np.testing.assert_allclose(u.history("K"), X[P:u.n_c], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(u.history("V"), Y[P:u.n_c], rtol=0, atol=1e-10)
+    q = rng.standard_normal((1, 2, d))
+    scale = 1 / math.sqrt(d)
+    got = o.decode_attn(0, q, L + 3)[0]
+    ref = exact_attention(q[0], X, Y, L + 3, scale)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-10
+
+
+def test_prefix_longer_than_history_is_exact_attention_bf16():
+    """P beyond the history: no fold ever happens and decode is uncompressed
+    attention over the bf16-rounded rows (rounding by torch)."""
+    rng = np.random.default_rng(32)
+    d, r, W, P, L = 64, 16, 64, 256, 200
+    # float32 inputs, as the library receives them (one rounding step to bf16)
+    X = rng.standard_normal((L, d)).astype(np.float32).astype(np.float64)
+    Y = rng.standard_normal((L, d)).astype(np.float32).astype(np.float64)
+    u = Unit(d, r, W, 512, "bf16", 64, prefix=P)
+    for t in range(L):
+        u.append(X[t], Y[t])
+        assert not u.ready
+    assert u.compressed == 0
+    to_bf16 = lambda a: torch.as_tensor(a, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    q = rng.standard_normal((3, d))
+    got = u.decode(q, L - 1, 0.125)
+    ref = exact_attention(q, to_bf16(X), to_bf16(Y), L - 1, 0.125)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-12
+
+
+def test_prefix_must_be_block_multiple():
+    with pytest.raises(ValueError):
+        Unit(64, 16, 64, 512, "f64", 64, prefix=100)
