@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--rank", type=int, default=32)
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--protected-prefix", type=int, default=0,
+                    help="leading positions kept exact and never folded (multiple of 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--async-maintenance", action="store_true",
                     help="run block updates and syncs on a second stream (each layer "
@@ -246,7 +248,8 @@ def main():
     total_steps = args.warmup + args.steps
     per_inst_steps = (total_steps + I - 1) // I
     max_tokens = args.context + per_inst_steps + 64
-    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16)
+    P = args.protected_prefix
+    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16, protected_prefix=P)
     cache = binding.IskvCache(cfg)
     stream = torch.cuda.current_stream()
     gen = Generator(torch, I, B, H, D, 32, args.seed)
@@ -255,7 +258,7 @@ def main():
     t_pre = time.perf_counter()
     length, n_c = 0, 0
     while length < args.context:
-        n = min(64, args.context - length, (W + 64) - (length - n_c))
+        n = min(64, args.context - length, (W + 64) - (length - P - n_c))
         ready = False
         for inst in range(I):
             k, v = gen.tokens(inst, n)
@@ -417,7 +420,9 @@ def main():
             "workload": (f"one GQA layer: {H} KV / {HQ} q heads, head_dim {D}, rank {R}, "
                          f"{args.context}-token context (grows by 1 per step), window {W}, "
                          f"bf16 storage, fp32 accumulate, batch {B}, block update + sync every "
-                         f"64 steps; K/V rank-32 signal + 1% noise"),
+                         f"64 steps; K/V rank-32 signal + 1% noise"
+                         + (f"; first {P} positions kept exact (protected prefix)" if P else "")),
+            "protected_prefix": P,
             "instances_rotated": I,
             "global_batch": B,
             "seq_len": args.context,

@@ -19,6 +19,10 @@
  *   - each new query scores every earlier key         [re-attention paragraph]
  *   - persistent-KV bytes = factors + exact rows      [Jargon "Persistent-KV
  *                                                      compression"]
+ *   - a set of protected prompt positions also stays exact
+ *                                                     [window paragraph; the
+ *                                                      page does not say which:
+ *                                                      here a leading prefix]
  * The page gives no interface; the verbs below follow its statement of the
  * problem: append tokens, fold a block, synchronize, attend.
  *
@@ -79,11 +83,15 @@ typedef struct {
   int32_t storage;        /* iskv_dtype of ring rows and coefficients */
   float rope_base;        /* RoPE base, e.g. 10000 */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t protected_prefix; /* P: positions 0..P-1 stay exact and are never
+                               folded (protected prompt rows); a multiple of 64,
+                               0 <= P <= max_tokens; 0 = none */
 } iskv_config;
 
 typedef struct {
   int64_t length;             /* tokens appended to the layer (per sequence) */
-  int64_t compressed;         /* tokens held as coefficients (N_c, multiple of 64) */
+  int64_t compressed;         /* tokens held as coefficients (N_c, multiple of 64:
+                                 positions P .. P+N_c-1) */
   int32_t blocks_ready;       /* 1: ring is full, a block must be folded before the next append */
   int32_t pending_sync;       /* 1: iskv_block_update ran and iskv_sync has not */
   int64_t folds;              /* iskv_block_update calls that folded this layer */
@@ -102,8 +110,10 @@ size_t iskv_workspace_bytes(const iskv_config *cfg);
  * (0 if cfg is invalid). Layout, all little-endian:
  *   int64 length, int64 compressed, then for b in [0,batch), h in [0,kv_heads),
  *   X in (K, V):  float basis[head_dim][rank], float S[rank],
- *                 float coeff[max_tokens][rank]   (rows >= compressed are 0),
- *                 float ring[window+64][head_dim] (slot = position % (window+64)). */
+ *                 float coeff[max_tokens][rank]   (row = position; rows outside
+ *                                                  P .. P+compressed-1 are 0),
+ *                 float ring[window+64][head_dim] (slot = position % (window+64)),
+ *                 float prefix[P][head_dim]       (protected rows, P = protected_prefix). */
 size_t iskv_state_bytes(const iskv_config *cfg);
 
 /* Validate cfg, carve the caller's device workspace (dev_ws, ws_bytes >=
@@ -117,9 +127,10 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
 /* Append n_tokens tokens of every sequence to one layer.
  * dev_k, dev_v: [batch][n_tokens][num_kv_heads][head_dim] of dtype in_dtype,
  * keys before RoPE.  Each row is rounded to the storage dtype (round to nearest
- * even) and written to ring slot position % (window+64).
- * ESTATE if n_tokens exceeds the free ring slots (window+64 - (length -
- * compressed)) or if length would pass max_tokens.
+ * even) and written to the protected prefix row (position < P) or to ring slot
+ * position % (window+64).
+ * ESTATE if the ring would hold more than window+64 tokens (the positions from
+ * P + compressed on) or if length would pass max_tokens.
  * *blocks_ready (may be NULL) is set to 1 when the ring is full, i.e. the next
  * call must be iskv_block_update. */
 int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
@@ -149,7 +160,8 @@ int iskv_discard_sync(iskv_ctx *c, int layer);
  * the layer: keys rebuilt from coefficients (or read exact from the ring),
  * rotated by RoPE at their position; the query rotated at q_pos; softmax with
  * the configured scale; values accumulated in coefficient space and mapped
- * back by the value basis.  dev_q: float [batch][num_q_heads][head_dim], before
+ * back by the value basis; protected prefix rows are exact like the ring rows.
+ * dev_q: float [batch][num_q_heads][head_dim], before
  * RoPE.  dev_out: float [batch][num_q_heads][head_dim].  Query head h reads KV
  * head h / (num_q_heads / num_kv_heads).  q_pos must lie in [0, max_tokens + 128)
  * (the range of the RoPE tables built at init), else EINVAL.  ESTATE if the

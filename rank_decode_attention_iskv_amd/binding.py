@@ -30,6 +30,7 @@ class Config(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32), ("window", ctypes.c_int32),
         ("block", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("storage", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("protected_prefix", ctypes.c_int32),
     ]
 
 
@@ -109,9 +110,10 @@ def strerror(code: int) -> str:
 
 
 def make_config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window,
-                max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64) -> Config:
+                max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64,
+                protected_prefix=0) -> Config:
     return Config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window, block,
-                  max_tokens, storage, rope_base, softmax_scale)
+                  max_tokens, storage, rope_base, softmax_scale, protected_prefix)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -252,13 +254,15 @@ class IskvCache:
 # -- state blob helpers (layout documented at iskv_state_bytes) --------------
 
 def unpack_state(cfg: Config, blob):
-    """Split a state blob into numpy arrays per (unit, K|V)."""
+    """Split a state blob into numpy arrays per (unit, K|V); n_c is the
+    compressed token count (rows protected_prefix .. protected_prefix+n_c-1)."""
     import numpy as np
     d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    Pp = cfg.protected_prefix
     length, n_c = np.frombuffer(bytes(blob[:16]), dtype=np.int64)
     f = np.frombuffer(bytes(blob[16:]), dtype=np.float32)
     units = cfg.batch * cfg.num_kv_heads
-    per = d * r + r + T * r + S * d
+    per = d * r + r + T * r + S * d + Pp * d
     out = []
     for u in range(units):
         xs = []
@@ -267,17 +271,20 @@ def unpack_state(cfg: Config, blob):
             B = f[o: o + d * r].reshape(d, r); o += d * r
             Sv = f[o: o + r]; o += r
             C = f[o: o + T * r].reshape(T, r); o += T * r
-            ring = f[o: o + S * d].reshape(S, d)
-            xs.append(dict(basis=B, S=Sv, coef=C, ring=ring))
+            ring = f[o: o + S * d].reshape(S, d); o += S * d
+            prefix = f[o: o + Pp * d].reshape(Pp, d)
+            xs.append(dict(basis=B, S=Sv, coef=C, ring=ring, prefix=prefix))
         out.append(xs)
     return int(length), int(n_c), out
 
 
 def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
-    """Inverse of unpack_state; units[u][x] holds basis, S, coef, ring arrays."""
+    """Inverse of unpack_state; units[u][x] holds basis, S, coef (rows by
+    position), ring and, with a protected prefix, prefix arrays."""
     import numpy as np
     parts = [np.array([length, n_c], dtype=np.int64).tobytes()]
     d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    Pp = cfg.protected_prefix
     for xs in units:
         for x in xs:
             C = np.zeros((T, r), dtype=np.float32)
@@ -285,4 +292,6 @@ def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
             parts += [np.asarray(x["basis"], np.float32).reshape(d, r).tobytes(),
                       np.asarray(x["S"], np.float32).reshape(r).tobytes(),
                       C.tobytes(), np.asarray(x["ring"], np.float32).reshape(S, d).tobytes()]
+            if Pp:
+                parts.append(np.asarray(x["prefix"], np.float32).reshape(Pp, d).tobytes())
     return bytearray(b"".join(parts))

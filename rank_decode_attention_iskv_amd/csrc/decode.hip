@@ -53,10 +53,13 @@ constexpr int kThreads = 256;
 constexpr float kRescale = 8.f;
 
 struct SplitPlan {
-  int n_comp;        // splits over compressed tokens
+  int n_comp;        // splits over compressed tokens (positions P .. n_c-1)
   int comp_len;      // tokens per compressed split (multiple of 64)
-  int n_win;         // splits over window tokens
+  int n_win;         // splits over window tokens (positions n_c .. length-1)
   int win_len;       // tokens per window split (multiple of 16)
+  int n_pre;         // splits over the protected prefix (positions 0 .. P-1)
+  int pre_len;       // tokens per prefix split (multiple of 16)
+  // records: compressed splits first, then prefix splits, then window splits
 };
 
 // A float store performed at agent scope (coherent across the XCDs' L2s).
@@ -244,7 +247,8 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   const floatx4 *s_bv = reinterpret_cast<const floatx4 *>(lds + ML::oBv);
   const Dims &D = M.D;
   const int G = D.group, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n_comp = plan.n_comp, n_win = plan.n_win, n_rec = n_comp + n_win;
+  // exact records (prefix and window splits) follow the compressed ones
+  const int n_comp = plan.n_comp, n_win = plan.n_pre + plan.n_win, n_rec = n_comp + n_win;
   float *wt = reinterpret_cast<float *>(lds + ML::oWt) + wave * 64;
   float *sacc = reinterpret_cast<float *>(lds + ML::oAcc) + wave * (R + kHeadDim);
   const float *ml = M.sh.recml + (size_t)u * D.max_rec * G * 2;
@@ -449,13 +453,19 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
   const int split = blockIdx.x, u = blockIdx.y;
   const int b = u / D.kv_heads, hk = u % D.kv_heads;
   const bool comp = split < plan.n_comp;
+  const int xs = split - plan.n_comp;                    // exact split index
+  const bool pre = !comp && xs < plan.n_pre;             // a protected-prefix split
 
   int64_t r_begin, r_end;
   if (comp) {
-    r_begin = (int64_t)split * plan.comp_len;
+    r_begin = D.prefix + (int64_t)split * plan.comp_len;
     r_end = r_begin + plan.comp_len < n_c ? r_begin + plan.comp_len : n_c;
+  } else if (pre) {
+    const int64_t pend = length < D.prefix ? length : D.prefix;
+    r_begin = (int64_t)xs * plan.pre_len;
+    r_end = r_begin + plan.pre_len < pend ? r_begin + plan.pre_len : pend;
   } else {
-    r_begin = n_c + (int64_t)(split - plan.n_comp) * plan.win_len;
+    r_begin = n_c + (int64_t)(xs - plan.n_pre) * plan.win_len;
     r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
   const int ntiles = (int)((r_end - r_begin + 15) / 16);
@@ -838,12 +848,15 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
     if (nt > 0) anchor_finish();
     query_finish(false);
     if (nt > 0) {
-      const T *RK = reinterpret_cast<const T *>(P.ringk) + (size_t)u * D.slots * kHeadDim;
-      const T *RV = reinterpret_cast<const T *>(P.ringv) + (size_t)u * D.slots * kHeadDim;
+      // exact rows: the protected prefix (row = position) or the ring (row =
+      // position % slots); V transposed in both, row stride `rows`
+      const int rows = pre ? D.prefix : D.slots;
+      const T *RK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
+      const T *RV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
       for (int it = 0; it < nt; ++it) {
         const int64_t t0 = w_begin + 16 * (int64_t)it;
-        const int slot = (int)((t0 + n16) % D.slots);
-        const int slot0 = (int)(t0 % D.slots);          // tiles never wrap (16 | slots)
+        const int slot = (int)((t0 + n16) % rows);
+        const int slot0 = (int)(t0 % rows);             // tiles never wrap (16 | slots, 64 | P)
         floatx4 ka[8];
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
@@ -869,7 +882,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
             const uint2_ v = *reinterpret_cast<const uint2_ *>(
-                RV + (size_t)(16 * nb + n16) * D.slots + slot0 + 4 * rho);
+                RV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
             wacc[nb] = mfma16(uint2_{h0, h1}, v, wacc[nb]);
             wacc[nb] = mfma16(uint2_{l0, l1}, v, wacc[nb]);
           }
@@ -877,7 +890,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
             const floatx4 v = *reinterpret_cast<const floatx4 *>(
-                RV + (size_t)(16 * nb + n16) * D.slots + slot0 + 4 * rho);
+                RV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
 #pragma unroll
             for (int i = 0; i < 4; ++i) wacc[nb] = mfma4(p[i], v[i], wacc[nb]);
           }
@@ -971,9 +984,13 @@ int target_workgroups(const Dims &D, int64_t length, int waves) {
   return (int)(t / cus * cus);
 }
 
+// n_c: end position of the compressed rows (the protected prefix P .. n_c-1
+// compressed, 0 .. P-1 exact, n_c .. length-1 in the ring).
 SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
   SplitPlan plan{};
-  const int64_t n_e = length - n_c;
+  const int64_t n_e = length > n_c ? length - n_c : 0;           // ring tokens
+  const int64_t n_p = length < D.prefix ? length : D.prefix;     // prefix tokens
+  const int64_t n_k = n_c - D.prefix;                             // compressed tokens
   const int target = target_workgroups(D, length, waves);
   if (n_e > 0) {
     // about 4 tiles per wave for the window
@@ -983,15 +1000,23 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
     plan.win_len = (int)(((n_e + nw - 1) / nw + 15) / 16 * 16);
     plan.n_win = (int)((n_e + plan.win_len - 1) / plan.win_len);
   }
-  if (n_c > 0) {
-    int64_t want = target / D.units - plan.n_win;
+  if (n_p > 0) {
+    // the prefix as exact splits of about 256 tokens
+    int64_t np = (n_p + 255) / 256;
+    if (np > D.max_rec / 4) np = D.max_rec / 4;
+    plan.pre_len = (int)(((n_p + np - 1) / np + 15) / 16 * 16);
+    plan.n_pre = (int)((n_p + plan.pre_len - 1) / plan.pre_len);
+  }
+  if (n_k > 0) {
+    const int n_x = plan.n_win + plan.n_pre;
+    int64_t want = target / D.units - n_x;
     if (want < 1) want = 1;
-    int64_t nc = (n_c + 32 * waves - 1) / (32 * waves);   // at least 2 tiles per wave
+    int64_t nc = (n_k + 32 * waves - 1) / (32 * waves);   // at least 2 tiles per wave
     if (nc > want) nc = want;
-    if (nc > D.max_rec - plan.n_win) nc = D.max_rec - plan.n_win;
+    if (nc > D.max_rec - n_x) nc = D.max_rec - n_x;
     if (nc < 1) nc = 1;
-    plan.comp_len = (int)(((n_c + nc - 1) / nc + 63) / 64 * 64);
-    plan.n_comp = (int)((n_c + plan.comp_len - 1) / plan.comp_len);
+    plan.comp_len = (int)(((n_k + nc - 1) / nc + 63) / 64 * 64);
+    plan.n_comp = (int)((n_k + plan.comp_len - 1) / plan.comp_len);
   }
   return plan;
 }
@@ -1001,7 +1026,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
                        int64_t length, int64_t n_c, const SplitPlan &plan, hipStream_t s,
                        FusedAppend app) {
   using C = Cfg<R, T, NW>;
-  dim3 grid(plan.n_comp + plan.n_win, M.D.units);
+  dim3 grid(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
   constexpr int dyn = C::kDynBytes;
   static bool dattr = false;
   hipError_t e;
@@ -1040,7 +1065,7 @@ hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos,
                        int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
   if constexpr (std::is_same<T, bf16_t>::value && R <= 64) {
     const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
-    if ((int64_t)(p8.n_comp + p8.n_win) * M.D.units <= M.D.cus)
+    if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
       return launch_mfma<R, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app);
   }
   return launch_mfma<R, T, 4>(M, layer, q, q_pos, out, length, n_c, make_plan(M.D, length, n_c, 4), s, app);

@@ -25,7 +25,7 @@ namespace {
 
 struct LayerState {
   int64_t length = 0;
-  int64_t n_c = 0;
+  int64_t n_c = 0;          // end position of the compressed rows (P + N_c)
   bool pending = false;
   int64_t folds = 0;
   int64_t syncs = 0;
@@ -46,6 +46,8 @@ bool valid_config(const iskv_config *c) {
   if (c->storage != ISKV_F32 && c->storage != ISKV_BF16) return false;
   if (!(c->rope_base > 1.f) || !std::isfinite(c->rope_base)) return false;
   if (!std::isfinite(c->softmax_scale)) return false;
+  if (c->protected_prefix < 0 || c->protected_prefix % kBlock || c->protected_prefix > c->max_tokens)
+    return false;
   return true;
 }
 
@@ -76,6 +78,7 @@ Dims make_dims(const iskv_config *c) {
   if (per_unit * D.group > 4096) per_unit = 4096 / D.group;
   D.max_rec = per_unit;
   D.rope_anchors = (c->max_tokens + kBlock) / kRopeAnchor + 2;
+  D.prefix = c->protected_prefix;
   return D;
 }
 
@@ -160,8 +163,11 @@ uint64_t persistent_bytes(const iskv_ctx *c) {
   const Dims &D = c->D;
   uint64_t tot = 0;
   for (const LayerState &L : c->layers) {
-    const uint64_t n_e = (uint64_t)(L.length - L.n_c);
-    const uint64_t per = 2ull * ((uint64_t)L.n_c * D.r * D.elem + (uint64_t)D.d * D.r * 4 +
+    // exact rows: the protected prefix written so far and the ring
+    const uint64_t n_pre = (uint64_t)(L.length < D.prefix ? L.length : D.prefix);
+    const uint64_t n_e = (uint64_t)(L.length > L.n_c ? L.length - L.n_c : 0) + n_pre;
+    const uint64_t n_comp = (uint64_t)(L.n_c - D.prefix);
+    const uint64_t per = 2ull * (n_comp * D.r * D.elem + (uint64_t)D.d * D.r * 4 +
                                  (uint64_t)D.r * 4 + n_e * D.d * D.elem);
     tot += per * (uint64_t)D.units;
   }
@@ -180,7 +186,8 @@ size_t iskv_workspace_bytes(const iskv_config *cfg) {
 size_t iskv_state_bytes(const iskv_config *cfg) {
   if (!valid_config(cfg)) return 0;
   const Dims D = make_dims(cfg);
-  const size_t per_x = (size_t)D.d * D.r + D.r + (size_t)D.max_tokens * D.r + (size_t)D.slots * D.d;
+  const size_t per_x = (size_t)D.d * D.r + D.r + (size_t)D.max_tokens * D.r +
+                       (size_t)D.slots * D.d + (size_t)D.prefix * D.d;
   return 16 + (size_t)D.units * 2 * per_x * 4;
 }
 
@@ -206,7 +213,9 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
     delete c;
     return ISKV_EDEVICE;
   }
-  c->layers.assign(c->D.layers, LayerState{});
+  LayerState empty;
+  empty.n_c = c->D.prefix;                  // compression starts after the protected prefix
+  c->layers.assign(c->D.layers, empty);
   uint8_t *base = reinterpret_cast<uint8_t *>(dev_ws);
   Model &M = c->M;
   M.base = base;
@@ -266,8 +275,8 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
   if (!c || check_layer(c, layer) || !dev_k || !dev_v || n_tokens < 0) return ISKV_EINVAL;
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
   LayerState &L = c->layers[layer];
-  const int64_t used = L.length - L.n_c;
-  if (used + n_tokens > c->D.slots) return ISKV_ESTATE;
+  // ring tokens after the append: the positions from n_c on (>= P)
+  if (L.length + n_tokens - L.n_c > c->D.slots) return ISKV_ESTATE;
   if (L.length + n_tokens > c->D.max_tokens) return ISKV_ESTATE;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   hipError_t e = launch_append(c->M, layer, dev_k, dev_v, n_tokens, in_dtype, L.length, c->stream);
@@ -390,6 +399,11 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
   LayerState &L = c->layers[layer];
   if (L.length - L.n_c + 1 > c->D.slots) return ISKV_ESTATE;
   if (L.length + 1 > c->D.max_tokens) return ISKV_ESTATE;
+  if (L.length < c->D.prefix) {
+    // the token lands in the protected prefix: the two calls, not fused
+    const int a = iskv_append(c, layer, dev_k, dev_v, 1, in_dtype, blocks_ready);
+    return a != ISKV_OK ? a : iskv_decode_attn(c, layer, dev_q, q_pos, dev_out);
+  }
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   const FusedAppend app{dev_k, dev_v, in_dtype};
   hipError_t e = launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length + 1, L.n_c, c->stream, app);
@@ -408,7 +422,7 @@ int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
   const LayerState &L = c->layers[layer];
   std::memset(st, 0, sizeof(*st));
   st->length = L.length;
-  st->compressed = L.n_c;
+  st->compressed = L.n_c - c->D.prefix;
   st->blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
   st->pending_sync = L.pending ? 1 : 0;
   st->folds = L.folds;
@@ -445,8 +459,9 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   };
   uint8_t *o = reinterpret_cast<uint8_t *>(host_buf);
   const LayerState &L = c->layers[layer];
+  const int64_t n_comp = L.n_c - D.prefix;
   std::memcpy(o, &L.length, 8);
-  std::memcpy(o + 8, &L.n_c, 8);
+  std::memcpy(o + 8, &n_comp, 8);
   float *f = reinterpret_cast<float *>(o + 16);
   for (int u = 0; u < D.units; ++u) {
     for (int x = 0; x < 2; ++x) {
@@ -457,7 +472,7 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
       f += D.r;
       const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
       for (size_t i = 0; i < (size_t)D.max_tokens * D.r; ++i)
-        f[i] = (i < (size_t)L.n_c * D.r) ? elem(coff, i) : 0.f;
+        f[i] = (i >= (size_t)D.prefix * D.r && i < (size_t)L.n_c * D.r) ? elem(coff, i) : 0.f;
       f += (size_t)D.max_tokens * D.r;
       for (int s = 0; s < D.slots; ++s)
         for (int d = 0; d < D.d; ++d) {
@@ -467,6 +482,14 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
           f[(size_t)s * D.d + d] = elem(x == 0 ? Ly.ringk : Ly.ringv, i);
         }
       f += (size_t)D.slots * D.d;
+      for (int p = 0; p < D.prefix; ++p)
+        for (int d = 0; d < D.d; ++d) {
+          const size_t i = (x == 0)
+              ? (size_t)u * D.prefix * D.d + (size_t)p * D.d + d
+              : (size_t)u * D.prefix * D.d + (size_t)d * D.prefix + p;
+          f[(size_t)p * D.d + d] = elem(x == 0 ? Ly.prek : Ly.prev, i);
+        }
+      f += (size_t)D.prefix * D.d;
     }
   }
   return ISKV_OK;
@@ -477,11 +500,12 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
   const Dims &D = c->D;
   const uint8_t *in = reinterpret_cast<const uint8_t *>(host_buf);
-  int64_t length, n_c;
+  int64_t length, n_comp;
   std::memcpy(&length, in, 8);
-  std::memcpy(&n_c, in + 8, 8);
-  if (length < 0 || n_c < 0 || n_c % kBlock || n_c > length || length > D.max_tokens ||
-      length - n_c > D.slots)
+  std::memcpy(&n_comp, in + 8, 8);
+  const int64_t n_c = D.prefix + n_comp;    // end position of the compressed rows
+  if (length < 0 || n_comp < 0 || n_comp % kBlock || length > D.max_tokens ||
+      (n_comp > 0 && n_c > length) || length - n_c > D.slots)
     return ISKV_EINVAL;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
@@ -505,7 +529,7 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
       std::memcpy(raw.data() + Ly.sing + ux * D.r * 4, f, (size_t)D.r * 4);
       f += D.r;
       const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
-      for (size_t i = 0; i < (size_t)n_c * D.r; ++i) put(coff, i, f[i]);
+      for (size_t i = (size_t)D.prefix * D.r; i < (size_t)n_c * D.r; ++i) put(coff, i, f[i]);
       f += (size_t)D.max_tokens * D.r;
       for (int s = 0; s < D.slots; ++s)
         for (int d = 0; d < D.d; ++d) {
@@ -515,6 +539,14 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
           put(x == 0 ? Ly.ringk : Ly.ringv, i, f[(size_t)s * D.d + d]);
         }
       f += (size_t)D.slots * D.d;
+      for (int p = 0; p < D.prefix; ++p)
+        for (int d = 0; d < D.d; ++d) {
+          const size_t i = (x == 0)
+              ? (size_t)u * D.prefix * D.d + (size_t)p * D.d + d
+              : (size_t)u * D.prefix * D.d + (size_t)d * D.prefix + p;
+          put(x == 0 ? Ly.prek : Ly.prev, i, f[(size_t)p * D.d + d]);
+        }
+      f += (size_t)D.prefix * D.d;
     }
   }
   uint8_t *dst = c->M.base + c->G.layers_base + (size_t)layer * lb;

@@ -9,6 +9,8 @@
 //   coef   T     [U][2][max_tokens][r]  coefficient rows (row = token)
 //   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
 //   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
+//   prek   T     [U][P][d]           protected prefix keys, row = position (pre-RoPE)
+//   prev   T     [U][d][P]           protected prefix values, transposed
 // plus, shared by all layers:
 //   rec    float [U][max_rec][G][128]         split-K partial accumulators of decode
 //   recml  float [U][max_rec][G][2]           split-K running max m and sum l
@@ -40,13 +42,14 @@ struct Dims {
   int max_rec;            // decode records per unit
   int rope_anchors;       // anchors in the RoPE table
   int cus;                // compute units of the device (decode grid sizing)
+  int prefix;             // P: protected exact positions 0..P-1 (multiple of 64)
 };
 
 // Pointers of one layer.
 struct LayerPtrs {
   float *basis, *sing, *msync;
   uint8_t *frag;
-  uint8_t *coef, *ringk, *ringv;
+  uint8_t *coef, *ringk, *ringv, *prek, *prev;
 };
 
 struct Shared {
@@ -61,7 +64,7 @@ struct Shared {
 inline __host__ __device__ size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 struct LayerLayout {
-  size_t basis, sing, msync, frag, coef, ringk, ringv, bytes;
+  size_t basis, sing, msync, frag, coef, ringk, ringv, prek, prev, bytes;
 };
 
 inline LayerLayout layer_layout(const Dims &D) {
@@ -75,6 +78,8 @@ inline LayerLayout layer_layout(const Dims &D) {
   L.coef = o;  o = align_up(o + U2 * (size_t)D.max_tokens * D.r * D.elem);
   L.ringk = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.ringv = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
+  L.prek = o;  o = align_up(o + (size_t)D.units * D.prefix * D.d * D.elem);
+  L.prev = o;  o = align_up(o + (size_t)D.units * D.prefix * D.d * D.elem);
   L.bytes = o;
   return L;
 }
@@ -125,6 +130,8 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
   P.coef = b + M.lay.coef;
   P.ringk = b + M.lay.ringk;
   P.ringv = b + M.lay.ringv;
+  P.prek = b + M.lay.prek;
+  P.prev = b + M.lay.prev;
   return P;
 }
 
@@ -136,7 +143,8 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
 // Reset one layer: basis = I[:, :r], S = 0, M = 0, coefficients and rings 0.
 hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s);
 
-// Write n tokens at positions pos0.. into the rings (in_dtype 0 f32, 1 bf16).
+// Write n tokens at positions pos0.. into the protected prefix (positions < P)
+// or the rings (in_dtype 0 f32, 1 bf16).
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
                          int in_dtype, int64_t pos0, hipStream_t s);
 

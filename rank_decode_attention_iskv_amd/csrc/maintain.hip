@@ -51,11 +51,16 @@ __global__ void append_kernel(Model M, int layer, const In *k, const In *v, int 
   const float vx = Store<In>::load(v, src);
   if (!isfinite(kx) || !isfinite(vx)) set_flag(M.sh, 4);
   LayerPtrs P = layer_ptrs(M, layer);
-  const int slot = (int)((pos0 + t) % D.slots);
-  T *rk = reinterpret_cast<T *>(P.ringk) + (size_t)u * D.slots * D.d;
-  T *rv = reinterpret_cast<T *>(P.ringv) + (size_t)u * D.slots * D.d;
+  const int64_t pos = pos0 + t;
+  // protected prefix rows (positions < P) keep their own exact store; later
+  // positions go to ring slot pos % slots.  Both keep V transposed.
+  const bool pre = pos < D.prefix;
+  const int rows = pre ? D.prefix : D.slots;
+  const int slot = pre ? (int)pos : (int)(pos % D.slots);
+  T *rk = reinterpret_cast<T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * D.d;
+  T *rv = reinterpret_cast<T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * D.d;
   Store<T>::store(rk, (size_t)slot * D.d + f, kx);
-  Store<T>::store(rv, (size_t)f * D.slots + slot, vx);
+  Store<T>::store(rv, (size_t)f * rows + slot, vx);
 }
 
 // ---------------------------------------------------------------------------

@@ -32,18 +32,20 @@ def subspace_dist(B1, B2):
 class Pair:
     """A GPU cache and an oracle fed with identical float32 inputs."""
 
-    def __init__(self, w: workloads.Workload, max_tokens=None, oracle=True, layers=1):
+    def __init__(self, w: workloads.Workload, max_tokens=None, oracle=True, layers=1, prefix=0):
         import torch
         from rank_decode_attention_iskv_amd import binding
         self.torch, self.binding, self.w = torch, binding, w
         self.layers = layers
         self.max_tokens = max_tokens or w.context + 64
         storage = binding.BF16 if w.storage == "bf16" else binding.F32
+        self.prefix = prefix
         self.cfg = binding.make_config(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim,
-                                       w.rank, w.window, self.max_tokens, storage)
+                                       w.rank, w.window, self.max_tokens, storage,
+                                       protected_prefix=prefix)
         self.gpu = binding.IskvCache(self.cfg)
         self.ora = (Oracle(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
-                           self.max_tokens, storage=w.storage) if oracle else None)
+                           self.max_tokens, storage=w.storage, prefix=prefix) if oracle else None)
         self.length = [0] * layers
 
     def feed(self, layer, count, sync=True, chunk=64, on_fold=None):
@@ -54,7 +56,8 @@ class Pair:
         end = self.length[layer] + count
         while self.length[layer] < end:
             st = self.gpu.status(layer)
-            free = slots - (st.length - st.compressed)
+            # ring positions start at prefix + compressed; earlier ones fill the prefix
+            free = slots - (st.length - self.prefix - st.compressed)
             n = min(chunk, free, end - self.length[layer])
             k, v = workloads.tokens(self.w, layer, self.length[layer], n)
             k32, v32 = k.astype(np.float32), v.astype(np.float32)
@@ -98,10 +101,10 @@ class Pair:
         for b in range(w.batch):
             for h in range(w.kv_heads):
                 u = self.ora.unit(b, layer, h)
-                units.append([dict(basis=f.B, S=f.S, coef=f.C[: u.n_c], ring=f.ring)
-                              for f in (u.K, u.V)])
+                units.append([dict(basis=f.B, S=f.S, coef=f.C[: u.n_c], ring=f.ring,
+                                   prefix=f.prefix) for f in (u.K, u.V)])
         u0 = self.ora.unit(0, layer, 0)
-        return self.binding.pack_state(self.cfg, u0.length, u0.n_c, units)
+        return self.binding.pack_state(self.cfg, u0.length, u0.compressed, units)
 
 
 def exact_attention(w, L, q, q_pos):

@@ -47,6 +47,7 @@ def test_workspace_bytes_valid_and_monotone():
     dict(head_dim=64), dict(rank=48), dict(rank=256), dict(window=100), dict(window=0),
     dict(block=32), dict(num_q_heads=12), dict(num_q_heads=136), dict(storage=7),
     dict(batch=0), dict(max_tokens=0), dict(rope_base=0.5),
+    dict(protected_prefix=100), dict(protected_prefix=-64), dict(protected_prefix=4160),
 ])
 def test_invalid_configs_rejected(kw):
     assert binding.workspace_bytes(base_cfg(**kw)) == 0
@@ -57,6 +58,17 @@ def test_state_bytes_layout():
     cfg = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000)
     d, r, T, S = 128, 32, 1000, 256 + 64
     assert binding.state_bytes(cfg) == 16 + 2 * 2 * (d * r + r + T * r + S * d) * 4
+    # the protected prefix adds its exact rows per (unit, K|V)
+    cfg = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000, protected_prefix=192)
+    assert binding.state_bytes(cfg) == 16 + 2 * 2 * (d * r + r + T * r + S * d + 192 * d) * 4
+
+
+def test_protected_prefix_workspace():
+    """The prefix rows (K and V, storage dtype) add at least 2 x units x P x d
+    elements per layer to the workspace."""
+    a = binding.workspace_bytes(base_cfg())
+    b = binding.workspace_bytes(base_cfg(protected_prefix=512))
+    assert b - a >= 3 * 2 * 16 * 512 * 128 * 2
 
 
 def test_init_rejects_bad_arguments_without_device_work():

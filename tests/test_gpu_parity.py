@@ -42,12 +42,12 @@ def test_ring_slots_bit_exact_bf16_and_f32():
             np.testing.assert_array_equal(units[1][1]["ring"][s].astype(np.float64), ora.V.ring[s])
 
 
-def _oracle_only(w, L, storage, fold_last=True):
+def _oracle_only(w, L, storage, fold_last=True, prefix=0):
     """Oracle state after L tokens (fold + sync every 64 past the window); with
     fold_last=False a full ring at the end is left unfolded."""
     from oracle import Oracle
     o = Oracle(w.batch, 1, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window, L + 64,
-               storage=storage)
+               storage=storage, prefix=prefix)
     pos = 0
     while pos < L:
         n = min(64, L - pos, w.window + 64 - (o.unit(0, 0, 0).length - o.unit(0, 0, 0).n_c))
@@ -405,3 +405,130 @@ def test_multilayer_hot_keys_window_1024():
         np.testing.assert_array_equal(check(layer, 0), before[layer])
     check(1, 1)
     assert p.gpu.status(1).compressed == o.unit(0, 1, 0).n_c
+
+
+
+# ---------------------------------------------------------------------------
+# Protected prompt prefix: positions 0..P-1 exact, never folded
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wid,kw,P,L", [
+    (2, dict(kv_heads=2, q_heads=8, window=128), 192, 192 + 128 + 64 * 6 + 33),   # bf16 r=32
+    (1, dict(), 128, 128 + 256 + 64 * 5 + 7),                                      # f32 G=1
+    (2, dict(kv_heads=2, q_heads=8, window=128, rank=64), 256, 200),             # inside the prefix
+    (2, dict(kv_heads=1, q_heads=16, window=64, rank=16), 64, 64 + 64 + 64 * 3 + 64),  # G=16, r=16
+])
+def test_protected_prefix_decode_on_imported_state(wid, kw, P, L):
+    """Decode over prefix + compressed + window rows on an oracle-made state;
+    the exported prefix rows equal the oracle's stored rows bit for bit."""
+    w = small(wid, **kw)
+    o = _oracle_only(w, L, w.storage, prefix=P)
+    p = Pair(w, max_tokens=L + 64, oracle=False, prefix=P)
+    p.ora = o
+    p.gpu.import_state(0, p.oracle_blob(0))
+    st = p.gpu.status(0)
+    assert (st.length, st.compressed) == (L, o.unit(0, 0, 0).compressed)
+    length, n_comp, units = p.state(0)
+    for ui in range(w.batch * w.kv_heads):
+        ou = o.unit(ui // w.kv_heads, 0, ui % w.kv_heads)
+        for x, f in enumerate((ou.K, ou.V)):
+            np.testing.assert_array_equal(units[ui][x]["prefix"].astype(np.float64), f.prefix)
+    for step, q_pos in enumerate([L - 1, L + 9, 5]):
+        q = q32(workloads.query(w, 0, step))
+        got = p.decode(0, q, q_pos)
+        ref = o.decode_attn(0, q, q_pos)
+        assert rel_err_per_head(got, ref) < ATOL_OUT, (step, rel_err_per_head(got, ref))
+
+
+def test_protected_prefix_fold_and_sync_on_imported_state():
+    """One block update + sync with a prefix: the block is positions
+    n_c..n_c+63 after the prefix; prefix rows stay untouched."""
+    w = small(1)                                     # f32, r=32, window 256
+    P = 128
+    L = P + w.window + 64 * 4                        # ring full after 3 folds
+    o = _oracle_only(w, L, w.storage, fold_last=False, prefix=P)
+    p = Pair(w, max_tokens=L + 128, oracle=False, prefix=P)
+    p.ora = o
+    p.gpu.import_state(0, p.oracle_blob(0))
+    assert p.gpu.status(0).blocks_ready == 1
+    before = p.state(0)[2]
+    p.gpu.block_update(0)
+    p.gpu.sync(0)
+    o.block_update(0)
+    o.sync(0)
+    length, n_comp, units = p.state(0)
+    ou = o.unit(0, 0, 0)
+    assert (length, n_comp) == (ou.length, ou.compressed) == (L, 64 * 4)
+    for x, f in enumerate((ou.K, ou.V)):
+        np.testing.assert_array_equal(units[0][x]["prefix"], before[0][x]["prefix"])
+        B = units[0][x]["basis"].astype(np.float64)
+        assert np.linalg.norm(B.T @ B - np.eye(B.shape[1]), 2) < 1e-5
+        H_gpu = units[0][x]["coef"][P:ou.n_c].astype(np.float64) @ B.T
+        H_ora = f.C[P:ou.n_c] @ f.B.T
+        assert np.linalg.norm(H_gpu - H_ora) / np.linalg.norm(H_ora) < 1e-4
+        assert not np.any(units[0][x]["coef"][:P])
+    for step, q_pos in enumerate([L - 1, L + 3]):
+        q = q32(workloads.query(w, 0, step))
+        got = p.decode(0, q, q_pos)
+        ref = o.decode_attn(0, q, q_pos)
+        assert rel_err_per_head(got, ref) < ATOL_OUT, rel_err_per_head(got, ref)
+
+
+def test_protected_prefix_end_to_end_f32():
+    """Appends that straddle the prefix end (48-token chunks), folds and syncs
+    through the GPU against the oracle fed the same stream."""
+    w = small(1, window=128)
+    P = 192
+    p = Pair(w, max_tokens=2048, prefix=P)
+    p.feed(0, P + 128 + 64 * 7 + 21, chunk=48)
+    length, n_comp, units = p.state(0)
+    ou = p.ora.unit(0, 0, 0)
+    assert (length, n_comp) == (ou.length, ou.compressed) and n_comp == 64 * 7
+    for x, f in enumerate((ou.K, ou.V)):
+        np.testing.assert_array_equal(units[0][x]["prefix"].astype(np.float64), f.prefix)
+    for step, q_pos in enumerate([length - 1, length]):
+        q = q32(workloads.query(w, 0, step))
+        got = p.decode(0, q, q_pos)
+        ref = p.ora.decode_attn(0, q, q_pos)
+        assert rel_err_per_head(got, ref) < ATOL_OUT, rel_err_per_head(got, ref)
+
+
+def test_protected_prefix_append_decode_matches_two_calls():
+    """iskv_append_decode across the prefix end (the first tokens land in the
+    prefix, where it runs the two calls) and through a fold is bit-identical
+    to iskv_append + iskv_decode_attn."""
+    import torch
+    w = small(2, kv_heads=2, q_heads=8, window=64)
+    P = 128
+    a = Pair(w, max_tokens=64 * 8, oracle=False, prefix=P)
+    b = Pair(w, max_tokens=64 * 8, oracle=False, prefix=P)
+    a.feed(0, P - 5)
+    b.feed(0, P - 5)
+    folds = 0
+    for step in range(150):
+        pos = a.length[0]
+        k, v = workloads.tokens(w, 0, pos, 1)
+        kt = torch.from_numpy(k.astype(np.float32)).cuda()
+        vt = torch.from_numpy(v.astype(np.float32)).cuda()
+        qt = torch.from_numpy(q32(workloads.query(w, 0, step)).astype(np.float32)).cuda()
+        oa, ob = torch.empty_like(qt), torch.empty_like(qt)
+        ra = a.gpu.append(0, kt, vt)
+        a.gpu.decode_attn(0, qt, pos, oa)
+        rb = b.gpu.append_decode(0, kt, vt, qt, pos, ob)
+        a.length[0] += 1
+        b.length[0] += 1
+        torch.cuda.synchronize()
+        assert ra == rb
+        assert torch.equal(oa, ob), step
+        if ra:
+            for pp in (a, b):
+                pp.gpu.block_update(0)
+                pp.gpu.sync(0)
+            folds += 1
+    assert folds >= 1
+    (la, na, ua), (lb, nb, ub) = a.state(0), b.state(0)
+    assert (la, na) == (lb, nb)
+    for xa, xb in zip(ua, ub):
+        for fa, fb in zip(xa, xb):
+            for key in ("basis", "S", "coef", "ring", "prefix"):
+                np.testing.assert_array_equal(fa[key], fb[key])
