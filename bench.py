@@ -7,12 +7,15 @@ and values are a rank-32 Gaussian signal plus 1% noise (synthetic, seeded).
 
 A step is one decode step of that layer: append one token (k, v) and decode
 attention of 32 query heads over the whole mixed cache (one launch,
-iskv_append_decode), and -- whenever the ring holds window + 64 tokens -- a
-block update (Brand fold of 64 tokens for all 8 heads, K and V) followed by
-the coefficient sync.  The bench holds
-several independent instances of the layer and runs the steps round-robin
-over them, so every step reads its cache from HBM rather than from the 256 MB
-Infinity Cache (one instance is ~35 MB).
+iskv_append_decode), plus the block updates (Brand fold of 64 tokens for all 8
+heads, K and V) and coefficient syncs that fall due.  The bench holds 16
+instances of the layer and runs the steps round-robin over them, as the
+layers of one model decode a token (so every step reads its cache from HBM
+rather than from the 256 MB Infinity Cache; one instance is ~35 MB).  All
+instances fill their rings at the same token; by default (--fold-mode layers)
+the step that completes that token folds every instance in one
+iskv_block_update(-1) + iskv_sync(-1), as a multi-layer model would; with
+--fold-mode instance each instance folds alone at its own step.
 
 Prints one JSON line (see --help).  Only one GPU: --gpus N > 1 exits.
 """
@@ -45,6 +48,11 @@ def parse():
     ap.add_argument("--rank", type=int, default=32)
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--fold-mode", choices=("layers", "instance"), default="layers",
+                    help="layers: the instances are the layers of one model, and the token at which "
+                         "they all fill their rings folds them in one block update + sync over every "
+                         "layer (iskv_block_update(-1), iskv_sync(-1)); instance: each instance folds "
+                         "alone at its own step")
     ap.add_argument("--protected-prefix", type=int, default=0,
                     help="leading positions kept exact and never folded (multiple of 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -291,6 +299,7 @@ def main():
     fold_ev, sync_ev = [], []
     bytes_total = 0
     folds = 0
+    n_ready = 0                  # instances whose ring is full (fold mode "layers")
 
     # The step loop calls the C ABI directly with precomputed device pointers
     # and pre-created events: the per-step host work must stay well below the
@@ -308,7 +317,7 @@ def main():
                for _ in range(args.warmup)]
 
     def step(s, timed, warm=False):
-        nonlocal bytes_total, folds, mstream
+        nonlocal bytes_total, folds, mstream, n_ready
         inst = s % I
         j = used[inst]
         used[inst] += 1
@@ -333,22 +342,32 @@ def main():
         if code != 0:
             raise binding.IskvError(code, "iskv_append_decode")
         ready = bool(ready_c.value)
-        if ready:
-            if warm or (timed and (not args.async_maintenance)):
-                f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-                f0.record(stream)
-                cache.block_update(inst)
-                f1.record(stream)
-                cache.sync(inst)
-                f2.record(stream)
-                fold_ev.append((f0, f1))
-                sync_ev.append((f1, f2))
-                folds += 0 if warm else 1
-            else:
-                folds += 0 if warm else 1
-                cache.block_update(inst)
-                cache.sync(inst)
-            comp[inst] += 64
+        if not ready:
+            return
+        comp[inst] += 64
+        if args.fold_mode == "layers":
+            # every instance (layer) fills its ring at the same token; the
+            # last one's step folds them all in one launch pair
+            n_ready += 1
+            if n_ready < I:
+                return
+            n_ready = 0
+            layer, nfold = -1, I
+        else:
+            layer, nfold = inst, 1
+        if warm or (timed and (not args.async_maintenance)):
+            f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            f0.record(stream)
+            cache.block_update(layer)
+            f1.record(stream)
+            cache.sync(layer)
+            f2.record(stream)
+            fold_ev.append((f0, f1))
+            sync_ev.append((f1, f2))
+        else:
+            cache.block_update(layer)
+            cache.sync(layer)
+        folds += 0 if warm else nfold
 
     # warm-up on one stream, with the fold and sync kernels timed by events
     for s in range(args.warmup):
@@ -395,6 +414,7 @@ def main():
     fold_ms = [a.elapsed_time(b) for a, b in fold_ev]
     sync_ms = [a.elapsed_time(b) for a, b in sync_ev]
     units_per_fold = B * H * 2
+    layers_per_launch = I if args.fold_mode == "layers" else 1
     st = cache.status(0)
     flags = max(cache.status(i).numeric_flags for i in range(I))
     finite = bool(torch.isfinite(out).all().item())
@@ -420,14 +440,17 @@ def main():
             "workload": (f"one GQA layer: {H} KV / {HQ} q heads, head_dim {D}, rank {R}, "
                          f"{args.context}-token context (grows by 1 per step), window {W}, "
                          f"bf16 storage, fp32 accumulate, batch {B}, block update + sync every "
-                         f"64 steps; K/V rank-32 signal + 1% noise"
+                         f"64 tokens; K/V rank-32 signal + 1% noise"
                          + (f"; first {P} positions kept exact (protected prefix)" if P else "")),
             "protected_prefix": P,
             "instances_rotated": I,
             "global_batch": B,
             "seq_len": args.context,
             "parallelism": "single GPU",
-            "step_calls": "iskv_append_decode; every 64 steps per instance iskv_block_update + iskv_sync",
+            "step_calls": ("iskv_append_decode; every 64 tokens iskv_block_update(-1) + iskv_sync(-1) "
+                           f"over all {I} instances (layers) at once" if args.fold_mode == "layers" else
+                           "iskv_append_decode; every 64 steps per instance iskv_block_update + iskv_sync"),
+            "fold_mode": args.fold_mode,
             "maintenance": "same stream" if (not args.async_maintenance) else
                            "second stream (each instance waits for its own fold + sync)",
         },
@@ -448,9 +471,11 @@ def main():
             "frac_of_measured_read": achieved / bw_read,
         },
         "decode_attn_calls_per_s_kernel_only": 1e3 / rl_avg_ms,
-        "block_updates_per_s": (units_per_fold * len(fold_ms) / (sum(fold_ms) * 1e-3)) if fold_ms else None,
-        "block_updates_per_s_with_sync": (units_per_fold * len(fold_ms) /
+        "block_updates_per_s": (units_per_fold * layers_per_launch * len(fold_ms) / (sum(fold_ms) * 1e-3))
+                               if fold_ms else None,
+        "block_updates_per_s_with_sync": (units_per_fold * layers_per_launch * len(fold_ms) /
                                           ((sum(fold_ms) + sum(sync_ms)) * 1e-3)) if fold_ms else None,
+        "fold_launch_layers": layers_per_launch,
         "fold_avg_us": (sum(fold_ms) / len(fold_ms) * 1e3) if fold_ms else None,
         "sync_avg_us": (sum(sync_ms) / len(sync_ms) * 1e3) if sync_ms else None,
         "timed_folds": folds,

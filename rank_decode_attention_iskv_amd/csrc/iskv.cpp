@@ -591,9 +591,9 @@ int iskv_destroy(iskv_ctx *c) {
   if (!c) return ISKV_EINVAL;
   hipError_t e = join_all(c);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-  if (c->ev_main) hipEventDestroy(c->ev_main);
+  if (c->ev_main) (void)hipEventDestroy(c->ev_main);
   for (hipEvent_t ev : c->ev_done)
-    if (ev) hipEventDestroy(ev);
+    if (ev) (void)hipEventDestroy(ev);
   delete c;
   return hip_err(e);
 }
