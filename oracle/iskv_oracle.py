@@ -33,9 +33,15 @@ paper), abbreviated [iS-KV explainer].
   stated; the reading here is a leading prefix of P positions (P a multiple
   of 64, default 0) that is never folded: compression starts at position P.
 
+* K and V may take different ranks [KV-CoRE page, Key Results, the
+  asymmetry of K and V: V needs more rank than K for the same energy].  The
+  two factors never interact before decode, so a V factor of rank r_V is the
+  same Brand fold and sync at a different r; the default is r_V = r.
+
 Readings taken where the page is silent (each is listed in the design doc):
   window of W exact tokens plus up to 63 not yet folded (ring of W+64 rows,
-  fold when it is full); basis per KV head, separate for K and V, one rank r;
+  fold when it is full); basis per KV head, separate for K and V, rank r for
+  both unless V is given its own rank r_V (see below);
   initial basis I[:, :r] with S = 0; core [[diag S, 0], [P, R_r^T]]; a
   rank-revealing residual basis and a unit-vector completion of null
   directions; half-split RoPE with base 10000 and fp64 angles; absolute
@@ -285,9 +291,9 @@ class Factor:
 class Unit:
     """One (sequence, layer, KV head): a K factor, a V factor and counters."""
 
-    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK, prefix=0):
+    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK, prefix=0, r_v=None):
         self.K = Factor(d, r, window, max_tokens, storage, block, prefix)
-        self.V = Factor(d, r, window, max_tokens, storage, block, prefix)
+        self.V = Factor(d, r_v or r, window, max_tokens, storage, block, prefix)
         self.length = 0          # tokens appended (L)
         self.P = prefix          # protected exact prefix
         self.n_c = prefix        # end of the compressed positions P..n_c-1
@@ -393,7 +399,7 @@ class Oracle:
 
     def __init__(self, batch, num_layers, kv_heads, q_heads, head_dim, rank, window,
                  max_tokens, storage="bf16", rope_base=10000.0, softmax_scale=None,
-                 block=BLOCK, prefix=0):
+                 block=BLOCK, prefix=0, rank_v=None):
         if q_heads % kv_heads:
             raise ValueError("q_heads must be a multiple of kv_heads")
         self.batch, self.num_layers = batch, num_layers
@@ -402,7 +408,9 @@ class Oracle:
         self.storage, self.rope_base = storage, rope_base
         self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale else float(softmax_scale)
         self.prefix = prefix
-        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix)
+        self.r_v = rank_v or rank
+        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix,
+                             self.r_v)
                         for _ in range(kv_heads)] for _ in range(num_layers)]
                       for _ in range(batch)]
 
@@ -453,10 +461,10 @@ def full_kv_bytes(tokens, layers, kv_heads, head_dim, elem_bytes):
 
 
 def persistent_kv_bytes(n_c, n_exact, layers, kv_heads, head_dim, rank, elem_bytes,
-                        basis_bytes=4):
+                        basis_bytes=4, rank_v=None):
     """Bytes kept between decode steps: coefficients, bases and singular values
     of K and V, plus the exact rows.  Model weights and temporary rebuild
-    buffers are excluded."""
-    per_head = 2 * (n_c * rank * elem_bytes + head_dim * rank * basis_bytes
-                    + rank * basis_bytes + n_exact * head_dim * elem_bytes)
+    buffers are excluded.  rank_v (default rank) is the rank of the V factor."""
+    per_head = sum(n_c * r * elem_bytes + head_dim * r * basis_bytes + r * basis_bytes
+                   + n_exact * head_dim * elem_bytes for r in (rank, rank_v or rank))
     return layers * kv_heads * per_head

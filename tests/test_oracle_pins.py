@@ -466,3 +466,71 @@ def test_prefix_longer_than_history_is_exact_attention_bf16():
 def test_prefix_must_be_block_multiple():
     with pytest.raises(ValueError):
         Unit(64, 16, 64, 512, "f64", 64, prefix=100)
+
+
+# ---------------------------------------------------------------------------
+# Separate K and V ranks [KV-CoRE page, Key Results: K and V are asymmetric]
+# ---------------------------------------------------------------------------
+
+def test_separate_v_rank_lossless_when_each_factor_fits():
+    """K of rank 8 and V of rank 24 (both in span): with r_K = 16 and
+    r_V = 32 every fold is lossless, so decode is exact attention; with
+    r_V = r_K = 16 the V history is truncated and decode moves."""
+    rng = np.random.default_rng(41)
+    d, L, W = 64, 400, 64
+    X = lowrank(rng, L, d, 8)
+    Y = lowrank(rng, L, d, 24)
+    q = rng.standard_normal((2, d))
+    scale = 1 / math.sqrt(d)
+    ref = exact_attention(q, X, Y, L + 1, scale)
+    o = Oracle(1, 1, 1, 2, d, 16, W, L + 64, storage="f64", rank_v=32)
+    u = o.unit(0, 0, 0)
+    assert u.K.r == 16 and u.V.r == 32
+    for t in range(L):
+        u.append(X[t], Y[t])
+        if u.ready:
+            u.fold()
+            u.sync()
+    assert u.compressed >= 256
+    got = u.decode(q, L + 1, scale)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-10
+    # the V history is rebuilt exactly, the K history too
+    np.testing.assert_allclose(u.history("V"), Y[: u.n_c], atol=1e-10)
+    np.testing.assert_allclose(u.history("K"), X[: u.n_c], atol=1e-10)
+    # same data with r_V = r_K: V is truncated (rank 24 > 16)
+    v = run_unit(X, Y, d, 16, W)
+    bad = v.decode(q, L + 1, scale)
+    assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 1e-3
+
+
+def test_separate_v_rank_leaves_k_factor_unchanged():
+    """The K factor of a unit with r_V = 2 r_K is the K factor of the same
+    stream with r_V = r_K: the factors never mix before decode."""
+    rng = np.random.default_rng(42)
+    d, L, W, r = 64, 330, 64, 16
+    X = lowrank(rng, L, d, 30, 0.05)
+    Y = lowrank(rng, L, d, 40, 0.05)
+    a = run_unit(X, Y, d, r, W)
+    b = Unit(d, r, W, L + 64, "f64", 64, r_v=2 * r)
+    for t in range(L):
+        b.append(X[t], Y[t])
+        if b.ready:
+            b.fold()
+            b.sync()
+    assert a.n_c == b.n_c
+    np.testing.assert_array_equal(a.K.B, b.K.B)
+    np.testing.assert_array_equal(a.K.C[: a.n_c], b.K.C[: b.n_c])
+    assert b.V.B.shape == (d, 2 * r)
+    # a wider V basis captures at least as much of the V history
+    ea = np.linalg.norm(a.history("V") - Y[: a.n_c])
+    eb = np.linalg.norm(b.history("V") - Y[: b.n_c])
+    assert eb < ea
+
+
+def test_persistent_bytes_with_separate_v_rank():
+    """Closed form: per head, K keeps n_c*r_K coefficient elements, d*r_K + r_K
+    fp32 basis/singular values and n_exact*d exact elements; V the same at r_V."""
+    got = persistent_kv_bytes(1000, 300, 2, 4, 128, 32, 2, rank_v=64)
+    k = 1000 * 32 * 2 + 128 * 32 * 4 + 32 * 4 + 300 * 128 * 2
+    v = 1000 * 64 * 2 + 128 * 64 * 4 + 64 * 4 + 300 * 128 * 2
+    assert got == 2 * 4 * (k + v)
