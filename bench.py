@@ -46,6 +46,8 @@ def parse():
                     help="independent copies of the layer, stepped round-robin")
     ap.add_argument("--context", type=int, default=32768, help="tokens in the cache when timing starts")
     ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--rank-v", type=int, default=0,
+                    help="rank of the V factor (0: same as --rank; else --rank or 2x --rank)")
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--fold-mode", choices=("layers", "instance"), default="layers",
@@ -139,10 +141,12 @@ class Generator:
         return self.torch.randn(count, self.shape[0], q_heads, d, device="cuda", generator=self.g)
 
 
-def decode_bytes(batch, kv_heads, q_heads, d, r, n_c, n_e, elem=2):
-    """Algorithmic bytes of one decode call: coefficients of K and V, exact
-    window rows of K and V, the two fp32 bases, the fp32 query and output."""
-    per_unit = n_c * r * 2 * elem + n_e * d * 2 * elem + 2 * d * r * 4
+def decode_bytes(batch, kv_heads, q_heads, d, r, n_c, n_e, elem=2, r_v=None):
+    """Algorithmic bytes of one decode call: coefficients of K (rank r) and V
+    (rank r_v, default r), exact window rows of K and V, the two fp32 bases,
+    the fp32 query and output."""
+    rs = r + (r_v or r)
+    per_unit = n_c * rs * elem + n_e * d * 2 * elem + d * rs * 4
     return batch * kv_heads * per_unit + batch * q_heads * d * 4 * 2
 
 
@@ -257,7 +261,9 @@ def main():
     per_inst_steps = (total_steps + I - 1) // I
     max_tokens = args.context + per_inst_steps + 64
     P = args.protected_prefix
-    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16, protected_prefix=P)
+    RV = args.rank_v or R
+    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16, protected_prefix=P,
+                              rank_v=RV)
     cache = binding.IskvCache(cfg)
     stream = torch.cuda.current_stream()
     gen = Generator(torch, I, B, H, D, 32, args.seed)
@@ -334,11 +340,11 @@ def main():
             code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
                                          ctypes.byref(ready_c))
             e1.record(stream)
-            ev.append((e0, e1, decode_bytes(B, H, HQ, D, R, n_c, L - n_c)))
+            ev.append((e0, e1, decode_bytes(B, H, HQ, D, R, n_c, L - n_c, r_v=RV)))
         else:
             code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
                                          ctypes.byref(ready_c))
-            bytes_total += decode_bytes(B, H, HQ, D, R, n_c, L - n_c)
+            bytes_total += decode_bytes(B, H, HQ, D, R, n_c, L - n_c, r_v=RV)
         if code != 0:
             raise binding.IskvError(code, "iskv_append_decode")
         ready = bool(ready_c.value)
@@ -405,7 +411,7 @@ def main():
         code = L_.iskv_decode_attn(ctx, inst, qp, lengths[inst] - 1, out_p)
         if code != 0:
             raise binding.IskvError(code, "iskv_decode_attn")
-        rl_bytes += decode_bytes(B, H, HQ, D, R, comp[inst], lengths[inst] - comp[inst])
+        rl_bytes += decode_bytes(B, H, HQ, D, R, comp[inst], lengths[inst] - comp[inst], r_v=RV)
     r1.record(stream)
     torch.cuda.synchronize()
     rl_avg_ms = r0.elapsed_time(r1) / rl_calls
@@ -441,8 +447,10 @@ def main():
                          f"{args.context}-token context (grows by 1 per step), window {W}, "
                          f"bf16 storage, fp32 accumulate, batch {B}, block update + sync every "
                          f"64 tokens; K/V rank-32 signal + 1% noise"
-                         + (f"; first {P} positions kept exact (protected prefix)" if P else "")),
+                         + (f"; first {P} positions kept exact (protected prefix)" if P else "")
+                         + (f"; V rank {RV}" if RV != R else "")),
             "protected_prefix": P,
+            "rank_v": RV,
             "instances_rotated": I,
             "global_batch": B,
             "seq_len": args.context,

@@ -37,8 +37,9 @@
  *     returns ISKV_EDEVICE.  Device-detected numeric trouble (non-finite input
  *     or core, Jacobi sweep cap reached) is reported by iskv_status.
  *   - A context is not thread-safe.  Sequences of a batch advance in lockstep.
- *   - head_dim must be 128; rank must be 16, 32, 64 or 128; window a multiple
- *     of 64; num_q_heads a multiple of num_kv_heads, at most 16 times it.
+ *   - head_dim must be 128; rank must be 16, 32, 64 or 128 (rank_v equal to it
+ *     or twice it); window a multiple of 64; num_q_heads a multiple of
+ *     num_kv_heads, at most 16 times it.
  */
 #ifndef ISKV_H
 #define ISKV_H
@@ -86,6 +87,11 @@ typedef struct {
   int32_t protected_prefix; /* P: positions 0..P-1 stay exact and are never
                                folded (protected prompt rows); a multiple of 64,
                                0 <= P <= max_tokens; 0 = none */
+  int32_t rank_v;         /* rank of the value factor: 0 (= rank), rank, or
+                             2 * rank (<= head_dim); `rank` is then the key
+                             rank.  Keys compress better than values
+                             [KV-CoRE page, Key Results "Asymmetry of K
+                             and V"] */
 } iskv_config;
 
 typedef struct {
@@ -109,8 +115,9 @@ size_t iskv_workspace_bytes(const iskv_config *cfg);
 /* Bytes of one layer's state blob for iskv_export_state / iskv_import_state
  * (0 if cfg is invalid). Layout, all little-endian:
  *   int64 length, int64 compressed, then for b in [0,batch), h in [0,kv_heads),
- *   X in (K, V):  float basis[head_dim][rank], float S[rank],
- *                 float coeff[max_tokens][rank]   (row = position; rows outside
+ *   X in (K, V), with r = rank for K and rank_v (or rank) for V:
+ *                 float basis[head_dim][r], float S[r],
+ *                 float coeff[max_tokens][r]      (row = position; rows outside
  *                                                  P .. P+compressed-1 are 0),
  *                 float ring[window+64][head_dim] (slot = position % (window+64)),
  *                 float prefix[P][head_dim]       (protected rows, P = protected_prefix). */

@@ -30,7 +30,7 @@ class Config(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32), ("window", ctypes.c_int32),
         ("block", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("storage", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-        ("protected_prefix", ctypes.c_int32),
+        ("protected_prefix", ctypes.c_int32), ("rank_v", ctypes.c_int32),
     ]
 
 
@@ -111,9 +111,14 @@ def strerror(code: int) -> str:
 
 def make_config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window,
                 max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64,
-                protected_prefix=0) -> Config:
+                protected_prefix=0, rank_v=0) -> Config:
     return Config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window, block,
-                  max_tokens, storage, rope_base, softmax_scale, protected_prefix)
+                  max_tokens, storage, rope_base, softmax_scale, protected_prefix, rank_v)
+
+
+def factor_ranks(cfg: Config):
+    """(rank of K, rank of V); rank_v 0 means V shares the K rank."""
+    return cfg.rank, (cfg.rank_v or cfg.rank)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -257,22 +262,23 @@ def unpack_state(cfg: Config, blob):
     """Split a state blob into numpy arrays per (unit, K|V); n_c is the
     compressed token count (rows protected_prefix .. protected_prefix+n_c-1)."""
     import numpy as np
-    d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    d, T, S = cfg.head_dim, cfg.max_tokens, cfg.window + cfg.block
+    ranks = factor_ranks(cfg)
     Pp = cfg.protected_prefix
     length, n_c = np.frombuffer(bytes(blob[:16]), dtype=np.int64)
     f = np.frombuffer(bytes(blob[16:]), dtype=np.float32)
     units = cfg.batch * cfg.num_kv_heads
-    per = d * r + r + T * r + S * d + Pp * d
     out = []
+    o = 0
     for u in range(units):
         xs = []
         for x in range(2):
-            o = (u * 2 + x) * per
+            r = ranks[x]
             B = f[o: o + d * r].reshape(d, r); o += d * r
             Sv = f[o: o + r]; o += r
             C = f[o: o + T * r].reshape(T, r); o += T * r
             ring = f[o: o + S * d].reshape(S, d); o += S * d
-            prefix = f[o: o + Pp * d].reshape(Pp, d)
+            prefix = f[o: o + Pp * d].reshape(Pp, d); o += Pp * d
             xs.append(dict(basis=B, S=Sv, coef=C, ring=ring, prefix=prefix))
         out.append(xs)
     return int(length), int(n_c), out
@@ -283,10 +289,11 @@ def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
     position), ring and, with a protected prefix, prefix arrays."""
     import numpy as np
     parts = [np.array([length, n_c], dtype=np.int64).tobytes()]
-    d, r, T, S = cfg.head_dim, cfg.rank, cfg.max_tokens, cfg.window + cfg.block
+    d, T, S = cfg.head_dim, cfg.max_tokens, cfg.window + cfg.block
+    ranks = factor_ranks(cfg)
     Pp = cfg.protected_prefix
     for xs in units:
-        for x in xs:
+        for r, x in zip(ranks, xs):
             C = np.zeros((T, r), dtype=np.float32)
             C[: x["coef"].shape[0]] = x["coef"][:T]
             parts += [np.asarray(x["basis"], np.float32).reshape(d, r).tobytes(),

@@ -255,7 +255,7 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
   const float *acc = M.sh.rec + (size_t)u * D.max_rec * G * kRecStride;
   const __amdgpu_buffer_rsrc_t rr = agent_rsrc(acc, n_rec * G * kRecStride * 4);
   LayerPtrs P = layer_ptrs(M, layer);
-  const uint8_t *Bv = reinterpret_cast<const uint8_t *>(P.basis + ((size_t)u * 2 + 1) * kHeadDim * R);
+  const uint8_t *Bv = reinterpret_cast<const uint8_t *>(P.basis[1] + (size_t)u * kHeadDim * R);
 
   // ---- value basis [128][R] -> LDS (R/2 KiB, 1 KiB per wave DMA).  16-byte
   // chunk c4 of row f lands at chunk c4 ^ bv_swz(f) of the row, so the output
@@ -380,17 +380,22 @@ __device__ void merge_unit(const Model &M, int layer, float *out, const SplitPla
 // Tunables per (rank, storage, waves per workgroup): occupancy, the LDS
 // layout and the per-wave ring.
 // ---------------------------------------------------------------------------
-template <int R, typename T, int NW> struct Cfg {
+// RK, RV: ranks of the key and value factors.
+template <int RK, int RV, typename T, int NW> struct Cfg {
+  static constexpr int R = RK;
   static constexpr bool BF = std::is_same<T, bf16_t>::value;
   static constexpr int kElem = BF ? 2 : 4;
-  static constexpr int kMatBytes = 16 * R * kElem;           // one 16-token tile of C_K or C_V
-  static constexpr int kDma = kMatBytes >= 1024 ? kMatBytes / 1024 : 1;   // dwordx4 DMAs per matrix
+  static constexpr int kMatK = 16 * RK * kElem;              // one 16-token tile of C_K
+  static constexpr int kMatV = 16 * RV * kElem;              // ... and of C_V
+  static constexpr int kSlot = kMatK + kMatV;                // ring slot [C_K tile | C_V tile]
+  static constexpr int kDmaK = kMatK >= 1024 ? kMatK / 1024 : 1;   // dwordx4 DMAs per matrix
+  static constexpr int kDmaV = kMatV >= 1024 ? kMatV / 1024 : 1;
   // Eight-wave workgroups (bf16, r <= 64; one per CU, two waves per SIMD)
   // share their prologue: the key-basis fragments and the RoPE rotations of
   // offsets 0..15 reach LDS once per workgroup by DMA, and each wave's base
   // angle takes one coalesced load per lane (lane = frequency).  Four-wave
   // workgroups load both per wave.
-  static_assert(NW == 4 || (NW == 8 && BF && R <= 64), "wave count");
+  static_assert(NW == 4 || (NW == 8 && BF && RK <= 64 && RV <= 64), "wave count");
   static constexpr bool kShared = NW == 8;
   // bf16 r = 64: the low bf16 parts of the key-basis fragments are read from
   // LDS in the loop instead of registers (which two waves per SIMD lack)
@@ -404,35 +409,36 @@ template <int R, typename T, int NW> struct Cfg {
   // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring.
   // Eight-wave workgroups keep four r <= 32 tiles per wave (eight waves per
   // CU hold enough bytes in flight, and a shorter ring is issued sooner)
-  static constexpr int kRingBytes = kShared ? (R == 64 ? 12288 : 8192)
-                                    : kLoLds ? 12288 : (kMatBytes >= 4096 ? 32768 : 16384);
-  static constexpr int kDepth = kRingBytes / (2 * kMatBytes) > 16 ? 16 : kRingBytes / (2 * kMatBytes);
+  static constexpr int kRingBytes = kShared ? (RK == 64 || RV == 64 ? 12288 : 8192)
+                                    : kLoLds ? 12288 : (kSlot >= 8192 ? 32768 : 16384);
+  static constexpr int kDepth = kRingBytes / kSlot > 16 ? 16 : kRingBytes / kSlot;
   static_assert(kDepth >= 2, "ring depth");
   static constexpr int kWaves = NW;
   static constexpr int kThr = 64 * NW;
-  static constexpr int kOcc = (BF && R <= 64 && NW == 4) ? 2 : 1;
+  static constexpr int kOcc = (BF && RK <= 64 && RV <= 64 && NW == 4) ? 2 : 1;
   // compressed tiles in pairs (two register sets for the angle state); wider
   // ranks lack the registers for it
-  static constexpr bool kPair = R <= 32;
+  static constexpr bool kPair = RK <= 32 && RV <= 32;
   static constexpr int kAccBytes = kWaves * 16 * kHeadDim * 4;    // per-wave results, after the loop
   static constexpr int kLoopBytes = (kRingOff + NW * kRingBytes > kAccBytes)
                                         ? kRingOff + NW * kRingBytes : kAccBytes;
-  static constexpr int kMrgBytes = MergeLds<R, kWaves>::bytes;
+  static constexpr int kMrgBytes = MergeLds<RV, kWaves>::bytes;
   static constexpr int kDynBytes = kLoopBytes > kMrgBytes ? kLoopBytes : kMrgBytes;
 };
 
 // ---------------------------------------------------------------------------
 // The MFMA decode kernel.  grid (splits, units), 64 * kWaves threads.
 // ---------------------------------------------------------------------------
-template <int R, typename T, int NW>
-__global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void decode_mfma_kernel(
+template <int RK, int RV, typename T, int NW>
+__global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
     int64_t n_c, SplitPlan plan, int fused, FusedAppend app) {
-  using C = Cfg<R, T, NW>;
+  using C = Cfg<RK, RV, T, NW>;
+  constexpr int R = RK;                                  // the key path below uses R
   constexpr bool BF = C::BF;
-  constexpr int NBV = R / 16;                            // value N-blocks (compressed)
+  constexpr int NBV = RV / 16;                           // value N-blocks (compressed)
   constexpr int DEPTH = C::kDepth;
-  constexpr int LPT = 2 * C::kDma;                       // DMA loads per tile
+  constexpr int LPT = C::kDmaK + C::kDmaV;               // DMA loads per tile
   constexpr int QK = 16 / NW;
   extern __shared__ __align__(16) uint8_t s_dyn[];       // per-wave rings, then results
   __shared__ float s_m[NW][16], s_l[NW][16];
@@ -590,20 +596,22 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
     for (int nb = 0; nb < NBV; ++nb) vacc[nb] = zero4();
     // per-wave LDS ring of DEPTH slots, each [C_K tile | C_V tile]
     uint8_t *ring = s_dyn + C::kRingOff + wave * C::kRingBytes;
-    const uint8_t *gk = P.coef + (((size_t)u * 2 + 0) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
-    const uint8_t *gv = P.coef + (((size_t)u * 2 + 1) * D.max_tokens * R + (size_t)w_begin * R) * C::kElem;
-    // one tile: kDma dwordx4 DMAs per matrix; lane l moves 16 bytes of chunk
-    // d*64 + l of the tile (lanes past the tile size idle)
+    const uint8_t *gk = P.coef[0] + ((size_t)u * D.max_tokens * RK + (size_t)w_begin * RK) * C::kElem;
+    const uint8_t *gv = P.coef[1] + ((size_t)u * D.max_tokens * RV + (size_t)w_begin * RV) * C::kElem;
+    // one tile: kDmaK / kDmaV dwordx4 DMAs per matrix; lane l moves 16 bytes
+    // of chunk d*64 + l of the tile (lanes past the tile size idle)
     // tile `src` into ring slot `it` % DEPTH
     auto issue_from = [&](int it, int src) {
-      uint8_t *slot = ring + (it % DEPTH) * 2 * C::kMatBytes;
+      uint8_t *slot = ring + (it % DEPTH) * C::kSlot;
 #pragma unroll
-      for (int d = 0; d < C::kDma; ++d) {
+      for (int d = 0; d < C::kDmaK; ++d) {
         const int off = (d * 64 + lane) * 16;
-        if (off < C::kMatBytes) {
-          dma16(gk + (size_t)src * C::kMatBytes + off, slot + d * 1024);
-          dma16(gv + (size_t)src * C::kMatBytes + off, slot + C::kMatBytes + d * 1024);
-        }
+        if (off < C::kMatK) dma16(gk + (size_t)src * C::kMatK + off, slot + d * 1024);
+      }
+#pragma unroll
+      for (int d = 0; d < C::kDmaV; ++d) {
+        const int off = (d * 64 + lane) * 16;
+        if (off < C::kMatV) dma16(gv + (size_t)src * C::kMatV + off, slot + C::kMatK + d * 1024);
       }
     };
     auto issue = [&](int it) { issue_from(it, it); };
@@ -615,7 +623,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
     // the ring issue would wait for the whole ring.)  Every wave's LDS copies
     // are older than its query loads, so they have completed before the
     // barrier in query_finish, after which all waves read them.
-    const uint8_t *FB = P.frag + ((size_t)u * 2 + 0) * 4 * kHeadDim * R;
+    const uint8_t *FB = P.frag + (size_t)u * 4 * kHeadDim * R;
     constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
     // LDS address of the low-part chunk (mb, kb) of the key-basis fragments
     auto lo_chunk = [&](int mb, int kb) -> const uint8_t * {
@@ -727,9 +735,9 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
       } else {
         wait_vmcnt<0>();
       }
-      const uint8_t *slot = ring + (it % DEPTH) * 2 * C::kMatBytes;
+      const uint8_t *slot = ring + (it % DEPTH) * C::kSlot;
       const T *tk = reinterpret_cast<const T *>(slot);
-      const T *tv = reinterpret_cast<const T *>(slot + C::kMatBytes);
+      const T *tv = reinterpret_cast<const T *>(slot + C::kMatK);
       // keys: rebuild from the basis fragments and this lane's coefficients
       floatx4 ka[8];
       if constexpr (BF) {
@@ -787,8 +795,8 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) {
           const int c = 16 * nb + n16;
-          const unsigned x0 = tl[(4 * rho + 0) * R + c], x1 = tl[(4 * rho + 1) * R + c];
-          const unsigned x2 = tl[(4 * rho + 2) * R + c], x3 = tl[(4 * rho + 3) * R + c];
+          const unsigned x0 = tl[(4 * rho + 0) * RV + c], x1 = tl[(4 * rho + 1) * RV + c];
+          const unsigned x2 = tl[(4 * rho + 2) * RV + c], x3 = tl[(4 * rho + 3) * RV + c];
           const uint2_ v = {x0 | (x1 << 16), x2 | (x3 << 16)};
           vacc[nb] = mfma16(uint2_{h0, h1}, v, vacc[nb]);
           vacc[nb] = mfma16(uint2_{l0, l1}, v, vacc[nb]);
@@ -799,7 +807,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
         for (int nb = 0; nb < NBV; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * R + 16 * nb + n16], vacc[nb]);
+            vacc[nb] = mfma4(p[i], tf[(4 * rho + i) * RV + 16 * nb + n16], vacc[nb]);
       }
     };
     // chunks of 32 tiles: the angle state is re-anchored from the table at
@@ -851,8 +859,8 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
       // exact rows: the protected prefix (row = position) or the ring (row =
       // position % slots); V transposed in both, row stride `rows`
       const int rows = pre ? D.prefix : D.slots;
-      const T *RK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
-      const T *RV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
+      const T *EK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
+      const T *EV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
       for (int it = 0; it < nt; ++it) {
         const int64_t t0 = w_begin + 16 * (int64_t)it;
         const int slot = (int)((t0 + n16) % rows);
@@ -860,7 +868,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
         floatx4 ka[8];
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
-          const T *src = RK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho;
+          const T *src = EK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho;
           if constexpr (BF) {
             const uint2_ v = *reinterpret_cast<const uint2_ *>(src);
             ka[mb] = floatx4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
@@ -882,7 +890,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
             const uint2_ v = *reinterpret_cast<const uint2_ *>(
-                RV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
+                EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
             wacc[nb] = mfma16(uint2_{h0, h1}, v, wacc[nb]);
             wacc[nb] = mfma16(uint2_{l0, l1}, v, wacc[nb]);
           }
@@ -890,7 +898,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
             const floatx4 v = *reinterpret_cast<const floatx4 *>(
-                RV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
+                EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
 #pragma unroll
             for (int i = 0; i < 4; ++i) wacc[nb] = mfma4(p[i], v[i], wacc[nb]);
           }
@@ -912,7 +920,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
   __syncthreads();
 
   // ---- combine the four waves into this split's record
-  const int width = comp ? R : kHeadDim;
+  const int width = comp ? RV : kHeadDim;
   const size_t rec0 = ((size_t)u * D.max_rec + split) * G;
   for (int e = threadIdx.x; e < G * (2 + width); e += C::kThr) {
     const int h = e / (2 + width), x = e % (2 + width);
@@ -950,7 +958,7 @@ __global__ __launch_bounds__((Cfg<R, T, NW>::kThr), (Cfg<R, T, NW>::kOcc)) void 
   }
   __syncthreads();
   if (!s_last) return;
-  merge_unit<R, NW>(M, layer, out, plan, u, s_dyn);
+  merge_unit<RV, NW>(M, layer, out, plan, u, s_dyn);
   if (threadIdx.x == 0) __hip_atomic_store(M.sh.cnt + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1021,17 +1029,17 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
   return plan;
 }
 
-template <int R, typename T, int NW>
+template <int RK, int RV, typename T, int NW>
 hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, const SplitPlan &plan, hipStream_t s,
                        FusedAppend app) {
-  using C = Cfg<R, T, NW>;
+  using C = Cfg<RK, RV, T, NW>;
   dim3 grid(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
   constexpr int dyn = C::kDynBytes;
   static bool dattr = false;
   hipError_t e;
   if (!dattr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<R, T, NW>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<RK, RV, T, NW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
     if (e != hipSuccess) return e;
     dattr = true;
@@ -1039,19 +1047,19 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   // fuse the merge when every workgroup is resident at once
   const int64_t slots = (int64_t)M.D.cus * C::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
-  hipLaunchKernelGGL((decode_mfma_kernel<R, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
+  hipLaunchKernelGGL((decode_mfma_kernel<RK, RV, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
                      out, length, n_c, plan, fused, app);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
-  constexpr int mbytes = MergeLds<R, 4>::bytes;
+  constexpr int mbytes = MergeLds<RV, 4>::bytes;
   static bool mattr = false;
   if (!mattr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_merge_kernel<R>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_merge_kernel<RV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
     if (e != hipSuccess) return e;
     mattr = true;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<R>), dim3(M.D.units), dim3(kThreads), mbytes, s, M, layer,
+  hipLaunchKernelGGL((decode_merge_kernel<RV>), dim3(M.D.units), dim3(kThreads), mbytes, s, M, layer,
                      out, plan);
   return hipGetLastError();
 }
@@ -1060,25 +1068,36 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
 // single launch wave, where two waves per SIMD and an even share per CU set
 // the time); four-wave workgroups, two per CU, for larger grids, where one
 // workgroup's set-up and merge overlap the other's loop.
-template <int R, typename T>
+template <int RK, int RV, typename T>
 hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
-  if constexpr (std::is_same<T, bf16_t>::value && R <= 64) {
+  if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
     const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
     if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
-      return launch_mfma<R, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app);
+      return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app);
   }
-  return launch_mfma<R, T, 4>(M, layer, q, q_pos, out, length, n_c, make_plan(M.D, length, n_c, 4), s, app);
+  return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c,
+                                   make_plan(M.D, length, n_c, 4), s, app);
 }
 
+// (r_K, r_V): equal ranks, or a value rank twice the key rank
 template <typename T>
 hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                            int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
-  switch (M.D.r) {
-    case 16: return launch_rank<16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 32: return launch_rank<32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 64: return launch_rank<64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-    case 128: return launch_rank<128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+  const int rk = M.D.rk, rv = M.D.rv;
+  if (rv == rk) {
+    switch (rk) {
+      case 16: return launch_rank<16, 16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 32: return launch_rank<32, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 64: return launch_rank<64, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 128: return launch_rank<128, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    }
+  } else if (rv == 2 * rk) {
+    switch (rk) {
+      case 16: return launch_rank<16, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 32: return launch_rank<32, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 64: return launch_rank<64, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -11,7 +11,7 @@
 // coefficients are U diag(S)) and a new block A (64 x d):
 //   P = A B, Res = A - P B^T (projected twice);
 //   Res = L Q with Q (64 x d) orthonormal rows, orthogonal to B (CholeskyQR2,
-//     with a pivot guard that drops directions at the rounding level);
+//     with a pivot guard that drops directions the fp32 Gram cannot resolve);
 //   [H; A] = diag(U, I) K [B Q^T]^T,  K = [[diag S, 0], [P, A Q^T]]  ((r+64)^2);
 //   K = U' diag(s') V'^T;  B_new = [B Q^T] V'[:, :r];  S_new = s'[:r];
 //   old coefficients map by M = B^T B_new; the block's are A B_new.
@@ -37,9 +37,18 @@ constexpr float kJacobiTol = 1.0e-6f;     // rotate while |y_p . y_q| > tol |y_p
 // rotations) was below this: the cyclic sweep leaves O(that^2) behind, which is
 // at the fp32 floor of the inner products, so a further sweep only chases noise.
 constexpr float kJacobiQuad = 1.0e-3f;
-// A residual direction is dropped when its squared norm is below
-// kGuard * ||A||_F^2 (so kept directions have condition number < ~1/sqrt(kGuard)).
+// First CholeskyQR pass: a pivot of the residual Gram G = Res Res^T is dropped
+// when it is at most max(kGuardAbs ||A||_F^2, min(kGuard ||A||_F^2, kGuardRel tr G)).
+// kGuard ||A||^2 keeps kept directions below condition number ~1/sqrt(kGuard)
+// when the residual is large (it holds signal, as in the first folds); when
+// the residual is small against A (steady state, and square when r = d - 64)
+// that guard would drop real directions and move the leading subspace by
+// ~5e-4, so the bound becomes relative to tr G = ||Res||_F^2 (condition number
+// below ~1000, where CholeskyQR2 still ends orthonormal).  kGuardAbs drops
+// only the rounding of the projection A - P B^T (~16 fp32 ulps of ||A||).
 constexpr float kGuard = 1.0e-7f;
+constexpr float kGuardRel = 1.0e-6f;
+constexpr float kGuardAbs = 1.0e-12f;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -539,7 +548,7 @@ __device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int
 
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSel sel,
-                                                                int64_t n_c) {
+                                                                int64_t n_c, int xsel) {
   using Ly = FoldLayout<R>;
   constexpr int D = kHeadDim, TB = kBlock, N = Ly::N, NC = Ly::NC;
   constexpr int LA = Ly::LA, LB = Ly::LB, LG = Ly::LG, LC = Ly::LC;
@@ -551,13 +560,14 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   __shared__ float s_f[4];
   const Dims &Dm = M.D;
   const int layer = sel.idx[blockIdx.y];
-  const int ux = blockIdx.x, u = ux >> 1, X = ux & 1;
+  // grid.x: units (one factor, xsel) or units x 2 (both factors, equal ranks)
+  const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
   const int tid = threadIdx.x;
   LayerPtrs P = layer_ptrs(M, layer);
-  float *basis = P.basis + (size_t)ux * D * R;
-  float *sing = P.sing + (size_t)ux * R;
-  float *msync = P.msync + (size_t)ux * R * R;
-  T *coef = reinterpret_cast<T *>(P.coef) + (size_t)ux * Dm.max_tokens * R;
+  float *basis = P.basis[X] + (size_t)u * D * R;
+  float *sing = P.sing[X] + (size_t)u * R;
+  float *msync = P.msync[X] + (size_t)u * R * R;
+  T *coef = reinterpret_cast<T *>(P.coef[X]) + (size_t)u * Dm.max_tokens * R;
   const T *ring = reinterpret_cast<const T *>(X == 0 ? P.ringk : P.ringv) +
                   (size_t)u * Dm.slots * D;
   const int s0 = (int)(n_c % Dm.slots);
@@ -603,15 +613,22 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
     __syncthreads();
 
     // ---------------- phase 2: Q by CholeskyQR2 ----------------
-    // pass 0 drops directions with sigma^2 <= kGuard ||A||^2 (float noise of
-    // the projection); pass 1 sees ~unit rows and drops those that lost
-    // their norm.
+    // pass 0 drops directions at the guard above (unresolved by the fp32
+    // Gram, or float noise of the projection); pass 1 sees ~unit rows and
+    // drops those that lost their norm.
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
       gemm4<TB, TB, D, false, true>(sQ, LA, sQ, LA,
                                     [&](int a, int b, float v) { sG[a * LG + b] = v; });
       __syncthreads();
-      chol_lds<TB>(sG, LG, pass == 0 ? kGuard * normA2 : 0.25f, invd);
+      float tau = 0.25f;
+      if (pass == 0) {
+        float tr = 0.f;                           // ||Res||_F^2 (LDS broadcast reads)
+#pragma unroll 8
+        for (int t = 0; t < TB; ++t) tr += sG[t * LG + t];
+        tau = fmaxf(kGuardAbs * normA2, fminf(kGuard * normA2, kGuardRel * tr));
+      }
+      chol_lds<TB>(sG, LG, tau, invd);
       if (tid < D) {
         float x[TB];
 #pragma unroll
@@ -859,7 +876,7 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
 }
 
 template <int R, typename T>
-hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
+hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
   static bool attr = false;
   const size_t bytes = FoldLayout<R>::bytes;
   if (!attr) {
@@ -868,27 +885,29 @@ hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, hipSt
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid(M.D.units * 2, sel.n);
-  hipLaunchKernelGGL((block_update_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, sel, n_c);
+  dim3 grid(x < 0 ? M.D.units * 2 : M.D.units, sel.n);
+  hipLaunchKernelGGL((block_update_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, sel, n_c, x);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
-  switch (M.D.r) {
-    case 16: return launch_fold_t<16, T>(M, sel, n_c, s);
-    case 32: return launch_fold_t<32, T>(M, sel, n_c, s);
-    case 64: return launch_fold_t<64, T>(M, sel, n_c, s);
-    case 128: return launch_fold_t<128, T>(M, sel, n_c, s);
+hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
+  const int r = x == 1 ? M.D.rv : M.D.rk;
+  if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
+  switch (r) {
+    case 16: return launch_fold_t<16, T>(M, sel, n_c, x, s);
+    case 32: return launch_fold_t<32, T>(M, sel, n_c, x, s);
+    case 64: return launch_fold_t<64, T>(M, sel, n_c, x, s);
+    case 128: return launch_fold_t<128, T>(M, sel, n_c, x, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s) {
-  return M.D.storage == 1 ? dispatch_fold<bf16_t>(M, sel, n_c, s)
-                          : dispatch_fold<float>(M, sel, n_c, s);
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
+  return M.D.storage == 1 ? dispatch_fold<bf16_t>(M, sel, n_c, x, s)
+                          : dispatch_fold<float>(M, sel, n_c, x, s);
 }
 
 }  // namespace iskv

@@ -40,6 +40,9 @@ bool valid_config(const iskv_config *c) {
   if (c->head_dim != kHeadDim) return false;
   if (c->rank != 16 && c->rank != 32 && c->rank != 64 && c->rank != 128) return false;
   if (c->rank > c->head_dim) return false;
+  // value rank: 0 (= rank), rank, or twice rank (<= head_dim)
+  if (c->rank_v != 0 && c->rank_v != c->rank && c->rank_v != 2 * c->rank) return false;
+  if (c->rank_v > c->head_dim) return false;
   if (c->block != kBlock) return false;
   if (c->window < kBlock || c->window % kBlock) return false;
   if (c->max_tokens < 1 || c->max_tokens > (1 << 24)) return false;
@@ -59,7 +62,8 @@ Dims make_dims(const iskv_config *c) {
   D.q_heads = c->num_q_heads;
   D.group = c->num_q_heads / c->num_kv_heads;
   D.d = c->head_dim;
-  D.r = c->rank;
+  D.rk = c->rank;
+  D.rv = c->rank_v ? c->rank_v : c->rank;
   D.window = c->window;
   D.slots = c->window + kBlock;
   D.max_tokens = c->max_tokens;
@@ -111,6 +115,10 @@ struct iskv_ctx {
   // that layer waits for them (per-layer events)
   hipStream_t mstream = nullptr;
   hipEvent_t ev_main = nullptr;
+  // different K and V ranks: the V fold / sync run on `aux`, forked from and
+  // joined back into the stream of the call, so both factors' kernels overlap
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<hipEvent_t> ev_done;
   std::vector<char> maint_pending;
 };
@@ -159,6 +167,21 @@ void fill_sel(LayerSel &sel, const std::vector<int> &idx, size_t from) {
   for (size_t i = from; i < idx.size() && sel.n < kMaxLayerSel; ++i) sel.idx[sel.n++] = idx[i];
 }
 
+// Run launch(x, stream) for both factors: one launch (x = -1) when the ranks
+// are equal; otherwise K on s and V on the helper stream, forked from s and
+// joined back into it.
+template <typename F>
+hipError_t for_factors(iskv_ctx *c, hipStream_t s, F launch) {
+  if (c->D.rk == c->D.rv) return launch(-1, s);
+  hipError_t e = hipEventRecord(c->ev_fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->aux, c->ev_fork, 0);
+  if (e == hipSuccess) e = launch(0, s);
+  if (e == hipSuccess) e = launch(1, c->aux);
+  if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->aux);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, c->ev_join, 0);
+  return e;
+}
+
 uint64_t persistent_bytes(const iskv_ctx *c) {
   const Dims &D = c->D;
   uint64_t tot = 0;
@@ -167,8 +190,11 @@ uint64_t persistent_bytes(const iskv_ctx *c) {
     const uint64_t n_pre = (uint64_t)(L.length < D.prefix ? L.length : D.prefix);
     const uint64_t n_e = (uint64_t)(L.length > L.n_c ? L.length - L.n_c : 0) + n_pre;
     const uint64_t n_comp = (uint64_t)(L.n_c - D.prefix);
-    const uint64_t per = 2ull * (n_comp * D.r * D.elem + (uint64_t)D.d * D.r * 4 +
-                                 (uint64_t)D.r * 4 + n_e * D.d * D.elem);
+    // per unit: both factors' coefficients, bases and singular values, and
+    // the exact rows of K and V
+    const uint64_t rs = (uint64_t)D.rk + D.rv;
+    const uint64_t per = n_comp * rs * D.elem + (uint64_t)D.d * rs * 4 + rs * 4 +
+                         2ull * n_e * D.d * D.elem;
     tot += per * (uint64_t)D.units;
   }
   return tot;
@@ -186,9 +212,13 @@ size_t iskv_workspace_bytes(const iskv_config *cfg) {
 size_t iskv_state_bytes(const iskv_config *cfg) {
   if (!valid_config(cfg)) return 0;
   const Dims D = make_dims(cfg);
-  const size_t per_x = (size_t)D.d * D.r + D.r + (size_t)D.max_tokens * D.r +
-                       (size_t)D.slots * D.d + (size_t)D.prefix * D.d;
-  return 16 + (size_t)D.units * 2 * per_x * 4;
+  size_t per_u = 0;
+  for (int x = 0; x < 2; ++x) {
+    const size_t r = x ? D.rv : D.rk;
+    per_u += (size_t)D.d * r + r + (size_t)D.max_tokens * r + (size_t)D.slots * D.d +
+             (size_t)D.prefix * D.d;
+  }
+  return 16 + (size_t)D.units * per_u * 4;
 }
 
 int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_stream,
@@ -216,6 +246,15 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   LayerState empty;
   empty.n_c = c->D.prefix;                  // compression starts after the protected prefix
   c->layers.assign(c->D.layers, empty);
+  if (c->D.rk != c->D.rv &&
+      (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)) {
+    if (c->aux) (void)hipStreamDestroy(c->aux);
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    delete c;
+    return ISKV_EDEVICE;
+  }
   uint8_t *base = reinterpret_cast<uint8_t *>(dev_ws);
   Model &M = c->M;
   M.base = base;
@@ -263,6 +302,9 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   }
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) {
+    if (c->aux) (void)hipStreamDestroy(c->aux);
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->ev_join) (void)hipEventDestroy(c->ev_join);
     delete c;
     return ISKV_EDEVICE;
   }
@@ -317,7 +359,9 @@ int iskv_block_update(iskv_ctx *c, int layer) {
     for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
       LayerSel sel;
       fill_sel(sel, grp, from);
-      hipError_t e = launch_block_update(c->M, sel, n_c, s);
+      hipError_t e = for_factors(c, s, [&](int x, hipStream_t st) {
+        return launch_block_update(c->M, sel, n_c, x, st);
+      });
       if (e == hipSuccess) e = launch_prep_frag(c->M, sel, s);
       if (e != hipSuccess) return ISKV_EDEVICE;
     }
@@ -358,7 +402,10 @@ int iskv_sync(iskv_ctx *c, int layer) {
     for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
       LayerSel sel;
       fill_sel(sel, grp, from);
-      if (launch_sync(c->M, sel, n_c - kBlock, s) != hipSuccess) return ISKV_EDEVICE;
+      if (for_factors(c, s, [&](int x, hipStream_t st) {
+            return launch_sync(c->M, sel, n_c - kBlock, x, st);
+          }) != hipSuccess)
+        return ISKV_EDEVICE;
     }
     for (int l : grp) {
       c->layers[l].pending = false;
@@ -465,15 +512,15 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   float *f = reinterpret_cast<float *>(o + 16);
   for (int u = 0; u < D.units; ++u) {
     for (int x = 0; x < 2; ++x) {
-      const size_t ux = (size_t)u * 2 + x;
-      std::memcpy(f, raw.data() + Ly.basis + ux * D.d * D.r * 4, (size_t)D.d * D.r * 4);
-      f += (size_t)D.d * D.r;
-      std::memcpy(f, raw.data() + Ly.sing + ux * D.r * 4, (size_t)D.r * 4);
-      f += D.r;
-      const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
-      for (size_t i = 0; i < (size_t)D.max_tokens * D.r; ++i)
-        f[i] = (i >= (size_t)D.prefix * D.r && i < (size_t)L.n_c * D.r) ? elem(coff, i) : 0.f;
-      f += (size_t)D.max_tokens * D.r;
+      const size_t r = x ? D.rv : D.rk;
+      std::memcpy(f, raw.data() + Ly.basis[x] + (size_t)u * D.d * r * 4, (size_t)D.d * r * 4);
+      f += (size_t)D.d * r;
+      std::memcpy(f, raw.data() + Ly.sing[x] + (size_t)u * r * 4, r * 4);
+      f += r;
+      const size_t coff = Ly.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
+      for (size_t i = 0; i < (size_t)D.max_tokens * r; ++i)
+        f[i] = (i >= (size_t)D.prefix * r && i < (size_t)L.n_c * r) ? elem(coff, i) : 0.f;
+      f += (size_t)D.max_tokens * r;
       for (int s = 0; s < D.slots; ++s)
         for (int d = 0; d < D.d; ++d) {
           const size_t i = (x == 0)
@@ -523,14 +570,14 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   const float *f = reinterpret_cast<const float *>(in + 16);
   for (int u = 0; u < D.units; ++u) {
     for (int x = 0; x < 2; ++x) {
-      const size_t ux = (size_t)u * 2 + x;
-      std::memcpy(raw.data() + Ly.basis + ux * D.d * D.r * 4, f, (size_t)D.d * D.r * 4);
-      f += (size_t)D.d * D.r;
-      std::memcpy(raw.data() + Ly.sing + ux * D.r * 4, f, (size_t)D.r * 4);
-      f += D.r;
-      const size_t coff = Ly.coef + ux * (size_t)D.max_tokens * D.r * D.elem;
-      for (size_t i = (size_t)D.prefix * D.r; i < (size_t)n_c * D.r; ++i) put(coff, i, f[i]);
-      f += (size_t)D.max_tokens * D.r;
+      const size_t r = x ? D.rv : D.rk;
+      std::memcpy(raw.data() + Ly.basis[x] + (size_t)u * D.d * r * 4, f, (size_t)D.d * r * 4);
+      f += (size_t)D.d * r;
+      std::memcpy(raw.data() + Ly.sing[x] + (size_t)u * r * 4, f, r * 4);
+      f += r;
+      const size_t coff = Ly.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
+      for (size_t i = (size_t)D.prefix * r; i < (size_t)n_c * r; ++i) put(coff, i, f[i]);
+      f += (size_t)D.max_tokens * r;
       for (int s = 0; s < D.slots; ++s)
         for (int d = 0; d < D.d; ++d) {
           const size_t i = (x == 0)
@@ -592,6 +639,9 @@ int iskv_destroy(iskv_ctx *c) {
   hipError_t e = join_all(c);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (c->ev_main) (void)hipEventDestroy(c->ev_main);
+  if (c->aux) (void)hipStreamDestroy(c->aux);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   for (hipEvent_t ev : c->ev_done)
     if (ev) (void)hipEventDestroy(ev);
   delete c;

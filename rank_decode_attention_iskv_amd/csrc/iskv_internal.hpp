@@ -1,12 +1,12 @@
 // Internal layout and kernel-launch interface of libiskv (not part of the ABI).
 //
-// Device workspace, per layer (u = sequence * kv_heads + kv_head, x = 0 for K,
-// 1 for V):
-//   basis  float [U][2][d][r]        row f, column c (orthonormal columns)
-//   sing   float [U][2][r]           singular values S
-//   msync  float [U][2][r][r]        pending synchronization matrix M = B_old^T B_new
-//   frag   bytes [U][2][4*d*r]       basis in the decode kernel's MFMA operand order
-//   coef   T     [U][2][max_tokens][r]  coefficient rows (row = token)
+// Device workspace, per layer (u = sequence * kv_heads + kv_head) and factor
+// X = K, V with its rank r_X (r_K = rank, r_V = rank_v):
+//   basis[X]  float [U][d][r_X]         row f, column c (orthonormal columns)
+//   sing[X]   float [U][r_X]            singular values S
+//   msync[X]  float [U][r_X][r_X]       pending synchronization matrix M = B_old^T B_new
+//   coef[X]   T     [U][max_tokens][r_X]  coefficient rows (row = position)
+//   frag      bytes [U][4*d*r_K]        key basis in the decode kernel's MFMA operand order
 //   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
 //   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
 //   prek   T     [U][P][d]           protected prefix keys, row = position (pre-RoPE)
@@ -33,7 +33,8 @@ constexpr int kRecStride = kHeadDim;           // accumulator floats per (record
 constexpr int kRopeAnchor = 64;                 // positions per anchor of the RoPE table
 
 struct Dims {
-  int batch, layers, kv_heads, q_heads, group, d, r, window, slots, max_tokens;
+  int batch, layers, kv_heads, q_heads, group, d, window, slots, max_tokens;
+  int rk, rv;             // ranks of the key and value factors
   int storage;            // 0 f32, 1 bf16
   int elem;               // bytes per stored element
   float scale_log2;       // softmax scale * log2(e)
@@ -47,9 +48,10 @@ struct Dims {
 
 // Pointers of one layer.
 struct LayerPtrs {
-  float *basis, *sing, *msync;
+  float *basis[2], *sing[2], *msync[2];   // [X]: K = 0, V = 1
+  uint8_t *coef[2];
   uint8_t *frag;
-  uint8_t *coef, *ringk, *ringv, *prek, *prev;
+  uint8_t *ringk, *ringv, *prek, *prev;
 };
 
 struct Shared {
@@ -64,18 +66,21 @@ struct Shared {
 inline __host__ __device__ size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 struct LayerLayout {
-  size_t basis, sing, msync, frag, coef, ringk, ringv, prek, prev, bytes;
+  size_t basis[2], sing[2], msync[2], coef[2], frag, ringk, ringv, prek, prev, bytes;
 };
 
 inline LayerLayout layer_layout(const Dims &D) {
   LayerLayout L{};
   size_t o = 0;
-  const size_t U2 = (size_t)D.units * 2;
-  L.basis = o; o = align_up(o + U2 * D.d * D.r * 4);
-  L.sing = o;  o = align_up(o + U2 * D.r * 4);
-  L.msync = o; o = align_up(o + U2 * D.r * D.r * 4);
-  L.frag = o;  o = align_up(o + U2 * 4 * (size_t)D.d * D.r);
-  L.coef = o;  o = align_up(o + U2 * (size_t)D.max_tokens * D.r * D.elem);
+  const size_t U = (size_t)D.units;
+  for (int x = 0; x < 2; ++x) {
+    const size_t r = x ? D.rv : D.rk;
+    L.basis[x] = o; o = align_up(o + U * D.d * r * 4);
+    L.sing[x] = o;  o = align_up(o + U * r * 4);
+    L.msync[x] = o; o = align_up(o + U * r * r * 4);
+    L.coef[x] = o;  o = align_up(o + U * (size_t)D.max_tokens * r * D.elem);
+  }
+  L.frag = o;  o = align_up(o + U * 4 * (size_t)D.d * D.rk);
   L.ringk = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.ringv = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.prek = o;  o = align_up(o + (size_t)D.units * D.prefix * D.d * D.elem);
@@ -123,11 +128,13 @@ struct LayerSel {
 __host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
   uint8_t *b = M.base + M.layers_base + (size_t)l * M.layer_stride;
   LayerPtrs P;
-  P.basis = (float *)(b + M.lay.basis);
-  P.sing = (float *)(b + M.lay.sing);
-  P.msync = (float *)(b + M.lay.msync);
+  for (int x = 0; x < 2; ++x) {
+    P.basis[x] = (float *)(b + M.lay.basis[x]);
+    P.sing[x] = (float *)(b + M.lay.sing[x]);
+    P.msync[x] = (float *)(b + M.lay.msync[x]);
+    P.coef[x] = b + M.lay.coef[x];
+  }
   P.frag = b + M.lay.frag;
-  P.coef = b + M.lay.coef;
   P.ringk = b + M.lay.ringk;
   P.ringv = b + M.lay.ringv;
   P.prek = b + M.lay.prek;
@@ -148,12 +155,13 @@ hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s);
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
                          int in_dtype, int64_t pos0, hipStream_t s);
 
-// Fold the block at positions n_c..n_c+63 of every unit (K and V) of the
-// selected layers.
-hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, hipStream_t s);
+// Fold the block at positions n_c..n_c+63 of every unit of the selected
+// layers: factor x (0 K, 1 V), or both (x = -1, one launch; equal ranks only).
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s);
 
-// C[0:n_old] <- C[0:n_old] * M for every unit and K|V of the selected layers.
-hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, hipStream_t s);
+// C[0:n_old] <- C[0:n_old] * M for every unit of the selected layers, factor
+// x (0 K, 1 V) or both (x = -1; equal ranks only).
+hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s);
 
 // Rebuild the decode operand copy of the basis from the fp32 basis.
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s);

@@ -29,12 +29,15 @@ constexpr int kThreads = 256;
 __global__ void reset_basis_kernel(Model M, int layer) {
   const Dims &D = M.D;
   LayerPtrs P = layer_ptrs(M, layer);
-  const size_t n = (size_t)D.units * 2 * D.d * D.r;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i % D.r);
-    const int f = (int)((i / D.r) % D.d);
-    P.basis[i] = (f == c) ? 1.f : 0.f;
+  for (int x = 0; x < 2; ++x) {
+    const int r = x ? D.rv : D.rk;
+    const size_t n = (size_t)D.units * D.d * r;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x) {
+      const int c = (int)(i % r);
+      const int f = (int)((i / r) % D.d);
+      P.basis[x][i] = (f == c) ? 1.f : 0.f;
+    }
   }
 }
 
@@ -79,11 +82,11 @@ __global__ void append_kernel(Model M, int layer, const In *k, const In *v, int 
 __global__ void prep_frag_kernel(Model M, LayerSel sel) {
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.y];
-  const int ux = blockIdx.x;
+  const int u = blockIdx.x;                    // key basis of unit u
   LayerPtrs P = layer_ptrs(M, l);
-  const float *B = P.basis + (size_t)ux * D.d * D.r;
-  uint8_t *F = P.frag + (size_t)ux * 4 * D.d * D.r;
-  const int r = D.r, per = r / 4;             // coefficients per lane
+  const float *B = P.basis[0] + (size_t)u * D.d * D.rk;
+  uint8_t *F = P.frag + (size_t)u * 4 * D.d * D.rk;
+  const int r = D.rk, per = r / 4;            // coefficients per lane
   const int chunks = r / 16;
   const int total = 8 * chunks * 64;           // (mb, chunk, lane)
   for (int i = threadIdx.x; i < total; i += blockDim.x) {
@@ -119,20 +122,21 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // (M = hi + lo to ~2^-16, so C M is exact to float accumulation), B operand =
 // 16 coefficient rows as stored (exact bf16), output rounded once to bf16.
 // f32 storage: one row per thread on the vector ALUs.
-// grid (row tiles, units*2, layers)
+// grid (row tiles, units (one factor) or units*2 (both), layers)
 // ---------------------------------------------------------------------------
 template <int R>
-__global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel sel, int64_t n_old) {
+__global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel sel, int64_t n_old, int xsel) {
   static_assert(R == 16 || R == 32 || R == 64 || R == 128, "MFMA sync ranks");
   constexpr int KB = R >= 32 ? R / 32 : 1;      // K blocks (32 wide; one of 16 at r = 16)
   constexpr int MB = R / 16;                    // output column blocks
   constexpr int TPW = R == 128 ? 4 : 8;         // 16-row tiles per wave
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
-  const int ux = blockIdx.y;
+  // grid.y: units (one factor, xsel) or units x 2 (both, equal ranks)
+  const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
   LayerPtrs P = layer_ptrs(M, l);
-  const float *Ms = P.msync + (size_t)ux * R * R;
-  uint16_t *C = reinterpret_cast<uint16_t *>(P.coef) + (size_t)ux * D.max_tokens * R;
+  const float *Ms = P.msync[x] + (size_t)u * R * R;
+  uint16_t *C = reinterpret_cast<uint16_t *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, rho = lane >> 4;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TPW * 16;
@@ -196,15 +200,15 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
 }
 
 template <int R>
-__global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel sel, int64_t n_old) {
+__global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel sel, int64_t n_old, int xsel) {
   __shared__ float4 sM4[R * R / 4];
   const float *sM = reinterpret_cast<const float *>(sM4);
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
-  const int ux = blockIdx.y;
+  const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
   LayerPtrs P = layer_ptrs(M, l);
-  const float4 *Ms = reinterpret_cast<const float4 *>(P.msync + (size_t)ux * R * R);
-  float *C = reinterpret_cast<float *>(P.coef) + (size_t)ux * D.max_tokens * R;
+  const float4 *Ms = reinterpret_cast<const float4 *>(P.msync[x] + (size_t)u * R * R);
+  float *C = reinterpret_cast<float *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
   for (int i = threadIdx.x; i < R * R / 4; i += blockDim.x) sM4[i] = Ms[i];
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -234,26 +238,29 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
 }
 
 template <int R, typename T>
-hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, hipStream_t s) {
+hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
   if (n_old <= 0) return hipSuccess;
+  const unsigned ny = x < 0 ? M.D.units * 2 : M.D.units;
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int64_t rows_per_block = (int64_t)(kThreads / 64) * (R == 128 ? 4 : 8) * 16;
-    dim3 grid((unsigned)((n_old + rows_per_block - 1) / rows_per_block), M.D.units * 2, sel.n);
-    hipLaunchKernelGGL((sync_mfma_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old);
+    dim3 grid((unsigned)((n_old + rows_per_block - 1) / rows_per_block), ny, sel.n);
+    hipLaunchKernelGGL((sync_mfma_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x);
   } else {
-    dim3 grid((unsigned)((n_old + kThreads - 1) / kThreads), M.D.units * 2, sel.n);
-    hipLaunchKernelGGL((sync_valu_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old);
+    dim3 grid((unsigned)((n_old + kThreads - 1) / kThreads), ny, sel.n);
+    hipLaunchKernelGGL((sync_valu_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x);
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_sync(const Model &M, const LayerSel &sel, int64_t n_old, hipStream_t s) {
-  switch (M.D.r) {
-    case 16: return launch_sync_t<16, T>(M, sel, n_old, s);
-    case 32: return launch_sync_t<32, T>(M, sel, n_old, s);
-    case 64: return launch_sync_t<64, T>(M, sel, n_old, s);
-    case 128: return launch_sync_t<128, T>(M, sel, n_old, s);
+hipError_t dispatch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
+  const int r = x == 1 ? M.D.rv : M.D.rk;
+  if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
+  switch (r) {
+    case 16: return launch_sync_t<16, T>(M, sel, n_old, x, s);
+    case 32: return launch_sync_t<32, T>(M, sel, n_old, x, s);
+    case 64: return launch_sync_t<64, T>(M, sel, n_old, x, s);
+    case 128: return launch_sync_t<128, T>(M, sel, n_old, x, s);
   }
   return hipErrorInvalidValue;
 }
@@ -287,13 +294,13 @@ hipError_t launch_append(const Model &M, int layer, const void *k, const void *v
   return hipGetLastError();
 }
 
-hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, hipStream_t s) {
-  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, s)
-                          : dispatch_sync<float>(M, sel, n_old, s);
+hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
+  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, x, s)
+                          : dispatch_sync<float>(M, sel, n_old, x, s);
 }
 
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s) {
-  dim3 grid(M.D.units * 2, sel.n);
+  dim3 grid(M.D.units, sel.n);
   hipLaunchKernelGGL(prep_frag_kernel, grid, dim3(256), 0, s, M, sel);
   return hipGetLastError();
 }

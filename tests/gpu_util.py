@@ -32,7 +32,8 @@ def subspace_dist(B1, B2):
 class Pair:
     """A GPU cache and an oracle fed with identical float32 inputs."""
 
-    def __init__(self, w: workloads.Workload, max_tokens=None, oracle=True, layers=1, prefix=0):
+    def __init__(self, w: workloads.Workload, max_tokens=None, oracle=True, layers=1, prefix=0,
+                 rank_v=0):
         import torch
         from rank_decode_attention_iskv_amd import binding
         self.torch, self.binding, self.w = torch, binding, w
@@ -42,10 +43,11 @@ class Pair:
         self.prefix = prefix
         self.cfg = binding.make_config(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim,
                                        w.rank, w.window, self.max_tokens, storage,
-                                       protected_prefix=prefix)
+                                       protected_prefix=prefix, rank_v=rank_v)
         self.gpu = binding.IskvCache(self.cfg)
         self.ora = (Oracle(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
-                           self.max_tokens, storage=w.storage, prefix=prefix) if oracle else None)
+                           self.max_tokens, storage=w.storage, prefix=prefix,
+                           rank_v=rank_v or None) if oracle else None)
         self.length = [0] * layers
 
     def feed(self, layer, count, sync=True, chunk=64, on_fold=None):

@@ -48,6 +48,7 @@ def test_workspace_bytes_valid_and_monotone():
     dict(block=32), dict(num_q_heads=12), dict(num_q_heads=136), dict(storage=7),
     dict(batch=0), dict(max_tokens=0), dict(rope_base=0.5),
     dict(protected_prefix=100), dict(protected_prefix=-64), dict(protected_prefix=4160),
+    dict(rank_v=48), dict(rank_v=16), dict(rank_v=-32), dict(rank=128, rank_v=256),
 ])
 def test_invalid_configs_rejected(kw):
     assert binding.workspace_bytes(base_cfg(**kw)) == 0
@@ -61,6 +62,23 @@ def test_state_bytes_layout():
     # the protected prefix adds its exact rows per (unit, K|V)
     cfg = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000, protected_prefix=192)
     assert binding.state_bytes(cfg) == 16 + 2 * 2 * (d * r + r + T * r + S * d + 192 * d) * 4
+
+
+def test_state_bytes_separate_v_rank():
+    """With rank_v the V factor's basis, singular values and coefficients take
+    r_V columns; rank_v equal to rank is the same as rank_v = 0."""
+    d, T, S = 128, 1000, 256 + 64
+    cfg = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000, rank_v=64)
+    per_k = d * 32 + 32 + T * 32 + S * d
+    per_v = d * 64 + 64 + T * 64 + S * d
+    assert binding.state_bytes(cfg) == 16 + 2 * (per_k + per_v) * 4
+    same = base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000, rank_v=32)
+    assert binding.state_bytes(same) == binding.state_bytes(
+        base_cfg(batch=1, num_kv_heads=2, num_q_heads=2, max_tokens=1000))
+    # workspace grows by at least the extra V coefficients (storage dtype)
+    a = binding.workspace_bytes(base_cfg())
+    b = binding.workspace_bytes(base_cfg(rank_v=64))
+    assert b - a >= 3 * 16 * 4096 * 32 * 2
 
 
 def test_protected_prefix_workspace():
