@@ -189,6 +189,38 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
  * any numeric flag is set (st is still filled), else ISKV_OK. */
 int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st);
 
+/* ---- Ragged batches: sequences of one batch at different lengths ----------
+ * The pages fold a single stream; a batch whose sequences advance at their
+ * own pace keeps one state per sequence: its own length, compressed count,
+ * ring and fold schedule.  The calls below need batch <= 64 (else EINVAL).
+ * A layer turns ragged at its first iskv_append_ragged; the uniform calls
+ * (iskv_append, iskv_decode_attn, iskv_append_decode, iskv_status,
+ * iskv_export_state) return ESTATE while its sequences differ, and work again
+ * once they agree.  On a ragged layer iskv_block_update folds every sequence
+ * whose ring is full (ESTATE for layer >= 0 if none is), iskv_sync and
+ * iskv_discard_sync act on every sequence with a pending fold; a sequence
+ * with a pending sync does not fold again until it is synchronized. */
+
+/* Append counts[b] tokens to sequence b (0 <= counts[b] <= n_tokens; counts:
+ * host int32 [batch]).  dev_k, dev_v: [batch][n_tokens][num_kv_heads][head_dim]
+ * (device, in_dtype ISKV_F32 or ISKV_BF16), sequence b's tokens in its first
+ * counts[b] rows; other rows are not read.  Positions continue each
+ * sequence's own length.  Checked for every sequence before anything is
+ * written: ESTATE if a ring would overflow or max_tokens be passed.
+ * *seqs_ready (optional): how many sequences have a full ring. */
+int iskv_append_ragged(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                       int in_dtype, const int32_t *counts, int *seqs_ready);
+
+/* iskv_decode_attn with each sequence at its own length and query position:
+ * q_pos host int64 [batch] (each in the range iskv_decode_attn accepts, else
+ * EINVAL).  Works on uniform layers too.  ESTATE if a sequence is empty. */
+int iskv_decode_attn_ragged(iskv_ctx *c, int layer, const float *dev_q, const int64_t *q_pos,
+                            float *dev_out);
+
+/* iskv_status for one sequence (length, compressed, blocks_ready and
+ * pending_sync are that sequence's; the rest as iskv_status). */
+int iskv_seq_status(iskv_ctx *c, int layer, int seq, iskv_status_t *st);
+
 /* Copy one layer's state to / from a host blob (layout: iskv_state_bytes).
  * Both synchronize the stream.  Import rounds coefficients and ring rows to
  * the storage dtype, clears any pending sync, and rebuilds derived operands. */

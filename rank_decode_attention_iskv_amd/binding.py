@@ -49,6 +49,7 @@ EXPORTED = (
     "iskv_block_update", "iskv_sync", "iskv_discard_sync", "iskv_decode_attn",
     "iskv_append_decode", "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_set_maintenance_stream",
     "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
+    "iskv_append_ragged", "iskv_decode_attn_ragged", "iskv_seq_status",
 )
 
 
@@ -74,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_import_state": (I, [P, I, P, SZ]),
         "iskv_set_maintenance_stream": (I, [P, P]),
         "iskv_join_maintenance": (I, [P, I]),
+        "iskv_append_ragged": (I, [P, I, P, P, I, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(I)]),
+        "iskv_decode_attn_ragged": (I, [P, I, P, ctypes.POINTER(I64), P]),
+        "iskv_seq_status": (I, [P, I, I, ctypes.POINTER(Status)]),
         "iskv_destroy": (I, [P]),
         "iskv_strerror": (ctypes.c_char_p, [I]),
     }
@@ -217,6 +221,47 @@ class IskvCache:
         code = lib().iskv_status(self.ctx, layer, ctypes.byref(st))
         if code not in (OK, ENUMERIC) or (raise_numeric and code == ENUMERIC):
             raise IskvError(code, "iskv_status")
+        return st
+
+    def append_ragged(self, layer: int, k, v, counts) -> int:
+        """Ragged append: k, v [batch, n, kv_heads, head_dim] device tensors;
+        sequence b takes its first counts[b] rows.  Returns how many sequences
+        have a full ring."""
+        torch = self.torch
+        if k.dtype != v.dtype or k.shape != v.shape or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k, v must be float32 or bfloat16")
+        if len(counts) != self.cfg.batch:
+            raise ValueError("one count per sequence")
+        dt = BF16 if k.dtype == torch.bfloat16 else F32
+        cnt = (ctypes.c_int32 * len(counts))(*[int(x) for x in counts])
+        ready = ctypes.c_int(0)
+        _check(lib().iskv_append_ragged(self.ctx, layer, ctypes.c_void_p(k.data_ptr()),
+                                        ctypes.c_void_p(v.data_ptr()), int(k.shape[1]), dt, cnt,
+                                        ctypes.byref(ready)), "iskv_append_ragged")
+        return ready.value
+
+    def decode_attn_ragged(self, layer: int, q, q_pos, out):
+        """decode_attn with one query position per sequence (q_pos: [batch])."""
+        torch = self.torch
+        if q.dtype != torch.float32 or out.dtype != torch.float32:
+            raise ValueError("q and out must be float32")
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        if len(q_pos) != self.cfg.batch:
+            raise ValueError("one query position per sequence")
+        qp = (ctypes.c_int64 * len(q_pos))(*[int(x) for x in q_pos])
+        _check(lib().iskv_decode_attn_ragged(self.ctx, layer, ctypes.c_void_p(q.data_ptr()), qp,
+                                             ctypes.c_void_p(out.data_ptr())),
+               "iskv_decode_attn_ragged")
+        return out
+
+    def seq_status(self, layer: int, seq: int) -> Status:
+        st = Status()
+        code = lib().iskv_seq_status(self.ctx, layer, seq, ctypes.byref(st))
+        if code not in (OK, ENUMERIC):
+            raise IskvError(code, "iskv_seq_status")
         return st
 
     def export_state(self, layer: int) -> bytearray:

@@ -34,6 +34,7 @@
 //           split bf16 hi/lo, C_V read transposed from the LDS ring.  Window
 //           tiles read V^T straight from the transposed ring (acc over 128
 //           features).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -431,8 +432,8 @@ template <int RK, int RV, typename T, int NW> struct Cfg {
 // ---------------------------------------------------------------------------
 template <int RK, int RV, typename T, int NW>
 __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kOcc)) void decode_mfma_kernel(
-    Model M, int layer, const float *__restrict__ q, int64_t q_pos, float *out, int64_t length,
-    int64_t n_c, SplitPlan plan, int fused, FusedAppend app) {
+    Model M, int layer, const float *__restrict__ q, int64_t q_pos_arg, float *out, int64_t length_arg,
+    int64_t n_c_arg, SplitPlan plan, int fused, FusedAppend app, SeqTab tab) {
   using C = Cfg<RK, RV, T, NW>;
   constexpr int R = RK;                                  // the key path below uses R
   constexpr bool BF = C::BF;
@@ -458,6 +459,12 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   const int n16 = lane & 15, rho = lane >> 4;
   const int split = blockIdx.x, u = blockIdx.y;
   const int b = u / D.kv_heads, hk = u % D.kv_heads;
+  // a ragged batch gives each sequence its own length, compressed end and
+  // query position; the plan covers the largest of each, and a split past a
+  // sequence's own range is empty (neutral record)
+  const int64_t length = tab.n ? (int64_t)tab.len[b] : length_arg;
+  const int64_t n_c = tab.n ? (int64_t)tab.nc[b] : n_c_arg;
+  const int64_t q_pos = tab.n ? (int64_t)tab.aux[b] : q_pos_arg;
   const bool comp = split < plan.n_comp;
   const int xs = split - plan.n_comp;                    // exact split index
   const bool pre = !comp && xs < plan.n_pre;             // a protected-prefix split
@@ -474,6 +481,7 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     r_begin = n_c + (int64_t)(xs - plan.n_pre) * plan.win_len;
     r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
+  if (r_end < r_begin) r_end = r_begin;
   const int ntiles = (int)((r_end - r_begin + 15) / 16);
   // even split: the first ntiles % NW waves take one tile more (waves w and
   // w + NW/2 share a SIMD, so every SIMD gets the same count within one)
@@ -931,10 +939,12 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
       store_agent(M.sh.recml + (rec0 + h) * 2, mx);
       continue;
     }
+    // an empty split (ragged batch) has no finite max: record l = 0, acc = 0
+    const float mref = mx == -INFINITY ? 0.f : mx;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
+      const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - mref);
       v += wt * (x == 1 ? s_l[w][h] : s_acc[w][h][x - 2]);
     }
     if (x == 1) store_agent(M.sh.recml + (rec0 + h) * 2 + 1, v);
@@ -994,11 +1004,11 @@ int target_workgroups(const Dims &D, int64_t length, int waves) {
 
 // n_c: end position of the compressed rows (the protected prefix P .. n_c-1
 // compressed, 0 .. P-1 exact, n_c .. length-1 in the ring).
-SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
+// n_k compressed, n_e ring and n_p prefix tokens (for a ragged batch, the
+// largest of each over the sequences; length the largest length).
+SplitPlan make_plan_parts(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, int64_t length,
+                          int waves) {
   SplitPlan plan{};
-  const int64_t n_e = length > n_c ? length - n_c : 0;           // ring tokens
-  const int64_t n_p = length < D.prefix ? length : D.prefix;     // prefix tokens
-  const int64_t n_k = n_c - D.prefix;                             // compressed tokens
   const int target = target_workgroups(D, length, waves);
   if (n_e > 0) {
     // about 4 tiles per wave for the window
@@ -1029,10 +1039,28 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
   return plan;
 }
 
+SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
+  const int64_t n_e = length > n_c ? length - n_c : 0;           // ring tokens
+  const int64_t n_p = length < D.prefix ? length : D.prefix;     // prefix tokens
+  return make_plan_parts(D, n_c - D.prefix, n_e, n_p, length, waves);
+}
+
+SplitPlan make_plan_tab(const Dims &D, const SeqTab &tab, int waves) {
+  int64_t n_k = 0, n_e = 0, n_p = 0, length = 0;
+  for (int b = 0; b < tab.n; ++b) {
+    const int64_t L = tab.len[b], c = tab.nc[b];
+    n_k = std::max<int64_t>(n_k, c - D.prefix);
+    n_e = std::max<int64_t>(n_e, L > c ? L - c : 0);
+    n_p = std::max<int64_t>(n_p, L < D.prefix ? L : D.prefix);
+    length = std::max<int64_t>(length, L);
+  }
+  return make_plan_parts(D, n_k, n_e, n_p, length, waves);
+}
+
 template <int RK, int RV, typename T, int NW>
 hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, const SplitPlan &plan, hipStream_t s,
-                       FusedAppend app) {
+                       FusedAppend app, const SeqTab &tab) {
   using C = Cfg<RK, RV, T, NW>;
   dim3 grid(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
   constexpr int dyn = C::kDynBytes;
@@ -1048,7 +1076,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   const int64_t slots = (int64_t)M.D.cus * C::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<RK, RV, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
-                     out, length, n_c, plan, fused, app);
+                     out, length, n_c, plan, fused, app, tab);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   constexpr int mbytes = MergeLds<RV, 4>::bytes;
@@ -1070,33 +1098,36 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
 // workgroup's set-up and merge overlap the other's loop.
 template <int RK, int RV, typename T>
 hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                       int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
+                       int64_t length, int64_t n_c, hipStream_t s, FusedAppend app, const SeqTab &tab) {
+  auto plan = [&](int waves) {
+    return tab.n ? make_plan_tab(M.D, tab, waves) : make_plan(M.D, length, n_c, waves);
+  };
   if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
-    const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
+    const SplitPlan p8 = plan(8);
     if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
-      return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app);
+      return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app, tab);
   }
-  return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c,
-                                   make_plan(M.D, length, n_c, 4), s, app);
+  return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, plan(4), s, app, tab);
 }
 
 // (r_K, r_V): equal ranks, or a value rank twice the key rank
 template <typename T>
 hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
-                           int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
+                           int64_t length, int64_t n_c, hipStream_t s, FusedAppend app,
+                           const SeqTab &tab) {
   const int rk = M.D.rk, rv = M.D.rv;
   if (rv == rk) {
     switch (rk) {
-      case 16: return launch_rank<16, 16, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-      case 32: return launch_rank<32, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-      case 64: return launch_rank<64, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-      case 128: return launch_rank<128, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 16: return launch_rank<16, 16, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
+      case 32: return launch_rank<32, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
+      case 64: return launch_rank<64, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
+      case 128: return launch_rank<128, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
     }
   } else if (rv == 2 * rk) {
     switch (rk) {
-      case 16: return launch_rank<16, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-      case 32: return launch_rank<32, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app);
-      case 64: return launch_rank<64, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app);
+      case 16: return launch_rank<16, 32, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
+      case 32: return launch_rank<32, 64, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
+      case 64: return launch_rank<64, 128, T>(M, layer, q, q_pos, out, length, n_c, s, app, tab);
     }
   }
   return hipErrorInvalidValue;
@@ -1106,8 +1137,16 @@ hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_
 
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                          int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {
-  return M.D.storage == 1 ? dispatch_decode<bf16_t>(M, layer, q, q_pos, out, length, n_c, s, app)
-                          : dispatch_decode<float>(M, layer, q, q_pos, out, length, n_c, s, app);
+  const SeqTab none{};
+  return M.D.storage == 1 ? dispatch_decode<bf16_t>(M, layer, q, q_pos, out, length, n_c, s, app, none)
+                          : dispatch_decode<float>(M, layer, q, q_pos, out, length, n_c, s, app, none);
+}
+
+hipError_t launch_decode_ragged(const Model &M, int layer, const float *q, float *out,
+                                const SeqTab &tab, hipStream_t s) {
+  const FusedAppend none{};
+  return M.D.storage == 1 ? dispatch_decode<bf16_t>(M, layer, q, 0, out, 0, 0, s, none, tab)
+                          : dispatch_decode<float>(M, layer, q, 0, out, 0, 0, s, none, tab);
 }
 
 }  // namespace iskv

@@ -548,7 +548,7 @@ __device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int
 
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSel sel,
-                                                                int64_t n_c, int xsel) {
+                                                                int64_t n_c, int xsel, SeqTab tab) {
   using Ly = FoldLayout<R>;
   constexpr int D = kHeadDim, TB = kBlock, N = Ly::N, NC = Ly::NC;
   constexpr int LA = Ly::LA, LB = Ly::LB, LG = Ly::LG, LC = Ly::LC;
@@ -562,6 +562,8 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   const int layer = sel.idx[blockIdx.y];
   // grid.x: units (one factor, xsel) or units x 2 (both factors, equal ranks)
   const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
+  if (!seq_in(tab, u / Dm.kv_heads)) return;    // ragged: a sequence whose ring is not full
+  if (tab.n) n_c = tab.nc[u / Dm.kv_heads];
   const int tid = threadIdx.x;
   LayerPtrs P = layer_ptrs(M, layer);
   float *basis = P.basis[X] + (size_t)u * D * R;
@@ -876,7 +878,8 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
 }
 
 template <int R, typename T>
-hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
+hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
+                         const SeqTab &tab) {
   static bool attr = false;
   const size_t bytes = FoldLayout<R>::bytes;
   if (!attr) {
@@ -886,28 +889,30 @@ hipError_t launch_fold_t(const Model &M, const LayerSel &sel, int64_t n_c, int x
     attr = true;
   }
   dim3 grid(x < 0 ? M.D.units * 2 : M.D.units, sel.n);
-  hipLaunchKernelGGL((block_update_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, sel, n_c, x);
+  hipLaunchKernelGGL((block_update_kernel<R, T>), grid, dim3(kThreads), bytes, s, M, sel, n_c, x, tab);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
+hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
+                         const SeqTab &tab) {
   const int r = x == 1 ? M.D.rv : M.D.rk;
   if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
   switch (r) {
-    case 16: return launch_fold_t<16, T>(M, sel, n_c, x, s);
-    case 32: return launch_fold_t<32, T>(M, sel, n_c, x, s);
-    case 64: return launch_fold_t<64, T>(M, sel, n_c, x, s);
-    case 128: return launch_fold_t<128, T>(M, sel, n_c, x, s);
+    case 16: return launch_fold_t<16, T>(M, sel, n_c, x, s, tab);
+    case 32: return launch_fold_t<32, T>(M, sel, n_c, x, s, tab);
+    case 64: return launch_fold_t<64, T>(M, sel, n_c, x, s, tab);
+    case 128: return launch_fold_t<128, T>(M, sel, n_c, x, s, tab);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s) {
-  return M.D.storage == 1 ? dispatch_fold<bf16_t>(M, sel, n_c, x, s)
-                          : dispatch_fold<float>(M, sel, n_c, x, s);
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
+                               const SeqTab &tab) {
+  return M.D.storage == 1 ? dispatch_fold<bf16_t>(M, sel, n_c, x, s, tab)
+                          : dispatch_fold<float>(M, sel, n_c, x, s, tab);
 }
 
 }  // namespace iskv

@@ -7,6 +7,7 @@
 // exact recent window, 64-token blocks folded by Brand's block-incremental
 // SVD, basis synchronization of old coefficients, decode attention over every
 // position; persistent-KV bytes as in its Jargon entry.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -23,12 +24,23 @@ using namespace iskv;
 
 namespace {
 
+struct SeqState {
+  int64_t length = 0;
+  int64_t n_c = 0;
+  bool pending = false;
+};
+
+// A layer whose sequences agree is uniform (length, n_c, pending).  The ragged
+// verbs split it into one SeqState per sequence (ragged = true); the uniform
+// verbs merge it back when every sequence agrees again.
 struct LayerState {
   int64_t length = 0;
   int64_t n_c = 0;          // end position of the compressed rows (P + N_c)
   bool pending = false;
   int64_t folds = 0;
   int64_t syncs = 0;
+  bool ragged = false;
+  std::vector<SeqState> seq;
 };
 
 bool valid_config(const iskv_config *c) {
@@ -131,6 +143,13 @@ int check_layer(const iskv_ctx *c, int layer) {
   return (layer >= 0 && layer < c->D.layers) ? ISKV_OK : ISKV_EINVAL;
 }
 
+void make_ragged(const iskv_ctx *c, LayerState &L);
+bool make_uniform(LayerState &L);
+
+SeqState seq_state(const LayerState &L, int b) {
+  return L.ragged ? L.seq[(size_t)b] : SeqState{L.length, L.n_c, L.pending};
+}
+
 // Main-stream work on `layer` from here on waits for its pending maintenance.
 hipError_t join_layer(iskv_ctx *c, int layer) {
   if (!c->mstream || !c->maint_pending[layer]) return hipSuccess;
@@ -186,18 +205,102 @@ uint64_t persistent_bytes(const iskv_ctx *c) {
   const Dims &D = c->D;
   uint64_t tot = 0;
   for (const LayerState &L : c->layers) {
-    // exact rows: the protected prefix written so far and the ring
-    const uint64_t n_pre = (uint64_t)(L.length < D.prefix ? L.length : D.prefix);
-    const uint64_t n_e = (uint64_t)(L.length > L.n_c ? L.length - L.n_c : 0) + n_pre;
-    const uint64_t n_comp = (uint64_t)(L.n_c - D.prefix);
-    // per unit: both factors' coefficients, bases and singular values, and
-    // the exact rows of K and V
-    const uint64_t rs = (uint64_t)D.rk + D.rv;
-    const uint64_t per = n_comp * rs * D.elem + (uint64_t)D.d * rs * 4 + rs * 4 +
-                         2ull * n_e * D.d * D.elem;
-    tot += per * (uint64_t)D.units;
+    for (int b = 0; b < D.batch; ++b) {
+      const SeqState q = seq_state(L, b);
+      // exact rows: the protected prefix written so far and the ring
+      const uint64_t n_pre = (uint64_t)(q.length < D.prefix ? q.length : D.prefix);
+      const uint64_t n_e = (uint64_t)(q.length > q.n_c ? q.length - q.n_c : 0) + n_pre;
+      const uint64_t n_comp = (uint64_t)(q.n_c - D.prefix);
+      // per unit: both factors' coefficients, bases and singular values, and
+      // the exact rows of K and V
+      const uint64_t rs = (uint64_t)D.rk + D.rv;
+      const uint64_t per = n_comp * rs * D.elem + (uint64_t)D.d * rs * 4 + rs * 4 +
+                           2ull * n_e * D.d * D.elem;
+      tot += per * (uint64_t)D.kv_heads;
+    }
   }
   return tot;
+}
+
+void make_ragged(const iskv_ctx *c, LayerState &L) {
+  if (L.ragged) return;
+  L.seq.assign((size_t)c->D.batch, SeqState{L.length, L.n_c, L.pending});
+  L.ragged = true;
+}
+
+bool make_uniform(LayerState &L) {
+  if (!L.ragged) return true;
+  const SeqState &a = L.seq[0];
+  for (const SeqState &q : L.seq)
+    if (q.length != a.length || q.n_c != a.n_c || q.pending != a.pending) return false;
+  L.length = a.length;
+  L.n_c = a.n_c;
+  L.pending = a.pending;
+  L.ragged = false;
+  return true;
+}
+
+uint64_t seq_bits(int batch) { return batch >= 64 ? ~0ull : (1ull << batch) - 1; }
+
+// Fold every sequence of a ragged layer whose ring is full (one launch per
+// factor; the others' workgroups return at once).  need: no sequence ready is
+// an error.
+int fold_ragged(iskv_ctx *c, int layer, bool need) {
+  LayerState &L = c->layers[layer];
+  SeqTab tab{};
+  tab.n = c->D.batch;
+  for (int b = 0; b < c->D.batch; ++b) {
+    const SeqState &q = L.seq[(size_t)b];
+    tab.nc[b] = (int32_t)q.n_c;
+    if (!q.pending && q.length - q.n_c == c->D.slots) tab.mask |= 1ull << b;
+  }
+  if (!tab.mask) return need ? ISKV_ESTATE : ISKV_OK;
+  hipError_t se;
+  hipStream_t s = maint_stream(c, &se);
+  if (se != hipSuccess) return ISKV_EDEVICE;
+  LayerSel sel;
+  fill_sel(sel, std::vector<int>{layer}, 0);
+  hipError_t e = for_factors(c, s, [&](int x, hipStream_t st) {
+    return launch_block_update(c->M, sel, 0, x, st, tab);
+  });
+  if (e == hipSuccess) e = launch_prep_frag(c->M, sel, s);
+  if (e != hipSuccess) return ISKV_EDEVICE;
+  for (int b = 0; b < c->D.batch; ++b)
+    if ((tab.mask >> b) & 1ull) {
+      L.seq[(size_t)b].n_c += kBlock;
+      L.seq[(size_t)b].pending = true;
+    }
+  L.folds += 1;
+  return maint_done(c, layer) != hipSuccess ? ISKV_EDEVICE : ISKV_OK;
+}
+
+// Synchronize every sequence of a ragged layer with a pending fold.
+int sync_ragged(iskv_ctx *c, int layer, bool need) {
+  LayerState &L = c->layers[layer];
+  SeqTab tab{};
+  tab.n = c->D.batch;
+  int64_t n_max = 0;
+  for (int b = 0; b < c->D.batch; ++b) {
+    const SeqState &q = L.seq[(size_t)b];
+    if (!q.pending) continue;
+    tab.mask |= 1ull << b;
+    tab.nc[b] = (int32_t)(q.n_c - kBlock);
+    n_max = std::max<int64_t>(n_max, q.n_c - kBlock);
+  }
+  if (!tab.mask) return need ? ISKV_ESTATE : ISKV_OK;
+  hipError_t se;
+  hipStream_t s = maint_stream(c, &se);
+  if (se != hipSuccess) return ISKV_EDEVICE;
+  LayerSel sel;
+  fill_sel(sel, std::vector<int>{layer}, 0);
+  if (for_factors(c, s, [&](int x, hipStream_t st) {
+        return launch_sync(c->M, sel, n_max, x, st, tab);
+      }) != hipSuccess)
+    return ISKV_EDEVICE;
+  for (int b = 0; b < c->D.batch; ++b)
+    if ((tab.mask >> b) & 1ull) L.seq[(size_t)b].pending = false;
+  L.syncs += 1;
+  return maint_done(c, layer) != hipSuccess ? ISKV_EDEVICE : ISKV_OK;
 }
 
 }  // namespace
@@ -317,6 +420,7 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
   if (!c || check_layer(c, layer) || !dev_k || !dev_v || n_tokens < 0) return ISKV_EINVAL;
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
   LayerState &L = c->layers[layer];
+  if (!make_uniform(L)) return ISKV_ESTATE;
   // ring tokens after the append: the positions from n_c on (>= P)
   if (L.length + n_tokens - L.n_c > c->D.slots) return ISKV_ESTATE;
   if (L.length + n_tokens > c->D.max_tokens) return ISKV_ESTATE;
@@ -333,12 +437,18 @@ int iskv_block_update(iskv_ctx *c, int layer) {
   std::vector<int> idx;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
-    const LayerState &L = c->layers[layer];
+    LayerState &L = c->layers[layer];
+    if (!make_uniform(L)) return fold_ragged(c, layer, true);
     if (L.pending || L.length - L.n_c != c->D.slots) return ISKV_ESTATE;
     idx.push_back(layer);
   } else if (layer == -1) {
     for (int l = 0; l < c->D.layers; ++l) {
-      const LayerState &L = c->layers[l];
+      LayerState &L = c->layers[l];
+      if (!make_uniform(L)) {
+        const int r = fold_ragged(c, l, false);
+        if (r != ISKV_OK) return r;
+        continue;
+      }
       if (!L.pending && L.length - L.n_c == c->D.slots) idx.push_back(l);
     }
   } else {
@@ -380,11 +490,18 @@ int iskv_sync(iskv_ctx *c, int layer) {
   std::vector<int> idx;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
+    if (!make_uniform(c->layers[layer])) return sync_ragged(c, layer, true);
     if (!c->layers[layer].pending) return ISKV_ESTATE;
     idx.push_back(layer);
   } else if (layer == -1) {
-    for (int l = 0; l < c->D.layers; ++l)
+    for (int l = 0; l < c->D.layers; ++l) {
+      if (!make_uniform(c->layers[l])) {
+        const int r = sync_ragged(c, l, false);
+        if (r != ISKV_OK) return r;
+        continue;
+      }
       if (c->layers[l].pending) idx.push_back(l);
+    }
   } else {
     return ISKV_EINVAL;
   }
@@ -420,19 +537,31 @@ int iskv_discard_sync(iskv_ctx *c, int layer) {
   if (!c) return ISKV_EINVAL;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
-    if (!c->layers[layer].pending) return ISKV_ESTATE;
-    c->layers[layer].pending = false;
+    LayerState &L = c->layers[layer];
+    if (L.ragged) {
+      bool any = false;
+      for (SeqState &q : L.seq) { any |= q.pending; q.pending = false; }
+      make_uniform(L);
+      return any ? ISKV_OK : ISKV_ESTATE;
+    }
+    if (!L.pending) return ISKV_ESTATE;
+    L.pending = false;
     return ISKV_OK;
   }
   if (layer != -1) return ISKV_EINVAL;
-  for (LayerState &L : c->layers) L.pending = false;
+  for (LayerState &L : c->layers) {
+    L.pending = false;
+    for (SeqState &q : L.seq) q.pending = false;
+    make_uniform(L);
+  }
   return ISKV_OK;
 }
 
 int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out) {
   if (!c || check_layer(c, layer) || !dev_q || !dev_out) return ISKV_EINVAL;
   if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
-  const LayerState &L = c->layers[layer];
+  LayerState &L = c->layers[layer];
+  if (!make_uniform(L)) return ISKV_ESTATE;
   if (L.length <= 0) return ISKV_ESTATE;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
@@ -444,6 +573,7 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
   if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
   LayerState &L = c->layers[layer];
+  if (!make_uniform(L)) return ISKV_ESTATE;
   if (L.length - L.n_c + 1 > c->D.slots) return ISKV_ESTATE;
   if (L.length + 1 > c->D.max_tokens) return ISKV_ESTATE;
   if (L.length < c->D.prefix) {
@@ -460,31 +590,101 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
   return ISKV_OK;
 }
 
-int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
-  if (!c || !st || check_layer(c, layer)) return ISKV_EINVAL;
+namespace {
+int fill_status(iskv_ctx *c, int layer, const SeqState &q, iskv_status_t *st) {
   if (join_all(c) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   int flags = 0;
   if (hipMemcpy(&flags, c->M.sh.flags, 4, hipMemcpyDeviceToHost) != hipSuccess) return ISKV_EDEVICE;
   const LayerState &L = c->layers[layer];
   std::memset(st, 0, sizeof(*st));
-  st->length = L.length;
-  st->compressed = L.n_c - c->D.prefix;
-  st->blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
-  st->pending_sync = L.pending ? 1 : 0;
+  st->length = q.length;
+  st->compressed = q.n_c - c->D.prefix;
+  st->blocks_ready = (q.length - q.n_c == c->D.slots) ? 1 : 0;
+  st->pending_sync = q.pending ? 1 : 0;
   st->folds = L.folds;
   st->syncs = L.syncs;
   st->persistent_bytes = persistent_bytes(c);
   uint64_t full = 0;
   for (const LayerState &S : c->layers)
-    full += 2ull * (uint64_t)S.length * c->D.units * c->D.d * c->D.elem;
+    for (int b = 0; b < c->D.batch; ++b)
+      full += 2ull * (uint64_t)seq_state(S, b).length * c->D.kv_heads * c->D.d * c->D.elem;
   st->full_bytes = full;
   st->numeric_flags = flags;
   return flags ? ISKV_ENUMERIC : ISKV_OK;
 }
+}  // namespace
+
+int iskv_status(iskv_ctx *c, int layer, iskv_status_t *st) {
+  if (!c || !st || check_layer(c, layer)) return ISKV_EINVAL;
+  LayerState &L = c->layers[layer];
+  if (!make_uniform(L)) return ISKV_ESTATE;
+  return fill_status(c, layer, seq_state(L, 0), st);
+}
+
+int iskv_seq_status(iskv_ctx *c, int layer, int seq, iskv_status_t *st) {
+  if (!c || !st || check_layer(c, layer) || seq < 0 || seq >= c->D.batch) return ISKV_EINVAL;
+  return fill_status(c, layer, seq_state(c->layers[layer], seq), st);
+}
+
+int iskv_append_ragged(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                       int in_dtype, const int32_t *counts, int *seqs_ready) {
+  if (!c || check_layer(c, layer) || !dev_k || !dev_v || !counts || n_tokens < 0) return ISKV_EINVAL;
+  if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
+  if (c->D.batch > kMaxSeqTab) return ISKV_EINVAL;
+  LayerState &L = c->layers[layer];
+  for (int b = 0; b < c->D.batch; ++b) {
+    if (counts[b] < 0 || counts[b] > n_tokens) return ISKV_EINVAL;
+    const SeqState q = seq_state(L, b);
+    if (q.length + counts[b] - q.n_c > c->D.slots) return ISKV_ESTATE;
+    if (q.length + counts[b] > c->D.max_tokens) return ISKV_ESTATE;
+  }
+  make_ragged(c, L);
+  SeqTab tab{};
+  tab.n = c->D.batch;
+  for (int b = 0; b < c->D.batch; ++b) {
+    tab.len[b] = (int32_t)L.seq[(size_t)b].length;
+    tab.aux[b] = counts[b];
+    if (counts[b] > 0) tab.mask |= 1ull << b;
+  }
+  if (tab.mask) {
+    if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
+    if (launch_append(c->M, layer, dev_k, dev_v, n_tokens, in_dtype, 0, c->stream, tab) != hipSuccess)
+      return ISKV_EDEVICE;
+  }
+  int ready = 0;
+  for (int b = 0; b < c->D.batch; ++b) {
+    SeqState &q = L.seq[(size_t)b];
+    q.length += counts[b];
+    ready += (q.length - q.n_c == c->D.slots) ? 1 : 0;
+  }
+  if (seqs_ready) *seqs_ready = ready;
+  return ISKV_OK;
+}
+
+int iskv_decode_attn_ragged(iskv_ctx *c, int layer, const float *dev_q, const int64_t *q_pos,
+                            float *dev_out) {
+  if (!c || check_layer(c, layer) || !dev_q || !q_pos || !dev_out) return ISKV_EINVAL;
+  if (c->D.batch > kMaxSeqTab) return ISKV_EINVAL;
+  const LayerState &L = c->layers[layer];
+  SeqTab tab{};
+  tab.n = c->D.batch;
+  tab.mask = seq_bits(c->D.batch);
+  for (int b = 0; b < c->D.batch; ++b) {
+    if (q_pos[b] < 0 || q_pos[b] >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
+    const SeqState q = seq_state(L, b);
+    if (q.length <= 0) return ISKV_ESTATE;
+    tab.len[b] = (int32_t)q.length;
+    tab.nc[b] = (int32_t)q.n_c;
+    tab.aux[b] = (int32_t)q_pos[b];
+  }
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
+  return hip_err(launch_decode_ragged(c->M, layer, dev_q, dev_out, tab, c->stream));
+}
 
 int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   if (!c || check_layer(c, layer) || !host_buf) return ISKV_EINVAL;
+  if (!make_uniform(c->layers[layer])) return ISKV_ESTATE;
   if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
@@ -607,6 +807,8 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   L.length = length;
   L.n_c = n_c;
   L.pending = false;
+  L.ragged = false;
+  L.seq.clear();
   return ISKV_OK;
 }
 

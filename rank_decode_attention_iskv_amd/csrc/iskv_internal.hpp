@@ -142,6 +142,27 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
   return P;
 }
 
+// Per-sequence values of a call over a ragged batch (sequences at different
+// lengths), passed to the kernels by value.  n == 0: every sequence takes the
+// call's scalar arguments and takes part.  Otherwise n == batch (at most
+// kMaxSeqTab), bit b of mask says whether sequence b takes part, and
+//   decode: len = tokens held, nc = end of the compressed rows, aux = query position
+//   append: len = first position written, aux = tokens written (<= the call's n)
+//   fold:   nc = end of the compressed rows before the fold
+//   sync:   nc = end of the rows the sync maps (n_old)
+constexpr int kMaxSeqTab = 64;
+struct SeqTab {
+  int n;
+  uint64_t mask;
+  int32_t len[kMaxSeqTab];
+  int32_t nc[kMaxSeqTab];
+  int32_t aux[kMaxSeqTab];
+};
+
+__host__ __device__ inline bool seq_in(const SeqTab &t, int b) {
+  return t.n == 0 || ((t.mask >> b) & 1ull) != 0;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel launchers (defined in the .hip files). Each returns hipSuccess or the
 // launch error.
@@ -153,15 +174,17 @@ hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s);
 // Write n tokens at positions pos0.. into the protected prefix (positions < P)
 // or the rings (in_dtype 0 f32, 1 bf16).
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
-                         int in_dtype, int64_t pos0, hipStream_t s);
+                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab = SeqTab{});
 
 // Fold the block at positions n_c..n_c+63 of every unit of the selected
 // layers: factor x (0 K, 1 V), or both (x = -1, one launch; equal ranks only).
-hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s);
+hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
+                               const SeqTab &tab = SeqTab{});
 
 // C[0:n_old] <- C[0:n_old] * M for every unit of the selected layers, factor
 // x (0 K, 1 V) or both (x = -1; equal ranks only).
-hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s);
+hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
+                       const SeqTab &tab = SeqTab{});
 
 // Rebuild the decode operand copy of the basis from the fp32 basis.
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s);
@@ -178,5 +201,10 @@ struct FusedAppend {
 // counts the appended token.
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                          int64_t length, int64_t n_c, hipStream_t s, FusedAppend app = FusedAppend{});
+
+// Decode attention over a ragged batch: tab (n == batch) holds every
+// sequence's length, compressed end and query position.
+hipError_t launch_decode_ragged(const Model &M, int layer, const float *q, float *out,
+                                const SeqTab &tab, hipStream_t s);
 
 }  // namespace iskv

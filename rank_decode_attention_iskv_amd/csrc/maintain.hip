@@ -45,9 +45,12 @@ __global__ void reset_basis_kernel(Model M, int layer) {
 // Append: grid (n tokens, kv heads, batch), block = head_dim threads.
 // ---------------------------------------------------------------------------
 template <typename T, typename In>
-__global__ void append_kernel(Model M, int layer, const In *k, const In *v, int n, int64_t pos0) {
+__global__ void append_kernel(Model M, int layer, const In *k, const In *v, int n, int64_t pos0,
+                              SeqTab tab) {
   const Dims &D = M.D;
   const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, f = threadIdx.x;
+  if (!seq_in(tab, b) || t >= (tab.n ? tab.aux[b] : n)) return;     // ragged: this sequence's count
+  if (tab.n) pos0 = tab.len[b];
   const int u = b * D.kv_heads + h;
   const size_t src = (((size_t)b * n + t) * D.kv_heads + h) * D.d + f;
   const float kx = Store<In>::load(k, src);
@@ -125,7 +128,8 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // grid (row tiles, units (one factor) or units*2 (both), layers)
 // ---------------------------------------------------------------------------
 template <int R>
-__global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel sel, int64_t n_old, int xsel) {
+__global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel sel, int64_t n_old, int xsel,
+                                                              SeqTab tab) {
   static_assert(R == 16 || R == 32 || R == 64 || R == 128, "MFMA sync ranks");
   constexpr int KB = R >= 32 ? R / 32 : 1;      // K blocks (32 wide; one of 16 at r = 16)
   constexpr int MB = R / 16;                    // output column blocks
@@ -134,6 +138,8 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   const int l = sel.idx[blockIdx.z];
   // grid.y: units (one factor, xsel) or units x 2 (both, equal ranks)
   const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
+  if (!seq_in(tab, u / D.kv_heads)) return;     // ragged: a sequence that did not fold
+  if (tab.n) n_old = tab.nc[u / D.kv_heads];
   LayerPtrs P = layer_ptrs(M, l);
   const float *Ms = P.msync[x] + (size_t)u * R * R;
   uint16_t *C = reinterpret_cast<uint16_t *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
@@ -200,12 +206,15 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
 }
 
 template <int R>
-__global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel sel, int64_t n_old, int xsel) {
+__global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel sel, int64_t n_old, int xsel,
+                                                              SeqTab tab) {
   __shared__ float4 sM4[R * R / 4];
   const float *sM = reinterpret_cast<const float *>(sM4);
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
   const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
+  if (!seq_in(tab, u / D.kv_heads)) return;     // block-uniform, before the barrier
+  if (tab.n) n_old = tab.nc[u / D.kv_heads];
   LayerPtrs P = layer_ptrs(M, l);
   const float4 *Ms = reinterpret_cast<const float4 *>(P.msync[x] + (size_t)u * R * R);
   float *C = reinterpret_cast<float *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
@@ -238,29 +247,31 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
 }
 
 template <int R, typename T>
-hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
+hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
+                         const SeqTab &tab) {
   if (n_old <= 0) return hipSuccess;
   const unsigned ny = x < 0 ? M.D.units * 2 : M.D.units;
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int64_t rows_per_block = (int64_t)(kThreads / 64) * (R == 128 ? 4 : 8) * 16;
     dim3 grid((unsigned)((n_old + rows_per_block - 1) / rows_per_block), ny, sel.n);
-    hipLaunchKernelGGL((sync_mfma_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x);
+    hipLaunchKernelGGL((sync_mfma_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab);
   } else {
     dim3 grid((unsigned)((n_old + kThreads - 1) / kThreads), ny, sel.n);
-    hipLaunchKernelGGL((sync_valu_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x);
+    hipLaunchKernelGGL((sync_valu_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab);
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
+hipError_t dispatch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
+                         const SeqTab &tab) {
   const int r = x == 1 ? M.D.rv : M.D.rk;
   if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
   switch (r) {
-    case 16: return launch_sync_t<16, T>(M, sel, n_old, x, s);
-    case 32: return launch_sync_t<32, T>(M, sel, n_old, x, s);
-    case 64: return launch_sync_t<64, T>(M, sel, n_old, x, s);
-    case 128: return launch_sync_t<128, T>(M, sel, n_old, x, s);
+    case 16: return launch_sync_t<16, T>(M, sel, n_old, x, s, tab);
+    case 32: return launch_sync_t<32, T>(M, sel, n_old, x, s, tab);
+    case 64: return launch_sync_t<64, T>(M, sel, n_old, x, s, tab);
+    case 128: return launch_sync_t<128, T>(M, sel, n_old, x, s, tab);
   }
   return hipErrorInvalidValue;
 }
@@ -273,30 +284,31 @@ hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s) {
 }
 
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
-                         int in_dtype, int64_t pos0, hipStream_t s) {
+                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab) {
   if (n <= 0) return hipSuccess;
   dim3 grid(n, M.D.kv_heads, M.D.batch);
   if (M.D.storage == 1) {
     if (in_dtype == 1)
       hipLaunchKernelGGL((append_kernel<bf16_t, bf16_t>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const bf16_t *)k, (const bf16_t *)v, n, pos0);
+                         (const bf16_t *)k, (const bf16_t *)v, n, pos0, tab);
     else
       hipLaunchKernelGGL((append_kernel<bf16_t, float>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const float *)k, (const float *)v, n, pos0);
+                         (const float *)k, (const float *)v, n, pos0, tab);
   } else {
     if (in_dtype == 1)
       hipLaunchKernelGGL((append_kernel<float, bf16_t>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const bf16_t *)k, (const bf16_t *)v, n, pos0);
+                         (const bf16_t *)k, (const bf16_t *)v, n, pos0, tab);
     else
       hipLaunchKernelGGL((append_kernel<float, float>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const float *)k, (const float *)v, n, pos0);
+                         (const float *)k, (const float *)v, n, pos0, tab);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s) {
-  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, x, s)
-                          : dispatch_sync<float>(M, sel, n_old, x, s);
+hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
+                       const SeqTab &tab) {
+  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, x, s, tab)
+                          : dispatch_sync<float>(M, sel, n_old, x, s, tab);
 }
 
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s) {
