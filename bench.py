@@ -61,6 +61,11 @@ def parse():
     ap.add_argument("--async-maintenance", action="store_true",
                     help="run block updates and syncs on a second stream (each layer "
                          "instance's later work waits for its own); default: the decode stream")
+    ap.add_argument("--ragged", action="store_true",
+                    help="separate measurement: one layer, --batch sequences (default 16) whose "
+                         "lengths are spread evenly up to --context; each step appends one token "
+                         "to every sequence (iskv_append_ragged), attends each at its own length "
+                         "(iskv_decode_attn_ragged), and folds the sequences whose ring fills")
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only stream a 256 MiB float32 tensor through an elementwise kernel "
@@ -241,14 +246,120 @@ def _cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries, samp
     }
 
 
+def ragged_bench(args):
+    """A ragged batch: sequence b holds about context * (b + 1) / B tokens."""
+    import torch
+
+    from rank_decode_attention_iskv_amd import binding
+    torch.cuda.set_device(0)
+    H, HQ, D, R, W = 8, 32, 128, args.rank, args.window
+    B = args.batch if args.batch > 1 else 16
+    RV = args.rank_v or R
+    target = [max(1, args.context * (b + 1) // B) for b in range(B)]
+    steps = args.warmup + args.steps
+    cfg = binding.make_config(B, 1, H, HQ, D, R, W, args.context + steps + 64, binding.BF16,
+                              protected_prefix=args.protected_prefix, rank_v=RV)
+    cache = binding.IskvCache(cfg)
+    gen = Generator(torch, 1, B, H, D, 32, args.seed)
+    slots = W + 64
+    length, n_c = [0] * B, [args.protected_prefix] * B
+    t_pre = time.perf_counter()
+    while any(length[b] < target[b] for b in range(B)):
+        counts = [max(0, min(64, target[b] - length[b], slots - (length[b] - n_c[b]))) for b in range(B)]
+        k, v = gen.tokens(0, max(counts))
+        ready = cache.append_ragged(0, k, v, counts)
+        for b in range(B):
+            length[b] += counts[b]
+        if ready:
+            cache.block_update(0)
+            cache.sync(0)
+            for b in range(B):
+                if length[b] - n_c[b] == slots:
+                    n_c[b] += 64
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t_pre
+    toks = [gen.tokens(0, 1) for _ in range(steps)]
+    q_all = gen.queries(steps, HQ, D)
+    out = torch.empty(B, HQ, D, device="cuda")
+    ones = [1] * B
+    folds = 0
+
+    def step(s):
+        nonlocal folds
+        k, v = toks[s]
+        ready = cache.append_ragged(0, k, v, ones)
+        for b in range(B):
+            length[b] += 1
+        cache.decode_attn_ragged(0, q_all[s], [L - 1 for L in length], out)
+        if ready:
+            cache.block_update(0)
+            cache.sync(0)
+            folds += 1
+            for b in range(B):
+                if length[b] - n_c[b] == slots:
+                    n_c[b] += 64
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, steps):
+        step(s)
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t0
+    # decode roofline: back-to-back ragged decode calls at the final lengths
+    calls = 64
+    rl_bytes = sum(decode_bytes(1, H, HQ, D, R, n_c[b] - args.protected_prefix,
+                                length[b] - (n_c[b] - args.protected_prefix), r_v=RV)
+                   for b in range(B))
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qp = [L - 1 for L in length]
+    e0.record(stream)
+    for _ in range(calls):
+        cache.decode_attn_ragged(0, q_all[0], qp, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg_ms = e0.elapsed_time(e1) / calls
+    achieved = rl_bytes / (avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC + " (ragged batch)",
+        "value": B * args.steps / total_s,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_s * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": (f"one GQA layer, ragged batch of {B} sequences at lengths "
+                         f"{target[0]}..{target[-1]} (spread evenly), {H} KV / {HQ} q heads, "
+                         f"head_dim {D}, rank {R} (V {RV}), window {W}, bf16 storage; per step one "
+                         "token per sequence (iskv_append_ragged), iskv_decode_attn_ragged, and a "
+                         "fold + sync of the sequences whose ring fills"),
+            "global_batch": B, "seq_len": args.context, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_attn_ragged", "achieved": achieved, "peak": 8000.0,
+            "unit": "GB/s", "frac": achieved / 8000.0, "traffic": None,
+            "algorithmic_bytes_per_launch": rl_bytes, "avg_launch_us": avg_ms * 1e3,
+        },
+        "cpu_baseline": None,
+        "folds_timed": folds, "prefill_s": t_pre,
+    }
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
-              "not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); runs over several "
+              "GPUs are not supported", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ragged:
+        ragged_bench(args)
         return
     import torch
 
