@@ -25,16 +25,16 @@ pytestmark = pytest.mark.gpu
 ATOL_OUT = 2e-3
 
 
-def _decode_vs_oracle(w, n_c, length, q_positions):
+def _decode_vs_oracle(w, n_c, length, q_positions, rank_v=0):
     import torch
     from rank_decode_attention_iskv_amd import binding
 
     max_tokens = length + 64
     storage = binding.BF16 if w.storage == "bf16" else binding.F32
     cfg = binding.make_config(w.batch, 1, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
-                              max_tokens, storage)
+                              max_tokens, storage, rank_v=rank_v)
     gpu = binding.IskvCache(cfg)
-    units = workloads.synthetic_state(w, length, n_c, max_tokens)
+    units = workloads.synthetic_state(w, length, n_c, max_tokens, rank_v=rank_v)
     gpu.import_state(0, binding.pack_state(cfg, length, n_c, units))
     st = gpu.status(0)
     assert (st.length, st.compressed) == (length, n_c)
@@ -51,7 +51,7 @@ def _decode_vs_oracle(w, n_c, length, q_positions):
         ref = np.zeros_like(got)
         for ui, (xk, xv) in enumerate(units):
             b, h = divmod(ui, w.kv_heads)
-            u = Unit(w.head_dim, w.rank, w.window, max_tokens, w.storage)
+            u = Unit(w.head_dim, w.rank, w.window, max_tokens, w.storage, r_v=rank_v or None)
             u.load_state(length, n_c, xk["ring"], xv["ring"], xk["basis"], xk["S"], xk["coef"],
                          xv["basis"], xv["S"], xv["coef"])
             ref[b, h * g:(h + 1) * g] = u.decode(q[b, h * g:(h + 1) * g], q_pos, scale)
@@ -99,4 +99,22 @@ def test_decode_many_splits_odd_group(kv_heads, q_heads, batch):
     n_c = 16384
     length = n_c + w.window + 7
     errs = _decode_vs_oracle(w, n_c, length, [length + 3])
+    assert max(errs) < ATOL_OUT, errs
+
+
+def test_decode_full_size_gqa_layer_32k_value_rank_64():
+    """The 32K layer with a value rank twice the key rank (r_K = 32, r_V = 64),
+    the configuration of bench.py --rank-v 64; single-round grid."""
+    w = workloads.WORKLOADS[2]
+    n_c = 32512
+    errs = _decode_vs_oracle(w, n_c, n_c + w.window + 40, [n_c + w.window + 39, 77], rank_v=64)
+    assert max(errs) < ATOL_OUT, errs
+
+
+def test_decode_full_size_batch16_16k_rank32_value64():
+    """Batch 16 x 16K, r_K = 32, r_V = 64, window 512: the multi-round grid
+    with the separate merge kernel at the value rank."""
+    w = workloads.with_(workloads.WORKLOADS[3], rank=32)
+    n_c = 15872
+    errs = _decode_vs_oracle(w, n_c, n_c + w.window + 3, [n_c + w.window + 2], rank_v=64)
     assert max(errs) < ATOL_OUT, errs

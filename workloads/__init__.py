@@ -174,7 +174,8 @@ def _bf16_grid(x: np.ndarray) -> np.ndarray:
     return u.view(np.float32)
 
 
-def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: int = 7):
+def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: int = 7,
+                    rank_v: int = 0):
     """A random cache state of the workload's shapes, for decode-only checks at
     full size without running the folds that would build it: per (sequence,
     KV head) and K|V, an orthonormal d x r basis (QR of a Gaussian matrix),
@@ -183,14 +184,16 @@ def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: i
     coefficients and ring rows are drawn on the bf16 grid.
 
     Returns a list over units (b * kv_heads + h) of [K, V] dicts with keys
-    basis, S, coef (max_tokens x r), ring ((window + 64) x d)."""
-    d, r, slots = w.head_dim, w.rank, w.window + 64
+    basis, S, coef (max_tokens x r), ring ((window + 64) x d).  rank_v > 0
+    gives the V factor that rank instead of w.rank."""
+    d, slots = w.head_dim, w.window + 64
     assert n_c % 64 == 0 and w.window <= length - n_c <= w.window + 63
     units = []
     for b in range(w.batch):
         for h in range(w.kv_heads):
             xs = []
             for x in range(2):
+                r = (rank_v or w.rank) if x else w.rank
                 rng = _rng(w, 9001, seed, b, h, x)          # 9001: state stream tag
                 B, _ = np.linalg.qr(rng.standard_normal((d, r)))
                 S = np.sort(rng.uniform(1.0, 50.0, r))[::-1].astype(np.float32)
