@@ -36,7 +36,9 @@
  *   - Return codes are from host-side validation (ISKV_E*); a launch failure
  *     returns ISKV_EDEVICE.  Device-detected numeric trouble (non-finite input
  *     or core, Jacobi sweep cap reached) is reported by iskv_status.
- *   - A context is not thread-safe.  Sequences of a batch advance in lockstep.
+ *   - A context is not thread-safe.  Sequences of a batch advance in lockstep
+ *     through the uniform calls, or each at its own pace through the ragged
+ *     calls (iskv_append_ragged and iskv_decode_attn_ragged below).
  *   - head_dim must be 128; rank must be 16, 32, 64 or 128 (rank_v equal to it
  *     or twice it); window a multiple of 64; num_q_heads a multiple of
  *     num_kv_heads, at most 16 times it.
@@ -72,7 +74,7 @@ enum {
 };
 
 typedef struct {
-  int32_t batch;          /* sequences, advanced in lockstep */
+  int32_t batch;          /* sequences (lockstep, or ragged: at most 64) */
   int32_t num_layers;
   int32_t num_kv_heads;
   int32_t num_q_heads;    /* multiple of num_kv_heads (grouped-query attention) */
