@@ -63,6 +63,31 @@ struct SplitPlan {
   // records: compressed splits first, then prefix splits, then window splits
 };
 
+// A ragged batch's plans, one per sequence: blockIdx.x runs over the
+// sequences' splits in order (sequence b owns off[b] .. off[b+1]-1), so each
+// sequence gets workgroups in proportion to its own tokens.  n == 0: one plan
+// for every unit (grid.y = units).
+struct SeqPlans {
+  int n;
+  int32_t off[kMaxSeqTab + 1];
+  int16_t n_comp[kMaxSeqTab], n_pre[kMaxSeqTab], n_win[kMaxSeqTab];
+  int32_t comp_len[kMaxSeqTab], pre_len[kMaxSeqTab], win_len[kMaxSeqTab];
+};
+
+__host__ __device__ inline SplitPlan seq_plan(const SeqPlans &sp, int b) {
+  SplitPlan p;
+  p.n_comp = sp.n_comp[b];
+  p.comp_len = sp.comp_len[b];
+  p.n_win = sp.n_win[b];
+  p.win_len = sp.win_len[b];
+  p.n_pre = sp.n_pre[b];
+  p.pre_len = sp.pre_len[b];
+  return p;
+}
+
+static_assert(sizeof(Model) + sizeof(SeqTab) + sizeof(SeqPlans) + sizeof(SplitPlan) + 128 <= 4096,
+              "decode kernel arguments must fit the 4 KiB argument segment");
+
 // A float store performed at agent scope (coherent across the XCDs' L2s).
 __device__ __forceinline__ void store_agent(float *p, float v) {
   __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
@@ -433,7 +458,7 @@ template <int RK, int RV, typename T, int NW> struct Cfg {
 template <int RK, int RV, typename T, int NW>
 __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos_arg, float *out, int64_t length_arg,
-    int64_t n_c_arg, SplitPlan plan, int fused, FusedAppend app, SeqTab tab) {
+    int64_t n_c_arg, SplitPlan plan_arg, int fused, FusedAppend app, SeqTab tab, SeqPlans sp) {
   using C = Cfg<RK, RV, T, NW>;
   constexpr int R = RK;                                  // the key path below uses R
   constexpr bool BF = C::BF;
@@ -457,8 +482,17 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   const int G = D.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, rho = lane >> 4;
-  const int split = blockIdx.x, u = blockIdx.y;
-  const int b = u / D.kv_heads, hk = u % D.kv_heads;
+  // ragged: blockIdx.x = (sequence, split) flattened, blockIdx.y = KV head
+  int split_i = blockIdx.x, b_i = (int)blockIdx.y / D.kv_heads;
+  if (sp.n) {
+    b_i = 0;
+    while (b_i + 1 < sp.n && sp.off[b_i + 1] <= split_i) ++b_i;
+    split_i -= sp.off[b_i];
+  }
+  const int split = split_i, b = b_i;
+  const int hk = sp.n ? (int)blockIdx.y : (int)blockIdx.y % D.kv_heads;
+  const int u = b * D.kv_heads + hk;
+  const SplitPlan plan = sp.n ? seq_plan(sp, b) : plan_arg;
   // a ragged batch gives each sequence its own length, compressed end and
   // query position; the plan covers the largest of each, and a split past a
   // sequence's own range is empty (neutral record)
@@ -964,7 +998,8 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   if (threadIdx.x == 0) {
     const unsigned done =
         __hip_atomic_fetch_add(M.sh.cnt + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (done + 1 == gridDim.x) ? 1 : 0;
+    const unsigned splits = sp.n ? (unsigned)(plan.n_comp + plan.n_pre + plan.n_win) : gridDim.x;
+    s_last = (done + 1 == splits) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
@@ -975,9 +1010,10 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 // Unfused: one workgroup per unit merges after the split kernel.
 template <int R>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int layer, float *out,
-                                                                SplitPlan plan) {
+                                                                SplitPlan plan, SeqPlans sp) {
   extern __shared__ __align__(16) uint8_t s_mrg[];
-  merge_unit<R, 4>(M, layer, out, plan, blockIdx.x, s_mrg);
+  const int u = blockIdx.x;
+  merge_unit<R, 4>(M, layer, out, sp.n ? seq_plan(sp, u / M.D.kv_heads) : plan, u, s_mrg);
 }
 
 // Workgroups (of `waves` waves) per decode call: about 16 tiles of 16 tokens
@@ -1006,10 +1042,9 @@ int target_workgroups(const Dims &D, int64_t length, int waves) {
 // compressed, 0 .. P-1 exact, n_c .. length-1 in the ring).
 // n_k compressed, n_e ring and n_p prefix tokens (for a ragged batch, the
 // largest of each over the sequences; length the largest length).
-SplitPlan make_plan_parts(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, int64_t length,
-                          int waves) {
+SplitPlan make_plan_core(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, int64_t per_unit,
+                         int waves) {
   SplitPlan plan{};
-  const int target = target_workgroups(D, length, waves);
   if (n_e > 0) {
     // about 4 tiles per wave for the window
     int64_t nw = (n_e + 255) / 256;
@@ -1027,7 +1062,7 @@ SplitPlan make_plan_parts(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, 
   }
   if (n_k > 0) {
     const int n_x = plan.n_win + plan.n_pre;
-    int64_t want = target / D.units - n_x;
+    int64_t want = per_unit - n_x;
     if (want < 1) want = 1;
     int64_t nc = (n_k + 32 * waves - 1) / (32 * waves);   // at least 2 tiles per wave
     if (nc > want) nc = want;
@@ -1042,27 +1077,43 @@ SplitPlan make_plan_parts(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, 
 SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
   const int64_t n_e = length > n_c ? length - n_c : 0;           // ring tokens
   const int64_t n_p = length < D.prefix ? length : D.prefix;     // prefix tokens
-  return make_plan_parts(D, n_c - D.prefix, n_e, n_p, length, waves);
+  return make_plan_core(D, n_c - D.prefix, n_e, n_p, target_workgroups(D, length, waves) / D.units,
+                        waves);
 }
 
-SplitPlan make_plan_tab(const Dims &D, const SeqTab &tab, int waves) {
-  int64_t n_k = 0, n_e = 0, n_p = 0, length = 0;
+// Ragged batch: the workgroups a batch of the average length would get,
+// shared out in proportion to each sequence's length.
+SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves) {
+  SeqPlans sp{};
+  sp.n = tab.n;
+  int64_t total = 0;
+  for (int b = 0; b < tab.n; ++b) total += tab.len[b];
+  const int64_t target = target_workgroups(D, (total + tab.n - 1) / tab.n, waves);
+  sp.off[0] = 0;
   for (int b = 0; b < tab.n; ++b) {
     const int64_t L = tab.len[b], c = tab.nc[b];
-    n_k = std::max<int64_t>(n_k, c - D.prefix);
-    n_e = std::max<int64_t>(n_e, L > c ? L - c : 0);
-    n_p = std::max<int64_t>(n_p, L < D.prefix ? L : D.prefix);
-    length = std::max<int64_t>(length, L);
+    const int64_t n_e = L > c ? L - c : 0;
+    const int64_t n_p = L < D.prefix ? L : D.prefix;
+    const int64_t per_unit = std::max<int64_t>(1, target * L / (total * D.kv_heads));
+    const SplitPlan p = make_plan_core(D, c - D.prefix, n_e, n_p, per_unit, waves);
+    sp.n_comp[b] = (int16_t)p.n_comp;
+    sp.n_pre[b] = (int16_t)p.n_pre;
+    sp.n_win[b] = (int16_t)p.n_win;
+    sp.comp_len[b] = p.comp_len;
+    sp.pre_len[b] = p.pre_len;
+    sp.win_len[b] = p.win_len;
+    sp.off[b + 1] = sp.off[b] + p.n_comp + p.n_pre + p.n_win;
   }
-  return make_plan_parts(D, n_k, n_e, n_p, length, waves);
+  return sp;
 }
 
 template <int RK, int RV, typename T, int NW>
 hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, const SplitPlan &plan, hipStream_t s,
-                       FusedAppend app, const SeqTab &tab) {
+                       FusedAppend app, const SeqTab &tab, const SeqPlans &sp) {
   using C = Cfg<RK, RV, T, NW>;
-  dim3 grid(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
+  const dim3 grid = sp.n ? dim3(sp.off[sp.n], M.D.kv_heads)
+                         : dim3(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
   constexpr int dyn = C::kDynBytes;
   static bool dattr = false;
   hipError_t e;
@@ -1076,7 +1127,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   const int64_t slots = (int64_t)M.D.cus * C::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<RK, RV, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
-                     out, length, n_c, plan, fused, app, tab);
+                     out, length, n_c, plan, fused, app, tab, sp);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   constexpr int mbytes = MergeLds<RV, 4>::bytes;
@@ -1088,7 +1139,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
     mattr = true;
   }
   hipLaunchKernelGGL((decode_merge_kernel<RV>), dim3(M.D.units), dim3(kThreads), mbytes, s, M, layer,
-                     out, plan);
+                     out, plan, sp);
   return hipGetLastError();
 }
 
@@ -1099,15 +1150,25 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
 template <int RK, int RV, typename T>
 hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, hipStream_t s, FusedAppend app, const SeqTab &tab) {
-  auto plan = [&](int waves) {
-    return tab.n ? make_plan_tab(M.D, tab, waves) : make_plan(M.D, length, n_c, waves);
-  };
-  if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
-    const SplitPlan p8 = plan(8);
-    if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
-      return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app, tab);
+  if (tab.n) {
+    // ragged: one plan per sequence, (sequence, split) flattened into grid.x
+    const SplitPlan none{};
+    if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
+      const SeqPlans s8 = make_seq_plans(M.D, tab, 8);
+      if ((int64_t)s8.off[s8.n] * M.D.kv_heads <= M.D.cus)
+        return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab, s8);
+    }
+    return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab,
+                                     make_seq_plans(M.D, tab, 4));
   }
-  return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, plan(4), s, app, tab);
+  const SeqPlans one{};
+  if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
+    const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
+    if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
+      return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app, tab, one);
+  }
+  return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c,
+                                   make_plan(M.D, length, n_c, 4), s, app, tab, one);
 }
 
 // (r_K, r_V): equal ranks, or a value rank twice the key rank
