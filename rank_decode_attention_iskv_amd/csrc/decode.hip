@@ -494,8 +494,9 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   const int u = b * D.kv_heads + hk;
   const SplitPlan plan = sp.n ? seq_plan(sp, b) : plan_arg;
   // a ragged batch gives each sequence its own length, compressed end and
-  // query position; the plan covers the largest of each, and a split past a
-  // sequence's own range is empty (neutral record)
+  // query position, and its own plan; a split with no tokens (none in a
+  // uniform or per-sequence plan, kept safe all the same) writes a neutral
+  // record
   const int64_t length = tab.n ? (int64_t)tab.len[b] : length_arg;
   const int64_t n_c = tab.n ? (int64_t)tab.nc[b] : n_c_arg;
   const int64_t q_pos = tab.n ? (int64_t)tab.aux[b] : q_pos_arg;
