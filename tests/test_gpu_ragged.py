@@ -237,3 +237,65 @@ def test_ragged_uniform_calls_refuse_differing_sequences():
     assert [r.gpu.seq_status(0, b).length for b in range(2)] == [5, 9]
     r.step([4, 0])                                 # equal again: uniform calls work
     assert r.gpu.status(0).length == 9
+
+
+def test_ragged_and_uniform_layers_fold_together():
+    """iskv_block_update(-1) / iskv_sync(-1) over a ragged layer and a uniform
+    layer give the same bits as the per-layer calls."""
+    import torch
+    from rank_decode_attention_iskv_amd import binding
+    w = small(2, batch=3, kv_heads=2, q_heads=8, window=64)
+    cfg = binding.make_config(w.batch, 2, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
+                              1024, binding.BF16)
+    caches = [binding.IskvCache(cfg), binding.IskvCache(cfg)]
+    rng = np.random.default_rng(5)
+    length = [[0] * w.batch, [0] * w.batch]
+    n_c = [[0] * w.batch, [0] * w.batch]
+    folds = 0
+    for step in range(24):
+        c0 = [int(min(rng.integers(0, 50), 128 - (length[0][b] - n_c[0][b]))) for b in range(w.batch)]
+        n1 = int(min(rng.integers(1, 50), 128 - (length[1][0] - n_c[1][0])))
+        n = max(max(c0), 1)
+        K0 = np.zeros((w.batch, n, w.kv_heads, w.head_dim), np.float32)
+        V0 = np.zeros_like(K0)
+        for b, c in enumerate(c0):
+            if c:
+                K0[b, :c], V0[b, :c] = seq_tokens(w, b, length[0][b], c)
+        k1, v1 = workloads.tokens(w, 1, length[1][0], n1)
+        for ci, cache in enumerate(caches):
+            cache.append_ragged(0, torch.from_numpy(K0).cuda(), torch.from_numpy(V0).cuda(), c0)
+            cache.append(1, torch.from_numpy(k1.astype(np.float32)).cuda(),
+                         torch.from_numpy(v1.astype(np.float32)).cuda())
+        for b in range(w.batch):
+            length[0][b] += c0[b]
+            length[1][b] += n1
+        full0 = [b for b in range(w.batch) if length[0][b] - n_c[0][b] == 128]
+        full1 = length[1][0] - n_c[1][0] == 128
+        if full0 or full1:
+            caches[0].block_update(-1)
+            caches[0].sync(-1)
+            if full0:
+                caches[1].block_update(0)
+                caches[1].sync(0)
+            if full1:
+                caches[1].block_update(1)
+                caches[1].sync(1)
+            for b in full0:
+                n_c[0][b] += 64
+            if full1:
+                for b in range(w.batch):
+                    n_c[1][b] += 64
+            folds += 1
+    assert folds >= 4 and len(set(n_c[0])) > 1
+    q = torch.from_numpy(q32(workloads.query(w, 0, 3)).astype(np.float32)).cuda()
+    outs = []
+    for cache in caches:
+        o0, o1 = torch.empty_like(q), torch.empty_like(q)
+        cache.decode_attn_ragged(0, q, [L + 1 for L in length[0]], o0)
+        cache.decode_attn(1, q, length[1][0] - 1, o1)
+        torch.cuda.synchronize()
+        outs.append((o0.cpu().numpy(), o1.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
+    for b in range(w.batch):
+        assert caches[0].seq_status(0, b).compressed == caches[1].seq_status(0, b).compressed == n_c[0][b]
