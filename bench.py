@@ -1,28 +1,49 @@
 """Throughput of the compressed-KV decode path on one MI355X.
 
-Workload (default): one GQA attention layer with 8 KV / 32 query heads,
-head_dim 128, rank 32, 32K-token context, exact window 256, bf16 storage with
-fp32 accumulation, batch 1; a block update + sync every 64 decode steps; keys
-and values are a rank-32 Gaussian signal plus 1% noise (synthetic, seeded).
+Five workloads (--config 1..5, default 3):
 
-A step is one decode step of that layer: append one token (k, v) and decode
-attention of 32 query heads over the whole mixed cache (one launch,
-iskv_append_decode), plus the block updates (Brand fold of 64 tokens for all 8
-heads, K and V) and coefficient syncs that fall due.  The bench holds 16
-instances of the layer and runs the steps round-robin over them, as the
-layers of one model decode a token (so every step reads its cache from HBM
-rather than from the 256 MB Infinity Cache; one instance is ~35 MB).  All
-instances fill their rings at the same token; by default (--fold-mode layers)
-the step that completes that token folds every instance in one
-iskv_block_update(-1) + iskv_sync(-1), as a multi-layer model would; with
---fold-mode instance each instance folds alone at its own step.
+  1  1 KV / 1 query head, head_dim 128, rank 32, 4,096-token context, window
+     256, fp32 storage; keys/values rank-24 Gaussian signal + 1% noise
+  2  one GQA layer: 8 KV / 32 query heads, rank 32, 32K context, window 256,
+     bf16 storage, batch 1; rank-32 signal + 1% noise
+  3  batch 16 x 16K context, 8 KV / 32 query heads, rank 64, window 512, bf16;
+     spectra decaying as sigma_i ~ 1/i, per-sequence bases
+  4  36 layers x 8 KV / 32 query heads, rank 32, window 1,024, bf16, 64K
+     context (--context: any point of the 4K -> 64K growth); 30% of old keys
+     high-norm and aligned with the later queries
+  5  batch 64 x 8K context, 8 KV / 32 query heads, bf16, one point of the sweep
+     rank {16,32,64,128} x window {128,1024} (--rank, --window; default 32/128)
 
-Prints one JSON line (see --help).  Only one GPU: --gpus N > 1 exits.
+A step is one decode step of the whole model of the workload (one layer for
+1, 2, 3 and 5; 36 layers for 4) for every sequence of the batch: append the
+new token's k, v and attend with every query head over the whole mixed cache
+(iskv_append_decode, one launch per layer), plus the block updates (Brand
+fold of the 64 tokens that left the window, every unit, K and V) and the
+syncs (rewrite of every older coefficient row) that fall due, one fold event
+per 64 steps.  Inputs are synthetic, seeded and resident in HBM before
+timing.  Workloads whose cache is smaller than 512 MB keep several
+instances of the model (--instances) and step them round-robin, so that
+every step reads its cache from HBM and not from the 256 MB Infinity Cache.
+
+Timing (HIP events on the launch stream): the timed steps run in segments of
+decode steps; each fold event that falls due between segments (block update
++ sync of every layer whose ring is full, all instances at once) is timed by
+its own event pair, and at least two fold events are timed per run (extra
+ones after the steps if the steps hold fewer).  ms_per_step = decode time
+per step + the fold event time amortized at its natural rate (one event per
+64 steps of every instance); value = tokens per second of the whole batch.
+
+The default run (config 3) also reports config 2 and the config-5 sweep
+points as extra keys (--no-extras skips them), and the float64 oracle timed
+on the host cores (cpu_baseline; --no-cpu-baseline skips it).
+
+Prints one JSON line.  Only one GPU: --gpus N > 1 exits.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -35,42 +56,66 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compressed-KV decode attn tokens/s + block updates/s; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512 << 20
+
+# workload presets: storage 0 = fp32, 1 = bf16
+PRESETS = {
+    1: dict(batch=1, layers=1, kv=1, q=1, rank=32, window=256, context=4096, storage=0,
+            spectrum="gauss", signal=24, hot=0.0),
+    2: dict(batch=1, layers=1, kv=8, q=32, rank=32, window=256, context=32768, storage=1,
+            spectrum="gauss", signal=32, hot=0.0),
+    3: dict(batch=16, layers=1, kv=8, q=32, rank=64, window=512, context=16384, storage=1,
+            spectrum="power", signal=128, hot=0.0),
+    4: dict(batch=1, layers=36, kv=8, q=32, rank=32, window=1024, context=65536, storage=1,
+            spectrum="gauss", signal=32, hot=0.3),
+    5: dict(batch=64, layers=1, kv=8, q=32, rank=32, window=128, context=8192, storage=1,
+            spectrum="gauss", signal=32, hot=0.0),
+}
+SWEEP5 = [(r, w) for r in (16, 32, 64, 128) for w in (128, 1024)]
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4096, help="timed decode steps")
-    ap.add_argument("--warmup", type=int, default=512, help="untimed decode steps")
-    ap.add_argument("--instances", type=int, default=16,
-                    help="independent copies of the layer, stepped round-robin")
-    ap.add_argument("--context", type=int, default=32768, help="tokens in the cache when timing starts")
-    ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(PRESETS))
+    ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="copies of the model stepped round-robin (0: enough for 512 MB of cache)")
+    ap.add_argument("--context", type=int, default=0, help="tokens in the cache when timing starts")
+    ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rank-v", type=int, default=0,
                     help="rank of the V factor (0: same as --rank; else --rank or 2x --rank)")
-    ap.add_argument("--window", type=int, default=256)
-    ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--fold-mode", choices=("layers", "instance"), default="layers",
-                    help="layers: the instances are the layers of one model, and the token at which "
-                         "they all fill their rings folds them in one block update + sync over every "
-                         "layer (iskv_block_update(-1), iskv_sync(-1)); instance: each instance folds "
-                         "alone at its own step")
+    ap.add_argument("--window", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0)
     ap.add_argument("--protected-prefix", type=int, default=0,
                     help="leading positions kept exact and never folded (multiple of 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--async-maintenance", action="store_true",
-                    help="run block updates and syncs on a second stream (each layer "
-                         "instance's later work waits for its own); default: the decode stream")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default config only: skip the config-2 and config-5 extra keys")
     ap.add_argument("--ragged", action="store_true",
                     help="separate measurement: one layer, --batch sequences (default 16) whose "
                          "lengths are spread evenly up to --context; each step appends one token "
                          "to every sequence (iskv_append_ragged), attends each at its own length "
                          "(iskv_decode_attn_ragged), and folds the sequences whose ring fills")
-    ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--seed", type=int, default=1000)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only stream a 256 MiB float32 tensor through an elementwise kernel "
                          "(x * 1 -> y) five times: the reference for HBM byte counters")
     return ap.parse_args()
+
+
+def preset(args, cfg_id=None, **over):
+    p = dict(PRESETS[cfg_id or args.config])
+    for k, a in (("context", "context"), ("rank", "rank"), ("window", "window"), ("batch", "batch")):
+        v = getattr(args, a) if cfg_id is None else 0
+        if v:
+            p[k] = v
+    p["rank_v"] = (args.rank_v if cfg_id is None else 0) or p["rank"]
+    p["prefix"] = args.protected_prefix if cfg_id is None else 0
+    p.update(over)
+    p["id"] = cfg_id or args.config
+    return p
 
 
 def copy_calibration():
@@ -89,33 +134,25 @@ def copy_calibration():
 
 
 def stream_bandwidth():
-    """HBM bandwidth this GPU actually reaches on trivial streaming kernels
-    (1 GiB float32): a read-only reduction (x.sum()) and a copy (y <- x, read
-    + write bytes).  The best of ten dispatches each, timed by events on the
-    current stream, outside the timed region; a second reference for the
-    roofline next to the nominal 8 TB/s."""
+    """HBM bandwidth of a plain copy (y <- x, 1 GiB float32, read + write
+    bytes), best of ten dispatches timed by events: a second reference for
+    the roofline next to the nominal 8 TB/s."""
     import torch
     n = 256 << 20
     src = torch.rand(n, device="cuda")
     dst = torch.empty_like(src)
-    acc = torch.empty((), device="cuda")
-
-    def best(fn, nbytes):
-        fn()
-        times = []
-        for _ in range(10):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b))
-        return nbytes / (min(times) * 1e-3) / 1e9
-
-    read = best(lambda: torch.sum(src, dim=0, out=acc), 4 * n)
-    copy = best(lambda: dst.copy_(src), 8 * n)
+    dst.copy_(src)
+    times = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
     del src, dst
-    return read, copy
+    torch.cuda.empty_cache()
+    return 8 * n / (min(times) * 1e-3) / 1e9
 
 
 # ---------------------------------------------------------------------------
@@ -123,36 +160,67 @@ def stream_bandwidth():
 # ---------------------------------------------------------------------------
 
 class Generator:
-    """x_t = G z_t + 0.01 e_t per (instance, KV head, K|V); G fixed, 128 x 32."""
+    """Per (instance-layer, sequence, KV head, K|V): x_t = G diag(s) z_t + 0.01 e_t
+    with G Gaussian (d x k, "gauss") or Haar-orthonormal columns with s_i ~ 1/i
+    ("power"); with hot > 0 a Bernoulli share of keys gets + 4 sqrt(d) u, u a unit
+    vector per (layer, KV head), and queries get + 2 u."""
 
-    def __init__(self, torch, n_inst, batch, kv_heads, d, signal_rank, seed):
-        self.torch = torch
+    def __init__(self, torch, p, n_layers, seed):
+        self.torch, self.p = torch, p
         self.g = torch.Generator(device="cuda")
         self.g.manual_seed(seed)
-        self.mix = torch.randn(n_inst, batch, kv_heads, 2, signal_rank, d, device="cuda",
-                               generator=self.g) / math.sqrt(signal_rank)
-        self.shape = (batch, kv_heads, d, signal_rank)
+        B, H, d, k = p["batch"], p["kv"], 128, p["signal"]
+        shape = (n_layers, B, H, 2)
+        if p["spectrum"] == "power":
+            z = torch.randn(*shape, d, d, device="cuda", generator=self.g)
+            o, _ = torch.linalg.qr(z)
+            s = 1.0 / torch.arange(1, k + 1, device="cuda", dtype=torch.float32)
+            s = s * math.sqrt(d / float((s ** 2).sum()))
+            self.mix = (o[..., :k] * s).transpose(-1, -2).contiguous()       # [.., k, d]
+            self.noise = 0.0
+        else:
+            self.mix = torch.randn(*shape, k, d, device="cuda", generator=self.g) / math.sqrt(k)
+            self.noise = 0.01
+        u = torch.randn(n_layers, H, d, device="cuda", generator=self.g)
+        self.hot_dir = u / u.norm(dim=-1, keepdim=True)
 
-    def tokens(self, inst, n):
-        torch = self.torch
-        b, h, d, k = self.shape
-        z = torch.randn(b, h, 2, n, k, device="cuda", generator=self.g)
-        x = torch.matmul(z, self.mix[inst]) + 0.01 * torch.randn(b, h, 2, n, d, device="cuda",
-                                                                generator=self.g)
-        x = x.permute(2, 0, 3, 1, 4).contiguous()          # [2, b, n, h, d]
+    def tokens(self, layer, n):
+        """k, v: [batch, n, kv_heads, d] float32."""
+        torch, p = self.torch, self.p
+        B, H, d, k = p["batch"], p["kv"], 128, p["signal"]
+        z = torch.randn(B, H, 2, n, k, device="cuda", generator=self.g)
+        x = torch.matmul(z, self.mix[layer])
+        if self.noise:
+            x = x + self.noise * torch.randn(B, H, 2, n, d, device="cuda", generator=self.g)
+        if p["hot"] > 0:
+            hot = (torch.rand(B, H, n, 1, device="cuda", generator=self.g) < p["hot"]).float()
+            x[:, :, 0] += hot * (4.0 * math.sqrt(d)) * self.hot_dir[layer][None, :, None, :]
+        x = x.permute(2, 0, 3, 1, 4).contiguous()          # [2, B, n, H, d]
         return x[0], x[1]
 
-    def queries(self, count, q_heads, d):
-        return self.torch.randn(count, self.shape[0], q_heads, d, device="cuda", generator=self.g)
+    def queries(self, count, layer):
+        torch, p = self.torch, self.p
+        q = torch.randn(count, p["batch"], p["q"], 128, device="cuda", generator=self.g)
+        if p["hot"] > 0:
+            g = p["q"] // p["kv"]
+            q += 2.0 * self.hot_dir[layer].repeat_interleave(g, dim=0)[None, None]
+        return q
 
 
-def decode_bytes(batch, kv_heads, q_heads, d, r, n_c, n_e, elem=2, r_v=None):
-    """Algorithmic bytes of one decode call: coefficients of K (rank r) and V
-    (rank r_v, default r), exact window rows of K and V, the two fp32 bases,
-    the fp32 query and output."""
-    rs = r + (r_v or r)
-    per_unit = n_c * rs * elem + n_e * d * 2 * elem + d * rs * 4
-    return batch * kv_heads * per_unit + batch * q_heads * d * 4 * 2
+def decode_bytes(p, n_c, n_e):
+    """Algorithmic bytes of one decode call of one layer: coefficients of K
+    (rank r) and V (rank r_v), the exact rows of K and V (window ring and
+    protected prefix), the two fp32 bases, the fp32 query and output."""
+    elem = 2 if p["storage"] == 1 else 4
+    rs = p["rank"] + p["rank_v"]
+    per_unit = n_c * rs * elem + n_e * 128 * 2 * elem + 128 * rs * 4
+    return p["batch"] * p["kv"] * per_unit + p["batch"] * p["q"] * 128 * 4 * 2
+
+
+def state_bytes(p, n_c, n_e):
+    elem = 2 if p["storage"] == 1 else 4
+    return p["layers"] * p["batch"] * p["kv"] * (n_c * (p["rank"] + p["rank_v"]) * elem +
+                                                  n_e * 256 * elem)
 
 
 def kernel_source_hash():
@@ -164,10 +232,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_hash):
+def committed_traffic(kernel_hash, cfg_id):
     """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "decode_attn_r32_ctx32k_counters.txt")
+    counter summary of this workload, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_config{cfg_id}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -184,67 +252,322 @@ def committed_traffic(kernel_hash):
         return None
 
 
+def describe(p):
+    names = {1: "1 KV / 1 query head", 2: "one GQA layer, 8 KV / 32 query heads",
+             3: "8 KV / 32 query heads", 4: "36 layers x 8 KV / 32 query heads",
+             5: "8 KV / 32 query heads"}
+    sig = ("sigma_i ~ 1/i spectra" if p["spectrum"] == "power" else
+           f"rank-{p['signal']} signal + 1% noise")
+    s = (f"config {p['id']}: batch {p['batch']} x {p['context']}-token context (grows by 1 per "
+         f"step), {names[p['id']]}, head_dim 128, rank {p['rank']}"
+         + (f" (V {p['rank_v']})" if p["rank_v"] != p["rank"] else "")
+         + f", window {p['window']}, {'bf16' if p['storage'] == 1 else 'fp32'} storage, fp32 "
+         f"accumulate; K/V {sig}"
+         + ("; 30% hot keys aligned with the queries" if p["hot"] else "")
+         + (f"; first {p['prefix']} positions exact" if p["prefix"] else "")
+         + "; block update + sync every 64 tokens")
+    return s
+
+
+# ---------------------------------------------------------------------------
+# one workload: prefill, timed steps, fold events, roofline
+# ---------------------------------------------------------------------------
+
+def measure(p, steps, warmup, instances, seed, quiet=False):
+    import torch
+
+    from rank_decode_attention_iskv_amd import binding
+    torch.cuda.set_device(0)
+    L0, W, P, ML = p["context"], p["window"], p["prefix"], p["layers"]
+    slots = W + 64
+    # the compressed count that leaves W exact tokens at L0 (fold events
+    # happen at the token that fills the rings)
+    n_c0 = max(P, (L0 - W - P) // 64 * 64 + P)
+    n_e0 = L0 - n_c0
+    if instances <= 0:
+        instances = max(1, math.ceil(ROTATE_BYTES / max(1, state_bytes(p, n_c0 - P, n_e0))))
+    I = min(instances, 64)
+    nl = I * ML
+    per_inst = (warmup + steps + I - 1) // I
+    max_tokens = L0 + per_inst + 64 * 3 + 64
+    cfg = binding.make_config(p["batch"], nl, p["kv"], p["q"], 128, p["rank"], W, max_tokens,
+                              p["storage"], protected_prefix=P, rank_v=p["rank_v"])
+    cache = binding.IskvCache(cfg)
+    stream = torch.cuda.current_stream()
+    gen = Generator(torch, p, nl, seed)
+
+    # ---- prefill every layer of every instance to L0 (fold + sync as the rings fill)
+    t_pre = time.perf_counter()
+    length, n_c = 0, P
+    while length < L0:
+        n = min(256, L0 - length, slots - (length - n_c) if length >= P else P - length)
+        ready = False
+        for layer in range(nl):
+            k, v = gen.tokens(layer, n)
+            ready = cache.append(layer, k, v)
+        length += n
+        if ready:
+            cache.block_update(-1)
+            cache.sync(-1)
+            n_c += 64
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t_pre
+    if not quiet:
+        print(f"# config {p['id']}: {nl} layers prefilled to {length} tokens in {t_pre:.1f} s",
+              file=sys.stderr, flush=True)
+
+    # ---- inputs of every step, resident before timing: per layer
+    # [step][batch][1][kv][d], one contiguous block per step
+    B, H, HQ = p["batch"], p["kv"], p["q"]
+    tok_bytes = B * H * 128 * 4
+    need = per_inst + 64 * 3
+    k_all, v_all = [], []
+    for layer in range(nl):
+        k, v = gen.tokens(layer, need)
+        k_all.append(k.permute(1, 0, 2, 3).contiguous())
+        v_all.append(v.permute(1, 0, 2, 3).contiguous())
+    q_all = [gen.queries(per_inst, layer) for layer in range(ML)]
+    q_bytes = B * HQ * 128 * 4
+    out = torch.empty(B, HQ, 128, device="cuda")
+    torch.cuda.synchronize()
+
+    lib = binding.lib()
+    ctx = cache.ctx
+    k_base = [t.data_ptr() for t in k_all]
+    v_base = [t.data_ptr() for t in v_all]
+    q_base = [t.data_ptr() for t in q_all]
+    out_p = ctypes.c_void_p(out.data_ptr())
+    ready_c = ctypes.c_int(0)
+    lens = [length] * nl            # per layer
+    comp = [n_c] * nl
+    used = [0] * nl
+    n_ready = [0]
+    fold_ms, sync_ms = [], []
+    bytes_steps = [0]
+
+    def fold_event():
+        f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        f0.record(stream)
+        cache.block_update(-1)
+        f1.record(stream)
+        cache.sync(-1)
+        f2.record(stream)
+        return f0, f1, f2
+
+    events = []
+
+    def step(s):
+        """Decode step s: instance s % I, every layer of it.  Returns True if
+        the step completed the token that fills every instance's rings."""
+        inst = s % I
+        due = False
+        for l in range(ML):
+            layer = inst * ML + l
+            j = used[layer]
+            used[layer] += 1
+            lens[layer] += 1
+            L = lens[layer]
+            code = lib.iskv_append_decode(ctx, layer, ctypes.c_void_p(k_base[layer] + j * tok_bytes),
+                                          ctypes.c_void_p(v_base[layer] + j * tok_bytes), binding.F32,
+                                          ctypes.c_void_p(q_base[l] + (s // I) * q_bytes), L - 1,
+                                          out_p, ctypes.byref(ready_c))
+            if code != 0:
+                raise binding.IskvError(code, "iskv_append_decode")
+            bytes_steps[0] += decode_bytes(p, comp[layer] - P, L - (comp[layer] - P))
+            if ready_c.value:
+                comp[layer] += 64
+                n_ready[0] += 1
+        if n_ready[0] == nl:
+            n_ready[0] = 0
+            due = True
+        return due
+
+    # warm-up: untimed steps, folds as they fall due
+    for s in range(warmup):
+        if step(s):
+            cache.block_update(-1)
+            cache.sync(-1)
+    torch.cuda.synchronize()
+    bytes_steps[0] = 0
+
+    # timed steps in segments; fold events between segments, timed alone
+    segs = []
+    s = warmup
+    wall0 = time.perf_counter()
+    while s < warmup + steps:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        due = False
+        while s < warmup + steps and not due:
+            due = step(s)
+            s += 1
+        e1.record(stream)
+        segs.append((e0, e1))
+        if due:
+            events.append(fold_event())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    timed_folds = len(events)
+    # at least two fold events per run: fill the rings (untimed appends of the
+    # prepared tokens) and fold
+    while len(events) < 2:
+        for layer in range(nl):
+            room = slots - (lens[layer] - (comp[layer] - P) - P) if lens[layer] >= P else 0
+            if room > 0:
+                j = used[layer]
+                kk = k_all[layer][j: j + room].permute(1, 0, 2, 3).contiguous()
+                vv = v_all[layer][j: j + room].permute(1, 0, 2, 3).contiguous()
+                used[layer] += room
+                lens[layer] += room
+                cache.append(layer, kk, vv)
+            comp[layer] += 64
+        events.append(fold_event())
+    torch.cuda.synchronize()
+    dec_ms = sum(a.elapsed_time(b) for a, b in segs)
+    fold_ms = [a.elapsed_time(b) for a, b, _ in events]
+    sync_ms = [b.elapsed_time(c) for _, b, c in events]
+    event_ms = (sum(fold_ms) + sum(sync_ms)) / len(events)
+    # natural rate: one event per 64 steps of every instance
+    ms_per_step = dec_ms / steps + event_ms / (64 * I)
+    units = nl * B * H * 2
+
+    # ---- roofline of the decode kernel: back-to-back decode calls over the
+    # layers at their current lengths, one event pair on the decode stream
+    rl_calls = max(2 * nl, 64)
+    rl_bytes = 0
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for c in range(rl_calls):
+        layer = c % nl
+        code = lib.iskv_decode_attn(ctx, layer, ctypes.c_void_p(q_base[layer % ML]), lens[layer] - 1,
+                                    out_p)
+        if code != 0:
+            raise binding.IskvError(code, "iskv_decode_attn")
+        rl_bytes += decode_bytes(p, comp[layer] - P, lens[layer] - (comp[layer] - P))
+    r1.record(stream)
+    torch.cuda.synchronize()
+    rl_avg_ms = r0.elapsed_time(r1) / rl_calls
+    bytes_avg = rl_bytes / rl_calls
+    achieved = bytes_avg / (rl_avg_ms * 1e-3) / 1e9
+    flags = max(cache.status(i).numeric_flags for i in range(nl))
+    st = cache.status(0)
+    finite = bool(torch.isfinite(out).all().item())
+    res = {
+        "value": B * steps / (ms_per_step * steps * 1e-3),
+        "ms_per_step": ms_per_step,
+        "decode_ms_per_step": dec_ms / steps,
+        "instances_rotated": I,
+        "layers_per_step": ML,
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_attn", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": bytes_avg, "avg_launch_us": rl_avg_ms * 1e3,
+            "launches_timed": rl_calls,
+        },
+        "block_updates_per_s": units * len(fold_ms) / (sum(fold_ms) * 1e-3),
+        "block_updates_per_s_with_sync": units * len(fold_ms) / ((sum(fold_ms) + sum(sync_ms)) * 1e-3),
+        "fold_event_units": units,
+        "fold_avg_us": sum(fold_ms) / len(fold_ms) * 1e3,
+        "sync_avg_us": sum(sync_ms) / len(sync_ms) * 1e3,
+        "fold_events_timed": len(events),
+        "fold_events_in_steps": timed_folds,
+        "prefill_s": t_pre,
+        "wall_s_timed": wall,
+        "numeric_flags": flags,
+        "output_finite": finite,
+        "persistent_kv_bytes_per_instance": st.persistent_bytes // I,
+        "full_kv_bytes_per_instance": st.full_bytes // I,
+        "context_at_end": max(lens),
+    }
+    cache.destroy()
+    del cache, k_all, v_all, q_all, gen
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores, bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries=4):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(p, sample_units=2, decode_calls=3):
+    """The oracle (numpy float64, LAPACK) builds `sample_units` (sequence, KV
+    head) units of the workload to its context, folding and syncing as the
+    ring fills, then runs decode calls; with BLAS on every core of the
+    process affinity and on one thread.  One step of the workload = every
+    unit of every layer decodes, plus its fold + sync every 64 steps
+    (averaged over the build) -- scaled linearly from the sample."""
     from threadpoolctl import threadpool_limits
 
-    # the oracle is plain numpy; its BLAS calls are held to one thread so the
-    # figure is per core and reproducible
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries)
-
-
-def _cpu_baseline(context, window, rank, kv_heads, q_heads, decode_queries, sample_heads=3):
     import workloads
     from oracle import Unit
 
-    cores = 1
-    w = workloads.with_(workloads.WORKLOADS[2], window=window, rank=rank, context=context)
-    units = [Unit(w.head_dim, rank, window, context + 64, "bf16") for _ in range(sample_heads)]
-    t0 = time.perf_counter()
-    fold_t = 0.0
-    folds = 0
-    pos = 0
-    while pos < context:
-        n = min(64, context - pos)
-        k, v = workloads.tokens(w, 0, pos, n)
-        for h, u in enumerate(units):
-            for i in range(n):
-                u.append(k[0, i, h], v[0, i, h])
-        pos += n
-        for u in units:
-            if u.ready:
-                f0 = time.perf_counter()
-                u.fold()
-                u.sync()
-                fold_t += time.perf_counter() - f0
-                folds += 1
-    build_t = time.perf_counter() - t0
-    g = q_heads // kv_heads
-    d0 = time.perf_counter()
-    for s in range(decode_queries):
-        q = workloads.query(w, 0, s)[0]
-        for h, u in enumerate(units):
-            u.decode(q[h * g:(h + 1) * g], u.length - 1, 1.0 / math.sqrt(w.head_dim))
-    dec_t = (time.perf_counter() - d0) / (decode_queries * sample_heads)
-    # one decode step of the layer: kv_heads units decode; every 64 steps each
-    # unit folds + syncs at the current history length (averaged over the
-    # sample's whole growth to `context`)
-    fold_avg = fold_t / max(folds, 1)
-    step_s = kv_heads * (dec_t + fold_avg / 64.0)
+    cores = len(os.sched_getaffinity(0))
+    spectrum = "power" if p["spectrum"] == "power" else "gauss"
+    w = workloads.with_(workloads.WORKLOADS[p["id"]], window=p["window"], rank=p["rank"],
+                        context=p["context"], batch=1, kv_heads=1, q_heads=p["q"] // p["kv"],
+                        spectrum=spectrum)
+    g = p["q"] // p["kv"]
+    storage = "bf16" if p["storage"] == 1 else "f32"
+    runs = {}
+    for threads in (cores, 1):
+        with threadpool_limits(limits=threads):
+            fold_t, folds, dec_t, t0 = 0.0, 0, 0.0, time.perf_counter()
+            for su in range(sample_units):
+                u = Unit(128, p["rank"], p["window"], p["context"] + 64, storage,
+                         r_v=p["rank_v"])
+                pos = 0
+                while pos < p["context"]:
+                    n = min(64, p["context"] - pos)
+                    k = workloads.unit_tokens(w, 0, su, 0, 0, pos, n)
+                    v = workloads.unit_tokens(w, 0, su, 0, 1, pos, n)
+                    for i in range(n):
+                        u.append(k[i], v[i])
+                        if u.ready:
+                            f0 = time.perf_counter()
+                            u.fold()
+                            u.sync()
+                            fold_t += time.perf_counter() - f0
+                            folds += 1
+                    pos += n
+                d0 = time.perf_counter()
+                for s in range(decode_calls):
+                    q = workloads.query(w, 0, s)[0]
+                    u.decode(q[:g], u.length - 1, 1.0 / math.sqrt(128))
+                dec_t += (time.perf_counter() - d0) / decode_calls
+            build_t = time.perf_counter() - t0
+        n_units = p["layers"] * p["batch"] * p["kv"]
+        dec_unit = dec_t / sample_units
+        fold_unit = fold_t / max(folds, 1)
+        step_s = n_units * (dec_unit + fold_unit / 64.0)
+        runs[threads] = dict(value=p["batch"] / step_s, decode_ms_per_unit=dec_unit * 1e3,
+                             fold_sync_ms_per_unit=fold_unit * 1e3, folds=folds, build_s=build_t)
+    best = max(runs, key=lambda t: runs[t]["value"])
     return {
-        "value": 1.0 / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"{sample_heads} KV heads (K and V each) of the layer built to {context} tokens by the "
-                   f"float64 oracle ({folds} folds + syncs, {build_t:.1f} s), then {decode_queries} decode "
-                   f"calls of {g} query heads per KV head ({dec_t * 1e3:.1f} ms each); one step = "
-                   f"{kv_heads} KV heads x (decode + average fold+sync / 64); BLAS held to one thread"),
-        "oracle_decode_ms_per_head": dec_t * 1e3,
-        "oracle_fold_sync_ms_avg": fold_avg * 1e3,
+        "value": runs[best]["value"], "unit": "tokens/s", "cores": best, "kind": "oracle",
+        "sample": (f"{sample_units} (sequence, KV head) units (K and V) of the workload built to "
+                   f"{p['context']} tokens by the float64 oracle ({runs[best]['folds']} folds + syncs), "
+                   f"then {decode_calls} decode calls of {g} query heads each; one step = "
+                   f"{p['layers'] * p['batch'] * p['kv']} units x (decode + fold+sync / 64); "
+                   + ("measured" if p["id"] == 1 else "extrapolated linearly from the sample")),
+        "cpu_model": cpu_model(),
+        "by_threads": {str(t): r for t, r in runs.items()},
     }
 
+
+# ---------------------------------------------------------------------------
+# ragged batch (separate measurement)
+# ---------------------------------------------------------------------------
 
 def ragged_bench(args):
     """A ragged batch: sequence b holds about context * (b + 1) / B tokens."""
@@ -252,15 +575,18 @@ def ragged_bench(args):
 
     from rank_decode_attention_iskv_amd import binding
     torch.cuda.set_device(0)
-    H, HQ, D, R, W = 8, 32, 128, args.rank, args.window
-    B = args.batch if args.batch > 1 else 16
-    RV = args.rank_v or R
-    target = [max(1, args.context * (b + 1) // B) for b in range(B)]
+    p = preset(args, 2 if not args.context else None)
+    p["batch"] = args.batch if args.batch > 1 else 16
+    H, HQ, D, R, W = p["kv"], p["q"], 128, p["rank"], p["window"]
+    B = p["batch"]
+    RV = p["rank_v"]
+    ctx_len = p["context"]
+    target = [max(1, ctx_len * (b + 1) // B) for b in range(B)]
     steps = args.warmup + args.steps
-    cfg = binding.make_config(B, 1, H, HQ, D, R, W, args.context + steps + 64, binding.BF16,
+    cfg = binding.make_config(B, 1, H, HQ, D, R, W, ctx_len + steps + 64, binding.BF16,
                               protected_prefix=args.protected_prefix, rank_v=RV)
     cache = binding.IskvCache(cfg)
-    gen = Generator(torch, 1, B, H, D, 32, args.seed)
+    gen = Generator(torch, p, 1, args.seed)
     slots = W + 64
     length, n_c = [0] * B, [args.protected_prefix] * B
     t_pre = time.perf_counter()
@@ -279,7 +605,7 @@ def ragged_bench(args):
     torch.cuda.synchronize()
     t_pre = time.perf_counter() - t_pre
     toks = [gen.tokens(0, 1) for _ in range(steps)]
-    q_all = gen.queries(steps, HQ, D)
+    q_all = gen.queries(steps, 0)
     out = torch.empty(B, HQ, D, device="cuda")
     ones = [1] * B
     folds = 0
@@ -307,11 +633,10 @@ def ragged_bench(args):
         step(s)
     torch.cuda.synchronize()
     total_s = time.perf_counter() - t0
-    # decode roofline: back-to-back ragged decode calls at the final lengths
     calls = 64
-    rl_bytes = sum(decode_bytes(1, H, HQ, D, R, n_c[b] - args.protected_prefix,
-                                length[b] - (n_c[b] - args.protected_prefix), r_v=RV)
-                   for b in range(B))
+    pp = dict(p, batch=1)
+    rl_bytes = sum(decode_bytes(pp, n_c[b] - args.protected_prefix,
+                                length[b] - (n_c[b] - args.protected_prefix)) for b in range(B))
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     qp = [L - 1 for L in length]
@@ -324,8 +649,7 @@ def ragged_bench(args):
     achieved = rl_bytes / (avg_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC + " (ragged batch)",
-        "value": B * args.steps / total_s,
-        "unit": "tokens/s",
+        "value": B * args.steps / total_s, "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_s * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -335,8 +659,8 @@ def ragged_bench(args):
                          f"{target[0]}..{target[-1]} (spread evenly), {H} KV / {HQ} q heads, "
                          f"head_dim {D}, rank {R} (V {RV}), window {W}, bf16 storage; per step one "
                          "token per sequence (iskv_append_ragged), iskv_decode_attn_ragged, and a "
-                         "fold + sync of the sequences whose ring fills"),
-            "global_batch": B, "seq_len": args.context, "parallelism": "single GPU",
+                         "fold + sync of the sequences whose ring fills; wall-clock timing"),
+            "global_batch": B, "seq_len": ctx_len, "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm", "kernel": "decode_attn_ragged", "achieved": achieved, "peak": 8000.0,
@@ -347,6 +671,22 @@ def ragged_bench(args):
         "folds_timed": folds, "prefill_s": t_pre,
     }
     print(json.dumps(res))
+
+
+def compact(r, p):
+    return {
+        "workload": describe(p),
+        "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+        "decode_us": r["roofline"]["avg_launch_us"],
+        "roofline_frac": r["roofline"]["frac"], "achieved_GBs": r["roofline"]["achieved"],
+        "algorithmic_bytes_per_launch": r["roofline"]["algorithmic_bytes_per_launch"],
+        "instances_rotated": r["instances_rotated"],
+        "block_updates_per_s": r["block_updates_per_s"],
+        "block_updates_per_s_with_sync": r["block_updates_per_s_with_sync"],
+        "fold_avg_us": r["fold_avg_us"], "sync_avg_us": r["sync_avg_us"],
+        "fold_event_units": r["fold_event_units"],
+        "numeric_flags": r["numeric_flags"], "output_finite": r["output_finite"],
+    }
 
 
 def main():
@@ -361,255 +701,53 @@ def main():
     if args.ragged:
         ragged_bench(args)
         return
-    import torch
-
-    from rank_decode_attention_iskv_amd import binding
-
-    torch.cuda.set_device(0)
-    H, HQ, D, R, W, B = 8, 32, 128, args.rank, args.window, args.batch
-    I = args.instances
-    total_steps = args.warmup + args.steps
-    per_inst_steps = (total_steps + I - 1) // I
-    max_tokens = args.context + per_inst_steps + 64
-    P = args.protected_prefix
-    RV = args.rank_v or R
-    cfg = binding.make_config(B, I, H, HQ, D, R, W, max_tokens, binding.BF16, protected_prefix=P,
-                              rank_v=RV)
-    cache = binding.IskvCache(cfg)
-    stream = torch.cuda.current_stream()
-    gen = Generator(torch, I, B, H, D, 32, args.seed)
-
-    # ---- prefill every instance to `context` tokens (fold + sync as the ring fills)
-    t_pre = time.perf_counter()
-    length, n_c = 0, 0
-    while length < args.context:
-        n = min(64, args.context - length, (W + 64) - (length - P - n_c))
-        ready = False
-        for inst in range(I):
-            k, v = gen.tokens(inst, n)
-            ready = cache.append(inst, k, v)
-        length += n
-        if ready:
-            cache.block_update(-1)
-            cache.sync(-1)
-            n_c += 64
-    torch.cuda.synchronize()
-    t_pre = time.perf_counter() - t_pre
-
-    # ---- inputs of the timed steps, resident before timing
-    # per instance [step][batch][1][kv_heads][d], so each step's token is one
-    # contiguous [batch, 1, kv_heads, d] block
-    k_all, v_all = [], []
-    for inst in range(I):
-        k, v = gen.tokens(inst, per_inst_steps)            # [B, n, H, D]
-        k_all.append(k.permute(1, 0, 2, 3).contiguous())
-        v_all.append(v.permute(1, 0, 2, 3).contiguous())
-    q_all = gen.queries(total_steps, HQ, D)
-    out = torch.empty(B, HQ, D, device="cuda")
-    torch.cuda.synchronize()
-
-    lengths = [cache.status(i).length for i in range(I)]
-    comp = [cache.status(i).compressed for i in range(I)]
-    used = [0] * I
-    ev = []                      # (start, end, bytes) per timed decode launch
-    mstream = None
-    fold_ev, sync_ev = [], []
-    bytes_total = 0
-    folds = 0
-    n_ready = 0                  # instances whose ring is full (fold mode "layers")
-
-    # The step loop calls the C ABI directly with precomputed device pointers
-    # and pre-created events: the per-step host work must stay well below the
-    # GPU time of a step, or the timeline measures the Python loop.
-    import ctypes
-    L_ = binding.lib()
-    ctx = cache.ctx
-    tok_bytes = B * H * D * 4
-    k_base = [t.data_ptr() for t in k_all]
-    v_base = [t.data_ptr() for t in v_all]
-    q_base, q_bytes = q_all.data_ptr(), B * HQ * D * 4
-    out_p = ctypes.c_void_p(out.data_ptr())
-    ready_c = ctypes.c_int(0)
-    ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.warmup)]
-
-    def step(s, timed, warm=False):
-        nonlocal bytes_total, folds, mstream, n_ready
-        inst = s % I
-        j = used[inst]
-        used[inst] += 1
-        lengths[inst] += 1
-        L, n_c = lengths[inst], comp[inst]
-        kp = ctypes.c_void_p(k_base[inst] + j * tok_bytes)
-        vp = ctypes.c_void_p(v_base[inst] + j * tok_bytes)
-        qp = ctypes.c_void_p(q_base + s * q_bytes)
-        # append + decode attention of the step in one launch (iskv_append_decode);
-        # warm-up steps carry an event pair around it, timed steps carry none
-        if warm:
-            e0, e1 = ev_pool[len(ev)]
-            e0.record(stream)
-            code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
-                                         ctypes.byref(ready_c))
-            e1.record(stream)
-            ev.append((e0, e1, decode_bytes(B, H, HQ, D, R, n_c, L - n_c, r_v=RV)))
-        else:
-            code = L_.iskv_append_decode(ctx, inst, kp, vp, binding.F32, qp, L - 1, out_p,
-                                         ctypes.byref(ready_c))
-            bytes_total += decode_bytes(B, H, HQ, D, R, n_c, L - n_c, r_v=RV)
-        if code != 0:
-            raise binding.IskvError(code, "iskv_append_decode")
-        ready = bool(ready_c.value)
-        if not ready:
-            return
-        comp[inst] += 64
-        if args.fold_mode == "layers":
-            # every instance (layer) fills its ring at the same token; the
-            # last one's step folds them all in one launch pair
-            n_ready += 1
-            if n_ready < I:
-                return
-            n_ready = 0
-            layer, nfold = -1, I
-        else:
-            layer, nfold = inst, 1
-        if warm or (timed and (not args.async_maintenance)):
-            f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            f0.record(stream)
-            cache.block_update(layer)
-            f1.record(stream)
-            cache.sync(layer)
-            f2.record(stream)
-            fold_ev.append((f0, f1))
-            sync_ev.append((f1, f2))
-        else:
-            cache.block_update(layer)
-            cache.sync(layer)
-        folds += 0 if warm else nfold
-
-    # warm-up on one stream, with the fold and sync kernels timed by events
-    for s in range(args.warmup):
-        step(s, True, warm=True)
-    torch.cuda.synchronize()
-    if args.async_maintenance:
-        mstream = torch.cuda.Stream()
-        cache.set_maintenance_stream(mstream)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for s in range(args.warmup, total_steps):
-        step(s, True)
-    if mstream is not None:
-        cache.join_maintenance()          # the timed region ends after every fold and sync
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-
-    dec_ms = [a.elapsed_time(b) for a, b, _ in ev]          # warm-up steps only
-    dec_avg_ms = sum(dec_ms) / len(dec_ms) if dec_ms else None
-
-    # ---- roofline of the decode kernel: one event pair around back-to-back
-    # decode calls over the instances at their final lengths (the per-step
-    # event pairs above also hold the dispatch gap before each kernel)
-    rl_calls = max(4 * I, 64)
-    rl_bytes = 0
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qp = ctypes.c_void_p(q_base)
-    r0.record(stream)
-    for c in range(rl_calls):
-        inst = c % I
-        code = L_.iskv_decode_attn(ctx, inst, qp, lengths[inst] - 1, out_p)
-        if code != 0:
-            raise binding.IskvError(code, "iskv_decode_attn")
-        rl_bytes += decode_bytes(B, H, HQ, D, R, comp[inst], lengths[inst] - comp[inst], r_v=RV)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    rl_avg_ms = r0.elapsed_time(r1) / rl_calls
-    bytes_avg = rl_bytes / rl_calls
-    achieved = bytes_avg / (rl_avg_ms * 1e-3) / 1e9
-    fold_ms = [a.elapsed_time(b) for a, b in fold_ev]
-    sync_ms = [a.elapsed_time(b) for a, b in sync_ev]
-    units_per_fold = B * H * 2
-    layers_per_launch = I if args.fold_mode == "layers" else 1
-    st = cache.status(0)
-    flags = max(cache.status(i).numeric_flags for i in range(I))
-    finite = bool(torch.isfinite(out).all().item())
-    value = args.steps / (total_ms * 1e-3)
+    p = preset(args)
+    r = measure(p, args.steps, args.warmup, args.instances, args.seed)
     kh = kernel_source_hash()
-    traffic = committed_traffic(kh)
-    bw_read, bw_copy = stream_bandwidth()
-
+    r["roofline"]["traffic"] = committed_traffic(kh, p["id"])
+    copy_gbs = stream_bandwidth()
+    r["roofline"]["measured_copy_GBs"] = copy_gbs
+    r["roofline"]["frac_of_measured_copy"] = r["roofline"]["achieved"] / copy_gbs
     res = {
         "metric": METRIC,
-        "value": value,
+        "value": r.pop("value"),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / args.steps,
+        "ms_per_step": r.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if p["storage"] == 1 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"one GQA layer: {H} KV / {HQ} q heads, head_dim {D}, rank {R}, "
-                         f"{args.context}-token context (grows by 1 per step), window {W}, "
-                         f"bf16 storage, fp32 accumulate, batch {B}, block update + sync every "
-                         f"64 tokens; K/V rank-32 signal + 1% noise"
-                         + (f"; first {P} positions kept exact (protected prefix)" if P else "")
-                         + (f"; V rank {RV}" if RV != R else "")),
-            "protected_prefix": P,
-            "rank_v": RV,
-            "instances_rotated": I,
-            "global_batch": B,
-            "seq_len": args.context,
-            "parallelism": "single GPU",
-            "step_calls": ("iskv_append_decode; every 64 tokens iskv_block_update(-1) + iskv_sync(-1) "
-                           f"over all {I} instances (layers) at once" if args.fold_mode == "layers" else
-                           "iskv_append_decode; every 64 steps per instance iskv_block_update + iskv_sync"),
-            "fold_mode": args.fold_mode,
-            "maintenance": "same stream" if (not args.async_maintenance) else
-                           "second stream (each instance waits for its own fold + sync)",
+            "workload": describe(p),
+            "config_id": p["id"], "global_batch": p["batch"], "seq_len": p["context"],
+            "layers": p["layers"], "rank": p["rank"], "rank_v": p["rank_v"], "window": p["window"],
+            "protected_prefix": p["prefix"], "parallelism": "single GPU",
+            "step_calls": ("per layer iskv_append_decode; when the rings fill, iskv_block_update(-1) "
+                           "+ iskv_sync(-1) over every layer of every instance"),
+            "timing": ("decode steps timed in segments by HIP events; each fold event (block update "
+                       "+ sync) timed by its own events, at least two per run; ms_per_step = decode "
+                       "per step + fold event / (64 x instances), the natural rate"),
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_attn",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": bytes_avg,
-            "avg_launch_us": rl_avg_ms * 1e3,
-            "launches_timed": rl_calls,
-            "avg_launch_us_in_step": dec_avg_ms * 1e3 if dec_avg_ms else None,
-            "measured_stream_read_GBs": bw_read,
-            "measured_stream_copy_GBs": bw_copy,
-            "frac_of_measured_read": achieved / bw_read,
-        },
-        "decode_attn_calls_per_s_kernel_only": 1e3 / rl_avg_ms,
-        "block_updates_per_s": (units_per_fold * layers_per_launch * len(fold_ms) / (sum(fold_ms) * 1e-3))
-                               if fold_ms else None,
-        "block_updates_per_s_with_sync": (units_per_fold * layers_per_launch * len(fold_ms) /
-                                          ((sum(fold_ms) + sum(sync_ms)) * 1e-3)) if fold_ms else None,
-        "fold_launch_layers": layers_per_launch,
-        "fold_avg_us": (sum(fold_ms) / len(fold_ms) * 1e3) if fold_ms else None,
-        "sync_avg_us": (sum(sync_ms) / len(sync_ms) * 1e3) if sync_ms else None,
-        "timed_folds": folds,
-        "prefill_s": t_pre,
-        "wall_s_timed": wall,
-        "numeric_flags": flags,
-        "output_finite": finite,
-        "kernel_sources_sha256_16": kh,
-        "persistent_kv_bytes_per_instance": st.persistent_bytes // I,
-        "full_kv_bytes_per_instance": st.full_bytes // I,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.context, W, R, H, HQ)
-    else:
-        res["cpu_baseline"] = None
+    res["roofline"] = r.pop("roofline")
+    res.update(r)
+    res["kernel_sources_sha256_16"] = kh
+    if p["id"] == 3 and not args.no_extras and not (args.context or args.rank or args.window or args.batch):
+        extras = {}
+        p2 = preset(args, 2)
+        extras["config2"] = compact(measure(p2, 128, 16, 0, args.seed + 2, quiet=True), p2)
+        pts = []
+        for rank, window in SWEEP5:
+            p5 = preset(args, 5, rank=rank, rank_v=rank, window=window)
+            pts.append(dict(rank=rank, window=window, **compact(measure(p5, 32, 8, 0, args.seed + 5,
+                                                                        quiet=True), p5)))
+        extras["config5_sweep"] = pts
+        res["extras"] = extras
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(p)
     print(json.dumps(res), flush=True)
 
 

@@ -330,20 +330,29 @@ def unpack_state(cfg: Config, blob):
 
 
 def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
-    """Inverse of unpack_state; units[u][x] holds basis, S, coef (rows by
-    position), ring and, with a protected prefix, prefix arrays."""
+    """Inverse of unpack_state; units (any iterable, consumed once, one entry
+    per unit in order) gives units[u][x] with basis, S, coef (rows by
+    position), ring and, with a protected prefix, prefix arrays.  The blob is
+    filled in place, so a generator of units never holds more than one unit."""
     import numpy as np
-    parts = [np.array([length, n_c], dtype=np.int64).tobytes()]
     d, T, S = cfg.head_dim, cfg.max_tokens, cfg.window + cfg.block
     ranks = factor_ranks(cfg)
     Pp = cfg.protected_prefix
+    blob = bytearray(state_bytes(cfg))
+    np.frombuffer(blob, dtype=np.int64, count=2)[:] = (length, n_c)
+    f = np.frombuffer(blob, dtype=np.float32, offset=16)
+    o = 0
     for xs in units:
         for r, x in zip(ranks, xs):
-            C = np.zeros((T, r), dtype=np.float32)
-            C[: x["coef"].shape[0]] = x["coef"][:T]
-            parts += [np.asarray(x["basis"], np.float32).reshape(d, r).tobytes(),
-                      np.asarray(x["S"], np.float32).reshape(r).tobytes(),
-                      C.tobytes(), np.asarray(x["ring"], np.float32).reshape(S, d).tobytes()]
+            f[o: o + d * r] = np.asarray(x["basis"], np.float32).reshape(d * r); o += d * r
+            f[o: o + r] = np.asarray(x["S"], np.float32).reshape(r); o += r
+            C = np.asarray(x["coef"], np.float32)[:T]
+            f[o: o + C.size] = C.reshape(-1)
+            f[o + C.size: o + T * r] = 0.0
+            o += T * r
+            f[o: o + S * d] = np.asarray(x["ring"], np.float32).reshape(S * d); o += S * d
             if Pp:
-                parts.append(np.asarray(x["prefix"], np.float32).reshape(Pp, d).tobytes())
-    return bytearray(b"".join(parts))
+                f[o: o + Pp * d] = np.asarray(x["prefix"], np.float32).reshape(Pp * d); o += Pp * d
+    if o != f.size:
+        raise ValueError("state blob: wrong number of units")
+    return blob

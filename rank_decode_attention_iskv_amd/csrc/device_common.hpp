@@ -86,6 +86,21 @@ __device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned 
   lo = __builtin_bit_cast(unsigned, l);
 }
 
+// (a, b) -> three packed bf16 parts: hi + mid + lo represents each value to
+// ~2^-24 relative (every float whose exponent leaves room for the low part).
+__device__ __forceinline__ void split3(float a, float b, unsigned &hi, unsigned &mid, unsigned &lo) {
+  const bf16x2 h = __builtin_convertvector((floatx2){a, b}, bf16x2);
+  const unsigned hb = __builtin_bit_cast(unsigned, h);
+  const float ra = a - __uint_as_float(hb << 16), rb = b - __uint_as_float(hb & 0xffff0000u);
+  const bf16x2 m = __builtin_convertvector((floatx2){ra, rb}, bf16x2);
+  const unsigned mb = __builtin_bit_cast(unsigned, m);
+  const bf16x2 l = __builtin_convertvector(
+      (floatx2){ra - __uint_as_float(mb << 16), rb - __uint_as_float(mb & 0xffff0000u)}, bf16x2);
+  hi = hb;
+  mid = mb;
+  lo = __builtin_bit_cast(unsigned, l);
+}
+
 // The same split with each residual x - hi(x) from one v_dot2c_f32_bf16: the
 // packed high parts dotted with bf16 (-1, 0) or (0, -1) and accumulated onto
 // x (exact: the products and the sum are exact in fp32).  The two constant

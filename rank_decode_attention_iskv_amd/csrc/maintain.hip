@@ -121,9 +121,12 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // basis).  An N x r by r x r product, streamed once through HBM.
 //
 // bf16 storage: MFMA.  Each wave takes 8 (4 at r = 128) tiles of 16 rows
-// and computes C_new^T = M^T C^T: A operand = M^T as bf16 high + low parts
-// (M = hi + lo to ~2^-16, so C M is exact to float accumulation), B operand =
-// 16 coefficient rows as stored (exact bf16), output rounded once to bf16.
+// and computes C_new^T = M^T C^T: A operand = M^T as three bf16 parts
+// (M = hi + mid + lo to ~2^-24, i.e. M as an fp32 value; with two parts the
+// ~2^-17 representation error of M moved one rounding of C M in a few
+// hundred to the neighbouring bf16 value, which accumulates sync after sync),
+// B operand = 16 coefficient rows as stored (exact bf16), so every product is
+// exact and the output is rounded once to bf16.
 // f32 storage: one row per thread on the vector ALUs.
 // grid (row tiles, units (one factor) or units*2 (both), layers)
 // ---------------------------------------------------------------------------
@@ -166,18 +169,19 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    // A operand: M^T rows mb*16 + n, high and low bf16 parts
-    uint4_ ahi[KB], alo[KB];
+    // A operand: M^T rows mb*16 + n, as high, middle and low bf16 parts
+    uint4_ ahi[KB], amid[KB], alo[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       constexpr int PAIRS = R >= 32 ? 4 : 2;
-      unsigned h[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+      unsigned h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < PAIRS; ++i) {
         const int c = R >= 32 ? kb * 32 + 8 * rho + 2 * i : 4 * rho + 2 * i;
-        split2(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], lo[i]);
+        split3(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], md[i], lo[i]);
       }
       ahi[kb] = uint4_{h[0], h[1], h[2], h[3]};
+      amid[kb] = uint4_{md[0], md[1], md[2], md[3]};
       alo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
     }
 #pragma unroll
@@ -185,13 +189,17 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
       floatx4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
+        // smallest parts first: they are added to the accumulator while it
+        // is still small
         if constexpr (R >= 32) {
-          acc = mfma32(ahi[kb], b[t][kb], acc);
           acc = mfma32(alo[kb], b[t][kb], acc);
+          acc = mfma32(amid[kb], b[t][kb], acc);
+          acc = mfma32(ahi[kb], b[t][kb], acc);
         } else {
           const uint2_ bb{b[t][kb].x, b[t][kb].y};
-          acc = mfma16(uint2_{ahi[kb].x, ahi[kb].y}, bb, acc);
           acc = mfma16(uint2_{alo[kb].x, alo[kb].y}, bb, acc);
+          acc = mfma16(uint2_{amid[kb].x, amid[kb].y}, bb, acc);
+          acc = mfma16(uint2_{ahi[kb].x, ahi[kb].y}, bb, acc);
         }
       }
       const int64_t tok = base + 16 * t + n;

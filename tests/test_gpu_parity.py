@@ -132,11 +132,10 @@ def test_end_to_end_fp32_config1_shape():
 
 
 def test_end_to_end_bf16_gqa_quality():
-    """bf16 storage, 24 folds through the GPU.  Independent bf16 re-rounding at
-    every sync makes any two implementations drift apart like a random walk
-    (two oracle runs whose M differs by 1e-6 already differ by ~1e-3 after 20
-    folds), so the end-to-end check is on quality: the GPU's error against
-    uncompressed attention is no worse than the oracle's."""
+    """bf16 storage, 24 folds through the GPU: the GPU's error against
+    uncompressed attention is no worse than the oracle's.  (The distance
+    between the two, which bf16 re-rounding makes grow fold after fold, is
+    bounded in tests/test_gpu_fold_numerics.py by the walk pinned on the CPU.)"""
     w = small(2, kv_heads=2, q_heads=8, window=256)
     L = 64 * 24 + 40
     p = Pair(w, max_tokens=4096)
@@ -148,7 +147,6 @@ def test_end_to_end_bf16_gqa_quality():
         exact = exact_attention(w, L, q, L - 1)
         e_gpu, e_ora = rel_err_per_head(got, exact), rel_err_per_head(ora, exact)
         assert e_gpu < 1.5 * e_ora + 2e-3, (e_gpu, e_ora)
-        assert rel_err_per_head(got, ora) < 2e-2
     _, _, units = p.state(0)
     for u in units:
         for x in u:
@@ -196,8 +194,12 @@ def test_fold_and_sync_on_imported_oracle_state(wid, kw, folds):
             np.testing.assert_allclose(units[ui][x]["S"][:k], s[:k], rtol=1e-4, atol=1e-5 * s[0])
             H_gpu = units[ui][x]["coef"][:n_c].astype(np.float64) @ B.T
             H_ora = f.C[:n_c] @ f.B.T
-            tol = 1e-4 if w.storage == "f32" else 4e-3
-            assert np.linalg.norm(H_gpu - H_ora) / np.linalg.norm(H_ora) < tol
+            # bf16: one fold on identical state agrees to the float32 level of
+            # the fold (measured <= 3.4e-4 at r = 32, 1-12 folds)
+            tol = 1e-4 if w.storage == "f32" else 1e-3
+            err = np.linalg.norm(H_gpu - H_ora) / np.linalg.norm(H_ora)
+            print(f"{w.storage} r={r} folds={folds} history error {err:.2e}")
+            assert err < tol
     for step, q_pos in enumerate([L - 1, L + 3]):
         q = q32(workloads.query(w, 0, step))
         got = p.decode(0, q, q_pos)
@@ -594,10 +596,12 @@ def test_separate_v_rank_fold_and_sync_on_imported_state(wid, kw, rv):
             # data is not, so it is checked through the rebuilt history only
             S = np.asarray(f.S)
             k = 1 + int(np.argmax((S[:-1] - S[1:]) / S[0]))
-            assert subspace_dist(B[:, :k], f.B[:, :k]) < (1e-4 if w.storage == "f32" else 2e-2), k
+            # the ring rows are identical on both sides, so the subspace agrees
+            # to float32 level in either storage
+            assert subspace_dist(B[:, :k], f.B[:, :k]) < 1e-4, k
             H_gpu = units[ui][x]["coef"][: ou.n_c].astype(np.float64) @ B.T
             H_ora = f.C[: ou.n_c] @ f.B.T
-            tol = 1e-4 if w.storage == "f32" else 2e-2
+            tol = 1e-4 if w.storage == "f32" else 1e-3
             assert np.linalg.norm(H_gpu - H_ora) / np.linalg.norm(H_ora) < tol
     for step, q_pos in enumerate([L - 1, L + 3]):
         q = q32(workloads.query(w, 0, step))

@@ -386,6 +386,39 @@ def test_persistent_bytes_full_rank_window_only():
     assert kept - full == 2 * 4 * 2 * (128 * 32 * 4 + 32 * 4)
 
 
+def test_persistent_bytes_counts_the_arrays_a_unit_keeps():
+    """The byte model against a count of what an oracle unit actually stores
+    after a stream (protected prefix, several folds, a ragged ring, r_V != r_K):
+    coefficient rows that hold data, basis and singular-value entries, and the
+    exact rows decode reads (positions written below P or at or after the
+    compressed end).  Counted from the arrays and a log of the writes, not from
+    the formula."""
+    rng = np.random.default_rng(23)
+    d, r, rv, window, P = 128, 16, 32, 64, 64
+    L = P + 64 * 5 + 37
+    u = Unit(d, r, window, L + 64, "bf16", prefix=P, r_v=rv)
+    written = []
+    for f in (u.K, u.V):
+        orig = f.write
+
+        def logged(pos, x, orig=orig, log=written):
+            log.append(pos)
+            orig(pos, x)
+        f.write = logged
+    for t in range(L):
+        u.append(rng.standard_normal(d), rng.standard_normal(d))
+        if u.ready:
+            u.fold()
+            u.sync()
+    live = {p for p in written if p < P or p >= u.n_c}
+    counted = 0
+    for f, rf in ((u.K, r), (u.V, rv)):
+        held = int(np.sum(np.any(f.C != 0.0, axis=1)))        # coefficient rows with data
+        assert held == u.n_c - P and f.C.shape[1] == rf
+        counted += held * rf * 2 + (f.B.size + f.S.size) * 4 + len(live) * d * 2
+    assert counted == persistent_kv_bytes(u.n_c - P, len(live), 1, 1, d, r, 2, rank_v=rv)
+
+
 # ---------------------------------------------------------------------------
 # Brand step alone: the single-block special case is a truncated SVD
 # ---------------------------------------------------------------------------

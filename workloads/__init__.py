@@ -174,36 +174,47 @@ def _bf16_grid(x: np.ndarray) -> np.ndarray:
     return u.view(np.float32)
 
 
-def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: int = 7,
-                    rank_v: int = 0):
-    """A random cache state of the workload's shapes, for decode-only checks at
-    full size without running the folds that would build it: per (sequence,
-    KV head) and K|V, an orthonormal d x r basis (QR of a Gaussian matrix),
-    singular values, coefficient rows [0, n_c) and ring rows for the exact
-    positions [n_c, length) at slot p mod (window + 64).  With bf16 storage the
-    coefficients and ring rows are drawn on the bf16 grid.
+def synthetic_unit(w: Workload, b: int, h: int, length: int, n_c: int, max_tokens: int,
+                   seed: int = 7, rank_v: int = 0, ring_in_span: bool = False):
+    """One (sequence b, KV head h) of a random cache state of the workload's
+    shapes, for checks at full size without running the folds that would build
+    it: per K|V an orthonormal d x r basis (QR of a Gaussian matrix), singular
+    values, coefficient rows [0, n_c) and ring rows for the exact positions
+    [n_c, length) at slot p mod (window + 64).  With bf16 storage the
+    coefficients and ring rows are drawn on the bf16 grid.  ring_in_span: ring
+    rows lie in the span of the basis (plus 1e-3 noise), so that a fold of the
+    state has a well separated rank-r truncation.
 
-    Returns a list over units (b * kv_heads + h) of [K, V] dicts with keys
-    basis, S, coef (max_tokens x r), ring ((window + 64) x d).  rank_v > 0
-    gives the V factor that rank instead of w.rank."""
+    Returns [K, V] dicts with keys basis, S, coef (max_tokens x r), ring
+    ((window + 64) x d).  rank_v > 0 gives the V factor that rank instead of
+    w.rank."""
     d, slots = w.head_dim, w.window + 64
-    assert n_c % 64 == 0 and w.window <= length - n_c <= w.window + 63
-    units = []
-    for b in range(w.batch):
-        for h in range(w.kv_heads):
-            xs = []
-            for x in range(2):
-                r = (rank_v or w.rank) if x else w.rank
-                rng = _rng(w, 9001, seed, b, h, x)          # 9001: state stream tag
-                B, _ = np.linalg.qr(rng.standard_normal((d, r)))
-                S = np.sort(rng.uniform(1.0, 50.0, r))[::-1].astype(np.float32)
-                C = np.zeros((max_tokens, r), np.float32)
-                C[:n_c] = rng.standard_normal((n_c, r)).astype(np.float32) * (2.0 / np.sqrt(r))
-                ring = np.zeros((slots, d), np.float32)
-                for p in range(n_c, length):
-                    ring[p % slots] = rng.standard_normal(d).astype(np.float32) * 0.25
-                if w.storage == "bf16":
-                    C, ring = _bf16_grid(C), _bf16_grid(ring)
-                xs.append(dict(basis=B.astype(np.float32), S=S, coef=C, ring=ring))
-            units.append(xs)
-    return units
+    assert n_c % 64 == 0 and w.window <= length - n_c <= w.window + 64
+    xs = []
+    for x in range(2):
+        r = (rank_v or w.rank) if x else w.rank
+        rng = _rng(w, 9001, seed, b, h, x)          # 9001: state stream tag
+        B, _ = np.linalg.qr(rng.standard_normal((d, r)))
+        S = np.sort(rng.uniform(1.0, 50.0, r))[::-1].astype(np.float32)
+        C = np.zeros((max_tokens, r), np.float32)
+        C[:n_c] = rng.standard_normal((n_c, r)).astype(np.float32) * (2.0 / np.sqrt(r))
+        ring = np.zeros((slots, d), np.float32)
+        pos = np.arange(n_c, length)
+        if ring_in_span:
+            z = rng.standard_normal((len(pos), r)) * (2.0 / np.sqrt(r))
+            rows = z @ B.T + 1e-3 * rng.standard_normal((len(pos), d))
+        else:
+            rows = rng.standard_normal((len(pos), d)) * 0.25
+        ring[pos % slots] = rows.astype(np.float32)
+        if w.storage == "bf16":
+            C, ring = _bf16_grid(C), _bf16_grid(ring)
+        xs.append(dict(basis=B.astype(np.float32), S=S, coef=C, ring=ring))
+    return xs
+
+
+def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: int = 7,
+                    rank_v: int = 0, ring_in_span: bool = False):
+    """synthetic_unit for every (sequence, KV head), as a list over units
+    (b * kv_heads + h)."""
+    return [synthetic_unit(w, b, h, length, n_c, max_tokens, seed, rank_v, ring_in_span)
+            for b in range(w.batch) for h in range(w.kv_heads)]
