@@ -63,7 +63,9 @@ enum {
   ISKV_ESTATE = -2,   /* verb not allowed in the current state */
   ISKV_ENOMEM = -3,   /* workspace smaller than iskv_workspace_bytes() */
   ISKV_EDEVICE = -4,  /* HIP runtime error */
-  ISKV_ENUMERIC = -5  /* device-side numeric flag raised (see iskv_status) */
+  ISKV_ENUMERIC = -5, /* device-side numeric flag raised (see iskv_status) */
+  ISKV_ESCRATCH = -6  /* iskv_decode_attn_noalloc: the configuration's split
+                         records exceed its static array */
 };
 
 /* Device numeric flags reported in iskv_status_t.numeric_flags. */
@@ -186,6 +188,25 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
  * each new token enters the exact window and is attended to at once]. */
 int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int in_dtype,
                        const float *dev_q, int64_t q_pos, float *dev_out, int *blocks_ready);
+
+/* iskv_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels, arguments, results (bit for bit), and errors, but the
+ * split-K partial records and merge counters live in a file-scope device
+ * array of the library (32 MiB per GPU, held until the process ends) instead
+ * of the context's workspace.  Nothing is allocated or freed by the call.
+ * The array's address is looked up once per device by iskv_init.  Limit:
+ * iskv_noalloc_scratch_bytes(cfg) must be <= 32 MiB (else ISKV_ESCRATCH;
+ * with 8 KV heads: batch <= 126 at 4 query heads per KV head, <= 63 at 8).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other contexts, other threads) race and must be ordered by
+ * the caller. */
+int iskv_decode_attn_noalloc(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos,
+                             float *dev_out);
+
+/* Bytes of the static array that iskv_decode_attn_noalloc needs for cfg (0 if
+ * cfg is invalid). */
+size_t iskv_noalloc_scratch_bytes(const iskv_config *cfg);
 
 /* Synchronizes the stream; fills *st for one layer.  Returns ISKV_ENUMERIC if
  * any numeric flag is set (st is still filled), else ISKV_OK. */

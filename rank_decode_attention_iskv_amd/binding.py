@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libiskv.so")
 
 F32, BF16 = 0, 1
-OK, EINVAL, ESTATE, ENOMEM, EDEVICE, ENUMERIC = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ESTATE, ENOMEM, EDEVICE, ENUMERIC, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 FLAG_NONFINITE_CORE, FLAG_JACOBI_CAP, FLAG_NONFINITE_INPUT = 1, 2, 4
 
 
@@ -50,6 +50,7 @@ EXPORTED = (
     "iskv_append_decode", "iskv_status", "iskv_export_state", "iskv_import_state", "iskv_set_maintenance_stream",
     "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
     "iskv_append_ragged", "iskv_decode_attn_ragged", "iskv_seq_status",
+    "iskv_decode_attn_noalloc", "iskv_noalloc_scratch_bytes",
 )
 
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_append_ragged": (I, [P, I, P, P, I, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(I)]),
         "iskv_decode_attn_ragged": (I, [P, I, P, ctypes.POINTER(I64), P]),
         "iskv_seq_status": (I, [P, I, I, ctypes.POINTER(Status)]),
+        "iskv_decode_attn_noalloc": (I, [P, I, P, I64, P]),
+        "iskv_noalloc_scratch_bytes": (SZ, [cfgp]),
         "iskv_destroy": (I, [P]),
         "iskv_strerror": (ctypes.c_char_p, [I]),
     }
@@ -131,6 +134,10 @@ def workspace_bytes(cfg: Config) -> int:
 
 def state_bytes(cfg: Config) -> int:
     return lib().iskv_state_bytes(ctypes.byref(cfg))
+
+
+def noalloc_scratch_bytes(cfg: Config) -> int:
+    return lib().iskv_noalloc_scratch_bytes(ctypes.byref(cfg))
 
 
 def _ptr(t) -> int:
@@ -190,6 +197,19 @@ class IskvCache:
         _check(lib().iskv_decode_attn(self.ctx, layer, ctypes.c_void_p(q.data_ptr()),
                                       int(q_pos), ctypes.c_void_p(out.data_ptr())),
                "iskv_decode_attn")
+        return out
+
+    def decode_attn_noalloc(self, layer: int, q, q_pos: int, out):
+        """decode_attn with the split records in the library's static device
+        array (allocates nothing)."""
+        torch = self.torch
+        if q.dtype != torch.float32 or out.dtype != torch.float32:
+            raise ValueError("q and out must be float32")
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        _check(lib().iskv_decode_attn_noalloc(self.ctx, layer, ctypes.c_void_p(q.data_ptr()),
+                                              int(q_pos), ctypes.c_void_p(out.data_ptr())),
+               "iskv_decode_attn_noalloc")
         return out
 
     def append_decode(self, layer: int, k, v, q, q_pos: int, out) -> bool:

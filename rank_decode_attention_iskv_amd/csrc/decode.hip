@@ -38,6 +38,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_runtime.h>
@@ -1196,6 +1197,45 @@ hipError_t dispatch_decode(const Model &M, int layer, const float *q, int64_t q_
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Split records of the allocation-free decode entry point: a file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// uses only the address hipGetSymbolAddress returns for the current device.
+// Its merge counters start at zero when the code object loads and every
+// completed decode call leaves them at zero again (the merging workgroup
+// resets its unit's counter), so no per-call clear is needed; calls that
+// overlap on one GPU would share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device) return hipErrorInvalidDevice;
+  void *ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void *scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                          int64_t length, int64_t n_c, hipStream_t s, FusedAppend app) {

@@ -388,7 +388,9 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
       step[((size_t)o * 64 + i) * 2 + 1] = (float)std::sin(ang);
     }
   }
-  hipError_t e = hipMemsetAsync(dev_ws, 0, c->G.total, c->stream);
+  // the allocation-free decode's split records (one lookup per device)
+  hipError_t e = scratch_setup(c->device);
+  if (e == hipSuccess) e = hipMemsetAsync(dev_ws, 0, c->G.total, c->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(base + c->G.rope_anchor, anchor.data(), anchor.size() * 4,
                        hipMemcpyHostToDevice, c->stream);
@@ -565,6 +567,30 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
   if (L.length <= 0) return ISKV_ESTATE;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
+}
+
+int iskv_decode_attn_noalloc(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos,
+                             float *dev_out) {
+  if (!c || check_layer(c, layer) || !dev_q || !dev_out) return ISKV_EINVAL;
+  if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
+  const RecLayout R = rec_layout(c->D);
+  if (R.bytes > kScratchBytes) return ISKV_ESCRATCH;
+  LayerState &L = c->layers[layer];
+  if (!make_uniform(L)) return ISKV_ESTATE;
+  if (L.length <= 0) return ISKV_ESTATE;
+  uint8_t *base = reinterpret_cast<uint8_t *>(scratch_address(c->device));
+  if (!base) return ISKV_EDEVICE;
+  Model M = c->M;
+  M.sh.rec = reinterpret_cast<float *>(base + R.rec);
+  M.sh.recml = reinterpret_cast<float *>(base + R.recml);
+  M.sh.cnt = reinterpret_cast<unsigned *>(base + R.cnt);
+  if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
+  return hip_err(launch_decode(M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
+}
+
+size_t iskv_noalloc_scratch_bytes(const iskv_config *cfg) {
+  if (!valid_config(cfg)) return 0;
+  return rec_layout(make_dims(cfg)).bytes;
 }
 
 int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int in_dtype,
@@ -858,6 +884,9 @@ const char *iskv_strerror(int code) {
     case ISKV_ENOMEM: return "workspace too small";
     case ISKV_EDEVICE: return "HIP runtime error";
     case ISKV_ENUMERIC: return "device numeric flag raised";
+    case ISKV_ESCRATCH:
+      return "configuration needs more split-record memory than the allocation-free decode's "
+             "static array holds (see iskv_noalloc_scratch_bytes)";
   }
   return "unknown error";
 }

@@ -202,6 +202,29 @@ struct FusedAppend {
 hipError_t launch_decode(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                          int64_t length, int64_t n_c, hipStream_t s, FusedAppend app = FusedAppend{});
 
+// Allocation-free decode: the split records live in a file-scope device
+// array of kScratchBytes (decode.hip).  scratch_setup looks its address up
+// once per device (that device current); scratch_address returns it (null
+// before setup).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_setup(int device);
+void *scratch_address(int device);
+
+// Bytes of the split records (rec, recml, cnt) a decode call of D uses, and
+// their offsets when carved from one buffer.
+struct RecLayout {
+  size_t rec, recml, cnt, bytes;
+};
+inline RecLayout rec_layout(const Dims &D) {
+  RecLayout R{};
+  size_t o = 0;
+  R.rec = o;   o = align_up(o + (size_t)D.units * D.max_rec * D.group * kRecStride * 4);
+  R.recml = o; o = align_up(o + (size_t)D.units * D.max_rec * D.group * 2 * 4);
+  R.cnt = o;   o = align_up(o + (size_t)D.units * 4);
+  R.bytes = o;
+  return R;
+}
+
 // Decode attention over a ragged batch: tab (n == batch) holds every
 // sequence's length, compressed end and query position.
 hipError_t launch_decode_ragged(const Model &M, int layer, const float *q, float *out,
