@@ -144,6 +144,21 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
 #endif
 }
 
+// LDS transpose read (ds_read_b64_tr_b16) of a bf16 tile.  Within each group
+// of 16 lanes, slot i of lane j receives element j % 4 of the 8 bytes that
+// lane 4 i + j / 4 of the group addresses.  A lane addressing row
+// 4 (lane / 16) + (lane % 16) / 4, columns 4 (lane % 4) .. + 3 of a
+// row-major [token][coefficient] tile thus receives tokens 4 (lane / 16) ..
+// + 3 of column lane % 16: the B operand of a 16x16x16 MFMA whose K index is
+// the token.  (Layout checked with a probe kernel on gfx950.)
+template <typename T>
+__device__ __forceinline__ uint2_ lds_read_tr16(const T *p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4 *)(reinterpret_cast<const void *>(p)));
+  return __builtin_bit_cast(uint2_, v);
+}
+
 // s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -830,18 +845,16 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
       const floatx4 sc = rope_scores(ka);
       float p[4];
       softmax_tile<NBV>(sc, 0xf, m, l, vacc, rho, p);
-      // values: C_V tokens 4*rho..+3 of coefficient 16*nb + n16, transposed reads
+      // values: the B operand (C_V tokens 4*rho..+3 of coefficient 16*nb +
+      // n16) straight from the row-major tile by the LDS transpose read
       if constexpr (BF) {
         unsigned h0, l0, h1, l1;
         split2(p[0], p[1], h0, l0, sk);
         split2(p[2], p[3], h1, l1, sk);
-        const uint16_t *tl = reinterpret_cast<const uint16_t *>(tv);
+        const T *vsrc = tv + (4 * rho + (n16 >> 2)) * RV + 4 * (n16 & 3);
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) {
-          const int c = 16 * nb + n16;
-          const unsigned x0 = tl[(4 * rho + 0) * RV + c], x1 = tl[(4 * rho + 1) * RV + c];
-          const unsigned x2 = tl[(4 * rho + 2) * RV + c], x3 = tl[(4 * rho + 3) * RV + c];
-          const uint2_ v = {x0 | (x1 << 16), x2 | (x3 << 16)};
+          const uint2_ v = lds_read_tr16(vsrc + 16 * nb);
           vacc[nb] = mfma16(uint2_{h0, h1}, v, vacc[nb]);
           vacc[nb] = mfma16(uint2_{l0, l1}, v, vacc[nb]);
         }
