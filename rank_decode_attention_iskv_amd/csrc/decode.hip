@@ -61,8 +61,16 @@ struct SplitPlan {
   int win_len;       // tokens per window split (multiple of 16)
   int n_pre;         // splits over the protected prefix (positions 0 .. P-1)
   int pre_len;       // tokens per prefix split (multiple of 16)
+  int win_rides;     // 1: n_win == n_comp and window split i is handled by the
+                     // workgroup of compressed split i, after its compressed
+                     // range (no workgroups of their own)
   // records: compressed splits first, then prefix splits, then window splits
 };
+
+// workgroups of one unit under a plan
+__host__ __device__ inline int plan_workgroups(const SplitPlan &p) {
+  return p.n_comp + p.n_pre + (p.win_rides ? 0 : p.n_win);
+}
 
 // A ragged batch's plans, one per sequence: blockIdx.x runs over the
 // sequences' splits in order (sequence b owns off[b] .. off[b+1]-1), so each
@@ -73,6 +81,7 @@ struct SeqPlans {
   int32_t off[kMaxSeqTab + 1];
   int16_t n_comp[kMaxSeqTab], n_pre[kMaxSeqTab], n_win[kMaxSeqTab];
   int32_t comp_len[kMaxSeqTab], pre_len[kMaxSeqTab], win_len[kMaxSeqTab];
+  uint8_t win_rides[kMaxSeqTab];
 };
 
 __host__ __device__ inline SplitPlan seq_plan(const SeqPlans &sp, int b) {
@@ -81,6 +90,7 @@ __host__ __device__ inline SplitPlan seq_plan(const SeqPlans &sp, int b) {
   p.comp_len = sp.comp_len[b];
   p.n_win = sp.n_win[b];
   p.win_len = sp.win_len[b];
+  p.win_rides = sp.win_rides[b];
   p.n_pre = sp.n_pre[b];
   p.pre_len = sp.pre_len[b];
   return p;
@@ -151,12 +161,36 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
 // row-major [token][coefficient] tile thus receives tokens 4 (lane / 16) ..
 // + 3 of column lane % 16: the B operand of a 16x16x16 MFMA whose K index is
 // the token.  (Layout checked with a probe kernel on gfx950.)
-template <typename T>
-__device__ __forceinline__ uint2_ lds_read_tr16(const T *p) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4 *)(reinterpret_cast<const void *>(p)));
-  return __builtin_bit_cast(uint2_, v);
+// N such reads at 32-byte steps from p (the B operands of N consecutive
+// 16-column blocks), issued together and completed in the same asm block.
+// (Through the builtin, the compiler cannot tell that these reads miss the
+// LDS DMA writes still in flight into other ring slots and drains all of
+// them first: a full memory latency per tile.)
+template <int N, typename T>
+__device__ __forceinline__ void lds_read_tr16(const T *p, uint2_ (&v)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "blocks per read group");
+  const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void *)(
+      reinterpret_cast<const void *>(p));
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b64_tr_b16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a));
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:32\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&v"(v[0]), "=&v"(v[1]) : "v"(a));
+  } else if constexpr (N == 4) {
+    asm volatile("ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:32\n\t"
+                 "ds_read_b64_tr_b16 %2, %4 offset:64\n\tds_read_b64_tr_b16 %3, %4 offset:96\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a));
+  } else {
+    asm volatile("ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+                 "ds_read_b64_tr_b16 %2, %8 offset:64\n\tds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+                 "ds_read_b64_tr_b16 %4, %8 offset:128\n\tds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+                 "ds_read_b64_tr_b16 %6, %8 offset:192\n\tds_read_b64_tr_b16 %7, %8 offset:224\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7])
+                 : "v"(a));
+  }
 }
 
 // s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
@@ -516,55 +550,16 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   const int64_t length = tab.n ? (int64_t)tab.len[b] : length_arg;
   const int64_t n_c = tab.n ? (int64_t)tab.nc[b] : n_c_arg;
   const int64_t q_pos = tab.n ? (int64_t)tab.aux[b] : q_pos_arg;
-  const bool comp = split < plan.n_comp;
+  // a compressed workgroup (split < n_comp) may also take window split
+  // `split` after its compressed range (plan.win_rides): two parts, each
+  // with its own record
+  const bool cwg = split < plan.n_comp;
   const int xs = split - plan.n_comp;                    // exact split index
-  const bool pre = !comp && xs < plan.n_pre;             // a protected-prefix split
-
-  int64_t r_begin, r_end;
-  if (comp) {
-    r_begin = D.prefix + (int64_t)split * plan.comp_len;
-    r_end = r_begin + plan.comp_len < n_c ? r_begin + plan.comp_len : n_c;
-  } else if (pre) {
-    const int64_t pend = length < D.prefix ? length : D.prefix;
-    r_begin = (int64_t)xs * plan.pre_len;
-    r_end = r_begin + plan.pre_len < pend ? r_begin + plan.pre_len : pend;
-  } else {
-    r_begin = n_c + (int64_t)(xs - plan.n_pre) * plan.win_len;
-    r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
-  }
-  if (r_end < r_begin) r_end = r_begin;
-  const int ntiles = (int)((r_end - r_begin + 15) / 16);
-  // even split: the first ntiles % NW waves take one tile more (waves w and
-  // w + NW/2 share a SIMD, so every SIMD gets the same count within one)
-  const int tb = ntiles / NW, tx = ntiles % NW;
-  const int tile_lo = wave * tb + (wave < tx ? wave : tx);
-  const int tile_hi = tile_lo + tb + (wave < tx ? 1 : 0);
-  const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
-  const int nt = __builtin_amdgcn_readfirstlane(tile_hi - tile_lo);   // wave-uniform
+  const int nparts = (cwg && plan.win_rides) ? 2 : 1;
 
   LayerPtrs P = layer_ptrs(M, layer);
 
   const SplitK sk = split_consts();
-
-  // ---- RoPE angle state of the lane's token for its 16 frequencies; the
-  // table loads (anchor_issue) and the products (anchor_finish) are apart so
-  // the prologue issues every load before its first wait
-  float cs_c[16], cs_s[16];          // separate arrays: no 64-bit register pairs
-  float2 an_A[16], an_B[16];
-  auto anchor_issue = [&](int64_t t) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rope_load(M.sh, t, 16 * mb + 4 * rho + i, an_A[mb * 4 + i], an_B[mb * 4 + i]);
-  };
-  auto anchor_finish = [&]() {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) rope_combine(an_A[j], an_B[j], cs_c[j], cs_s[j]);
-  };
-  auto anchor = [&](int64_t t) {
-    anchor_issue(t);
-    anchor_finish();
-  };
 
   // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS:
   // thread (frequency qi, heads qh0 + NW k) loads (query_issue), then rotates
@@ -612,6 +607,29 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     }
   };
 
+
+  bool q_ready = false;                                 // query operands built (first part)
+  auto run_part = [&](const int part) {
+  // ---- RoPE angle state of the lane's token for its 16 frequencies; the
+  // table loads (anchor_issue) and the products (anchor_finish) are apart so
+  // the prologue issues every load before its first wait
+  float cs_c[16], cs_s[16];          // separate arrays: no 64-bit register pairs
+  float2 an_A[16], an_B[16];
+  auto anchor_issue = [&](int64_t t) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rope_load(M.sh, t, 16 * mb + 4 * rho + i, an_A[mb * 4 + i], an_B[mb * 4 + i]);
+  };
+  auto anchor_finish = [&]() {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rope_combine(an_A[j], an_B[j], cs_c[j], cs_s[j]);
+  };
+  auto anchor = [&](int64_t t) {
+    anchor_issue(t);
+    anchor_finish();
+  };
+
   // rotate the key tile by the angle state (then advance it 16 positions),
   // then the score product
   auto rope_scores = [&](floatx4 (&ka)[8]) -> floatx4 {
@@ -644,6 +662,32 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     }
     return sc[0] + sc[1];
   };
+  const bool comp = cwg && part == 0;                    // compressed range
+  const bool pre = !cwg && xs < plan.n_pre;              // a protected-prefix split
+  // record of this part: compressed records first, then prefix, then window
+  const int rec_idx = comp ? split : (cwg ? plan.n_comp + plan.n_pre + split : split);
+  int64_t r_begin, r_end;
+  if (comp) {
+    r_begin = D.prefix + (int64_t)split * plan.comp_len;
+    r_end = r_begin + plan.comp_len < n_c ? r_begin + plan.comp_len : n_c;
+  } else if (pre) {
+    const int64_t pend = length < D.prefix ? length : D.prefix;
+    r_begin = (int64_t)xs * plan.pre_len;
+    r_end = r_begin + plan.pre_len < pend ? r_begin + plan.pre_len : pend;
+  } else {
+    const int wi = cwg ? split : xs - plan.n_pre;
+    r_begin = n_c + (int64_t)wi * plan.win_len;
+    r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
+  }
+  if (r_end < r_begin) r_end = r_begin;
+  const int ntiles = (int)((r_end - r_begin + 15) / 16);
+  // even split: the first ntiles % NW waves take one tile more (waves w and
+  // w + NW/2 share a SIMD, so every SIMD gets the same count within one)
+  const int tb = ntiles / NW, tx = ntiles % NW;
+  const int tile_lo = wave * tb + (wave < tx ? wave : tx);
+  const int tile_hi = tile_lo + tb + (wave < tx ? 1 : 0);
+  const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
+  const int nt = __builtin_amdgcn_readfirstlane(tile_hi - tile_lo);   // wave-uniform
 
   float m = -INFINITY, l = 0.f;
   const int64_t w_end = r_end;
@@ -851,12 +895,12 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
         unsigned h0, l0, h1, l1;
         split2(p[0], p[1], h0, l0, sk);
         split2(p[2], p[3], h1, l1, sk);
-        const T *vsrc = tv + (4 * rho + (n16 >> 2)) * RV + 4 * (n16 & 3);
+        uint2_ v[NBV];
+        lds_read_tr16<NBV>(tv + (4 * rho + (n16 >> 2)) * RV + 4 * (n16 & 3), v);
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) {
-          const uint2_ v = lds_read_tr16(vsrc + 16 * nb);
-          vacc[nb] = mfma16(uint2_{h0, h1}, v, vacc[nb]);
-          vacc[nb] = mfma16(uint2_{l0, l1}, v, vacc[nb]);
+          vacc[nb] = mfma16(uint2_{h0, h1}, v[nb], vacc[nb]);
+          vacc[nb] = mfma16(uint2_{l0, l1}, v[nb], vacc[nb]);
         }
       } else {
         const float *tf = reinterpret_cast<const float *>(tv);
@@ -891,9 +935,9 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
       for (int i = 0; i < 4; ++i) s_acc[wave][4 * rho + i][16 * nb + n16] = vacc[nb][i];
   } else {
     // ================= exact window tokens =================
-    if (app.k != nullptr && split == (int)gridDim.x - 1 && threadIdx.x < 2 * kHeadDim) {
-      // fused append: this split ends at the newest position; write its ring
-      // rows (rounded to the storage type) before the barrier in query_finish,
+    if (app.k != nullptr && !pre && r_end == length && r_begin < length && threadIdx.x < 2 * kHeadDim) {
+      // fused append: this window split ends at the newest position; write
+      // its ring rows (rounded to the storage type) before the barrier below,
       // after which this workgroup reads them
       const int e = threadIdx.x & (kHeadDim - 1), x = threadIdx.x >> 7;   // K for x = 0, V for x = 1
       const size_t src = ((size_t)b * D.kv_heads + hk) * kHeadDim + e;
@@ -907,31 +951,45 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     floatx4 wacc[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) wacc[nb] = zero4();
-    query_issue();
+    if (!q_ready) query_issue();
     if (nt > 0) anchor_issue(w_begin + n16);
     __builtin_amdgcn_sched_barrier(0);
     if (nt > 0) anchor_finish();
-    query_finish(false);
+    if (!q_ready) query_finish(false);
+    else __syncthreads();               // the fused append's ring rows are visible
     if (nt > 0) {
       // exact rows: the protected prefix (row = position) or the ring (row =
       // position % slots); V transposed in both, row stride `rows`
       const int rows = pre ? D.prefix : D.slots;
       const T *EK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
       const T *EV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
-      for (int it = 0; it < nt; ++it) {
+      // raw K rows and V columns of a tile, both issued at the tile start
+      // (one memory latency per tile instead of a second one for V)
+      using Raw = typename std::conditional<BF, uint2_, floatx4>::type;
+      auto load_raw = [&](int it, Raw (&k)[8], Raw (&v)[8]) {
         const int64_t t0 = w_begin + 16 * (int64_t)it;
         const int slot = (int)((t0 + n16) % rows);
         const int slot0 = (int)(t0 % rows);             // tiles never wrap (16 | slots, 64 | P)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+          k[mb] = *reinterpret_cast<const Raw *>(EK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+          v[nb] = *reinterpret_cast<const Raw *>(EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
+      };
+      for (int it = 0; it < nt; ++it) {
+        const int64_t t0 = w_begin + 16 * (int64_t)it;
+        Raw kc[8], vc[8];
+        load_raw(it, kc, vc);
         floatx4 ka[8];
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
-          const T *src = EK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho;
           if constexpr (BF) {
-            const uint2_ v = *reinterpret_cast<const uint2_ *>(src);
+            const uint2_ v = kc[mb];
             ka[mb] = floatx4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                              __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
           } else {
-            ka[mb] = *reinterpret_cast<const floatx4 *>(src);
+            ka[mb] = kc[mb];
           }
         }
         const floatx4 sc = rope_scores(ka);
@@ -946,19 +1004,14 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
           split2(p[2], p[3], h1, l1, sk);
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
-            const uint2_ v = *reinterpret_cast<const uint2_ *>(
-                EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
-            wacc[nb] = mfma16(uint2_{h0, h1}, v, wacc[nb]);
-            wacc[nb] = mfma16(uint2_{l0, l1}, v, wacc[nb]);
+            wacc[nb] = mfma16(uint2_{h0, h1}, vc[nb], wacc[nb]);
+            wacc[nb] = mfma16(uint2_{l0, l1}, vc[nb], wacc[nb]);
           }
         } else {
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(
-                EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
+          for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wacc[nb] = mfma4(p[i], v[i], wacc[nb]);
-          }
+            for (int i = 0; i < 4; ++i) wacc[nb] = mfma4(p[i], vc[nb][i], wacc[nb]);
         }
         if ((it & 31) == 31) anchor(t0 + 16 + n16);
       }
@@ -976,9 +1029,9 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   }
   __syncthreads();
 
-  // ---- combine the four waves into this split's record
+  // ---- combine the waves into this part's record
   const int width = comp ? RV : kHeadDim;
-  const size_t rec0 = ((size_t)u * D.max_rec + split) * G;
+  const size_t rec0 = ((size_t)u * D.max_rec + rec_idx) * G;
   for (int e = threadIdx.x; e < G * (2 + width); e += C::kThr) {
     const int h = e / (2 + width), x = e % (2 + width);
     float mx = -INFINITY;
@@ -999,6 +1052,10 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     if (x == 1) store_agent(M.sh.recml + (rec0 + h) * 2 + 1, v);
     else store_agent(M.sh.rec + (rec0 + h) * kRecStride + x - 2, v);
   }
+  q_ready = true;
+  };
+  run_part(0);
+  if (nparts == 2) run_part(1);
 
   // ---- fused: the last split workgroup of this unit to finish merges all
   // records (used when the whole grid is resident at once, so no merge holds
@@ -1013,7 +1070,7 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   if (threadIdx.x == 0) {
     const unsigned done =
         __hip_atomic_fetch_add(M.sh.cnt + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned splits = sp.n ? (unsigned)(plan.n_comp + plan.n_pre + plan.n_win) : gridDim.x;
+    const unsigned splits = sp.n ? (unsigned)plan_workgroups(plan) : gridDim.x;
     s_last = (done + 1 == splits) ? 1 : 0;
   }
   __syncthreads();
@@ -1031,11 +1088,12 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(Model M, int lay
   merge_unit<R, 4>(M, layer, out, sp.n ? seq_plan(sp, u / M.D.kv_heads) : plan, u, s_mrg);
 }
 
-// Workgroups (of `waves` waves) per decode call: about 16 tiles of 16 tokens
-// per wave (enough to amortize the per-workgroup set-up and keep the merge
-// short), between one per CU and 64 waves per CU, rounded down to a whole
-// number per CU.  ISKV_DECODE_WORKGROUPS overrides it.
-int target_workgroups(const Dims &D, int64_t length, int waves) {
+// Workgroups (of `waves` waves, `occ` per CU) per decode call: one resident
+// round (every workgroup on a CU at once: one set-up per workgroup, the merge
+// in the split kernel, no tail of late workgroups) when there are at least
+// two tiles per wave, else enough for two tiles per wave.
+// ISKV_DECODE_WORKGROUPS overrides it.
+int target_workgroups(const Dims &D, int64_t length, int waves, int occ) {
   static int v = -1;
   if (v < 0) {
     const char *e = std::getenv("ISKV_DECODE_WORKGROUPS");
@@ -1044,30 +1102,21 @@ int target_workgroups(const Dims &D, int64_t length, int waves) {
   }
   if (v > 0) return v;
   const int64_t tiles = (int64_t)D.units * ((length + 15) / 16);
-  const int64_t cus = D.cus;
-  int64_t t = (tiles + 16 * waves - 1) / (16 * waves);
-  if (t < cus) t = cus;
-  if (t > 64 / waves * cus) t = 64 / waves * cus;
-  // a grid just past one workgroup per CU would put a second one on a few
-  // CUs and make them the tail of the launch
-  return (int)(t / cus * cus);
+  const int64_t slots = (int64_t)D.cus * occ;
+  int64_t t = (tiles + 2 * waves - 1) / (2 * waves);
+  return (int)(t < slots ? t : slots);
 }
 
-// n_c: end position of the compressed rows (the protected prefix P .. n_c-1
-// compressed, 0 .. P-1 exact, n_c .. length-1 in the ring).
 // n_k compressed, n_e ring and n_p prefix tokens (for a ragged batch, the
-// largest of each over the sequences; length the largest length).
+// sequence's own); per_unit workgroups for the unit.  The window either gets
+// workgroups of its own (about four tiles per wave each) or rides on the
+// compressed workgroups (one window split after each compressed range),
+// whichever gives the smaller largest workgroup: an exact tile costs about two
+// compressed ones (its rows are 128 wide and loaded without the DMA ring),
+// and a ride adds a second record (about two tiles).
 SplitPlan make_plan_core(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, int64_t per_unit,
                          int waves) {
   SplitPlan plan{};
-  if (n_e > 0) {
-    // about 4 tiles per wave for the window
-    int64_t nw = (n_e + 255) / 256;
-    if (nw > D.max_rec / 2) nw = D.max_rec / 2;
-    plan.n_win = (int)nw;
-    plan.win_len = (int)(((n_e + nw - 1) / nw + 15) / 16 * 16);
-    plan.n_win = (int)((n_e + plan.win_len - 1) / plan.win_len);
-  }
   if (n_p > 0) {
     // the prefix as exact splits of about 256 tokens
     int64_t np = (n_p + 255) / 256;
@@ -1075,35 +1124,65 @@ SplitPlan make_plan_core(const Dims &D, int64_t n_k, int64_t n_e, int64_t n_p, i
     plan.pre_len = (int)(((n_p + np - 1) / np + 15) / 16 * 16);
     plan.n_pre = (int)((n_p + plan.pre_len - 1) / plan.pre_len);
   }
-  if (n_k > 0) {
-    const int n_x = plan.n_win + plan.n_pre;
-    int64_t want = per_unit - n_x;
-    if (want < 1) want = 1;
-    int64_t nc = (n_k + 32 * waves - 1) / (32 * waves);   // at least 2 tiles per wave
+  // compressed splits: `want` workgroups, at least 2 tiles per wave, records
+  // within max_rec (n_comp compressed + up to n_comp window + n_pre prefix)
+  auto comp_splits = [&](int64_t want) {
+    int64_t nc = (n_k + 32 * waves - 1) / (32 * waves);
     if (nc > want) nc = want;
-    if (nc > D.max_rec - n_x) nc = D.max_rec - n_x;
+    if (nc > (D.max_rec - plan.n_pre) / 2) nc = (D.max_rec - plan.n_pre) / 2;
     if (nc < 1) nc = 1;
     plan.comp_len = (int)(((n_k + nc - 1) / nc + 63) / 64 * 64);
     plan.n_comp = (int)((n_k + plan.comp_len - 1) / plan.comp_len);
+  };
+  const int64_t kt = (n_k + 15) / 16, et = (n_e + 15) / 16;     // tiles
+  int64_t nw = (et + 4 * waves - 1) / (4 * waves);               // own window splits
+  if (nw > D.max_rec / 2) nw = D.max_rec / 2;
+  const int64_t avail = per_unit - plan.n_pre;
+  bool rides = false;
+  if (n_k > 0 && n_e > 0) {
+    const int64_t sep_comp = avail - nw;
+    if (sep_comp < 1) {
+      rides = true;
+    } else {
+      const int64_t sep = std::max((kt + sep_comp - 1) / sep_comp, (2 * et + nw - 1) / nw);
+      const int64_t ride = (kt + 2 * et + avail - 1) / std::max<int64_t>(avail, 1) + 2 * waves;
+      rides = ride < sep;
+    }
+  }
+  if (n_k > 0) {
+    comp_splits(rides ? avail : (n_e > 0 ? avail - nw : avail));
+    if (rides) {
+      plan.win_rides = 1;
+      plan.n_win = plan.n_comp;
+      plan.win_len = (int)(((n_e + plan.n_comp - 1) / plan.n_comp + 15) / 16 * 16);
+      return plan;
+    }
+  }
+  if (n_e > 0) {
+    if (nw > avail - (n_k > 0 ? plan.n_comp : 0)) nw = std::max<int64_t>(1, avail - (n_k > 0 ? plan.n_comp : 0));
+    if (nw > D.max_rec - plan.n_pre - plan.n_comp) nw = D.max_rec - plan.n_pre - plan.n_comp;
+    if (nw < 1) nw = 1;
+    plan.win_len = (int)(((n_e + nw - 1) / nw + 15) / 16 * 16);
+    plan.n_win = (int)((n_e + plan.win_len - 1) / plan.win_len);
   }
   return plan;
 }
 
-SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves) {
+SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves, int occ) {
   const int64_t n_e = length > n_c ? length - n_c : 0;           // ring tokens
   const int64_t n_p = length < D.prefix ? length : D.prefix;     // prefix tokens
-  return make_plan_core(D, n_c - D.prefix, n_e, n_p, target_workgroups(D, length, waves) / D.units,
-                        waves);
+  const int64_t per_unit = target_workgroups(D, length, waves, occ) / D.units;
+  return make_plan_core(D, n_c - D.prefix, n_e, n_p, per_unit < 1 ? 1 : per_unit, waves);
 }
 
 // Ragged batch: the workgroups a batch of the average length would get,
 // shared out in proportion to each sequence's length.
-SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves) {
+SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ) {
   SeqPlans sp{};
   sp.n = tab.n;
   int64_t total = 0;
   for (int b = 0; b < tab.n; ++b) total += tab.len[b];
-  const int64_t target = target_workgroups(D, (total + tab.n - 1) / tab.n, waves);
+  const int64_t target = target_workgroups(D, (total + tab.n - 1) / tab.n, waves, occ);
   sp.off[0] = 0;
   for (int b = 0; b < tab.n; ++b) {
     const int64_t L = tab.len[b], c = tab.nc[b];
@@ -1117,7 +1196,8 @@ SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves) {
     sp.comp_len[b] = p.comp_len;
     sp.pre_len[b] = p.pre_len;
     sp.win_len[b] = p.win_len;
-    sp.off[b + 1] = sp.off[b] + p.n_comp + p.n_pre + p.n_win;
+    sp.win_rides[b] = (uint8_t)p.win_rides;
+    sp.off[b + 1] = sp.off[b] + plan_workgroups(p);
   }
   return sp;
 }
@@ -1128,7 +1208,7 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
                        FusedAppend app, const SeqTab &tab, const SeqPlans &sp) {
   using C = Cfg<RK, RV, T, NW>;
   const dim3 grid = sp.n ? dim3(sp.off[sp.n], M.D.kv_heads)
-                         : dim3(plan.n_comp + plan.n_pre + plan.n_win, M.D.units);
+                         : dim3(plan_workgroups(plan), M.D.units);
   constexpr int dyn = C::kDynBytes;
   static bool dattr = false;
   hipError_t e;
@@ -1160,30 +1240,43 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
 
 // bf16, r <= 64: eight-wave workgroups when their grid fits one per CU (a
 // single launch wave, where two waves per SIMD and an even share per CU set
-// the time); four-wave workgroups, two per CU, for larger grids, where one
-// workgroup's set-up and merge overlap the other's loop.
+// the time); four-wave workgroups, two per CU (one for wider ranks and fp32),
+// for larger grids.  ISKV_DECODE_WAVES=4 or 8 forces a form where it exists.
+int forced_waves() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = std::getenv("ISKV_DECODE_WAVES");
+    v = e ? std::atoi(e) : 0;
+  }
+  return v;
+}
+
 template <int RK, int RV, typename T>
 hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos, float *out,
                        int64_t length, int64_t n_c, hipStream_t s, FusedAppend app, const SeqTab &tab) {
+  constexpr int occ4 = Cfg<RK, RV, T, 4>::kOcc;
+  constexpr bool has8 = std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64;
   if (tab.n) {
     // ragged: one plan per sequence, (sequence, split) flattened into grid.x
     const SplitPlan none{};
-    if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
-      const SeqPlans s8 = make_seq_plans(M.D, tab, 8);
-      if ((int64_t)s8.off[s8.n] * M.D.kv_heads <= M.D.cus)
+    if constexpr (has8) {
+      const SeqPlans s8 = make_seq_plans(M.D, tab, 8, 1);
+      if (forced_waves() == 8 ||
+          (forced_waves() != 4 && (int64_t)s8.off[s8.n] * M.D.kv_heads <= M.D.cus))
         return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab, s8);
     }
     return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab,
-                                     make_seq_plans(M.D, tab, 4));
+                                     make_seq_plans(M.D, tab, 4, occ4));
   }
   const SeqPlans one{};
-  if constexpr (std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64) {
-    const SplitPlan p8 = make_plan(M.D, length, n_c, 8);
-    if ((int64_t)(p8.n_comp + p8.n_pre + p8.n_win) * M.D.units <= M.D.cus)
+  if constexpr (has8) {
+    const SplitPlan p8 = make_plan(M.D, length, n_c, 8, 1);
+    if (forced_waves() == 8 ||
+        (forced_waves() != 4 && (int64_t)plan_workgroups(p8) * M.D.units <= M.D.cus))
       return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, p8, s, app, tab, one);
   }
   return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c,
-                                   make_plan(M.D, length, n_c, 4), s, app, tab, one);
+                                   make_plan(M.D, length, n_c, 4, occ4), s, app, tab, one);
 }
 
 // (r_K, r_V): equal ranks, or a value rank twice the key rank
