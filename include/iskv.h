@@ -16,10 +16,11 @@
  *                                                      synchronization?"]
  *   - keys are compressed before RoPE and RoPE is re-applied on rebuild
  *                                                     [Jargon "Pre-RoPE keys"]
- *   - each new query scores every earlier key         [re-attention paragraph]
+ *   - attention at a new position covers all predecessors, none evicted
+ *                                                     [re-attention paragraph]
  *   - persistent-KV bytes = factors + exact rows      [Jargon "Persistent-KV
  *                                                      compression"]
- *   - a set of protected prompt positions also stays exact
+ *   - some prompt positions are protected and kept uncompressed
  *                                                     [window paragraph; the
  *                                                      page does not say which:
  *                                                      here a leading prefix]
@@ -183,9 +184,9 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
  * [batch][1][num_kv_heads][head_dim], in_dtype ISKV_F32 or ISKV_BF16)
  * followed by iskv_decode_attn, with the same results, ring contents, error
  * codes and *blocks_ready as the two calls (the workgroup that attends over
- * the newest position writes its ring rows first).  Saves one launch per
- * step of an append-then-attend loop [iS-KV explainer, the window paragraph:
- * each new token enters the exact window and is attended to at once]. */
+ * the newest position writes its ring rows first).  A fused convenience of
+ * this library, not an operation of the pages: it saves one launch per step
+ * of an append-then-attend loop. */
 int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int in_dtype,
                        const float *dev_q, int64_t q_pos, float *dev_out, int *blocks_ready);
 

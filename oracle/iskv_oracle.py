@@ -18,17 +18,17 @@ paper), abbreviated [iS-KV explainer].
 * Maintenance [iS-KV explainer, Jargon "Block-incremental SVD" and the drift
   paragraph]: each time 64 tokens leave the exact window they are folded into
   the factorization as one block with Brand's block-incremental SVD, solved on a
-  small core matrix whose size is independent of the history length.
+  core of (r+64) x (r+64) entries, so its cost is fixed as the history grows.
 * Basis synchronization [iS-KV explainer, FAQ "What is basis synchronization?"
   and the drift paragraph]: when the basis changes, all stored coefficients are
   rewritten for the new basis in the same step.
 * Keys are compressed before RoPE and RoPE is re-applied when a key is rebuilt
   [iS-KV explainer, Jargon "Pre-RoPE keys"].
-* Every new query scores every earlier key [iS-KV explainer, the re-attention
-  paragraph ("Why not bin the quiet colors?")].
+* Attention at a new position runs over all of its predecessors, none dropped
+  [iS-KV explainer, the re-attention paragraph].
 * Persistent-KV bytes [iS-KV explainer, Jargon "Persistent-KV compression"].
 * Protected prompt positions stay exact [iS-KV explainer, the window
-  paragraph ("paint shop"); the Jargon entry "Persistent-KV compression"
+  paragraph (the paint-shop analogy); the Jargon entry "Persistent-KV compression"
   counts them among the kept bytes].  Which positions, and how many, is not
   stated; the reading here is a leading prefix of P positions (P a multiple
   of 64, default 0) that is never folded: compression starts at position P.

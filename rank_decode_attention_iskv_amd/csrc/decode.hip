@@ -1,10 +1,10 @@
 // Decode attention over the mixed cache (exact window + low-rank history).
 //
 // Page: "iS-KV -- Basis-synchronized online low-rank KV compression -- What does
-// it mean?" (learnaivisually.com), cited as [iS-KV explainer]: every new query
-// scores every earlier key (re-attention paragraph); old keys are rebuilt from
-// their coefficients over the shared basis and RoPE is re-applied at the key's
-// position (Jargon "Basis and coefficients", "Pre-RoPE keys").  Values are
+// it mean?" (learnaivisually.com), cited as [iS-KV explainer]: a new query
+// attends over all of its predecessors (re-attention paragraph); old keys are
+// rebuilt from their coefficients over the shared basis and RoPE is re-applied
+// at the key's position (Jargon "Basis and coefficients", "Pre-RoPE keys").  Values are
 // accumulated in coefficient space, sum_t p_t c_t, and mapped back once by the
 // value basis: (p^T C) B^T = p^T (C B^T).
 //
@@ -1059,10 +1059,28 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 
   // ---- fused: the last split workgroup of this unit to finish merges all
   // records (used when the whole grid is resident at once, so no merge holds
-  // a CU that later workgroups wait for).  Records are written with
-  // agent-scope stores (through to the coherence point shared by every XCD)
-  // and complete before the count is raised; the merging workgroup reads them
-  // with agent-scope loads.  No workgroup waits on another.
+  // a CU that later workgroups wait for).  No workgroup waits on another.
+  //
+  // Why the merging workgroup, possibly on another XCD with its own L2, sees
+  // every record:
+  //   1. every record word is written and read only by agent-scope atomics,
+  //      which are coherent across all XCDs of the device (the hardware keeps
+  //      no private L2 copy of them), so there is no data race and no stale
+  //      L2 line to write back or invalidate;
+  //   2. each thread waits for its record stores to complete (vmcnt(0): a
+  //      completed agent-scope store is performed at agent scope, the same
+  //      wait the compiler's own release sequence ends with) before the
+  //      barrier, and thread 0 increments the unit's count only after it;
+  //   3. the workgroup whose increment returns splits - 1 comes after every
+  //      other increment, hence after every record store completed; its
+  //      threads issue their record loads only after a barrier that follows
+  //      that return.
+  // The relaxed orders leave steps 2-3 to the hardware's in-order completion.
+  // The portable form (agent-scope release fence before the increment,
+  // acquire fence in the merging workgroup) adds an L2 write-back and
+  // invalidate meant for non-atomic data, which the records are not:
+  // measured at +5% per call for batch 16 x 16K and +15% for one 32K
+  // sequence, with identical results.
   if (!fused) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

@@ -3,9 +3,9 @@
 //
 // Page: "iS-KV -- Basis-synchronized online low-rank KV compression -- What does
 // it mean?" (learnaivisually.com), Jargon "Block-incremental SVD" and the drift
-// paragraph: the 64 tokens that leave the exact window are folded into the
-// rank-r basis as one block, on a small core whose size does not depend on the
-// history length.
+// paragraph: each 64-token block that ages out of the exact window joins the
+// rank-r factorization in one update; the SVD is taken of an (r+64)-square core
+// built from S and the block, so its cost is fixed however long the history.
 //
 // With the old history H = U diag(S) B^T (U orthonormal; the stored
 // coefficients are U diag(S)) and a new block A (64 x d):
@@ -443,7 +443,6 @@ __device__ __forceinline__ void qr_rows(float *core, float *vbuf0, float *vbuf1)
 }
 
 // ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // One-sided Jacobi on the N rows (length NC, stride LC) of `core`.  A pair
 // (x, y) is rotated while |x.y| > tol |x||y|.  The squared row norms are
 // computed at the start of each sweep and carried through its rotations
@@ -451,24 +450,44 @@ __device__ __forceinline__ void qr_rows(float *core, float *vbuf0, float *vbuf1)
 // carried over more than one sweep they drifted and stalled convergence on
 // clusters of near-equal singular values.  Rows whose squared norm is below
 // (64 eps)^2 times the largest are at the rounding level of the core and are
-// left alone.  The sweeps stop when one rotates nothing, or when its largest
-// pair measure was below kJacobiQuad.  Returns the number of rotating sweeps, or kMaxSweeps + 1 if
-// it did not converge within kMaxSweeps.
+// left alone.
+//
+// Only the `keep` largest singular values and their right vectors are used.
+// Each sweep therefore starts by choosing a leading set: the rows of the k
+// largest norms, k >= keep the smallest count for which the squared norms of
+// all other rows add up to less than kLeadMargin times the k-th largest.
+// Pairs of two rows outside the set are skipped.  When the set's rows are
+// orthogonal to each other and to every other row, the singular values of the
+// other rows form a matrix of spectral norm at most the square root of that
+// sum, below every leading norm, so the leading rows are the leading singular
+// triplets however the other rows stand among themselves.  (In the cores of
+// steady-state folds the non-leading rows are the residual directions, whose
+// near-equal small singular values took most of the sweeps.)  The sweeps stop
+// when one rotates nothing, or when its largest pair measure was below
+// kJacobiQuad, and the final norms certify the split (leading minimum above
+// the rest's sum); without the certificate every pair is taken from then on.
+// Returns the number of rotating sweeps, or kMaxSweeps + 1 if it did not
+// converge within kMaxSweeps.
 // ---------------------------------------------------------------------------
+constexpr float kLeadMargin = 0.25f;
+
 template <int N, int NC, int LC>
-__device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int *bigflag) {
+__device__ int jacobi_rows(float *core, float *nrm, int *rank, int *lead, int keep) {
   constexpr int GS = NC % 32 == 0 ? 8 : 4;      // lanes per pair
   constexpr int NP = N / 2, CPT = NC / (4 * GS);
-  static_assert(NC % (4 * GS) == 0 && N % 2 == 0, "row shape");
+  static_assert(NC % (4 * GS) == 0 && N % 2 == 0 && N <= kThreads, "row shape");
   constexpr float kNegl = (64.f * FLT_EPSILON) * (64.f * FLT_EPSILON);
+  __shared__ int s_flag, s_max, s_big, s_lead;
+  __shared__ float s_red[2][kThreads / 64];
   const int tid = threadIdx.x, li = tid & (GS - 1);
+  bool all_pairs = keep >= N;
   int sweep = 0;
   for (; sweep < kMaxSweeps; ++sweep) {
-    if (tid == 0) { *flag = 0; *maxbits = 0; *bigflag = 0; }
+    if (tid == 0) { s_flag = 0; s_max = 0; s_big = 0; s_lead = N; }
     int big = 0;                         // a pair measure of this thread reached kJacobiQuad
     __syncthreads();
-    for (int j = tid; j < N; j += kThreads) {
-      const float *row = core + j * LC;
+    if (tid < N) {
+      const float *row = core + tid * LC;
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll 4
       for (int i = 0; i < NC; i += 4) {
@@ -476,17 +495,47 @@ __device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int
         s0 = fmaf(v.x, v.x, s0); s1 = fmaf(v.y, v.y, s1);
         s0 = fmaf(v.z, v.z, s0); s1 = fmaf(v.w, v.w, s1);
       }
-      nrm[j] = s0 + s1;
-      atomicMax(maxbits, __float_as_int(s0 + s1));
+      nrm[tid] = s0 + s1;
+      atomicMax(&s_max, __float_as_int(s0 + s1));
     }
     __syncthreads();
-    const float negl = kNegl * __int_as_float(*maxbits);
-    const float inv_max = __int_as_float(*maxbits) > 0.f ? 1.f / __int_as_float(*maxbits) : 0.f;
+    if (!all_pairs) {
+      // rank by norm (ties by index), the norms in descending order, the
+      // leading set from their tail sums
+      float *sorted = reinterpret_cast<float *>(lead);
+      if (tid < N) {
+        const float nj = nrm[tid];
+        int rk = 0;
+#pragma unroll 4
+        for (int i = 0; i < N; i += 4) {
+          const float4 v = ld4(nrm + i);
+          rk += (v.x > nj || (v.x == nj && i < tid)) + (v.y > nj || (v.y == nj && i + 1 < tid)) +
+                (v.z > nj || (v.z == nj && i + 2 < tid)) + (v.w > nj || (v.w == nj && i + 3 < tid));
+        }
+        rank[tid] = rk;
+        sorted[rk] = nj;
+      }
+      __syncthreads();
+      if (tid < N && tid >= keep - 1) {
+        float tail = 0.f;
+        for (int i = tid + 1; i < N; ++i) tail += sorted[i];
+        if (tail < kLeadMargin * sorted[tid]) atomicMin(&s_lead, tid + 1);
+      }
+      __syncthreads();
+      if (tid < N) lead[tid] = rank[tid] < s_lead;
+      // a leading set of more than half the rows saves at most a quarter of
+      // the pairs: take every pair from here on
+      all_pairs = 2 * s_lead > N;
+      __syncthreads();
+    }
+    const float negl = kNegl * __int_as_float(s_max);
+    const float inv_max = __int_as_float(s_max) > 0.f ? 1.f / __int_as_float(s_max) : 0.f;
     for (int k = 0; k < N - 1; ++k) {
       for (int g = tid / GS; g < NP; g += kThreads / GS) {
         int p, q;
         if (g == 0) { p = k; q = N - 1; }
         else { p = (k + g) % (N - 1); q = (k - g + N - 1) % (N - 1); }
+        if (!all_pairs && !lead[p] && !lead[q]) continue;
         float *rp = core + p * LC + 4 * li, *rq = core + q * LC + 4 * li;
         float4 x[CPT], y[CPT];
 #pragma unroll
@@ -528,7 +577,7 @@ __device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int
                                          sn * u.z + cs * v.z, sn * u.w + cs * v.w));
           }
           if (li == 0) {
-            *flag = 1;
+            s_flag = 1;
             nrm[p] = fmaf(-t, c, a);          // |x'|^2 = a - t c, |y'|^2 = b + t c
             nrm[q] = fmaf(t, c, b);
           }
@@ -536,12 +585,28 @@ __device__ int jacobi_rows(float *core, float *nrm, int *flag, int *maxbits, int
       }
       __syncthreads();
     }
-    if (big) *bigflag = 1;
+    if (big) s_big = 1;
     __syncthreads();
-    const int rotated = *flag, any_big = *bigflag;
+    const int rotated = s_flag, any_big = s_big, n_lead = s_lead;
+    __syncthreads();                           // read before the next sweep resets them
+    if (rotated && any_big) continue;          // uniform: shared values
+    if (all_pairs || n_lead >= N) return rotated ? sweep + 1 : sweep;
+    // certificate: smallest leading norm above the sum of the others
+    float mn = INFINITY, rest = 0.f;
+    if (tid < N) {
+      if (lead[tid]) mn = nrm[tid];
+      else rest = nrm[tid];
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      rest += __shfl_xor(rest, o);
+    }
+    if ((tid & 63) == 0) { s_red[0][tid >> 6] = mn; s_red[1][tid >> 6] = rest; }
     __syncthreads();
-    if (!rotated) return sweep;
-    if (!any_big) return sweep + 1;
+    mn = INFINITY; rest = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) { mn = fminf(mn, s_red[0][w]); rest += s_red[1][w]; }
+    if (mn > rest) return rotated ? sweep + 1 : sweep;
+    all_pairs = true;                          // uniform
   }
   return kMaxSweeps + 1;
 }
@@ -686,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   // ---------------- phase 4: QR of the core, one-sided Jacobi on R ----------
   {
     qr_rows<N, NC, LC>(core, sig, reinterpret_cast<float *>(perm));
-    const int sweeps = jacobi_rows<NC, NC, LC>(core, lds + Ly::oNrm, &s_int[0], &s_int[2], &s_int[3]);
+    const int sweeps = jacobi_rows<NC, NC, LC>(core, lds + Ly::oNrm, reinterpret_cast<int *>(sig), perm, R);
     if (sweeps > kMaxSweeps && tid == 0) set_flag(M.sh, 2);
   }
 

@@ -438,7 +438,7 @@ def test_first_fold_is_truncated_svd_of_block():
 
 # ---------------------------------------------------------------------------
 # Protected prompt prefix: positions 0..P-1 stay exact and are never folded
-# [iS-KV explainer, the window paragraph ("paint shop"): protected prompt
+# [iS-KV explainer, the window paragraph (paint-shop analogy): protected prompt
 # positions stay exact; reading: a leading prefix of P positions]
 # ---------------------------------------------------------------------------
 
