@@ -99,6 +99,9 @@ def parse():
                          "to every sequence (iskv_append_ragged), attends each at its own length "
                          "(iskv_decode_attn_ragged), and folds the sequences whose ring fills")
     ap.add_argument("--seed", type=int, default=1000)
+    ap.add_argument("--async-maintenance", action="store_true",
+                    help="copy-on-write maintenance on a second stream (iskv_maintain / "
+                         "iskv_switch) instead of block update + sync between decode steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only stream a 256 MiB float32 tensor through an elementwise kernel "
                          "(x * 1 -> y) five times: the reference for HBM byte counters")
@@ -470,6 +473,7 @@ def measure(p, steps, warmup, instances, seed, quiet=False):
         "fold_avg_us": sum(fold_ms) / len(fold_ms) * 1e3,
         "sync_avg_us": sum(sync_ms) / len(sync_ms) * 1e3,
         "fold_events_timed": len(events),
+        "step_us_max_with_fold_event": (dec_ms / steps + event_ms) * 1e3,
         "fold_events_in_steps": timed_folds,
         "prefill_s": t_pre,
         "wall_s_timed": wall,
@@ -478,6 +482,172 @@ def measure(p, steps, warmup, instances, seed, quiet=False):
         "persistent_kv_bytes_per_instance": st.persistent_bytes // I,
         "full_kv_bytes_per_instance": st.full_bytes // I,
         "context_at_end": max(lens),
+    }
+    cache.destroy()
+    del cache, k_all, v_all, q_all, gen
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_async(p, steps, warmup, instances, seed, quiet=False):
+    """Copy-on-write maintenance: the same decode steps with every layer's fold
+    + sync enqueued on a second stream (iskv_maintain) as soon as its block is
+    ready, and switched to at a later decode boundary when finished
+    (iskv_switch before each decode call; an append that would overflow the
+    ring waits for it).  Timed as one interval on the decode stream, from the
+    first step to the switch of the last maintenance, over enough steps that
+    every instance passes three maintenances."""
+    import torch
+
+    from rank_decode_attention_iskv_amd import binding
+    torch.cuda.set_device(0)
+    L0, W, P, ML = p["context"], p["window"], p["prefix"], p["layers"]
+    n_c0 = max(P, (L0 - W - P) // 64 * 64 + P)
+    if instances <= 0:
+        instances = max(1, math.ceil(ROTATE_BYTES / max(1, state_bytes(p, n_c0 - P, L0 - n_c0))))
+    I = min(instances, 64)
+    nl = I * ML
+    steps = max(steps, 3 * 64 * I)
+    per_inst = (warmup + 2 * steps + I - 1) // I
+    max_tokens = L0 + per_inst + 64 * 4 + 64
+    cfg = binding.make_config(p["batch"], nl, p["kv"], p["q"], 128, p["rank"], W, max_tokens,
+                              p["storage"], protected_prefix=P, rank_v=p["rank_v"],
+                              async_maintenance=1)
+    cache = binding.IskvCache(cfg)
+    ms = torch.cuda.Stream()
+    cache.set_maintenance_stream(ms)
+    stream = torch.cuda.current_stream()
+    gen = Generator(torch, p, nl, seed)
+    lib = binding.lib()
+    ctx = cache.ctx
+
+    def fold_now():
+        cache.maintain(-1)
+        for layer in range(nl):
+            cache.switch(layer, wait=True)
+
+    t_pre = time.perf_counter()
+    length, n_c = 0, P
+    while length < L0:
+        n = min(256, L0 - length, W + 64 - (length - n_c) if length >= P else P - length)
+        ready = False
+        for layer in range(nl):
+            k, v = gen.tokens(layer, n)
+            ready = cache.append(layer, k, v)
+        length += n
+        if ready:
+            fold_now()
+            n_c += 64
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t_pre
+
+    B, H, HQ = p["batch"], p["kv"], p["q"]
+    tok_bytes = B * H * 128 * 4
+    need = per_inst + 64 * 4
+    k_all, v_all = [], []
+    for layer in range(nl):
+        k, v = gen.tokens(layer, need)
+        k_all.append(k.permute(1, 0, 2, 3).contiguous())
+        v_all.append(v.permute(1, 0, 2, 3).contiguous())
+    q_all = [gen.queries(per_inst, layer) for layer in range(ML)]
+    q_bytes = B * HQ * 128 * 4
+    out = torch.empty(B, HQ, 128, device="cuda")
+    torch.cuda.synchronize()
+    k_base = [t.data_ptr() for t in k_all]
+    v_base = [t.data_ptr() for t in v_all]
+    q_base = [t.data_ptr() for t in q_all]
+    out_p = ctypes.c_void_p(out.data_ptr())
+    ready_c = ctypes.c_int(0)
+    lens = [length] * nl
+    used = [0] * nl
+    count = {"maint": 0}
+
+    def step(s):
+        # the decode call switches a layer whose maintenance has finished
+        inst = s % I
+        for l in range(ML):
+            layer = inst * ML + l
+            j = used[layer]
+            used[layer] += 1
+            lens[layer] += 1
+            code = lib.iskv_append_decode(ctx, layer, ctypes.c_void_p(k_base[layer] + j * tok_bytes),
+                                          ctypes.c_void_p(v_base[layer] + j * tok_bytes), binding.F32,
+                                          ctypes.c_void_p(q_base[l] + (s // I) * q_bytes),
+                                          lens[layer] - 1, out_p, ctypes.byref(ready_c))
+            if code != 0:
+                raise binding.IskvError(code, "iskv_append_decode")
+            if ready_c.value:
+                code = lib.iskv_maintain(ctx, layer)
+                if code != 0:
+                    raise binding.IskvError(code, "iskv_maintain")
+                count["maint"] += 1
+
+    def run(first, n, marks=None):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i, s in enumerate(range(first, first + n)):
+            step(s)
+            if marks is not None:
+                marks[i].record(stream)
+        for layer in range(nl):
+            cache.switch(layer, wait=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0, e1
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    count["maint"] = 0
+    # throughput: the steps alone, then the last maintenances' switches
+    e0, e1 = run(warmup, steps)
+    total_ms = e0.elapsed_time(e1)
+    maint_timed = count["maint"]
+    # inter-token latency: the next steps again with an event after each
+    n_lat = min(steps, 64 * I * 2)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_lat)]
+    l0, _ = run(warmup + steps, n_lat, marks)
+    gaps = sorted([l0.elapsed_time(marks[0])] + [a.elapsed_time(b) for a, b in zip(marks, marks[1:])])
+
+    # maintenance events alone (decode stream idle): rings topped up to a
+    # ready block, every layer maintained and switched, timed on the decode stream
+    ev_ms = []
+    for _ in range(2):
+        for layer in range(nl):
+            n_c_l = cache.status(layer).compressed + P
+            room = W + 64 - (lens[layer] - n_c_l)
+            if room > 0:
+                j = used[layer]
+                kk = k_all[layer][j: j + room].permute(1, 0, 2, 3).contiguous()
+                vv = v_all[layer][j: j + room].permute(1, 0, 2, 3).contiguous()
+                used[layer] += room
+                lens[layer] += room
+                cache.append(layer, kk, vv)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        fold_now()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ev_ms.append(f0.elapsed_time(f1))
+    units = nl * B * H * 2
+    flags = max(cache.status(i).numeric_flags for i in range(nl))
+    finite = bool(torch.isfinite(out).all().item())
+    res = {
+        "value": B * steps / (total_ms * 1e-3),
+        "ms_per_step": total_ms / steps,
+        "steps_timed": steps,
+        "instances_rotated": I,
+        "maintenances_in_timed_steps": maint_timed,
+        "latency_steps": n_lat,
+        "maintenance_event_avg_us": sum(ev_ms) / len(ev_ms) * 1e3,
+        "step_us_p50": gaps[len(gaps) // 2] * 1e3,
+        "step_us_p99": gaps[min(len(gaps) - 1, (len(gaps) * 99) // 100)] * 1e3,
+        "step_us_max": gaps[-1] * 1e3,
+        "block_updates_per_s_with_sync": units * len(ev_ms) / (sum(ev_ms) * 1e-3),
+        "prefill_s": t_pre,
+        "numeric_flags": flags,
+        "output_finite": finite,
     }
     cache.destroy()
     del cache, k_all, v_all, q_all, gen
@@ -736,10 +906,31 @@ def main():
     res["roofline"] = r.pop("roofline")
     res.update(r)
     res["kernel_sources_sha256_16"] = kh
+    if args.async_maintenance:
+        a = measure_async(p, args.steps, args.warmup, args.instances, args.seed)
+        res["same_stream"] = {"value": res["value"], "ms_per_step": res["ms_per_step"]}
+        res["value"], res["ms_per_step"] = a.pop("value"), a.pop("ms_per_step")
+        res["steps"] = a["steps_timed"]
+        res["config"]["step_calls"] = (
+            "per layer iskv_switch (non-blocking) + iskv_append_decode; a layer whose block is "
+            "ready gets iskv_maintain (fold + sync into its other generation on a second stream)")
+        res["config"]["timing"] = (
+            "one HIP event interval on the decode stream over every step and the final switches; "
+            "decode and maintenance overlap")
+        res["async_maintenance"] = a
     if p["id"] == 3 and not args.no_extras and not (args.context or args.rank or args.window or args.batch):
         extras = {}
         p2 = preset(args, 2)
         extras["config2"] = compact(measure(p2, 128, 16, 0, args.seed + 2, quiet=True), p2)
+        a2 = measure_async(p2, 128, 16, 0, args.seed + 2, quiet=True)
+        extras["config2_async_maintenance"] = {
+            "value": a2["value"], "unit": "tokens/s", "ms_per_step": a2["ms_per_step"],
+            "same_stream_ms_per_step": extras["config2"]["ms_per_step"],
+            "steps_timed": a2["steps_timed"], "maintenances": a2["maintenances_in_timed_steps"],
+            "maintenance_event_avg_us": a2["maintenance_event_avg_us"],
+            "step_us_p50": a2["step_us_p50"], "step_us_p99": a2["step_us_p99"],
+            "step_us_max": a2["step_us_max"],
+        }
         pts = []
         for rank, window in SWEEP5:
             p5 = preset(args, 5, rank=rank, rank_v=rank, window=window)

@@ -97,6 +97,16 @@ typedef struct {
                              rank.  Keys compress better than values
                              [KV-CoRE page, Key Results "Asymmetry of K
                              and V"] */
+  int32_t async_maintenance; /* 0, or 1 for copy-on-write maintenance
+                             (iskv_maintain / iskv_switch): a second
+                             generation of bases, singular values and
+                             coefficients, and 64 more ring slots, so that
+                             decode goes on over the current generation
+                             while the next one is built on the maintenance
+                             stream ["ASKV" design report, Design
+                             requirements: maintenance off the critical
+                             path; copy-on-write, switched at a decode
+                             boundary].  At most 64 layers. */
 } iskv_config;
 
 typedef struct {
@@ -124,7 +134,8 @@ size_t iskv_workspace_bytes(const iskv_config *cfg);
  *                 float basis[head_dim][r], float S[r],
  *                 float coeff[max_tokens][r]      (row = position; rows outside
  *                                                  P .. P+compressed-1 are 0),
- *                 float ring[window+64][head_dim] (slot = position % (window+64)),
+ *                 float ring[S][head_dim]         (slot = position % S, S = window+64,
+ *                                                  window+128 with async_maintenance),
  *                 float prefix[P][head_dim]       (protected rows, P = protected_prefix). */
 size_t iskv_state_bytes(const iskv_config *cfg);
 
@@ -270,6 +281,43 @@ int iskv_set_maintenance_stream(iskv_ctx *c, void *hip_stream);
  * far.  (Verbs that touch a layer do this themselves; the call lets a caller
  * place the wait, e.g. outside a timed interval.)  EINVAL for a bad layer. */
 int iskv_join_maintenance(iskv_ctx *c, int layer);
+
+/* Copy-on-write maintenance (contexts with async_maintenance = 1; ESTATE
+ * otherwise) ["ASKV" design report, Design requirements: compression must not
+ * hold up generation; the new cache version is built aside and switched to
+ * at a decode boundary, the current one used until it is ready].
+ *
+ * iskv_maintain: for `layer` (-1: every layer with a block ready and none in
+ * flight) enqueue, on the maintenance stream (the init stream if none is
+ * set) and after all init-stream work issued so far, the fold of the oldest
+ * ring block (positions P+N_c .. +63) and the synchronization of rows
+ * P .. P+N_c-1, both reading the layer's current generation and writing the
+ * other one (new basis, S, synchronized coefficients and the block's own
+ * rows).  Returns at once.  The current generation is untouched: decode,
+ * append and status go on as if the fold had not happened, the block's rows
+ * still exact in the ring (which holds window + 128 rows in this mode).
+ * ESTATE if the layer (layer >= 0) has no block ready (fewer than window + 64
+ * ring rows) or a maintenance in flight.  The layer's folds and syncs
+ * counters advance here.
+ *
+ * iskv_switch: the decode boundary.  If the layer's maintenance has finished
+ * (wait = 0: a non-blocking query; wait = 1: the init stream is made to wait
+ * for it, the host does not block), the layer switches to the new generation
+ * (N_c grows by 64) and 1 is returned; 0 if nothing is in flight or it has
+ * not finished (decoding continues on the current generation).
+ * iskv_decode_attn, iskv_decode_attn_noalloc, iskv_append_decode and
+ * iskv_append make the non-blocking switch themselves on entry; an append
+ * that would overflow the ring waits for the switch instead.  Results do not
+ * depend on when the switch happens beyond which generation a decode reads:
+ * iskv_status after a decode reports the generation it used (compressed,
+ * and pending_sync = 1 while a maintenance is in flight).
+ *
+ * The block update, sync and discard verbs and the ragged verbs return
+ * ESTATE in this mode.  iskv_join_maintenance switches with wait = 1.  The
+ * second generation is maintenance workspace: persistent_bytes counts the
+ * current one only. */
+int iskv_maintain(iskv_ctx *c, int layer);
+int iskv_switch(iskv_ctx *c, int layer, int wait);
 
 /* Free the context (not the caller's workspace).  Joins pending maintenance,
  * then synchronizes the init stream. */

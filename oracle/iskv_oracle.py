@@ -33,6 +33,14 @@ paper), abbreviated [iS-KV explainer].
   stated; the reading here is a leading prefix of P positions (P a multiple
   of 64, default 0) that is never folded: compression starts at position P.
 
+* Deferred maintenance ["ASKV" design report, Design requirements:
+  maintenance kept off the critical path, copy-on-write with a switch at a
+  decode boundary].  With a slack of S extra ring rows, a block that is ready
+  may be folded later: decode keeps attending over the pre-fold state (the
+  block's rows still exact in the ring) while up to S more tokens arrive, and
+  the fold, when applied, is the same Brand step on the same block, basis and
+  singular values.  Default S = 0.
+
 * K and V may take different ranks [KV-CoRE page, Key Results, the
   asymmetry of K and V: V needs more rank than K for the same energy].  The
   two factors never interact before decode, so a V factor of rank r_V is the
@@ -235,14 +243,14 @@ class Factor:
     """K or V store of one (sequence, layer, KV head)."""
 
     def __init__(self, d: int, r: int, window: int, max_tokens: int, storage: str,
-                 block: int = BLOCK, prefix: int = 0):
+                 block: int = BLOCK, prefix: int = 0, slack: int = 0):
         if window % block:
             raise ValueError("window must be a multiple of the block size")
         if prefix % block or prefix < 0:
             raise ValueError("the protected prefix must be a multiple of the block size")
         self.d, self.r, self.window, self.block = d, r, window, block
         self.storage = storage
-        self.slots = window + block
+        self.slots = window + block + slack
         self.P = prefix
         self.prefix = np.zeros((prefix, d))   # exact rows of positions 0..P-1
         self.ring = np.zeros((self.slots, d))
@@ -291,9 +299,11 @@ class Factor:
 class Unit:
     """One (sequence, layer, KV head): a K factor, a V factor and counters."""
 
-    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK, prefix=0, r_v=None):
-        self.K = Factor(d, r, window, max_tokens, storage, block, prefix)
-        self.V = Factor(d, r_v or r, window, max_tokens, storage, block, prefix)
+    def __init__(self, d, r, window, max_tokens, storage, block=BLOCK, prefix=0, r_v=None,
+                 slack=0):
+        self.K = Factor(d, r, window, max_tokens, storage, block, prefix, slack)
+        self.V = Factor(d, r_v or r, window, max_tokens, storage, block, prefix, slack)
+        self.slack = slack
         self.length = 0          # tokens appended (L)
         self.P = prefix          # protected exact prefix
         self.n_c = prefix        # end of the compressed positions P..n_c-1
@@ -307,10 +317,10 @@ class Unit:
 
     @property
     def ready(self) -> bool:
-        return self.length - self.n_c == self.window + self.block
+        return self.length - self.n_c >= self.window + self.block
 
     def append(self, k, v):
-        if self.length >= self.P and self.length - self.n_c >= self.window + self.block:
+        if self.length >= self.P and self.length - self.n_c >= self.window + self.block + self.slack:
             raise RuntimeError("ring full: fold the oldest block first")
         self.K.write(self.length, k)
         self.V.write(self.length, v)
@@ -399,7 +409,7 @@ class Oracle:
 
     def __init__(self, batch, num_layers, kv_heads, q_heads, head_dim, rank, window,
                  max_tokens, storage="bf16", rope_base=10000.0, softmax_scale=None,
-                 block=BLOCK, prefix=0, rank_v=None):
+                 block=BLOCK, prefix=0, rank_v=None, slack=0):
         if q_heads % kv_heads:
             raise ValueError("q_heads must be a multiple of kv_heads")
         self.batch, self.num_layers = batch, num_layers
@@ -410,7 +420,7 @@ class Oracle:
         self.prefix = prefix
         self.r_v = rank_v or rank
         self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix,
-                             self.r_v)
+                             self.r_v, slack)
                         for _ in range(kv_heads)] for _ in range(num_layers)]
                       for _ in range(batch)]
 

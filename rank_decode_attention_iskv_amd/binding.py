@@ -31,6 +31,7 @@ class Config(ctypes.Structure):
         ("block", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("storage", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
         ("protected_prefix", ctypes.c_int32), ("rank_v", ctypes.c_int32),
+        ("async_maintenance", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,7 @@ EXPORTED = (
     "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
     "iskv_append_ragged", "iskv_decode_attn_ragged", "iskv_seq_status",
     "iskv_decode_attn_noalloc", "iskv_noalloc_scratch_bytes",
+    "iskv_maintain", "iskv_switch",
 )
 
 
@@ -81,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_seq_status": (I, [P, I, I, ctypes.POINTER(Status)]),
         "iskv_decode_attn_noalloc": (I, [P, I, P, I64, P]),
         "iskv_noalloc_scratch_bytes": (SZ, [cfgp]),
+        "iskv_maintain": (I, [P, I]),
+        "iskv_switch": (I, [P, I, I]),
         "iskv_destroy": (I, [P]),
         "iskv_strerror": (ctypes.c_char_p, [I]),
     }
@@ -118,9 +122,15 @@ def strerror(code: int) -> str:
 
 def make_config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window,
                 max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64,
-                protected_prefix=0, rank_v=0) -> Config:
+                protected_prefix=0, rank_v=0, async_maintenance=0) -> Config:
     return Config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window, block,
-                  max_tokens, storage, rope_base, softmax_scale, protected_prefix, rank_v)
+                  max_tokens, storage, rope_base, softmax_scale, protected_prefix, rank_v,
+                  async_maintenance)
+
+
+def ring_slots(cfg: Config) -> int:
+    """Ring rows per unit: window + 64, and 64 more with copy-on-write maintenance."""
+    return cfg.window + cfg.block * (2 if cfg.async_maintenance else 1)
 
 
 def factor_ranks(cfg: Config):
@@ -309,6 +319,19 @@ class IskvCache:
     def join_maintenance(self, layer: int = -1) -> None:
         _check(lib().iskv_join_maintenance(self.ctx, layer), "iskv_join_maintenance")
 
+    def maintain(self, layer: int = -1) -> None:
+        """Copy-on-write maintenance (async_maintenance contexts): enqueue the
+        fold + sync of the layer into its other generation and return."""
+        _check(lib().iskv_maintain(self.ctx, layer), "iskv_maintain")
+
+    def switch(self, layer: int, wait: bool = False) -> bool:
+        """Switch the layer to its new generation if its maintenance finished
+        (wait: order the init stream after it).  True if it switched."""
+        r = lib().iskv_switch(self.ctx, layer, 1 if wait else 0)
+        if r < 0:
+            _check(r, "iskv_switch")
+        return r == 1
+
     def destroy(self):
         if getattr(self, "ctx", None):
             lib().iskv_destroy(self.ctx)
@@ -327,7 +350,7 @@ def unpack_state(cfg: Config, blob):
     """Split a state blob into numpy arrays per (unit, K|V); n_c is the
     compressed token count (rows protected_prefix .. protected_prefix+n_c-1)."""
     import numpy as np
-    d, T, S = cfg.head_dim, cfg.max_tokens, cfg.window + cfg.block
+    d, T, S = cfg.head_dim, cfg.max_tokens, ring_slots(cfg)
     ranks = factor_ranks(cfg)
     Pp = cfg.protected_prefix
     length, n_c = np.frombuffer(bytes(blob[:16]), dtype=np.int64)
@@ -355,7 +378,7 @@ def pack_state(cfg: Config, length: int, n_c: int, units) -> bytearray:
     position), ring and, with a protected prefix, prefix arrays.  The blob is
     filled in place, so a generator of units never holds more than one unit."""
     import numpy as np
-    d, T, S = cfg.head_dim, cfg.max_tokens, cfg.window + cfg.block
+    d, T, S = cfg.head_dim, cfg.max_tokens, ring_slots(cfg)
     ranks = factor_ranks(cfg)
     Pp = cfg.protected_prefix
     blob = bytearray(state_bytes(cfg))

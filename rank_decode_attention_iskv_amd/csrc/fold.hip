@@ -630,11 +630,15 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   if (!seq_in(tab, u / Dm.kv_heads)) return;    // ragged: a sequence whose ring is not full
   if (tab.n) n_c = tab.nc[u / Dm.kv_heads];
   const int tid = threadIdx.x;
-  LayerPtrs P = layer_ptrs(M, layer);
-  float *basis = P.basis[X] + (size_t)u * D * R;
-  float *sing = P.sing[X] + (size_t)u * R;
+  // reads the layer's current generation; writes the new basis, S and block
+  // coefficients into the same one, or (copy-on-write) into the other
+  LayerPtrs P = layer_ptrs(M, layer), Po = layer_ptrs_out(M, layer);
+  const float *basis = P.basis[X] + (size_t)u * D * R;
+  const float *sing = P.sing[X] + (size_t)u * R;
+  float *basis_out = Po.basis[X] + (size_t)u * D * R;
+  float *sing_out = Po.sing[X] + (size_t)u * R;
   float *msync = P.msync[X] + (size_t)u * R * R;
-  T *coef = reinterpret_cast<T *>(P.coef[X]) + (size_t)u * Dm.max_tokens * R;
+  T *coef = reinterpret_cast<T *>(Po.coef[X]) + (size_t)u * Dm.max_tokens * R;
   const T *ring = reinterpret_cast<const T *>(X == 0 ? P.ringk : P.ringv) +
                   (size_t)u * Dm.slots * D;
   const int s0 = (int)(n_c % Dm.slots);
@@ -937,9 +941,9 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   __syncthreads();                 // M (which reads the old basis) is done
   for (int i = tid; i < D * R / 4; i += kThreads) {
     const int f = (4 * i) / R, c = (4 * i) % R;
-    st4(basis + 4 * i, ld4(sBn + f * LB + c));
+    st4(basis_out + 4 * i, ld4(sBn + f * LB + c));
   }
-  if (tid < R) sing[tid] = sig[perm[tid]];
+  if (tid < R) sing_out[tid] = sig[perm[tid]];
 }
 
 template <int R, typename T>

@@ -39,6 +39,7 @@ struct LayerState {
   bool pending = false;
   int64_t folds = 0;
   int64_t syncs = 0;
+  bool inflight = false;    // copy-on-write: a maintenance of this layer is enqueued
   bool ragged = false;
   std::vector<SeqState> seq;
 };
@@ -63,6 +64,8 @@ bool valid_config(const iskv_config *c) {
   if (!std::isfinite(c->softmax_scale)) return false;
   if (c->protected_prefix < 0 || c->protected_prefix % kBlock || c->protected_prefix > c->max_tokens)
     return false;
+  if (c->async_maintenance != 0 && c->async_maintenance != 1) return false;
+  if (c->async_maintenance && c->num_layers > 64) return false;   // one generation bit per layer
   return true;
 }
 
@@ -77,7 +80,8 @@ Dims make_dims(const iskv_config *c) {
   D.rk = c->rank;
   D.rv = c->rank_v ? c->rank_v : c->rank;
   D.window = c->window;
-  D.slots = c->window + kBlock;
+  D.cow = c->async_maintenance;
+  D.slots = c->window + kBlock * (1 + D.cow);     // copy-on-write: a block of slack
   D.max_tokens = c->max_tokens;
   D.storage = c->storage;
   D.elem = c->storage == ISKV_BF16 ? 2 : 4;
@@ -133,6 +137,8 @@ struct iskv_ctx {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<hipEvent_t> ev_done;
   std::vector<char> maint_pending;
+  // copy-on-write: per-layer event recorded after the layer's maintenance
+  std::vector<hipEvent_t> ev_cow;
 };
 
 namespace {
@@ -145,6 +151,33 @@ int check_layer(const iskv_ctx *c, int layer) {
 
 void make_ragged(const iskv_ctx *c, LayerState &L);
 bool make_uniform(LayerState &L);
+
+// A block can be folded: the ring holds window + 64 rows past the compressed
+// ones (and, with copy-on-write, no maintenance is in flight).
+bool block_ready(const iskv_ctx *c, const LayerState &L) {
+  const int64_t held = L.length - L.n_c;
+  if (c->D.cow) return !L.inflight && held >= c->D.window + kBlock;
+  return held == c->D.slots;
+}
+
+// Copy-on-write decode boundary: switch `layer` to the generation its
+// maintenance wrote once that has finished (wait: make the init stream wait
+// for it).  1 switched, 0 not, < 0 error code.
+int cow_switch(iskv_ctx *c, int layer, bool wait) {
+  LayerState &L = c->layers[layer];
+  if (!c->D.cow || !L.inflight) return 0;
+  if (!wait) {
+    const hipError_t q = hipEventQuery(c->ev_cow[layer]);
+    if (q == hipErrorNotReady) return 0;
+    if (q != hipSuccess) return ISKV_EDEVICE;
+  }
+  // finished or not, later init-stream work is ordered after it
+  if (hipStreamWaitEvent(c->stream, c->ev_cow[layer], 0) != hipSuccess) return ISKV_EDEVICE;
+  c->M.gen_mask ^= 1ull << layer;
+  L.n_c += kBlock;
+  L.inflight = false;
+  return 1;
+}
 
 SeqState seq_state(const LayerState &L, int b) {
   return L.ragged ? L.seq[(size_t)b] : SeqState{L.length, L.n_c, L.pending};
@@ -365,6 +398,8 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   M.layer_stride = c->G.layer.bytes;
   M.lay = c->G.layer;
   M.D = c->D;
+  M.gen_mask = 0;
+  M.out_flip = 0;
   M.sh.rec = reinterpret_cast<float *>(base + c->G.rec);
   M.sh.recml = reinterpret_cast<float *>(base + c->G.recml);
   M.sh.cnt = reinterpret_cast<unsigned *>(base + c->G.cnt);
@@ -390,6 +425,11 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
   }
   // the allocation-free decode's split records (one lookup per device)
   hipError_t e = scratch_setup(c->device);
+  if (c->D.cow) {
+    c->ev_cow.assign(c->D.layers, nullptr);
+    for (hipEvent_t &ev : c->ev_cow)
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  }
   if (e == hipSuccess) e = hipMemsetAsync(dev_ws, 0, c->G.total, c->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(base + c->G.rope_anchor, anchor.data(), anchor.size() * 4,
@@ -410,6 +450,8 @@ int iskv_init(const iskv_config *cfg, void *dev_ws, size_t ws_bytes, void *hip_s
     if (c->aux) (void)hipStreamDestroy(c->aux);
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+    for (hipEvent_t ev : c->ev_cow)
+      if (ev) (void)hipEventDestroy(ev);
     delete c;
     return ISKV_EDEVICE;
   }
@@ -423,6 +465,12 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
   LayerState &L = c->layers[layer];
   if (!make_uniform(L)) return ISKV_ESTATE;
+  if (c->D.cow) {
+    // decode boundary; an append that would overflow the ring waits for the switch
+    int r = cow_switch(c, layer, false);
+    if (r >= 0 && L.length + n_tokens - L.n_c > c->D.slots) r = cow_switch(c, layer, true);
+    if (r < 0) return r;
+  }
   // ring tokens after the append: the positions from n_c on (>= P)
   if (L.length + n_tokens - L.n_c > c->D.slots) return ISKV_ESTATE;
   if (L.length + n_tokens > c->D.max_tokens) return ISKV_ESTATE;
@@ -430,12 +478,13 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
   hipError_t e = launch_append(c->M, layer, dev_k, dev_v, n_tokens, in_dtype, L.length, c->stream);
   if (e != hipSuccess) return ISKV_EDEVICE;
   L.length += n_tokens;
-  if (blocks_ready) *blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
+  if (blocks_ready) *blocks_ready = block_ready(c, L) ? 1 : 0;
   return ISKV_OK;
 }
 
 int iskv_block_update(iskv_ctx *c, int layer) {
   if (!c) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;           // iskv_maintain
   std::vector<int> idx;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
@@ -489,6 +538,7 @@ int iskv_block_update(iskv_ctx *c, int layer) {
 
 int iskv_sync(iskv_ctx *c, int layer) {
   if (!c) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;
   std::vector<int> idx;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
@@ -537,6 +587,7 @@ int iskv_sync(iskv_ctx *c, int layer) {
 
 int iskv_discard_sync(iskv_ctx *c, int layer) {
   if (!c) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;
   if (layer >= 0) {
     if (check_layer(c, layer)) return ISKV_EINVAL;
     LayerState &L = c->layers[layer];
@@ -565,6 +616,8 @@ int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, 
   LayerState &L = c->layers[layer];
   if (!make_uniform(L)) return ISKV_ESTATE;
   if (L.length <= 0) return ISKV_ESTATE;
+  const int r = cow_switch(c, layer, false);   // decode boundary
+  if (r < 0) return r;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   return hip_err(launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length, L.n_c, c->stream));
 }
@@ -580,6 +633,8 @@ int iskv_decode_attn_noalloc(iskv_ctx *c, int layer, const float *dev_q, int64_t
   if (L.length <= 0) return ISKV_ESTATE;
   uint8_t *base = reinterpret_cast<uint8_t *>(scratch_address(c->device));
   if (!base) return ISKV_EDEVICE;
+  const int r = cow_switch(c, layer, false);   // decode boundary
+  if (r < 0) return r;
   Model M = c->M;
   M.sh.rec = reinterpret_cast<float *>(base + R.rec);
   M.sh.recml = reinterpret_cast<float *>(base + R.recml);
@@ -600,6 +655,11 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
   if (q_pos < 0 || q_pos >= (int64_t)c->D.rope_anchors * kRopeAnchor) return ISKV_EINVAL;
   LayerState &L = c->layers[layer];
   if (!make_uniform(L)) return ISKV_ESTATE;
+  if (c->D.cow) {
+    int r = cow_switch(c, layer, false);        // decode boundary
+    if (r >= 0 && L.length - L.n_c + 1 > c->D.slots) r = cow_switch(c, layer, true);
+    if (r < 0) return r;
+  }
   if (L.length - L.n_c + 1 > c->D.slots) return ISKV_ESTATE;
   if (L.length + 1 > c->D.max_tokens) return ISKV_ESTATE;
   if (L.length < c->D.prefix) {
@@ -612,7 +672,7 @@ int iskv_append_decode(iskv_ctx *c, int layer, const void *dev_k, const void *de
   hipError_t e = launch_decode(c->M, layer, dev_q, q_pos, dev_out, L.length + 1, L.n_c, c->stream, app);
   if (e != hipSuccess) return ISKV_EDEVICE;
   L.length += 1;
-  if (blocks_ready) *blocks_ready = (L.length - L.n_c == c->D.slots) ? 1 : 0;
+  if (blocks_ready) *blocks_ready = block_ready(c, L) ? 1 : 0;
   return ISKV_OK;
 }
 
@@ -626,8 +686,8 @@ int fill_status(iskv_ctx *c, int layer, const SeqState &q, iskv_status_t *st) {
   std::memset(st, 0, sizeof(*st));
   st->length = q.length;
   st->compressed = q.n_c - c->D.prefix;
-  st->blocks_ready = (q.length - q.n_c == c->D.slots) ? 1 : 0;
-  st->pending_sync = q.pending ? 1 : 0;
+  st->blocks_ready = L.ragged ? ((q.length - q.n_c == c->D.slots) ? 1 : 0) : (block_ready(c, L) ? 1 : 0);
+  st->pending_sync = (q.pending || L.inflight) ? 1 : 0;
   st->folds = L.folds;
   st->syncs = L.syncs;
   st->persistent_bytes = persistent_bytes(c);
@@ -658,6 +718,7 @@ int iskv_append_ragged(iskv_ctx *c, int layer, const void *dev_k, const void *de
   if (!c || check_layer(c, layer) || !dev_k || !dev_v || !counts || n_tokens < 0) return ISKV_EINVAL;
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
   if (c->D.batch > kMaxSeqTab) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;
   LayerState &L = c->layers[layer];
   for (int b = 0; b < c->D.batch; ++b) {
     if (counts[b] < 0 || counts[b] > n_tokens) return ISKV_EINVAL;
@@ -692,6 +753,7 @@ int iskv_decode_attn_ragged(iskv_ctx *c, int layer, const float *dev_q, const in
                             float *dev_out) {
   if (!c || check_layer(c, layer) || !dev_q || !q_pos || !dev_out) return ISKV_EINVAL;
   if (c->D.batch > kMaxSeqTab) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;
   const LayerState &L = c->layers[layer];
   SeqTab tab{};
   tab.n = c->D.batch;
@@ -712,10 +774,13 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   if (!c || check_layer(c, layer) || !host_buf) return ISKV_EINVAL;
   if (!make_uniform(c->layers[layer])) return ISKV_ESTATE;
   if (bytes < iskv_state_bytes(&c->cfg)) return ISKV_EINVAL;
+  const int sw = cow_switch(c, layer, true);   // a maintenance in flight is joined first
+  if (sw < 0) return sw;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   const Dims &D = c->D;
   const LayerLayout &Ly = c->G.layer;
+  const GenLayout &Gn = Ly.gen[layer_gen(c->M, layer)];
   const size_t lb = Ly.bytes;
   std::vector<uint8_t> raw(lb);
   const uint8_t *src = c->M.base + c->G.layers_base + (size_t)layer * lb;
@@ -739,11 +804,11 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   for (int u = 0; u < D.units; ++u) {
     for (int x = 0; x < 2; ++x) {
       const size_t r = x ? D.rv : D.rk;
-      std::memcpy(f, raw.data() + Ly.basis[x] + (size_t)u * D.d * r * 4, (size_t)D.d * r * 4);
+      std::memcpy(f, raw.data() + Gn.basis[x] + (size_t)u * D.d * r * 4, (size_t)D.d * r * 4);
       f += (size_t)D.d * r;
-      std::memcpy(f, raw.data() + Ly.sing[x] + (size_t)u * r * 4, r * 4);
+      std::memcpy(f, raw.data() + Gn.sing[x] + (size_t)u * r * 4, r * 4);
       f += r;
-      const size_t coff = Ly.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
+      const size_t coff = Gn.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
       for (size_t i = 0; i < (size_t)D.max_tokens * r; ++i)
         f[i] = (i >= (size_t)D.prefix * r && i < (size_t)L.n_c * r) ? elem(coff, i) : 0.f;
       f += (size_t)D.max_tokens * r;
@@ -780,9 +845,12 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   if (length < 0 || n_comp < 0 || n_comp % kBlock || length > D.max_tokens ||
       (n_comp > 0 && n_c > length) || length - n_c > D.slots)
     return ISKV_EINVAL;
+  const int sw = cow_switch(c, layer, true);   // a maintenance in flight is joined first
+  if (sw < 0) return sw;
   if (join_layer(c, layer) != hipSuccess) return ISKV_EDEVICE;
   if (hipStreamSynchronize(c->stream) != hipSuccess) return ISKV_EDEVICE;
   const LayerLayout &Ly = c->G.layer;
+  const GenLayout &Gn = Ly.gen[layer_gen(c->M, layer)];
   const size_t lb = Ly.bytes;
   std::vector<uint8_t> raw(lb, 0);
   auto put = [&](size_t off, size_t i, float v) {
@@ -797,11 +865,11 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   for (int u = 0; u < D.units; ++u) {
     for (int x = 0; x < 2; ++x) {
       const size_t r = x ? D.rv : D.rk;
-      std::memcpy(raw.data() + Ly.basis[x] + (size_t)u * D.d * r * 4, f, (size_t)D.d * r * 4);
+      std::memcpy(raw.data() + Gn.basis[x] + (size_t)u * D.d * r * 4, f, (size_t)D.d * r * 4);
       f += (size_t)D.d * r;
-      std::memcpy(raw.data() + Ly.sing[x] + (size_t)u * r * 4, f, r * 4);
+      std::memcpy(raw.data() + Gn.sing[x] + (size_t)u * r * 4, f, r * 4);
       f += r;
-      const size_t coff = Ly.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
+      const size_t coff = Gn.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
       for (size_t i = (size_t)D.prefix * r; i < (size_t)n_c * r; ++i) put(coff, i, f[i]);
       f += (size_t)D.max_tokens * r;
       for (int s = 0; s < D.slots; ++s)
@@ -857,15 +925,82 @@ int iskv_set_maintenance_stream(iskv_ctx *c, void *hip_stream) {
 
 int iskv_join_maintenance(iskv_ctx *c, int layer) {
   if (!c) return ISKV_EINVAL;
+  if (c->D.cow) {
+    if (layer != -1 && check_layer(c, layer)) return ISKV_EINVAL;
+    for (int l = (layer == -1 ? 0 : layer); l < (layer == -1 ? c->D.layers : layer + 1); ++l) {
+      const int r = cow_switch(c, l, true);
+      if (r < 0) return r;
+    }
+    return ISKV_OK;
+  }
   if (layer == -1) return hip_err(join_all(c));
   if (check_layer(c, layer)) return ISKV_EINVAL;
   return hip_err(join_layer(c, layer));
 }
 
+int iskv_maintain(iskv_ctx *c, int layer) {
+  if (!c) return ISKV_EINVAL;
+  if (!c->D.cow) return ISKV_ESTATE;
+  std::vector<int> idx;
+  if (layer >= 0) {
+    if (check_layer(c, layer)) return ISKV_EINVAL;
+    if (!block_ready(c, c->layers[layer])) return ISKV_ESTATE;
+    idx.push_back(layer);
+  } else if (layer == -1) {
+    for (int l = 0; l < c->D.layers; ++l)
+      if (block_ready(c, c->layers[l])) idx.push_back(l);
+  } else {
+    return ISKV_EINVAL;
+  }
+  if (idx.empty()) return ISKV_OK;
+  hipError_t se;
+  hipStream_t s = maint_stream(c, &se);     // after the init stream's work so far
+  if (se != hipSuccess) return ISKV_EDEVICE;
+  Model Mo = c->M;
+  Mo.out_flip = 1;                           // read the current generation, write the other
+  std::vector<bool> done(idx.size(), false);
+  for (size_t i = 0; i < idx.size(); ++i) {
+    if (done[i]) continue;
+    const int64_t n_c = c->layers[idx[i]].n_c;
+    std::vector<int> grp;
+    for (size_t j = i; j < idx.size(); ++j)
+      if (!done[j] && c->layers[idx[j]].n_c == n_c) { grp.push_back(idx[j]); done[j] = true; }
+    for (size_t from = 0; from < grp.size(); from += kMaxLayerSel) {
+      LayerSel sel;
+      fill_sel(sel, grp, from);
+      hipError_t e = for_factors(c, s, [&](int x, hipStream_t st) {
+        return launch_block_update(Mo, sel, n_c, x, st);
+      });
+      if (e == hipSuccess)
+        e = for_factors(c, s, [&](int x, hipStream_t st) { return launch_sync(Mo, sel, n_c, x, st); });
+      if (e == hipSuccess) e = launch_prep_frag(Mo, sel, s);
+      if (e != hipSuccess) return ISKV_EDEVICE;
+    }
+    for (int l : grp) {
+      LayerState &L = c->layers[l];
+      L.inflight = true;
+      L.folds += 1;
+      L.syncs += 1;
+      if (hipEventRecord(c->ev_cow[l], s) != hipSuccess) return ISKV_EDEVICE;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_switch(iskv_ctx *c, int layer, int wait) {
+  if (!c || check_layer(c, layer)) return ISKV_EINVAL;
+  if (!c->D.cow) return ISKV_ESTATE;
+  return cow_switch(c, layer, wait != 0);
+}
+
 int iskv_destroy(iskv_ctx *c) {
   if (!c) return ISKV_EINVAL;
   hipError_t e = join_all(c);
+  for (int l = 0; l < c->D.layers && e == hipSuccess && c->D.cow; ++l)
+    if (cow_switch(c, l, true) < 0) e = hipErrorUnknown;
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  for (hipEvent_t ev : c->ev_cow)
+    if (ev) (void)hipEventDestroy(ev);
   if (c->ev_main) (void)hipEventDestroy(c->ev_main);
   if (c->aux) (void)hipStreamDestroy(c->aux);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);

@@ -1,12 +1,15 @@
 // Internal layout and kernel-launch interface of libiskv (not part of the ABI).
 //
 // Device workspace, per layer (u = sequence * kv_heads + kv_head) and factor
-// X = K, V with its rank r_X (r_K = rank, r_V = rank_v):
+// X = K, V with its rank r_X (r_K = rank, r_V = rank_v), in one generation
+// (two with copy-on-write maintenance: the layer's current one, read by
+// decode, and the one its maintenance writes):
 //   basis[X]  float [U][d][r_X]         row f, column c (orthonormal columns)
 //   sing[X]   float [U][r_X]            singular values S
-//   msync[X]  float [U][r_X][r_X]       pending synchronization matrix M = B_old^T B_new
 //   coef[X]   T     [U][max_tokens][r_X]  coefficient rows (row = position)
 //   frag      bytes [U][4*d*r_K]        key basis in the decode kernel's MFMA operand order
+// and once per layer:
+//   msync[X]  float [U][r_X][r_X]       pending synchronization matrix M = B_old^T B_new
 //   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
 //   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
 //   prek   T     [U][P][d]           protected prefix keys, row = position (pre-RoPE)
@@ -44,6 +47,7 @@ struct Dims {
   int rope_anchors;       // anchors in the RoPE table
   int cus;                // compute units of the device (decode grid sizing)
   int prefix;             // P: protected exact positions 0..P-1 (multiple of 64)
+  int cow;                // 1: copy-on-write maintenance (two generations, 64 more slots)
 };
 
 // Pointers of one layer.
@@ -65,22 +69,34 @@ struct Shared {
 
 inline __host__ __device__ size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+struct GenLayout {
+  size_t basis[2], sing[2], coef[2], frag;
+};
+
 struct LayerLayout {
-  size_t basis[2], sing[2], msync[2], coef[2], frag, ringk, ringv, prek, prev, bytes;
+  GenLayout gen[2];       // gen[1] == gen[0] without copy-on-write
+  size_t msync[2], ringk, ringv, prek, prev, bytes;
 };
 
 inline LayerLayout layer_layout(const Dims &D) {
   LayerLayout L{};
   size_t o = 0;
   const size_t U = (size_t)D.units;
+  for (int g = 0; g < (D.cow ? 2 : 1); ++g) {
+    GenLayout &G = L.gen[g];
+    for (int x = 0; x < 2; ++x) {
+      const size_t r = x ? D.rv : D.rk;
+      G.basis[x] = o; o = align_up(o + U * D.d * r * 4);
+      G.sing[x] = o;  o = align_up(o + U * r * 4);
+      G.coef[x] = o;  o = align_up(o + U * (size_t)D.max_tokens * r * D.elem);
+    }
+    G.frag = o;  o = align_up(o + U * 4 * (size_t)D.d * D.rk);
+  }
+  if (!D.cow) L.gen[1] = L.gen[0];
   for (int x = 0; x < 2; ++x) {
     const size_t r = x ? D.rv : D.rk;
-    L.basis[x] = o; o = align_up(o + U * D.d * r * 4);
-    L.sing[x] = o;  o = align_up(o + U * r * 4);
     L.msync[x] = o; o = align_up(o + U * r * r * 4);
-    L.coef[x] = o;  o = align_up(o + U * (size_t)D.max_tokens * r * D.elem);
   }
-  L.frag = o;  o = align_up(o + U * 4 * (size_t)D.d * D.rk);
   L.ringk = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.ringv = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.prek = o;  o = align_up(o + (size_t)D.units * D.prefix * D.d * D.elem);
@@ -109,7 +125,9 @@ inline GlobalLayout global_layout(const Dims &D) {
   return G;
 }
 
-// Whole-workspace view handed to kernels by value.
+// Whole-workspace view handed to kernels by value.  Layer l's current
+// generation is bit l of gen_mask (copy-on-write, at most 64 layers); a launch
+// with out_flip = 1 reads the current generation and writes the other one.
 struct Model {
   uint8_t *base;          // workspace base
   size_t layers_base;     // offset of layer 0
@@ -117,6 +135,8 @@ struct Model {
   LayerLayout lay;        // offsets inside a layer
   Shared sh;
   Dims D;
+  uint64_t gen_mask;
+  int out_flip;
 };
 
 constexpr int kMaxLayerSel = 64;
@@ -125,21 +145,35 @@ struct LayerSel {
   int idx[kMaxLayerSel];
 };
 
-__host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
+__host__ __device__ inline int layer_gen(const Model &M, int l) {
+  return l < 64 ? (int)((M.gen_mask >> l) & 1ull) : 0;
+}
+
+// Pointers of layer l in generation g (the per-layer parts are shared).
+__host__ __device__ inline LayerPtrs layer_ptrs_gen(const Model &M, int l, int g) {
   uint8_t *b = M.base + M.layers_base + (size_t)l * M.layer_stride;
+  const GenLayout &G = M.lay.gen[g];
   LayerPtrs P;
   for (int x = 0; x < 2; ++x) {
-    P.basis[x] = (float *)(b + M.lay.basis[x]);
-    P.sing[x] = (float *)(b + M.lay.sing[x]);
+    P.basis[x] = (float *)(b + G.basis[x]);
+    P.sing[x] = (float *)(b + G.sing[x]);
     P.msync[x] = (float *)(b + M.lay.msync[x]);
-    P.coef[x] = b + M.lay.coef[x];
+    P.coef[x] = b + G.coef[x];
   }
-  P.frag = b + M.lay.frag;
+  P.frag = b + G.frag;
   P.ringk = b + M.lay.ringk;
   P.ringv = b + M.lay.ringv;
   P.prek = b + M.lay.prek;
   P.prev = b + M.lay.prev;
   return P;
+}
+
+// The generation a launch reads, and the one it writes.
+__host__ __device__ inline LayerPtrs layer_ptrs(const Model &M, int l) {
+  return layer_ptrs_gen(M, l, layer_gen(M, l));
+}
+__host__ __device__ inline LayerPtrs layer_ptrs_out(const Model &M, int l) {
+  return layer_ptrs_gen(M, l, layer_gen(M, l) ^ M.out_flip);
 }
 
 // Per-sequence values of a call over a ragged batch (sequences at different

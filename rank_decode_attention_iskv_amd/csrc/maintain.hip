@@ -86,7 +86,7 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.y];
   const int u = blockIdx.x;                    // key basis of unit u
-  LayerPtrs P = layer_ptrs(M, l);
+  LayerPtrs P = layer_ptrs_out(M, l);           // the generation the maintenance wrote
   const float *B = P.basis[0] + (size_t)u * D.d * D.rk;
   uint8_t *F = P.frag + (size_t)u * 4 * D.d * D.rk;
   const int r = D.rk, per = r / 4;            // coefficients per lane
@@ -118,7 +118,9 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // ---------------------------------------------------------------------------
 // Sync: C[t] <- C[t] M for rows t < n_old (page: FAQ "What is basis
 // synchronization?" -- every stored coefficient row is rewritten for the new
-// basis).  An N x r by r x r product, streamed once through HBM.
+// basis).  An N x r by r x r product, streamed once through HBM.  In place,
+// or, with copy-on-write maintenance, from the current generation into the
+// other one (a row is read in full before its output is written either way).
 //
 // bf16 storage: MFMA.  Each wave takes 8 (4 at r = 128) tiles of 16 rows
 // and computes C_new^T = M^T C^T: A operand = M^T as three bf16 parts
@@ -145,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   if (tab.n) n_old = tab.nc[u / D.kv_heads];
   LayerPtrs P = layer_ptrs(M, l);
   const float *Ms = P.msync[x] + (size_t)u * R * R;
-  uint16_t *C = reinterpret_cast<uint16_t *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
+  const uint16_t *C = reinterpret_cast<const uint16_t *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
+  uint16_t *Co = reinterpret_cast<uint16_t *>(layer_ptrs_out(M, l).coef[x]) + (size_t)u * D.max_tokens * R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, rho = lane >> 4;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TPW * 16;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
       if (tok < n_old) {
         const bf16x2 p0 = __builtin_convertvector((floatx2){acc[0], acc[1]}, bf16x2);
         const bf16x2 p1 = __builtin_convertvector((floatx2){acc[2], acc[3]}, bf16x2);
-        *reinterpret_cast<uint2_ *>(C + tok * R + mb * 16 + 4 * rho) =
+        *reinterpret_cast<uint2_ *>(Co + tok * R + mb * 16 + 4 * rho) =
             uint2_{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
       }
     }
@@ -225,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
   if (tab.n) n_old = tab.nc[u / D.kv_heads];
   LayerPtrs P = layer_ptrs(M, l);
   const float4 *Ms = reinterpret_cast<const float4 *>(P.msync[x] + (size_t)u * R * R);
-  float *C = reinterpret_cast<float *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
+  const float *C = reinterpret_cast<const float *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
+  float *Co = reinterpret_cast<float *>(layer_ptrs_out(M, l).coef[x]) + (size_t)u * D.max_tokens * R;
   for (int i = threadIdx.x; i < R * R / 4; i += blockDim.x) sM4[i] = Ms[i];
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
       // keep the scheduler from hoisting every LDS read of M at once
       if ((c & 15) == 15) __builtin_amdgcn_sched_barrier(0);
     }
-    *reinterpret_cast<float4 *>(C + t * R + k0) = make_float4(a0, a1, a2, a3);
+    *reinterpret_cast<float4 *>(Co + t * R + k0) = make_float4(a0, a1, a2, a3);
   }
 }
 

@@ -567,3 +567,55 @@ def test_persistent_bytes_with_separate_v_rank():
     k = 1000 * 32 * 2 + 128 * 32 * 4 + 32 * 4 + 300 * 128 * 2
     v = 1000 * 64 * 2 + 128 * 64 * 4 + 64 * 4 + 300 * 128 * 2
     assert got == 2 * 4 * (k + v)
+
+
+# ---------------------------------------------------------------------------
+# Deferred maintenance ["ASKV" design report, Design requirements: the new
+# version is built aside and switched to later].  With 64 rows of ring slack,
+# folding the ready block after k more appends gives exactly the state of a
+# unit that folded on time and then took the same k appends: the fold reads
+# only the block, B and S, none of which the later appends touch.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage,k", [("f32", 1), ("f32", 37), ("bf16", 64)])
+def test_deferred_fold_commutes_with_later_appends(storage, k):
+    rng = np.random.default_rng(55)
+    d, r, W, T = 128, 16, 128, 64
+    n = W + 2 * T + 64                        # two on-time folds, then the deferred one
+    X = rng.standard_normal((n + k, 2, d)) @ np.diag(np.linspace(2, 0.1, d))
+    on_time = Unit(d, r, W, 1024, storage)
+    late = Unit(d, r, W, 1024, storage, slack=64)
+    for p in range(n):
+        for u in (on_time, late):
+            u.append(X[p, 0], X[p, 1])
+            if u.ready and p < n - 1:
+                u.fold()
+                u.sync()
+    # the next block is ready (n - n_c = W + 64) in both; only on_time folds now
+    assert on_time.ready and late.ready
+    on_time.fold()
+    on_time.sync()
+    q = rng.standard_normal((4, d))
+    for p in range(n, n + k):
+        on_time.append(X[p, 0], X[p, 1])
+        late.append(X[p, 0], X[p, 1])         # the ring slack holds them
+    before = late.decode(q, n + k - 1, 1 / math.sqrt(d))
+    late.fold()
+    late.sync()
+    assert late.n_c == on_time.n_c
+    for a, b in ((late.K, on_time.K), (late.V, on_time.V)):
+        np.testing.assert_array_equal(a.B, b.B)
+        np.testing.assert_array_equal(a.S, b.S)
+        np.testing.assert_array_equal(a.C[:late.n_c], b.C[:late.n_c])
+    np.testing.assert_array_equal(late.decode(q, n + k - 1, 1 / math.sqrt(d)),
+                                  on_time.decode(q, n + k - 1, 1 / math.sqrt(d)))
+    # before the fold, the deferred unit is the pre-fold state: its block rows
+    # are still exact, so its decode differs from the folded one by the
+    # compression of that block (and the projection of the older history)
+    assert np.abs(before - on_time.decode(q, n + k - 1, 1 / math.sqrt(d))).max() > 0
+    # the slack is bounded: window + 128 rows past the compressed ones, no more
+    full = Unit(d, r, W, 1024, storage, slack=64)
+    for p in range(W + 128):
+        full.append(X[p, 0], X[p, 1])
+    with pytest.raises(RuntimeError):
+        full.append(X[0, 0], X[0, 1])
