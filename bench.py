@@ -175,8 +175,11 @@ class Generator:
         B, H, d, k = p["batch"], p["kv"], 128, p["signal"]
         shape = (n_layers, B, H, 2)
         if p["spectrum"] == "power":
+            # Haar-orthonormal columns: QR of a Gaussian matrix, on the host
+            # (a device QR is a library call the profilers' counter mode can fail in)
             z = torch.randn(*shape, d, d, device="cuda", generator=self.g)
-            o, _ = torch.linalg.qr(z)
+            o, _ = torch.linalg.qr(z.cpu())
+            o = o.cuda()
             s = 1.0 / torch.arange(1, k + 1, device="cuda", dtype=torch.float32)
             s = s * math.sqrt(d / float((s ** 2).sum()))
             self.mix = (o[..., :k] * s).transpose(-1, -2).contiguous()       # [.., k, d]
@@ -226,10 +229,15 @@ def state_bytes(p, n_c, n_e):
                                                   n_e * 256 * elem)
 
 
+DECODE_SOURCES = ("decode.hip", "device_common.hpp", "iskv_internal.hpp")
+
+
 def kernel_source_hash():
+    """Hash of the decode kernel's sources (the kernel the roofline and the
+    committed counter summaries describe)."""
     h = hashlib.sha256()
     src = os.path.join(ROOT, "rank_decode_attention_iskv_amd", "csrc")
-    for name in sorted(os.listdir(src)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(src, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
