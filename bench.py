@@ -102,6 +102,9 @@ def parse():
     ap.add_argument("--async-maintenance", action="store_true",
                     help="copy-on-write maintenance on a second stream (iskv_maintain / "
                          "iskv_switch) instead of block update + sync between decode steps")
+    ap.add_argument("--prefill", action="store_true",
+                    help="only compare prefill paths: a 32K prompt into 16 layers of the "
+                         "32K GQA workload, block by block vs iskv_prefill_layers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only stream a 256 MiB float32 tensor through an elementwise kernel "
                          "(x * 1 -> y) five times: the reference for HBM byte counters")
@@ -663,6 +666,57 @@ def measure_async(p, steps, warmup, instances, seed, quiet=False):
     return res
 
 
+def prefill_compare(p, layers=16, tokens=32768, seed=77):
+    """A prompt of `tokens` tokens into `layers` layers of one workload (the
+    32K GQA layer: 16 instances), twice: block by block (appends of up to 64
+    tokens, iskv_block_update(-1) + iskv_sync(-1) whenever the rings fill)
+    and with iskv_prefill_layers (every block folded in one pass, one
+    deferred synchronization per pass).  Inputs resident before timing; each
+    path timed by one HIP event pair on the stream."""
+    import torch
+
+    from rank_decode_attention_iskv_amd import binding
+    torch.cuda.set_device(0)
+    W = p["window"]
+    gen = Generator(torch, p, layers, seed)
+    ks, vs = [], []
+    for layer in range(layers):
+        k, v = gen.tokens(layer, tokens)
+        ks.append(k.contiguous())
+        vs.append(v.contiguous())
+    out = {"tokens": tokens, "layers": layers, "folds_per_layer": (tokens - W) // 64}
+    for mode in ("block_by_block", "bulk"):
+        cfg = binding.make_config(p["batch"], layers, p["kv"], p["q"], 128, p["rank"], W, tokens + 64,
+                                  p["storage"], rank_v=p["rank_v"])
+        cache = binding.IskvCache(cfg)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if mode == "bulk":
+            cache.prefill_layers(list(range(layers)), ks, vs)
+        else:
+            pos, n_c = 0, 0
+            while pos < tokens:
+                take = min(64, tokens - pos, W + 64 - (pos - n_c))
+                ready = False
+                for layer in range(layers):
+                    ready = cache.append(layer, ks[layer][:, pos:pos + take].contiguous(),
+                                         vs[layer][:, pos:pos + take].contiguous())
+                pos += take
+                if ready:
+                    cache.block_update(-1)
+                    cache.sync(-1)
+                    n_c += 64
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[mode + "_ms"] = e0.elapsed_time(e1)
+        out[mode + "_compressed"] = cache.status(0).compressed
+        cache.destroy()
+    out["speedup"] = out["block_by_block_ms"] / out["bulk_ms"]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on the host cores, bounded sample
 # ---------------------------------------------------------------------------
@@ -876,6 +930,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.prefill:
+        print(json.dumps(prefill_compare(preset(args, 2))), flush=True)
+        return
     if args.ragged:
         ragged_bench(args)
         return
@@ -945,6 +1002,7 @@ def main():
             pts.append(dict(rank=rank, window=window, **compact(measure(p5, 32, 8, 0, args.seed + 5,
                                                                         quiet=True), p5)))
         extras["config5_sweep"] = pts
+        extras["config2_prefill_32k_16_layers"] = prefill_compare(preset(args, 2))
         res["extras"] = extras
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(p)
     print(json.dumps(res), flush=True)

@@ -282,6 +282,36 @@ int iskv_set_maintenance_stream(iskv_ctx *c, void *hip_stream);
  * place the wait, e.g. outside a timed interval.)  EINVAL for a bad layer. */
 int iskv_join_maintenance(iskv_ctx *c, int layer);
 
+/* Prefill: append n_tokens prompt tokens (dev_k, dev_v: [batch][n_tokens]
+ * [num_kv_heads][head_dim], device, in_dtype ISKV_F32 or ISKV_BF16) to a
+ * layer whose ring is empty (length = P + N_c, P positions of protected
+ * prefix already appended), folding every block that leaves the window in
+ * one pass: m = (n_tokens - window) / 64 blocks (0 if n_tokens < window + 64),
+ * the same blocks, in the same order, that appending the tokens and folding
+ * + synchronizing each time the ring fills would fold [iS-KV explainer, the
+ * trade-off paragraph: the prompt is compressed like the generated tokens].
+ * The folds read the blocks straight from the input (rounded to the storage
+ * type, as the ring would hold them) and are the same fold; the
+ * synchronizations are deferred: each older row is mapped once by the
+ * product of every later M instead of once per fold, which reads and writes
+ * the history once per pass (a pass covers up to 64 MiB of M matrices)
+ * instead of once per block; the results equal block-by-block
+ * synchronization up to the rounding order of those products.  The last
+ * n_tokens - 64 m tokens (window .. window + 63 of them) go to the ring.
+ * ESTATE: ring not empty, pending sync, protected prefix not yet full,
+ * max_tokens exceeded, or a copy-on-write context.  Counters: folds += m,
+ * syncs += passes. */
+int iskv_prefill(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                 int in_dtype);
+
+/* iskv_prefill of n_layers distinct layers (layers: host int32 array;
+ * dev_k, dev_v: host arrays of device pointers, one input per layer) in the
+ * same launches: every layer must hold the same length and compressed count.
+ * The layers' folds run side by side (one workgroup per layer, unit and
+ * factor), up to 16 layers per launch, sharing the M slots of one pass. */
+int iskv_prefill_layers(iskv_ctx *c, int n_layers, const int *layers, const void *const *dev_k,
+                        const void *const *dev_v, int n_tokens, int in_dtype);
+
 /* Copy-on-write maintenance (contexts with async_maintenance = 1; ESTATE
  * otherwise) ["ASKV" design report, Design requirements: compression must not
  * hold up generation; the new cache version is built aside and switched to

@@ -341,6 +341,52 @@ class Unit:
         self.K.sync(old)
         self.V.sync(old)
 
+    def prefill(self, ks, vs):
+        """Append prompt rows ks, vs (n x d) to a unit whose ring is empty,
+        folding every block that leaves the window with its synchronization
+        deferred: the blocks are folded in order exactly as appends would fold
+        them, and afterwards each older row is multiplied once by the product
+        of every M that came after it was written (the rows before the first
+        block by M_0 ... M_{m-1}, block j's rows by M_{j+1} ... M_{m-1}).  Equal
+        to folding and synchronizing block by block, by associativity, up to
+        where the stores round.  Reading of the pages: the prompt is compressed
+        like generated tokens [iS-KV explainer, the trade-off paragraph]; the
+        single deferred synchronization is this library's restructuring."""
+        ks = np.asarray(ks, dtype=np.float64)
+        vs = np.asarray(vs, dtype=np.float64)
+        if self.length != self.n_c or self.length < self.P:
+            raise RuntimeError("prefill needs an empty ring")
+        n = ks.shape[0]
+        m = (n - self.window) // self.block if n >= self.window + self.block else 0
+        n_c0 = self.n_c
+        for f, xs in ((self.K, ks), (self.V, vs)):
+            Ms = []
+            for j in range(m):
+                rows = store_round(xs[j * self.block:(j + 1) * self.block], f.storage)
+                Bn, Sn, M, C_blk = brand_fold(rows, f.B, f.S)
+                f.C[n_c0 + j * self.block: n_c0 + (j + 1) * self.block] = store_round(C_blk, f.storage)
+                f.B, f.S = Bn, Sn
+                Ms.append(M)
+            if m:
+                # suffix products S_j = M_j ... M_{m-1}
+                suf = [None] * (m + 1)
+                suf[m] = np.eye(f.r)
+                for j in range(m - 1, -1, -1):
+                    suf[j] = Ms[j] @ suf[j + 1]
+                P = f.P
+                f.C[P:n_c0] = store_round(f.C[P:n_c0] @ suf[0], f.storage)
+                for j in range(m - 1):
+                    a, b = n_c0 + j * self.block, n_c0 + (j + 1) * self.block
+                    f.C[a:b] = store_round(f.C[a:b] @ suf[j + 1], f.storage)
+        self.n_c = n_c0 + m * self.block
+        for t in range(n):
+            pos = self.length + t
+            if pos >= self.n_c:
+                self.K.write(pos, ks[t])
+                self.V.write(pos, vs[t])
+        self.length += n
+        return m
+
     def decode(self, q, q_pos, scale, rope_base=10000.0):
         """Softmax attention of the query rows q (g x d) over every position.
 
@@ -448,6 +494,15 @@ class Oracle:
         for b in range(self.batch):
             for h in range(self.kv_heads):
                 self.units[b][layer][h].sync()
+
+    def prefill(self, layer, k, v):
+        """Unit.prefill for every (sequence, KV head) of the layer; k, v are
+        [batch, n, kv_heads, d]."""
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        for b in range(self.batch):
+            for h in range(self.kv_heads):
+                self.units[b][layer][h].prefill(k[b, :, h], v[b, :, h])
 
     def decode_attn(self, layer, q, q_pos):
         q = np.asarray(q, dtype=np.float64)

@@ -52,7 +52,7 @@ EXPORTED = (
     "iskv_join_maintenance", "iskv_destroy", "iskv_strerror",
     "iskv_append_ragged", "iskv_decode_attn_ragged", "iskv_seq_status",
     "iskv_decode_attn_noalloc", "iskv_noalloc_scratch_bytes",
-    "iskv_maintain", "iskv_switch",
+    "iskv_maintain", "iskv_switch", "iskv_prefill", "iskv_prefill_layers",
 )
 
 
@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "iskv_noalloc_scratch_bytes": (SZ, [cfgp]),
         "iskv_maintain": (I, [P, I]),
         "iskv_switch": (I, [P, I, I]),
+        "iskv_prefill": (I, [P, I, P, P, I, I]),
+        "iskv_prefill_layers": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(P), ctypes.POINTER(P), I, I]),
         "iskv_destroy": (I, [P]),
         "iskv_strerror": (ctypes.c_char_p, [I]),
     }
@@ -318,6 +320,39 @@ class IskvCache:
 
     def join_maintenance(self, layer: int = -1) -> None:
         _check(lib().iskv_join_maintenance(self.ctx, layer), "iskv_join_maintenance")
+
+    def prefill(self, layer: int, k, v) -> None:
+        """Prompt tokens k, v (device tensors [batch, n, kv_heads, head_dim],
+        float32 or bfloat16) appended to a layer with an empty ring, every
+        block that leaves the window folded in one pass (iskv_prefill)."""
+        torch = self.torch
+        if k.dtype != v.dtype or k.shape != v.shape or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k, v must be float32 or bfloat16")
+        dt = BF16 if k.dtype == torch.bfloat16 else F32
+        _check(lib().iskv_prefill(self.ctx, layer, ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), int(k.shape[1]), dt), "iskv_prefill")
+
+    def prefill_layers(self, layers, ks, vs) -> None:
+        """iskv_prefill_layers: one input (k, v device tensors [batch, n, kv_heads,
+        head_dim], all of one shape and dtype) per layer."""
+        torch = self.torch
+        n = len(layers)
+        if not (len(ks) == len(vs) == n) or n == 0:
+            raise ValueError("one k and one v per layer")
+        for k, v in zip(ks, vs):
+            if k.dtype != ks[0].dtype or k.shape != ks[0].shape or v.shape != k.shape or \
+                    v.dtype != k.dtype or not k.is_contiguous() or not v.is_contiguous():
+                raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        if ks[0].dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k, v must be float32 or bfloat16")
+        dt = BF16 if ks[0].dtype == torch.bfloat16 else F32
+        la = (ctypes.c_int * n)(*layers)
+        kp = (ctypes.c_void_p * n)(*[k.data_ptr() for k in ks])
+        vp = (ctypes.c_void_p * n)(*[v.data_ptr() for v in vs])
+        _check(lib().iskv_prefill_layers(self.ctx, n, la, kp, vp, int(ks[0].shape[1]), dt),
+               "iskv_prefill_layers")
 
     def maintain(self, layer: int = -1) -> None:
         """Copy-on-write maintenance (async_maintenance contexts): enqueue the

@@ -611,37 +611,23 @@ __device__ int jacobi_rows(float *core, float *nrm, int *rank, int *lead, int ke
   return kMaxSweeps + 1;
 }
 
-template <int R, typename T>
-__global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSel sel,
-                                                                int64_t n_c, int xsel, SeqTab tab) {
+// One Brand fold of a unit's factor: the block's 64 rows come from load_A
+// (fills sA, row stride LA, and returns this thread's share of ||A||_F^2;
+// called twice), B and S are read from basis / sing, the new ones written to
+// basis_out / sing_out (which may be the same arrays), M to msync and the
+// block's coefficient rows to coef at rows n_c .. n_c + 63.
+template <int R, typename T, typename Loader>
+__device__ __forceinline__ void fold_one(const Model &M, float *lds, const float *basis, const float *sing,
+                                         float *basis_out, float *sing_out, float *msync, T *coef,
+                                         int64_t n_c, Loader load_A) {
   using Ly = FoldLayout<R>;
   constexpr int D = kHeadDim, TB = kBlock, N = Ly::N, NC = Ly::NC;
   constexpr int LA = Ly::LA, LB = Ly::LB, LG = Ly::LG, LC = Ly::LC;
   constexpr bool kRes = Ly::kRes;
-  extern __shared__ float4 lds4[];
-  float *lds = reinterpret_cast<float *>(lds4);
   __shared__ float red[kThreads / 64];
   __shared__ int s_int[4];
   __shared__ float s_f[4];
-  const Dims &Dm = M.D;
-  const int layer = sel.idx[blockIdx.y];
-  // grid.x: units (one factor, xsel) or units x 2 (both factors, equal ranks)
-  const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
-  if (!seq_in(tab, u / Dm.kv_heads)) return;    // ragged: a sequence whose ring is not full
-  if (tab.n) n_c = tab.nc[u / Dm.kv_heads];
   const int tid = threadIdx.x;
-  // reads the layer's current generation; writes the new basis, S and block
-  // coefficients into the same one, or (copy-on-write) into the other
-  LayerPtrs P = layer_ptrs(M, layer), Po = layer_ptrs_out(M, layer);
-  const float *basis = P.basis[X] + (size_t)u * D * R;
-  const float *sing = P.sing[X] + (size_t)u * R;
-  float *basis_out = Po.basis[X] + (size_t)u * D * R;
-  float *sing_out = Po.sing[X] + (size_t)u * R;
-  float *msync = P.msync[X] + (size_t)u * R * R;
-  T *coef = reinterpret_cast<T *>(Po.coef[X]) + (size_t)u * Dm.max_tokens * R;
-  const T *ring = reinterpret_cast<const T *>(X == 0 ? P.ringk : P.ringv) +
-                  (size_t)u * Dm.slots * D;
-  const int s0 = (int)(n_c % Dm.slots);
 
   float *sB = lds + Ly::oB, *sQ = lds + Ly::oQ, *sA = lds + Ly::oA, *sP = lds + Ly::oP;
   float *sG = lds + Ly::oG, *core = lds + Ly::oCore;
@@ -654,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   if constexpr (kRes) { Bsrc = sB; ldB = LB; } else { Bsrc = basis; ldB = R; }
 
   // ---------------- phase 1: load, projection (twice) ----------------
-  const float asq = load_block<T, LA>(ring, X, s0, Dm.slots, sA);
+  const float asq = load_A(sA);
   if constexpr (kRes) {
     for (int i = tid; i < D * R / 4; i += kThreads) {
       const int f = (4 * i) / R, c = (4 * i) % R;
@@ -933,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
   gemm4<R, R, D, true, false>(Bsrc, ldB, sBn, LB,
                               [&](int c, int k, float v) { msync[c * R + k] = v; });
   // the block again (the core region over A is free now)
-  (void)load_block<T, LA>(ring, X, s0, Dm.slots, sA);
+  (void)load_A(sA);
   __syncthreads();
   gemm4<TB, R, D, false, false>(sA, LA, sBn, LB, [&](int t, int k, float v) {
     Store<T>::store(coef, (size_t)(n_c + t) * R + k, v);
@@ -944,6 +930,95 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSe
     st4(basis_out + 4 * i, ld4(sBn + f * LB + c));
   }
   if (tid < R) sing_out[tid] = sig[perm[tid]];
+}
+
+template <int R, typename T>
+__global__ __launch_bounds__(kThreads) void block_update_kernel(Model M, LayerSel sel,
+                                                                int64_t n_c, int xsel, SeqTab tab) {
+  constexpr int D = kHeadDim;
+  extern __shared__ float4 lds4[];
+  float *lds = reinterpret_cast<float *>(lds4);
+  const Dims &Dm = M.D;
+  const int layer = sel.idx[blockIdx.y];
+  // grid.x: units (one factor, xsel) or units x 2 (both factors, equal ranks)
+  const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
+  if (!seq_in(tab, u / Dm.kv_heads)) return;    // ragged: a sequence whose ring is not full
+  if (tab.n) n_c = tab.nc[u / Dm.kv_heads];
+  // reads the layer's current generation; writes the new basis, S and block
+  // coefficients into the same one, or (copy-on-write) into the other
+  LayerPtrs P = layer_ptrs(M, layer), Po = layer_ptrs_out(M, layer);
+  const T *ring = reinterpret_cast<const T *>(X == 0 ? P.ringk : P.ringv) + (size_t)u * Dm.slots * D;
+  const int s0 = (int)(n_c % Dm.slots), slots = Dm.slots;
+  fold_one<R, T>(M, lds, P.basis[X] + (size_t)u * D * R, P.sing[X] + (size_t)u * R,
+                 Po.basis[X] + (size_t)u * D * R, Po.sing[X] + (size_t)u * R,
+                 P.msync[X] + (size_t)u * R * R,
+                 reinterpret_cast<T *>(Po.coef[X]) + (size_t)u * Dm.max_tokens * R, n_c,
+                 [&](float *sA) { return load_block<T, FoldLayout<R>::LA>(ring, X, s0, slots, sA); });
+}
+
+// ---------------------------------------------------------------------------
+// Bulk folding of a prompt (prefill): one workgroup per (unit, factor) folds
+// nblk consecutive blocks in order, each read from the caller's input rows
+// (rounded to the storage type, as the ring would hold them) instead of the
+// ring, and leaves every block's M in mbulk (slot j) for one deferred
+// synchronization.  The fold itself is the same as above, block after block;
+// B and S pass from one block to the next through global memory, which the
+// workgroup's own barrier orders.
+// ---------------------------------------------------------------------------
+template <typename T, typename IN, int LA>
+__device__ float load_input_block(const IN *x, int64_t row0, int n_in, int b, int h, int kv, float *sA,
+                                  const Shared &S) {
+  constexpr int D = kHeadDim, TB = kBlock;
+  float asq = 0.f;
+  int bad = 0;
+  for (int i = threadIdx.x; i < TB * D / 8; i += kThreads) {
+    const int t = i / (D / 8), f0 = (i % (D / 8)) * 8;
+    float v[8];
+    load8<IN>(x + (((size_t)b * n_in + row0 + t) * kv + h) * D + f0, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (std::is_same<T, bf16_t>::value && std::is_same<IN, float>::value)
+        v[j] = bf16_to_f32(f32_to_bf16(v[j]));     // the value a bf16 ring row would hold
+      bad |= !isfinite(v[j]);
+      asq = fmaf(v[j], v[j], asq);
+    }
+    st4(sA + t * LA + f0, make_float4(v[0], v[1], v[2], v[3]));
+    st4(sA + t * LA + f0 + 4, make_float4(v[4], v[5], v[6], v[7]));
+  }
+  if (bad) set_flag(S, 4);
+  return asq;
+}
+
+template <int R, typename T, typename IN>
+__global__ __launch_bounds__(kThreads) void bulk_fold_kernel(Model M, BulkIn in, int64_t n_c0, int nblk,
+                                                             int xsel, int64_t row0, int n_in, float *mbulk,
+                                                             int bulk_blocks) {
+  constexpr int D = kHeadDim;
+  extern __shared__ float4 lds4[];
+  float *lds = reinterpret_cast<float *>(lds4);
+  const Dims &Dm = M.D;
+  const int li = blockIdx.y, layer = in.layer[li];
+  const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
+  const int b = u / Dm.kv_heads, h = u % Dm.kv_heads;
+  const IN *kin = reinterpret_cast<const IN *>(in.k[li]), *vin = reinterpret_cast<const IN *>(in.v[li]);
+  mbulk += (size_t)li * bulk_layer_floats(Dm, bulk_blocks);
+  LayerPtrs P = layer_ptrs(M, layer);
+  float *basis = P.basis[X] + (size_t)u * D * R;
+  float *sing = P.sing[X] + (size_t)u * R;
+  T *coef = reinterpret_cast<T *>(P.coef[X]) + (size_t)u * Dm.max_tokens * R;
+  const IN *x = X == 0 ? kin : vin;
+  // [factor][unit][block][R][R]; the V part follows the K part
+  float *mb = mbulk + (X ? (size_t)Dm.units * bulk_blocks * Dm.rk * Dm.rk : 0) +
+              (size_t)u * bulk_blocks * R * R;
+  for (int j = 0; j < nblk; ++j) {
+    const int64_t r0 = row0 + (int64_t)j * kBlock;
+    fold_one<R, T>(M, lds, basis, sing, basis, sing, mb + (size_t)j * R * R, coef,
+                   n_c0 + (int64_t)j * kBlock, [&](float *sA) {
+                     return load_input_block<T, IN, FoldLayout<R>::LA>(x, r0, n_in, b, h, Dm.kv_heads,
+                                                                       sA, M.sh);
+                   });
+    __syncthreads();                 // B, S of this block visible to the next one
+  }
 }
 
 template <int R, typename T>
@@ -976,7 +1051,108 @@ hipError_t dispatch_fold(const Model &M, const LayerSel &sel, int64_t n_c, int x
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Suffix products of a bulk fold's M_0 .. M_{n-1}: slot j becomes
+// S_j = M_j M_{j+1} ... M_{n-1} (slot n-1 keeps M_{n-1}).  Rows older than the
+// first block are synchronized by S_0, the rows of block j by S_{j+1}, the
+// last block's rows need nothing: each row then carries the product of every
+// M applied after it was written, as block-by-block synchronization would
+// have applied them one at a time.  One workgroup per (unit, factor); both
+// matrices of a step in LDS.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(256) void bulk_suffix_kernel(Model M, int nblk, int xsel, float *mbulk,
+                                                          int bulk_blocks) {
+  extern __shared__ float4 sfx4[];
+  float *sA = reinterpret_cast<float *>(sfx4), *sS = sA + R * R;
+  const Dims &Dm = M.D;
+  mbulk += (size_t)blockIdx.y * bulk_layer_floats(Dm, bulk_blocks);
+  const int u = xsel < 0 ? blockIdx.x >> 1 : blockIdx.x, X = xsel < 0 ? blockIdx.x & 1 : xsel;
+  float *mb = mbulk + (X ? (size_t)Dm.units * bulk_blocks * Dm.rk * Dm.rk : 0) +
+              (size_t)u * bulk_blocks * R * R;
+  constexpr int PER = (R * R + 255) / 256;
+  for (int e = threadIdx.x; e < R * R; e += 256) sS[e] = mb[(size_t)(nblk - 1) * R * R + e];
+  for (int j = nblk - 2; j >= 0; --j) {
+    for (int e = threadIdx.x; e < R * R; e += 256) sA[e] = mb[(size_t)j * R * R + e];
+    __syncthreads();
+    float acc[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = threadIdx.x + 256 * q;
+      float a = 0.f;
+      if (e < R * R) {
+        const int i = e / R, cc = e % R;
+#pragma unroll 8
+        for (int k = 0; k < R; ++k) a = fmaf(sA[i * R + k], sS[k * R + cc], a);
+      }
+      acc[q] = a;
+    }
+    __syncthreads();                 // every read of S done before it is replaced
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = threadIdx.x + 256 * q;
+      if (e < R * R) {
+        sS[e] = acc[q];
+        mb[(size_t)j * R * R + e] = acc[q];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int R, typename T, typename IN>
+hipError_t launch_bulk_t(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x,
+                         int64_t row0, int n_in, float *mbulk, int bulk_blocks, hipStream_t s) {
+  static bool attr = false;
+  const size_t bytes = FoldLayout<R>::bytes;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bulk_fold_kernel<R, T, IN>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid(x < 0 ? M.D.units * 2 : M.D.units, in.n);
+  hipLaunchKernelGGL((bulk_fold_kernel<R, T, IN>), grid, dim3(kThreads), bytes, s, M, in, n_c0, nblk, x,
+                     row0, n_in, mbulk, bulk_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nblk < 2) return e;
+  static bool sattr = false;
+  const size_t sbytes = (size_t)2 * R * R * 4;
+  if (!sattr) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bulk_suffix_kernel<R>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sbytes);
+    if (e != hipSuccess) return e;
+    sattr = true;
+  }
+  hipLaunchKernelGGL((bulk_suffix_kernel<R>), grid, dim3(256), sbytes, s, M, nblk, x, mbulk, bulk_blocks);  // grid.y: layers
+  return hipGetLastError();
+}
+
+template <typename T, typename IN>
+hipError_t dispatch_bulk(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x, int64_t row0,
+                         int n_in, float *mbulk, int bulk_blocks, hipStream_t s) {
+  const int r = x == 1 ? M.D.rv : M.D.rk;
+  if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
+  switch (r) {
+    case 16: return launch_bulk_t<16, T, IN>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+    case 32: return launch_bulk_t<32, T, IN>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+    case 64: return launch_bulk_t<64, T, IN>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+    case 128: return launch_bulk_t<128, T, IN>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_bulk_fold(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x, int in_dtype,
+                            int64_t row0, int n_in, float *mbulk, int bulk_blocks, hipStream_t s) {
+  if (nblk <= 0 || in.n <= 0) return hipSuccess;
+  if (M.D.storage == 1)
+    return in_dtype == 1 ? dispatch_bulk<bf16_t, bf16_t>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s)
+                         : dispatch_bulk<bf16_t, float>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+  return in_dtype == 1 ? dispatch_bulk<float, bf16_t>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s)
+                       : dispatch_bulk<float, float>(M, in, n_c0, nblk, x, row0, n_in, mbulk, bulk_blocks, s);
+}
 
 hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
                                const SeqTab &tab) {

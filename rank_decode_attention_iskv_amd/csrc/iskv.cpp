@@ -99,6 +99,16 @@ Dims make_dims(const iskv_config *c) {
   D.max_rec = per_unit;
   D.rope_anchors = (c->max_tokens + kBlock) / kRopeAnchor + 2;
   D.prefix = c->protected_prefix;
+  // prefill: M slots per unit for one bulk pass, within 64 MiB (ISKV_BULK_BLOCKS
+  // lowers the count, e.g. to exercise several passes)
+  const size_t per_block = (size_t)D.units * ((size_t)D.rk * D.rk + (size_t)D.rv * D.rv) * 4;
+  int64_t nb = (int64_t)((64ull << 20) / per_block);
+  nb = std::min<int64_t>(nb, c->max_tokens / kBlock + 1);
+  if (const char *e = std::getenv("ISKV_BULK_BLOCKS")) {
+    const int64_t v = std::atoll(e);
+    if (v > 0) nb = std::min<int64_t>(nb, v);
+  }
+  D.bulk_blocks = (int)std::max<int64_t>(1, nb);
   return D;
 }
 
@@ -985,6 +995,86 @@ int iskv_maintain(iskv_ctx *c, int layer) {
     }
   }
   return ISKV_OK;
+}
+
+int iskv_prefill_layers(iskv_ctx *c, int n_layers, const int *layers, const void *const *dev_k,
+                        const void *const *dev_v, int n_tokens, int in_dtype) {
+  if (!c || n_layers < 1 || !layers || !dev_k || !dev_v || n_tokens < 0) return ISKV_EINVAL;
+  if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
+  if (c->D.cow) return ISKV_ESTATE;
+  const Dims &D = c->D;
+  for (int i = 0; i < n_layers; ++i) {
+    if (check_layer(c, layers[i]) || !dev_k[i] || !dev_v[i]) return ISKV_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (layers[j] == layers[i]) return ISKV_EINVAL;
+    LayerState &L = c->layers[layers[i]];
+    if (!make_uniform(L)) return ISKV_ESTATE;
+    if (L.pending || L.length != L.n_c || L.length < D.prefix) return ISKV_ESTATE;
+    if (L.length + n_tokens > D.max_tokens) return ISKV_ESTATE;
+    const LayerState &L0 = c->layers[layers[0]];
+    if (L.length != L0.length || L.n_c != L0.n_c) return ISKV_ESTATE;
+  }
+  const LayerState &L0 = c->layers[layers[0]];
+  const int64_t length0 = L0.length, n_c_start = L0.n_c;
+  // blocks that leave the window: the same count block-by-block appends would fold
+  const int m = n_tokens >= D.window + kBlock ? (n_tokens - D.window) / kBlock : 0;
+  for (int i = 0; i < n_layers; ++i)
+    if (join_layer(c, layers[i]) != hipSuccess) return ISKV_EDEVICE;
+  hipStream_t s = c->stream;
+  float *mbulk = reinterpret_cast<float *>(c->M.base + c->G.bulk);
+  const size_t row_bytes = (size_t)D.kv_heads * D.d * (in_dtype == ISKV_BF16 ? 2 : 4);
+  const int tail = n_tokens - m * kBlock;
+  int passes = 0;
+  for (int first = 0; first < n_layers; first += kMaxBulkLayers) {
+    BulkIn in{};
+    in.n = std::min(kMaxBulkLayers, n_layers - first);
+    for (int i = 0; i < in.n; ++i) {
+      in.layer[i] = layers[first + i];
+      in.k[i] = dev_k[first + i];
+      in.v[i] = dev_v[first + i];
+    }
+    // M slots: one layer's worth of the workspace shared by the launch's layers
+    const int per_pass = std::max(1, D.bulk_blocks / in.n);
+    passes = 0;
+    for (int done = 0; done < m; done += per_pass, ++passes) {
+      const int nb = std::min(per_pass, m - done);
+      const int64_t n_c0 = n_c_start + (int64_t)done * kBlock;
+      hipError_t e = for_factors(c, s, [&](int x, hipStream_t st) {
+        hipError_t r = launch_bulk_fold(c->M, in, n_c0, nb, x, in_dtype, (int64_t)done * kBlock, n_tokens,
+                                        mbulk, per_pass, st);
+        if (r == hipSuccess) r = launch_sync_bulk(c->M, in, n_c0, nb, x, mbulk, per_pass, st);
+        return r;
+      });
+      if (e != hipSuccess) return ISKV_EDEVICE;
+    }
+    // the rows that stay exact go to the ring
+    for (int i = 0; i < in.n; ++i) {
+      const uint8_t *kt = reinterpret_cast<const uint8_t *>(in.k[i]) + (size_t)m * kBlock * row_bytes;
+      const uint8_t *vt = reinterpret_cast<const uint8_t *>(in.v[i]) + (size_t)m * kBlock * row_bytes;
+      if (launch_append(c->M, in.layer[i], kt, vt, tail, in_dtype, length0 + (int64_t)m * kBlock, s,
+                        SeqTab{}, n_tokens) != hipSuccess)
+        return ISKV_EDEVICE;
+    }
+    if (m > 0) {
+      LayerSel sel;
+      sel.n = in.n;
+      for (int i = 0; i < in.n; ++i) sel.idx[i] = in.layer[i];
+      if (launch_prep_frag(c->M, sel, s) != hipSuccess) return ISKV_EDEVICE;
+    }
+    for (int i = 0; i < in.n; ++i) {
+      LayerState &L = c->layers[in.layer[i]];
+      L.length += n_tokens;
+      L.n_c += (int64_t)m * kBlock;
+      L.folds += m;
+      L.syncs += passes;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_prefill(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
+                 int in_dtype) {
+  return iskv_prefill_layers(c, 1, &layer, &dev_k, &dev_v, n_tokens, in_dtype);
 }
 
 int iskv_switch(iskv_ctx *c, int layer, int wait) {

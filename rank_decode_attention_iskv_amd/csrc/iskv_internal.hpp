@@ -48,6 +48,7 @@ struct Dims {
   int cus;                // compute units of the device (decode grid sizing)
   int prefix;             // P: protected exact positions 0..P-1 (multiple of 64)
   int cow;                // 1: copy-on-write maintenance (two generations, 64 more slots)
+  int bulk_blocks;        // prefill: blocks folded per bulk pass (M slots per unit)
 };
 
 // Pointers of one layer.
@@ -107,7 +108,7 @@ inline LayerLayout layer_layout(const Dims &D) {
 
 struct GlobalLayout {
   LayerLayout layer;
-  size_t layers_base, rec, recml, cnt, flags, rope_anchor, rope_step, total;
+  size_t layers_base, rec, recml, cnt, flags, rope_anchor, rope_step, bulk, total;
 };
 
 inline GlobalLayout global_layout(const Dims &D) {
@@ -121,6 +122,7 @@ inline GlobalLayout global_layout(const Dims &D) {
   G.flags = o; o = align_up(o + 4);
   G.rope_anchor = o; o = align_up(o + (size_t)D.rope_anchors * 64 * 2 * 4);
   G.rope_step = o;   o = align_up(o + (size_t)kRopeAnchor * 64 * 2 * 4);
+  G.bulk = o;        o = align_up(o + (size_t)D.units * D.bulk_blocks * ((size_t)D.rk * D.rk + (size_t)D.rv * D.rv) * 4);
   G.total = o;
   return G;
 }
@@ -207,8 +209,11 @@ hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s);
 
 // Write n tokens at positions pos0.. into the protected prefix (positions < P)
 // or the rings (in_dtype 0 f32, 1 bf16).
+// n_stride: tokens per sequence in the input (0: n), so that a range of a
+// longer input can be appended.
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
-                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab = SeqTab{});
+                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab = SeqTab{},
+                         int n_stride = 0);
 
 // Fold the block at positions n_c..n_c+63 of every unit of the selected
 // layers: factor x (0 K, 1 V), or both (x = -1, one launch; equal ranks only).
@@ -219,6 +224,30 @@ hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c,
 // x (0 K, 1 V) or both (x = -1; equal ranks only).
 hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
                        const SeqTab &tab = SeqTab{});
+
+// Prefill of up to kMaxBulkLayers layers at once (the same length and
+// compressed count): per layer i its input k[i], v[i] ([batch][n_in]
+// [kv_heads][d], in_dtype 0 f32 / 1 bf16).
+constexpr int kMaxBulkLayers = 16;
+struct BulkIn {
+  int n;
+  int layer[kMaxBulkLayers];
+  const void *k[kMaxBulkLayers], *v[kMaxBulkLayers];
+};
+
+// M slots of one layer in a bulk pass: [factor][unit][block][r][r].
+__host__ __device__ inline size_t bulk_layer_floats(const Dims &D, int bulk_blocks) {
+  return (size_t)D.units * bulk_blocks * ((size_t)D.rk * D.rk + (size_t)D.rv * D.rv);
+}
+
+// Fold nblk consecutive blocks of the inputs (rows row0..), the first at
+// positions n_c0.., leaving each block's M in mbulk (bulk_blocks slots per
+// unit, layer i at i * bulk_layer_floats) replaced by its suffix product;
+// then launch_sync_bulk maps every older row by the product of the later M's.
+hipError_t launch_bulk_fold(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x, int in_dtype,
+                            int64_t row0, int n_in, float *mbulk, int bulk_blocks, hipStream_t s);
+hipError_t launch_sync_bulk(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x,
+                            const float *mbulk, int bulk_blocks, hipStream_t s);
 
 // Rebuild the decode operand copy of the basis from the fp32 basis.
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s);

@@ -45,14 +45,14 @@ __global__ void reset_basis_kernel(Model M, int layer) {
 // Append: grid (n tokens, kv heads, batch), block = head_dim threads.
 // ---------------------------------------------------------------------------
 template <typename T, typename In>
-__global__ void append_kernel(Model M, int layer, const In *k, const In *v, int n, int64_t pos0,
-                              SeqTab tab) {
+__global__ void append_kernel(Model M, int layer, const In *k, const In *v, int n, int n_stride,
+                              int64_t pos0, SeqTab tab) {
   const Dims &D = M.D;
   const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, f = threadIdx.x;
   if (!seq_in(tab, b) || t >= (tab.n ? tab.aux[b] : n)) return;     // ragged: this sequence's count
   if (tab.n) pos0 = tab.len[b];
   const int u = b * D.kv_heads + h;
-  const size_t src = (((size_t)b * n + t) * D.kv_heads + h) * D.d + f;
+  const size_t src = (((size_t)b * n_stride + t) * D.kv_heads + h) * D.d + f;
   const float kx = Store<In>::load(k, src);
   const float vx = Store<In>::load(v, src);
   if (!isfinite(kx) || !isfinite(vx)) set_flag(M.sh, 4);
@@ -132,13 +132,32 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // f32 storage: one row per thread on the vector ALUs.
 // grid (row tiles, units (one factor) or units*2 (both), layers)
 // ---------------------------------------------------------------------------
-template <int R>
+// Bulk mode (prefill): the matrix depends on the row's 64-row block (see
+// bulk_suffix_kernel): rows older than n_c0 take slot 0, rows of bulk block j
+// slot j + 1, the last bulk block's rows are skipped; one block per wave.
+struct BulkSync {
+  const float *mbulk;     // null: plain sync with the layer's M
+  int bulk_blocks;
+  int nblk;
+  int64_t n_c0;
+};
+
+__device__ __forceinline__ const float *bulk_matrix(const Model &M, const BulkSync &bk, int li, int x, int u,
+                                                    int R, int64_t row) {
+  const int64_t blk = row < bk.n_c0 ? 0 : (row - bk.n_c0) / kBlock + 1;
+  if (blk >= bk.nblk) return nullptr;
+  return bk.mbulk + (size_t)li * bulk_layer_floats(M.D, bk.bulk_blocks) +
+         (x ? (size_t)M.D.units * bk.bulk_blocks * M.D.rk * M.D.rk : 0) +
+         ((size_t)u * bk.bulk_blocks + blk) * R * R;
+}
+
+template <int R, bool BULK>
 __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel sel, int64_t n_old, int xsel,
-                                                              SeqTab tab) {
+                                                              SeqTab tab, BulkSync bk) {
   static_assert(R == 16 || R == 32 || R == 64 || R == 128, "MFMA sync ranks");
   constexpr int KB = R >= 32 ? R / 32 : 1;      // K blocks (32 wide; one of 16 at r = 16)
   constexpr int MB = R / 16;                    // output column blocks
-  constexpr int TPW = R == 128 ? 4 : 8;         // 16-row tiles per wave
+  constexpr int TPW = BULK ? 4 : (R == 128 ? 4 : 8);   // 16-row tiles per wave
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
   // grid.y: units (one factor, xsel) or units x 2 (both, equal ranks)
@@ -153,6 +172,10 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   const int n = lane & 15, rho = lane >> 4;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TPW * 16;
   if (base >= n_old) return;                    // uniform per wave
+  if constexpr (BULK) {
+    Ms = bulk_matrix(M, bk, blockIdx.z, x, u, R, base);
+    if (!Ms) return;
+  }
   // every input row of the wave is in registers before any output is written
   uint4_ b[TPW][KB];
 #pragma unroll
@@ -216,9 +239,9 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   }
 }
 
-template <int R>
+template <int R, bool BULK>
 __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel sel, int64_t n_old, int xsel,
-                                                              SeqTab tab) {
+                                                              SeqTab tab, BulkSync bk) {
   __shared__ float4 sM4[R * R / 4];
   const float *sM = reinterpret_cast<const float *>(sM4);
   const Dims &D = M.D;
@@ -228,6 +251,11 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
   if (tab.n) n_old = tab.nc[u / D.kv_heads];
   LayerPtrs P = layer_ptrs(M, l);
   const float4 *Ms = reinterpret_cast<const float4 *>(P.msync[x] + (size_t)u * R * R);
+  if constexpr (BULK) {                         // one 64-row block per workgroup (block-uniform)
+    const float *mb = bulk_matrix(M, bk, blockIdx.z, x, u, R, (int64_t)blockIdx.x * blockDim.x);
+    if (!mb) return;
+    Ms = reinterpret_cast<const float4 *>(mb);
+  }
   const float *C = reinterpret_cast<const float *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
   float *Co = reinterpret_cast<float *>(layer_ptrs_out(M, l).coef[x]) + (size_t)u * D.max_tokens * R;
   for (int i = threadIdx.x; i < R * R / 4; i += blockDim.x) sM4[i] = Ms[i];
@@ -260,30 +288,38 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
 
 template <int R, typename T>
 hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
-                         const SeqTab &tab) {
+                         const SeqTab &tab, const BulkSync &bk) {
   if (n_old <= 0) return hipSuccess;
   const unsigned ny = x < 0 ? M.D.units * 2 : M.D.units;
+  const bool bulk = bk.mbulk != nullptr;
   if constexpr (std::is_same<T, bf16_t>::value) {
-    const int64_t rows_per_block = (int64_t)(kThreads / 64) * (R == 128 ? 4 : 8) * 16;
+    const int64_t rows_per_block = (int64_t)(kThreads / 64) * (bulk ? 4 : (R == 128 ? 4 : 8)) * 16;
     dim3 grid((unsigned)((n_old + rows_per_block - 1) / rows_per_block), ny, sel.n);
-    hipLaunchKernelGGL((sync_mfma_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab);
+    if (bulk)
+      hipLaunchKernelGGL((sync_mfma_kernel<R, true>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab, bk);
+    else
+      hipLaunchKernelGGL((sync_mfma_kernel<R, false>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab, bk);
   } else {
-    dim3 grid((unsigned)((n_old + kThreads - 1) / kThreads), ny, sel.n);
-    hipLaunchKernelGGL((sync_valu_kernel<R>), grid, dim3(kThreads), 0, s, M, sel, n_old, x, tab);
+    const int threads = bulk ? kBlock : kThreads;
+    dim3 grid((unsigned)((n_old + threads - 1) / threads), ny, sel.n);
+    if (bulk)
+      hipLaunchKernelGGL((sync_valu_kernel<R, true>), grid, dim3(threads), 0, s, M, sel, n_old, x, tab, bk);
+    else
+      hipLaunchKernelGGL((sync_valu_kernel<R, false>), grid, dim3(threads), 0, s, M, sel, n_old, x, tab, bk);
   }
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
-                         const SeqTab &tab) {
+                         const SeqTab &tab, const BulkSync &bk) {
   const int r = x == 1 ? M.D.rv : M.D.rk;
   if (x < 0 && M.D.rk != M.D.rv) return hipErrorInvalidValue;
   switch (r) {
-    case 16: return launch_sync_t<16, T>(M, sel, n_old, x, s, tab);
-    case 32: return launch_sync_t<32, T>(M, sel, n_old, x, s, tab);
-    case 64: return launch_sync_t<64, T>(M, sel, n_old, x, s, tab);
-    case 128: return launch_sync_t<128, T>(M, sel, n_old, x, s, tab);
+    case 16: return launch_sync_t<16, T>(M, sel, n_old, x, s, tab, bk);
+    case 32: return launch_sync_t<32, T>(M, sel, n_old, x, s, tab, bk);
+    case 64: return launch_sync_t<64, T>(M, sel, n_old, x, s, tab, bk);
+    case 128: return launch_sync_t<128, T>(M, sel, n_old, x, s, tab, bk);
   }
   return hipErrorInvalidValue;
 }
@@ -296,31 +332,45 @@ hipError_t launch_reset_layer(const Model &M, int layer, hipStream_t s) {
 }
 
 hipError_t launch_append(const Model &M, int layer, const void *k, const void *v, int n,
-                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab) {
+                         int in_dtype, int64_t pos0, hipStream_t s, const SeqTab &tab, int n_stride) {
   if (n <= 0) return hipSuccess;
+  if (n_stride <= 0) n_stride = n;
   dim3 grid(n, M.D.kv_heads, M.D.batch);
   if (M.D.storage == 1) {
     if (in_dtype == 1)
       hipLaunchKernelGGL((append_kernel<bf16_t, bf16_t>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const bf16_t *)k, (const bf16_t *)v, n, pos0, tab);
+                         (const bf16_t *)k, (const bf16_t *)v, n, n_stride, pos0, tab);
     else
       hipLaunchKernelGGL((append_kernel<bf16_t, float>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const float *)k, (const float *)v, n, pos0, tab);
+                         (const float *)k, (const float *)v, n, n_stride, pos0, tab);
   } else {
     if (in_dtype == 1)
       hipLaunchKernelGGL((append_kernel<float, bf16_t>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const bf16_t *)k, (const bf16_t *)v, n, pos0, tab);
+                         (const bf16_t *)k, (const bf16_t *)v, n, n_stride, pos0, tab);
     else
       hipLaunchKernelGGL((append_kernel<float, float>), grid, dim3(kHeadDim), 0, s, M, layer,
-                         (const float *)k, (const float *)v, n, pos0, tab);
+                         (const float *)k, (const float *)v, n, n_stride, pos0, tab);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_sync(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
                        const SeqTab &tab) {
-  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, x, s, tab)
-                          : dispatch_sync<float>(M, sel, n_old, x, s, tab);
+  const BulkSync none{nullptr, 0, 0, 0};
+  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, n_old, x, s, tab, none)
+                          : dispatch_sync<float>(M, sel, n_old, x, s, tab, none);
+}
+
+hipError_t launch_sync_bulk(const Model &M, const BulkIn &in, int64_t n_c0, int nblk, int x,
+                            const float *mbulk, int bulk_blocks, hipStream_t s) {
+  if (nblk < 2 && n_c0 <= M.D.prefix) return hipSuccess;     // nothing older than the last block
+  LayerSel sel;
+  sel.n = in.n;
+  for (int i = 0; i < in.n; ++i) sel.idx[i] = in.layer[i];
+  const BulkSync bk{mbulk, bulk_blocks, nblk, n_c0};
+  const int64_t rows = n_c0 + (int64_t)(nblk - 1) * kBlock;  // up to the last bulk block
+  return M.D.storage == 1 ? dispatch_sync<bf16_t>(M, sel, rows, x, s, SeqTab{}, bk)
+                          : dispatch_sync<float>(M, sel, rows, x, s, SeqTab{}, bk);
 }
 
 hipError_t launch_prep_frag(const Model &M, const LayerSel &sel, hipStream_t s) {

@@ -619,3 +619,52 @@ def test_deferred_fold_commutes_with_later_appends(storage, k):
         full.append(X[p, 0], X[p, 1])
     with pytest.raises(RuntimeError):
         full.append(X[0, 0], X[0, 1])
+
+
+# ---------------------------------------------------------------------------
+# Bulk prefill [iS-KV explainer, the trade-off paragraph: prompts are
+# compressed too]: folding a prompt's blocks with one deferred
+# synchronization (suffix products of the M's) equals appending the tokens
+# and folding + synchronizing each time the ring fills -- by associativity of
+# the products, exactly in float64 storage.  A plausible mistake (a product
+# in the wrong order, the wrong suffix for a block, the last block mapped)
+# changes the history by O(1).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prefix,n,hist", [(0, 640 + 37, 0), (64, 448, 0), (128, 128 + 64 * 3, 0)])
+def test_bulk_prefill_equals_block_by_block(prefix, n, hist):
+    rng = np.random.default_rng(71)
+    d, r, W = 128, 16, 128
+    X = rng.standard_normal((prefix + hist + n, 2, d)) @ np.diag(np.linspace(2, 0.05, d))
+    a = Unit(d, r, W, 2048, "f64", prefix=prefix)
+    b = Unit(d, r, W, 2048, "f64", prefix=prefix)
+    # protected prefix and some history first (block by block in both)
+    for p in range(prefix + hist):
+        for u in (a, b):
+            u.append(X[p, 0], X[p, 1])
+            if u.ready:
+                u.fold()
+                u.sync()
+    # a: the rest of the ring drains first when history was appended
+    for u in (a, b):
+        while u.length > u.n_c and u.length - u.n_c >= W + 64:
+            u.fold()
+            u.sync()
+    if a.length != a.n_c:
+        pytest.skip("ring not empty after the history")
+    m = a.prefill(X[prefix + hist:, 0], X[prefix + hist:, 1])
+    for p in range(prefix + hist, prefix + hist + n):
+        b.append(X[p, 0], X[p, 1])
+        if b.ready:
+            b.fold()
+            b.sync()
+    assert m == (n - W) // 64 and a.n_c == b.n_c and a.length == b.length
+    for fa, fb in ((a.K, b.K), (a.V, b.V)):
+        np.testing.assert_allclose(fa.B, fb.B, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(fa.C[:a.n_c], fb.C[:a.n_c], rtol=0,
+                                   atol=1e-10 * np.abs(fb.C).max())
+        live = [p % fa.slots for p in range(a.n_c, a.length)]     # slots of the exact rows
+        np.testing.assert_array_equal(fa.ring[live], fb.ring[live])
+    q = rng.standard_normal((4, d))
+    np.testing.assert_allclose(a.decode(q, a.length - 1, 1 / math.sqrt(d)),
+                               b.decode(q, b.length - 1, 1 / math.sqrt(d)), rtol=0, atol=1e-10)
