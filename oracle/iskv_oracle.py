@@ -41,6 +41,12 @@ paper), abbreviated [iS-KV explainer].
   the fold, when applied, is the same Brand step on the same block, basis and
   singular values.  Default S = 0.
 
+* A basis may span every KV head of a layer (JointUnit, Oracle(joint_heads=True)):
+  ranks of 64-128 reach 4-7x compression of 128-dim heads [iS-KV explainer,
+  the worked example and Table 1], which only a basis over several heads can
+  give.  A token's row is then its heads' rows side by side, and the Brand
+  fold, the sync and the coefficients are the same steps on those rows.
+
 * K and V may take different ranks [KV-CoRE page, Key Results, the
   asymmetry of K and V: V needs more rank than K for the same energy].  The
   two factors never interact before decode, so a V factor of rank r_V is the
@@ -441,6 +447,56 @@ def drift(before, after):
     return float(np.linalg.norm(after - before) / nb) if nb > 0 else 0.0
 
 
+class JointUnit(Unit):
+    """One (sequence, layer) whose KV heads share one basis per factor.
+
+    A token's row is its H heads' pre-RoPE rows side by side (H*d wide); the
+    fold, the synchronization and the stored coefficient vector (rank r, one
+    per token for all H heads) are Unit's on those rows.  Decode for KV head
+    h rebuilds columns h*d..(h+1)*d of each row, rotates them at the row's
+    position with d-dim RoPE and attends exactly as Unit does.
+
+    Reading: the page reaches 4-7x compression at ranks 64-128 with 128-dim
+    heads [iS-KV explainer, the worked example and Table 1], which a basis of
+    one head cannot do at rank 128, so a basis must span several heads; the
+    pages do not say which, and the group here is every KV head of a layer
+    (Unit, one basis per head, is the other reading)."""
+
+    def __init__(self, H, d, r, window, max_tokens, storage, block=BLOCK, prefix=0, r_v=None,
+                 slack=0):
+        super().__init__(H * d, r, window, max_tokens, storage, block, prefix, r_v, slack)
+        self.H, self.hd = H, d
+
+    def append(self, k, v):
+        """k, v: (H, d) rows of the H KV heads at the next position."""
+        super().append(np.asarray(k, dtype=np.float64).reshape(-1),
+                       np.asarray(v, dtype=np.float64).reshape(-1))
+
+    def prefill(self, ks, vs):
+        """ks, vs: (n, H, d) prompt rows (see Unit.prefill)."""
+        n = np.shape(ks)[0]
+        return super().prefill(np.asarray(ks, dtype=np.float64).reshape(n, -1),
+                               np.asarray(vs, dtype=np.float64).reshape(n, -1))
+
+    def decode(self, q, q_pos, scale, rope_base=10000.0):
+        """q: (H*g, d) query rows, g per KV head; rows h*g..(h+1)*g read KV head h."""
+        q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+        g = q.shape[0] // self.H
+        d, L = self.hd, self.length
+        K = self.K.rebuilt(self.n_c, L)
+        V = self.V.rebuilt(self.n_c, L)
+        out = np.empty((q.shape[0], d))
+        for h in range(self.H):
+            keys = rope(K[:, h * d:(h + 1) * d], np.arange(L), rope_base)
+            qr = rope(q[h * g:(h + 1) * g], q_pos, rope_base)
+            s = (qr @ keys.T) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[h * g:(h + 1) * g] = p @ V[:, h * d:(h + 1) * d]
+        return out
+
+
 # ----------------------------------------------------------------------------
 # Whole cache: batch x layers x KV heads, with grouped query heads
 # ----------------------------------------------------------------------------
@@ -455,7 +511,7 @@ class Oracle:
 
     def __init__(self, batch, num_layers, kv_heads, q_heads, head_dim, rank, window,
                  max_tokens, storage="bf16", rope_base=10000.0, softmax_scale=None,
-                 block=BLOCK, prefix=0, rank_v=None, slack=0):
+                 block=BLOCK, prefix=0, rank_v=None, slack=0, joint_heads=False):
         if q_heads % kv_heads:
             raise ValueError("q_heads must be a multiple of kv_heads")
         self.batch, self.num_layers = batch, num_layers
@@ -465,19 +521,39 @@ class Oracle:
         self.scale = (1.0 / math.sqrt(head_dim)) if not softmax_scale else float(softmax_scale)
         self.prefix = prefix
         self.r_v = rank_v or rank
-        self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix,
-                             self.r_v, slack)
-                        for _ in range(kv_heads)] for _ in range(num_layers)]
-                      for _ in range(batch)]
+        self.joint = bool(joint_heads)
+        if self.joint:
+            # one JointUnit per (sequence, layer), listed once per KV head so
+            # that unit(b, layer, h) and the per-head loops below still apply
+            self.units = []
+            for _ in range(batch):
+                per_layer = []
+                for _ in range(num_layers):
+                    j = JointUnit(kv_heads, head_dim, rank, window, max_tokens, storage, block,
+                                  prefix, self.r_v, slack)
+                    per_layer.append([j] * kv_heads)
+                self.units.append(per_layer)
+        else:
+            self.units = [[[Unit(head_dim, rank, window, max_tokens, storage, block, prefix,
+                                 self.r_v, slack)
+                            for _ in range(kv_heads)] for _ in range(num_layers)]
+                          for _ in range(batch)]
 
     def unit(self, b, layer, h) -> Unit:
         return self.units[b][layer][h]
+
+    def _heads(self):
+        """KV heads that own a distinct unit (all, or only head 0 when joint)."""
+        return range(1) if self.joint else range(self.kv_heads)
 
     def append(self, layer, k, v):
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         for b in range(self.batch):
             for t in range(k.shape[1]):
+                if self.joint:
+                    self.units[b][layer][0].append(k[b, t], v[b, t])
+                    continue
                 for h in range(self.kv_heads):
                     self.units[b][layer][h].append(k[b, t, h], v[b, t, h])
         return self.ready(layer)
@@ -487,12 +563,12 @@ class Oracle:
 
     def block_update(self, layer):
         for b in range(self.batch):
-            for h in range(self.kv_heads):
+            for h in self._heads():
                 self.units[b][layer][h].fold()
 
     def sync(self, layer):
         for b in range(self.batch):
-            for h in range(self.kv_heads):
+            for h in self._heads():
                 self.units[b][layer][h].sync()
 
     def prefill(self, layer, k, v):
@@ -501,6 +577,9 @@ class Oracle:
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         for b in range(self.batch):
+            if self.joint:
+                self.units[b][layer][0].prefill(k[b], v[b])
+                continue
             for h in range(self.kv_heads):
                 self.units[b][layer][h].prefill(k[b, :, h], v[b, :, h])
 
@@ -509,6 +588,9 @@ class Oracle:
         g = self.q_heads // self.kv_heads
         out = np.zeros((self.batch, self.q_heads, self.d))
         for b in range(self.batch):
+            if self.joint:
+                out[b] = self.units[b][layer][0].decode(q[b], q_pos, self.scale, self.rope_base)
+                continue
             for h in range(self.kv_heads):
                 u = self.units[b][layer][h]
                 out[b, h * g:(h + 1) * g] = u.decode(q[b, h * g:(h + 1) * g], q_pos,
@@ -526,10 +608,16 @@ def full_kv_bytes(tokens, layers, kv_heads, head_dim, elem_bytes):
 
 
 def persistent_kv_bytes(n_c, n_exact, layers, kv_heads, head_dim, rank, elem_bytes,
-                        basis_bytes=4, rank_v=None):
+                        basis_bytes=4, rank_v=None, joint_heads=False):
     """Bytes kept between decode steps: coefficients, bases and singular values
     of K and V, plus the exact rows.  Model weights and temporary rebuild
-    buffers are excluded.  rank_v (default rank) is the rank of the V factor."""
+    buffers are excluded.  rank_v (default rank) is the rank of the V factor.
+    joint_heads: one basis (kv_heads*head_dim rows) and one coefficient row per
+    token for all KV heads of a layer, instead of one per head."""
+    if joint_heads:
+        per_layer = sum(n_c * r * elem_bytes + kv_heads * head_dim * r * basis_bytes
+                        + r * basis_bytes for r in (rank, rank_v or rank))
+        return layers * (per_layer + 2 * kv_heads * n_exact * head_dim * elem_bytes)
     per_head = sum(n_c * r * elem_bytes + head_dim * r * basis_bytes + r * basis_bytes
                    + n_exact * head_dim * elem_bytes for r in (rank, rank_v or rank))
     return layers * kv_heads * per_head

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (Oracle, Unit, bf16_round, brand_fold, drift, full_kv_bytes,
+from oracle import (JointUnit, Oracle, Unit, bf16_round, brand_fold, drift, full_kv_bytes,
                     persistent_kv_bytes, rope)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -668,3 +668,175 @@ def test_bulk_prefill_equals_block_by_block(prefix, n, hist):
     q = rng.standard_normal((4, d))
     np.testing.assert_allclose(a.decode(q, a.length - 1, 1 / math.sqrt(d)),
                                b.decode(q, b.length - 1, 1 / math.sqrt(d)), rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# Joint-head basis: one basis over a layer's KV heads [iS-KV explainer, the
+# worked example and Table 1: ranks 64-128 compress 128-dim heads 4-7x]
+# ---------------------------------------------------------------------------
+
+def _joint_stream(rng, L, H, d, k):
+    """K and V rows of H heads whose concatenation (H*d wide) has rank k:
+    every head's rows are different mixtures of the same k latent factors."""
+    Z = rng.standard_normal((L, k))
+    X = (Z @ rng.standard_normal((k, H * d)) / math.sqrt(k)).reshape(L, H, d)
+    Y = (rng.standard_normal((L, k)) @ rng.standard_normal((k, H * d)) / math.sqrt(k)).reshape(L, H, d)
+    return X, Y
+
+
+def _joint_exact(q, X, Y, q_pos, scale, g):
+    """Per-head exact attention (torch SDPA): query rows h*g..(h+1)*g read head h."""
+    H = X.shape[1]
+    return np.concatenate([exact_attention(q[h * g:(h + 1) * g], X[:, h], Y[:, h], q_pos, scale)
+                           for h in range(H)])
+
+
+@pytest.mark.parametrize("H,d,r,k", [(4, 32, 16, 12), (2, 64, 32, 32), (3, 16, 48, 48)])
+def test_joint_rank_le_r_is_exact_attention_per_head(H, d, r, k):
+    """The heads' rows together have rank k <= r (r may exceed d, which a
+    per-head basis cannot hold): every fold is lossless, the history is the
+    stacked rows, S is the batch SVD of the (L x H*d) history, and decode of
+    every KV head equals exact attention on that head's own rows."""
+    rng = np.random.default_rng(61 + H)
+    W, L, g = 64, 64 * 6 + 29, 2
+    X, Y = _joint_stream(rng, L, H, d, k)
+    u = JointUnit(H, d, r, W, L + 64, "f64")
+    for t in range(L):
+        u.append(X[t], Y[t])
+        if u.ready:
+            u.fold()
+            u.sync()
+    assert u.compressed >= 256 and u.K.B.shape == (H * d, r)
+    Hk = X[: u.n_c].reshape(u.n_c, H * d)
+    np.testing.assert_allclose(u.history("K"), Hk, atol=1e-10)
+    s_batch = np.linalg.svd(Hk, compute_uv=False)
+    np.testing.assert_allclose(u.K.S[:k], s_batch[:k], rtol=1e-11, atol=1e-11 * s_batch[0])
+    q = rng.standard_normal((H * g, d))
+    scale = 1 / math.sqrt(d)
+    ref = _joint_exact(q, X, Y, L + 3, scale, g)
+    got = u.decode(q, L + 3, scale)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-10
+    # per-head bases sharing the same budget (rank r / H each) truncate
+    # whenever a head's own rows (rank min(k, d)) exceed it
+    if min(k, d) > r // H:
+        per = [run_unit(X[:, h], Y[:, h], d, max(r // H, 1), W) for h in range(H)]
+        bad = np.concatenate([per[h].decode(q[h * g:(h + 1) * g], L + 3, scale) for h in range(H)])
+        assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 1e-4
+
+
+def test_joint_full_rank_is_exact_attention():
+    """r = H*d: the joint basis is square, every row is rebuilt exactly for
+    arbitrary (full-rank) data, and decode is exact attention per head."""
+    rng = np.random.default_rng(67)
+    H, d, W, L, g = 2, 16, 64, 400, 3
+    X = rng.standard_normal((L, H, d))
+    Y = rng.standard_normal((L, H, d))
+    u = JointUnit(H, d, H * d, W, L + 64, "f64")
+    for t in range(L):
+        u.append(X[t], Y[t])
+        if u.ready:
+            u.fold()
+            u.sync()
+    assert u.compressed >= 256
+    q = rng.standard_normal((H * g, d))
+    scale = 1 / math.sqrt(d)
+    got = u.decode(q, L, scale)
+    ref = _joint_exact(q, X, Y, L, scale, g)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-11
+
+
+def test_joint_single_head_is_the_per_head_unit():
+    """H = 1: the joint unit is the per-head unit, bit for bit (bf16 mode)."""
+    rng = np.random.default_rng(71)
+    d, r, W, L = 64, 16, 64, 300
+    X, Y = rng.standard_normal((L, d)), rng.standard_normal((L, d))
+    j = JointUnit(1, d, r, W, L + 64, "bf16")
+    u = Unit(d, r, W, L + 64, "bf16")
+    for t in range(L):
+        j.append(X[t][None], Y[t][None])
+        u.append(X[t], Y[t])
+        if u.ready:
+            u.fold(); u.sync()
+            j.fold(); j.sync()
+    q = rng.standard_normal((4, d))
+    np.testing.assert_array_equal(j.decode(q, L, 0.125), u.decode(q, L, 0.125))
+
+
+def test_joint_oracle_layer_equals_joint_unit_and_gqa_map():
+    """Oracle(joint_heads=True) drives one JointUnit per (sequence, layer);
+    query head h reads KV head h // g, checked by permuting the KV heads'
+    data: the outputs of the query-head groups permute with them."""
+    rng = np.random.default_rng(73)
+    B, H, Hq, d, r, W, n = 2, 4, 8, 32, 24, 64, 200
+    o = Oracle(B, 1, H, Hq, d, r, W, n + 64, storage="f64", joint_heads=True)
+    k = rng.standard_normal((B, n, H, d))
+    v = rng.standard_normal((B, n, H, d))
+    for t in range(n):
+        if o.append(0, k[:, t:t + 1], v[:, t:t + 1]):
+            o.block_update(0)
+            o.sync(0)
+    assert o.unit(0, 0, 0) is o.unit(0, 0, 3) and o.unit(0, 0, 0) is not o.unit(1, 0, 0)
+    q = rng.standard_normal((B, Hq, d))
+    out = o.decode_attn(0, q, n)
+    for b in range(B):
+        np.testing.assert_array_equal(out[b], o.unit(b, 0, 0).decode(q[b], n, o.scale))
+    # permute the KV heads (and the query groups with them) in a fresh run
+    perm = np.array([2, 0, 3, 1])
+    qperm = q.reshape(B, H, Hq // H, d)[:, perm].reshape(B, Hq, d)
+    o2 = Oracle(B, 1, H, Hq, d, r, W, n + 64, storage="f64", joint_heads=True)
+    for t in range(n):
+        if o2.append(0, k[:, t:t + 1, perm], v[:, t:t + 1, perm]):
+            o2.block_update(0)
+            o2.sync(0)
+    out2 = o2.decode_attn(0, qperm, n)
+    want = out.reshape(B, H, Hq // H, d)[:, perm].reshape(B, Hq, d)
+    # a permutation of the row's columns leaves the SVD's spectrum and the
+    # rebuilt rows unchanged up to rounding
+    np.testing.assert_allclose(out2, want, rtol=0, atol=1e-9)
+
+
+def test_joint_prefill_equals_block_by_block():
+    """Bulk prefill of a joint unit (deferred sync by suffix products) equals
+    folding and synchronizing block by block, in f64."""
+    rng = np.random.default_rng(79)
+    H, d, r, W, n = 2, 32, 16, 64, 64 * 5 + 40
+    X = rng.standard_normal((n, H, d))
+    Y = rng.standard_normal((n, H, d))
+    a = JointUnit(H, d, r, W, n + 64, "f64")
+    a.prefill(X, Y)
+    b = JointUnit(H, d, r, W, n + 64, "f64")
+    for t in range(n):
+        b.append(X[t], Y[t])
+        if b.ready:
+            b.fold()
+            b.sync()
+    assert a.n_c == b.n_c and a.length == b.length
+    np.testing.assert_allclose(a.history("K"), b.history("K"), atol=1e-10)
+    q = rng.standard_normal((2 * H, d))
+    np.testing.assert_allclose(a.decode(q, n, 0.2), b.decode(q, n, 0.2), atol=1e-10)
+
+
+def test_joint_persistent_bytes_counts_the_arrays():
+    """The joint byte model against a count of a joint unit's arrays after a
+    stream: one coefficient row per token for all heads, one (H*d x r) basis
+    per factor, and every head's exact rows."""
+    rng = np.random.default_rng(83)
+    H, d, r, rv, W = 8, 128, 64, 128, 64
+    L = 64 * 4 + 21
+    u = JointUnit(H, d, r, W, L + 64, "bf16", r_v=rv)
+    for t in range(L):
+        u.append(rng.standard_normal((H, d)), rng.standard_normal((H, d)))
+        if u.ready:
+            u.fold()
+            u.sync()
+    n_e = u.length - u.n_c
+    counted = 0
+    for f, rf in ((u.K, r), (u.V, rv)):
+        held = int(np.sum(np.any(f.C != 0.0, axis=1)))
+        assert held == u.n_c and f.C.shape[1] == rf and f.B.shape == (H * d, rf)
+        counted += held * rf * 2 + (f.B.size + f.S.size) * 4 + n_e * H * d * 2
+    assert counted == persistent_kv_bytes(u.n_c, n_e, 1, H, d, r, 2, rank_v=rv, joint_heads=True)
+    # a joint basis at rank 64 keeps 1/8 of the per-head coefficient bytes at rank 64
+    per_head = persistent_kv_bytes(u.n_c, 0, 1, H, d, 64, 2)
+    joint = persistent_kv_bytes(u.n_c, 0, 1, H, d, 64, 2, joint_heads=True)
+    assert joint < per_head
