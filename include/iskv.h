@@ -107,6 +107,19 @@ typedef struct {
                              requirements: maintenance off the critical
                              path; copy-on-write, switched at a decode
                              boundary].  At most 64 layers. */
+  int32_t joint_heads;    /* 0: one basis per (sequence, layer, KV head), d x r.
+                             1: one basis per (sequence, layer) and factor over
+                             all KV heads: a token's row is its heads' rows
+                             side by side (num_kv_heads * head_dim wide), folded
+                             and synchronized as one, with one coefficient row
+                             per token for all heads; decode of KV head h
+                             rebuilds its keys and values from rows
+                             h*head_dim .. of that basis.  Ranks 64-128 over
+                             128-dim heads compress 4-7x [iS-KV explainer,
+                             the worked example and Table 1], which needs a
+                             basis over several heads.  Requires rank and
+                             rank_v <= 64, num_kv_heads <= 32 and
+                             async_maintenance = 0; iskv_prefill is ESTATE. */
 } iskv_config;
 
 typedef struct {
@@ -136,7 +149,10 @@ size_t iskv_workspace_bytes(const iskv_config *cfg);
  *                                                  P .. P+compressed-1 are 0),
  *                 float ring[S][head_dim]         (slot = position % S, S = window+64,
  *                                                  window+128 with async_maintenance),
- *                 float prefix[P][head_dim]       (protected rows, P = protected_prefix). */
+ *                 float prefix[P][head_dim]       (protected rows, P = protected_prefix).
+ * With joint_heads, basis is rows h*head_dim .. of the sequence's joint basis,
+ * and S and coeff (shared by its heads) are listed under every head: export
+ * writes them under each, import reads them from head 0. */
 size_t iskv_state_bytes(const iskv_config *cfg);
 
 /* Validate cfg, carve the caller's device workspace (dev_ws, ws_bytes >=
@@ -160,7 +176,8 @@ int iskv_append(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, in
                 int in_dtype, int *blocks_ready);
 
 /* Fold the oldest 64 exact tokens of every (sequence, KV head, K|V) of the
- * layer (layer = -1: every layer that has a full ring) into its rank-r basis
+ * layer (with joint_heads: every (sequence, K|V), the heads' rows side by
+ * side) (layer = -1: every layer that has a full ring) into its rank-r basis
  * by Brand's block-incremental SVD: projection, residual CholeskyQR2, core
  * [[diag S, 0], [P, R_r^T]] of size (r+64)^2, one-sided Jacobi SVD, truncation
  * to r.  Writes the new basis, S, the block's coefficients, and the pending
@@ -299,7 +316,7 @@ int iskv_join_maintenance(iskv_ctx *c, int layer);
  * synchronization up to the rounding order of those products.  The last
  * n_tokens - 64 m tokens (window .. window + 63 of them) go to the ring.
  * ESTATE: ring not empty, pending sync, protected prefix not yet full,
- * max_tokens exceeded, or a copy-on-write context.  Counters: folds += m,
+ * max_tokens exceeded, a copy-on-write or a joint_heads context.  Counters: folds += m,
  * syncs += passes. */
 int iskv_prefill(iskv_ctx *c, int layer, const void *dev_k, const void *dev_v, int n_tokens,
                  int in_dtype);

@@ -31,7 +31,7 @@ class Config(ctypes.Structure):
         ("block", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("storage", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
         ("protected_prefix", ctypes.c_int32), ("rank_v", ctypes.c_int32),
-        ("async_maintenance", ctypes.c_int32),
+        ("async_maintenance", ctypes.c_int32), ("joint_heads", ctypes.c_int32),
     ]
 
 
@@ -124,10 +124,10 @@ def strerror(code: int) -> str:
 
 def make_config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window,
                 max_tokens, storage=BF16, rope_base=10000.0, softmax_scale=0.0, block=64,
-                protected_prefix=0, rank_v=0, async_maintenance=0) -> Config:
+                protected_prefix=0, rank_v=0, async_maintenance=0, joint_heads=0) -> Config:
     return Config(batch, num_layers, num_kv_heads, num_q_heads, head_dim, rank, window, block,
                   max_tokens, storage, rope_base, softmax_scale, protected_prefix, rank_v,
-                  async_maintenance)
+                  async_maintenance, joint_heads)
 
 
 def ring_slots(cfg: Config) -> int:

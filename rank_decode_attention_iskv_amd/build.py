@@ -17,7 +17,7 @@ SRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libiskv.so")
 
-SOURCES = ["iskv.cpp", "maintain.hip", "fold.hip", "decode.hip"]
+SOURCES = ["iskv.cpp", "maintain.hip", "fold.hip", "fold_joint.hip", "decode.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -674,8 +674,9 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     for (int nb = 0; nb < NBV; ++nb) vacc[nb] = zero4();
     // per-wave LDS ring of DEPTH slots, each [C_K tile | C_V tile]
     uint8_t *ring = s_dyn + C::kRingOff + wave * C::kRingBytes;
-    const uint8_t *gk = P.coef[0] + ((size_t)u * D.max_tokens * RK + (size_t)w_begin * RK) * C::kElem;
-    const uint8_t *gv = P.coef[1] + ((size_t)u * D.max_tokens * RV + (size_t)w_begin * RV) * C::kElem;
+    const size_t cu = (size_t)coef_unit(D, u);     // a joint basis shares one stream per sequence
+    const uint8_t *gk = P.coef[0] + (cu * D.max_tokens * RK + (size_t)w_begin * RK) * C::kElem;
+    const uint8_t *gv = P.coef[1] + (cu * D.max_tokens * RV + (size_t)w_begin * RV) * C::kElem;
     // one tile: kDmaK / kDmaV dwordx4 DMAs per matrix; lane l moves 16 bytes
     // of chunk d*64 + l of the tile (lanes past the tile size idle)
     // tile `src` into ring slot `it` % DEPTH

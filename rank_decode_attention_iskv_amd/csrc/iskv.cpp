@@ -66,6 +66,14 @@ bool valid_config(const iskv_config *c) {
     return false;
   if (c->async_maintenance != 0 && c->async_maintenance != 1) return false;
   if (c->async_maintenance && c->num_layers > 64) return false;   // one generation bit per layer
+  if (c->joint_heads != 0 && c->joint_heads != 1) return false;
+  if (c->joint_heads) {
+    // the joint fold keeps an (r+64)-square core and a head's block columns in
+    // LDS: r <= 64, and at most 32 heads for its null-completion vectors
+    const int rv = c->rank_v ? c->rank_v : c->rank;
+    if (c->rank > 64 || rv > 64 || c->num_kv_heads > 32) return false;
+    if (c->async_maintenance) return false;
+  }
   return true;
 }
 
@@ -90,6 +98,8 @@ Dims make_dims(const iskv_config *c) {
   D.scale_log2 = (float)(scale * 1.4426950408889634);
   D.rope_base = c->rope_base;
   D.units = c->batch * c->num_kv_heads;
+  D.joint = c->joint_heads;
+  D.cunits = D.joint ? c->batch : D.units;
   // decode split records per unit: enough to spread the history over a few
   // waves of workgroups on 256 compute units, plus the window splits; the
   // merge keeps every (record, head) max and sum of a unit in LDS (<= 4096)
@@ -255,11 +265,13 @@ uint64_t persistent_bytes(const iskv_ctx *c) {
       const uint64_t n_e = (uint64_t)(q.length > q.n_c ? q.length - q.n_c : 0) + n_pre;
       const uint64_t n_comp = (uint64_t)(q.n_c - D.prefix);
       // per unit: both factors' coefficients, bases and singular values, and
-      // the exact rows of K and V
+      // the exact rows of K and V; a joint basis keeps one coefficient row and
+      // one S per sequence, its basis rows are the heads' slices
       const uint64_t rs = (uint64_t)D.rk + D.rv;
-      const uint64_t per = n_comp * rs * D.elem + (uint64_t)D.d * rs * 4 + rs * 4 +
-                           2ull * n_e * D.d * D.elem;
-      tot += per * (uint64_t)D.kv_heads;
+      const uint64_t H = (uint64_t)D.kv_heads;
+      const uint64_t shared = n_comp * rs * D.elem + rs * 4;
+      tot += (D.joint ? shared : shared * H) +
+             H * ((uint64_t)D.d * rs * 4 + 2ull * n_e * D.d * D.elem);
     }
   }
   return tot;
@@ -812,13 +824,14 @@ int iskv_export_state(iskv_ctx *c, int layer, void *host_buf, size_t bytes) {
   std::memcpy(o + 8, &n_comp, 8);
   float *f = reinterpret_cast<float *>(o + 16);
   for (int u = 0; u < D.units; ++u) {
+    const int cu = coef_unit(D, u);          // joint: every head lists its sequence's S and rows
     for (int x = 0; x < 2; ++x) {
       const size_t r = x ? D.rv : D.rk;
       std::memcpy(f, raw.data() + Gn.basis[x] + (size_t)u * D.d * r * 4, (size_t)D.d * r * 4);
       f += (size_t)D.d * r;
-      std::memcpy(f, raw.data() + Gn.sing[x] + (size_t)u * r * 4, r * 4);
+      std::memcpy(f, raw.data() + Gn.sing[x] + (size_t)cu * r * 4, r * 4);
       f += r;
-      const size_t coff = Gn.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
+      const size_t coff = Gn.coef[x] + (size_t)cu * D.max_tokens * r * D.elem;
       for (size_t i = 0; i < (size_t)D.max_tokens * r; ++i)
         f[i] = (i >= (size_t)D.prefix * r && i < (size_t)L.n_c * r) ? elem(coff, i) : 0.f;
       f += (size_t)D.max_tokens * r;
@@ -873,14 +886,18 @@ int iskv_import_state(iskv_ctx *c, int layer, const void *host_buf, size_t bytes
   };
   const float *f = reinterpret_cast<const float *>(in + 16);
   for (int u = 0; u < D.units; ++u) {
+    // joint: S and the coefficient rows of a sequence come from its head 0
+    const int cu = coef_unit(D, u);
+    const bool owner = !D.joint || u % D.kv_heads == 0;
     for (int x = 0; x < 2; ++x) {
       const size_t r = x ? D.rv : D.rk;
       std::memcpy(raw.data() + Gn.basis[x] + (size_t)u * D.d * r * 4, f, (size_t)D.d * r * 4);
       f += (size_t)D.d * r;
-      std::memcpy(raw.data() + Gn.sing[x] + (size_t)u * r * 4, f, r * 4);
+      if (owner) std::memcpy(raw.data() + Gn.sing[x] + (size_t)cu * r * 4, f, r * 4);
       f += r;
-      const size_t coff = Gn.coef[x] + (size_t)u * D.max_tokens * r * D.elem;
-      for (size_t i = (size_t)D.prefix * r; i < (size_t)n_c * r; ++i) put(coff, i, f[i]);
+      const size_t coff = Gn.coef[x] + (size_t)cu * D.max_tokens * r * D.elem;
+      if (owner)
+        for (size_t i = (size_t)D.prefix * r; i < (size_t)n_c * r; ++i) put(coff, i, f[i]);
       f += (size_t)D.max_tokens * r;
       for (int s = 0; s < D.slots; ++s)
         for (int d = 0; d < D.d; ++d) {
@@ -1001,7 +1018,7 @@ int iskv_prefill_layers(iskv_ctx *c, int n_layers, const int *layers, const void
                         const void *const *dev_v, int n_tokens, int in_dtype) {
   if (!c || n_layers < 1 || !layers || !dev_k || !dev_v || n_tokens < 0) return ISKV_EINVAL;
   if (in_dtype != ISKV_F32 && in_dtype != ISKV_BF16) return ISKV_EINVAL;
-  if (c->D.cow) return ISKV_ESTATE;
+  if (c->D.cow || c->D.joint) return ISKV_ESTATE;
   const Dims &D = c->D;
   for (int i = 0; i < n_layers; ++i) {
     if (check_layer(c, layers[i]) || !dev_k[i] || !dev_v[i]) return ISKV_EINVAL;

@@ -5,11 +5,18 @@
 // (two with copy-on-write maintenance: the layer's current one, read by
 // decode, and the one its maintenance writes):
 //   basis[X]  float [U][d][r_X]         row f, column c (orthonormal columns)
-//   sing[X]   float [U][r_X]            singular values S
-//   coef[X]   T     [U][max_tokens][r_X]  coefficient rows (row = position)
+//   sing[X]   float [CU][r_X]           singular values S
+//   coef[X]   T     [CU][max_tokens][r_X]  coefficient rows (row = position)
 //   frag      bytes [U][4*d*r_K]        key basis in the decode kernel's MFMA operand order
 // and once per layer:
-//   msync[X]  float [U][r_X][r_X]       pending synchronization matrix M = B_old^T B_new
+//   msync[X]  float [CU][r_X][r_X]      pending synchronization matrix M = B_old^T B_new
+//   jres[X]   float [CU][64][H*d]       joint fold only: residual / Q rows of the block
+//   jbn[X]    float [CU][H*d][r_X]      joint fold only: the new basis before it is stored
+// CU, the coefficient units, is U (one basis per KV head) or, with a joint
+// basis over a layer's H = kv_heads heads, the batch: sequence b's joint basis
+// (H*d x r_X) is then the H slices [u = b*H .. b*H+H-1][d][r_X], row h*d + f
+// of it being row f of unit b*H + h, and its one coefficient row per token
+// serves all H heads.
 //   ringk  T     [U][slots][d]       exact keys, row = ring slot (pre-RoPE)
 //   ringv  T     [U][d][slots]       exact values, transposed (column = ring slot)
 //   prek   T     [U][P][d]           protected prefix keys, row = position (pre-RoPE)
@@ -49,11 +56,18 @@ struct Dims {
   int prefix;             // P: protected exact positions 0..P-1 (multiple of 64)
   int cow;                // 1: copy-on-write maintenance (two generations, 64 more slots)
   int bulk_blocks;        // prefill: blocks folded per bulk pass (M slots per unit)
+  int joint;              // 1: one basis per (sequence, layer) over all KV heads
+  int cunits;             // coefficient units per layer: units, or batch when joint
 };
+
+// Coefficient unit of unit u, and the sequence of coefficient unit cu.
+__host__ __device__ inline int coef_unit(const Dims &D, int u) { return D.joint ? u / D.kv_heads : u; }
+__host__ __device__ inline int cunit_seq(const Dims &D, int cu) { return D.joint ? cu : cu / D.kv_heads; }
 
 // Pointers of one layer.
 struct LayerPtrs {
   float *basis[2], *sing[2], *msync[2];   // [X]: K = 0, V = 1
+  float *jres[2], *jbn[2];                // joint fold scratch
   uint8_t *coef[2];
   uint8_t *frag;
   uint8_t *ringk, *ringv, *prek, *prev;
@@ -76,27 +90,30 @@ struct GenLayout {
 
 struct LayerLayout {
   GenLayout gen[2];       // gen[1] == gen[0] without copy-on-write
-  size_t msync[2], ringk, ringv, prek, prev, bytes;
+  size_t msync[2], jres[2], jbn[2], ringk, ringv, prek, prev, bytes;
 };
 
 inline LayerLayout layer_layout(const Dims &D) {
   LayerLayout L{};
   size_t o = 0;
-  const size_t U = (size_t)D.units;
+  const size_t U = (size_t)D.units, CU = (size_t)D.cunits;
   for (int g = 0; g < (D.cow ? 2 : 1); ++g) {
     GenLayout &G = L.gen[g];
     for (int x = 0; x < 2; ++x) {
       const size_t r = x ? D.rv : D.rk;
       G.basis[x] = o; o = align_up(o + U * D.d * r * 4);
-      G.sing[x] = o;  o = align_up(o + U * r * 4);
-      G.coef[x] = o;  o = align_up(o + U * (size_t)D.max_tokens * r * D.elem);
+      G.sing[x] = o;  o = align_up(o + CU * r * 4);
+      G.coef[x] = o;  o = align_up(o + CU * (size_t)D.max_tokens * r * D.elem);
     }
     G.frag = o;  o = align_up(o + U * 4 * (size_t)D.d * D.rk);
   }
   if (!D.cow) L.gen[1] = L.gen[0];
+  const size_t hd = D.joint ? (size_t)D.kv_heads * D.d : 0;
   for (int x = 0; x < 2; ++x) {
     const size_t r = x ? D.rv : D.rk;
-    L.msync[x] = o; o = align_up(o + U * r * r * 4);
+    L.msync[x] = o; o = align_up(o + CU * r * r * 4);
+    L.jres[x] = o;  o = align_up(o + CU * kBlock * hd * 4);
+    L.jbn[x] = o;   o = align_up(o + CU * hd * r * 4);
   }
   L.ringk = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
   L.ringv = o; o = align_up(o + (size_t)D.units * D.slots * D.d * D.elem);
@@ -160,6 +177,8 @@ __host__ __device__ inline LayerPtrs layer_ptrs_gen(const Model &M, int l, int g
     P.basis[x] = (float *)(b + G.basis[x]);
     P.sing[x] = (float *)(b + G.sing[x]);
     P.msync[x] = (float *)(b + M.lay.msync[x]);
+    P.jres[x] = (float *)(b + M.lay.jres[x]);
+    P.jbn[x] = (float *)(b + M.lay.jbn[x]);
     P.coef[x] = b + G.coef[x];
   }
   P.frag = b + G.frag;
@@ -217,6 +236,9 @@ hipError_t launch_append(const Model &M, int layer, const void *k, const void *v
 
 // Fold the block at positions n_c..n_c+63 of every unit of the selected
 // layers: factor x (0 K, 1 V), or both (x = -1, one launch; equal ranks only).
+// With a joint basis this is launch_joint_fold.
+hipError_t launch_joint_fold(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
+                             const SeqTab &tab);
 hipError_t launch_block_update(const Model &M, const LayerSel &sel, int64_t n_c, int x, hipStream_t s,
                                const SeqTab &tab = SeqTab{});
 

@@ -24,7 +24,8 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// Reset: basis = I[:, :r] (the basis before any block has been seen).
+// Reset: basis = I[:, :r] (the basis before any block has been seen).  A joint
+// basis is the identity over its H*d rows: only head 0's slice holds ones.
 // ---------------------------------------------------------------------------
 __global__ void reset_basis_kernel(Model M, int layer) {
   const Dims &D = M.D;
@@ -36,7 +37,8 @@ __global__ void reset_basis_kernel(Model M, int layer) {
          i += (size_t)gridDim.x * blockDim.x) {
       const int c = (int)(i % r);
       const int f = (int)((i / r) % D.d);
-      P.basis[x][i] = (f == c) ? 1.f : 0.f;
+      const int h = D.joint ? (int)(i / ((size_t)D.d * r)) % D.kv_heads : 0;
+      P.basis[x][i] = (h * D.d + f == c) ? 1.f : 0.f;
     }
   }
 }
@@ -130,7 +132,7 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
 // B operand = 16 coefficient rows as stored (exact bf16), so every product is
 // exact and the output is rounded once to bf16.
 // f32 storage: one row per thread on the vector ALUs.
-// grid (row tiles, units (one factor) or units*2 (both), layers)
+// grid (row tiles, coefficient units (one factor) or twice that (both), layers)
 // ---------------------------------------------------------------------------
 // Bulk mode (prefill): the matrix depends on the row's 64-row block (see
 // bulk_suffix_kernel): rows older than n_c0 take slot 0, rows of bulk block j
@@ -160,10 +162,10 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   constexpr int TPW = BULK ? 4 : (R == 128 ? 4 : 8);   // 16-row tiles per wave
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
-  // grid.y: units (one factor, xsel) or units x 2 (both, equal ranks)
+  // grid.y: coefficient units (one factor, xsel) or twice that (both, equal ranks)
   const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
-  if (!seq_in(tab, u / D.kv_heads)) return;     // ragged: a sequence that did not fold
-  if (tab.n) n_old = tab.nc[u / D.kv_heads];
+  if (!seq_in(tab, cunit_seq(D, u))) return;    // ragged: a sequence that did not fold
+  if (tab.n) n_old = tab.nc[cunit_seq(D, u)];
   LayerPtrs P = layer_ptrs(M, l);
   const float *Ms = P.msync[x] + (size_t)u * R * R;
   const uint16_t *C = reinterpret_cast<const uint16_t *>(P.coef[x]) + (size_t)u * D.max_tokens * R;
@@ -247,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void sync_valu_kernel(Model M, LayerSel s
   const Dims &D = M.D;
   const int l = sel.idx[blockIdx.z];
   const int u = xsel < 0 ? blockIdx.y >> 1 : blockIdx.y, x = xsel < 0 ? blockIdx.y & 1 : xsel;
-  if (!seq_in(tab, u / D.kv_heads)) return;     // block-uniform, before the barrier
-  if (tab.n) n_old = tab.nc[u / D.kv_heads];
+  if (!seq_in(tab, cunit_seq(D, u))) return;    // block-uniform, before the barrier
+  if (tab.n) n_old = tab.nc[cunit_seq(D, u)];
   LayerPtrs P = layer_ptrs(M, l);
   const float4 *Ms = reinterpret_cast<const float4 *>(P.msync[x] + (size_t)u * R * R);
   if constexpr (BULK) {                         // one 64-row block per workgroup (block-uniform)
@@ -290,7 +292,7 @@ template <int R, typename T>
 hipError_t launch_sync_t(const Model &M, const LayerSel &sel, int64_t n_old, int x, hipStream_t s,
                          const SeqTab &tab, const BulkSync &bk) {
   if (n_old <= 0) return hipSuccess;
-  const unsigned ny = x < 0 ? M.D.units * 2 : M.D.units;
+  const unsigned ny = x < 0 ? M.D.cunits * 2 : M.D.cunits;
   const bool bulk = bk.mbulk != nullptr;
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int64_t rows_per_block = (int64_t)(kThreads / 64) * (bulk ? 4 : (R == 128 ? 4 : 8)) * 16;

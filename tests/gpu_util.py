@@ -33,7 +33,7 @@ class Pair:
     """A GPU cache and an oracle fed with identical float32 inputs."""
 
     def __init__(self, w: workloads.Workload, max_tokens=None, oracle=True, layers=1, prefix=0,
-                 rank_v=0):
+                 rank_v=0, joint=False):
         import torch
         from rank_decode_attention_iskv_amd import binding
         self.torch, self.binding, self.w = torch, binding, w
@@ -43,11 +43,13 @@ class Pair:
         self.prefix = prefix
         self.cfg = binding.make_config(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim,
                                        w.rank, w.window, self.max_tokens, storage,
-                                       protected_prefix=prefix, rank_v=rank_v)
+                                       protected_prefix=prefix, rank_v=rank_v,
+                                       joint_heads=int(joint))
+        self.joint = joint
         self.gpu = binding.IskvCache(self.cfg)
         self.ora = (Oracle(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
                            self.max_tokens, storage=w.storage, prefix=prefix,
-                           rank_v=rank_v or None) if oracle else None)
+                           rank_v=rank_v or None, joint_heads=joint) if oracle else None)
         self.length = [0] * layers
 
     def feed(self, layer, count, sync=True, chunk=64, on_fold=None):
@@ -100,11 +102,15 @@ class Pair:
         """State blob made from the oracle's state (for iskv_import_state)."""
         w = self.w
         units = []
+        d = w.head_dim
         for b in range(w.batch):
             for h in range(w.kv_heads):
                 u = self.ora.unit(b, layer, h)
-                units.append([dict(basis=f.B, S=f.S, coef=f.C[: u.n_c], ring=f.ring,
-                                   prefix=f.prefix) for f in (u.K, u.V)])
+                # a joint unit's rows are its heads' rows side by side: head h
+                # lists its slice of the basis, ring and prefix columns
+                cols = slice(h * d, (h + 1) * d) if self.joint else slice(None)
+                units.append([dict(basis=f.B[cols], S=f.S, coef=f.C[: u.n_c], ring=f.ring[:, cols],
+                                   prefix=f.prefix[:, cols]) for f in (u.K, u.V)])
         u0 = self.ora.unit(0, layer, 0)
         return self.binding.pack_state(self.cfg, u0.length, u0.compressed, units)
 

@@ -49,6 +49,8 @@ def test_workspace_bytes_valid_and_monotone():
     dict(batch=0), dict(max_tokens=0), dict(rope_base=0.5),
     dict(protected_prefix=100), dict(protected_prefix=-64), dict(protected_prefix=4160),
     dict(rank_v=48), dict(rank_v=16), dict(rank_v=-32), dict(rank=128, rank_v=256),
+    dict(joint_heads=2), dict(joint_heads=1, rank=128), dict(joint_heads=1, rank=64, rank_v=128),
+    dict(joint_heads=1, num_kv_heads=64, num_q_heads=64), dict(joint_heads=1, async_maintenance=1),
 ])
 def test_invalid_configs_rejected(kw):
     assert binding.workspace_bytes(base_cfg(**kw)) == 0
@@ -109,3 +111,17 @@ def test_strerror_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert binding.strerror(code)
     assert binding.strerror(99) == "unknown error"
+
+
+def test_joint_heads_workspace():
+    """A joint basis keeps one coefficient row per token for all heads: the
+    coefficient arrays shrink by the head count (the fold adds its scratch of
+    64 + r rows of heads x d floats per sequence and factor)."""
+    per_head = binding.workspace_bytes(base_cfg(rank=64))
+    joint = binding.workspace_bytes(base_cfg(rank=64, joint_heads=1))
+    assert joint > 0
+    coef_per_head = 3 * 2 * 16 * 4096 * 64 * 2       # layers x factors x units x tokens x r x bf16
+    scratch = 3 * 2 * 2 * (64 + 64) * 8 * 128 * 4    # layers x factors x sequences x rows x H*d x f32
+    assert per_head - joint >= coef_per_head * 7 // 8 - scratch - (1 << 16)
+    # the state blob keeps its per-head layout
+    assert binding.state_bytes(base_cfg(rank=64, joint_heads=1)) == binding.state_bytes(base_cfg(rank=64))

@@ -42,6 +42,10 @@ class Workload:
     hot_alpha: float = 4.0      # hot key norm, in units of the RMS key norm
     hot_beta: float = 2.0       # query alignment to the hot direction
     seed: int = 1000
+    # True: the KV heads of a (sequence, layer) mix the same latent z_t (each
+    # through its own G), so their rows side by side have rank signal_rank --
+    # the structure a basis over all heads of a layer compresses
+    shared_latent: bool = False
     extra: dict = field(default_factory=dict)
 
 
@@ -117,7 +121,8 @@ def unit_tokens(w: Workload, b: int, layer: int, head: int, which: int,
                 start: int, count: int) -> np.ndarray:
     """Rows start..start+count-1 of one unit's K (which=0) or V (which=1) stream.
 
-    x_t = G diag(scales) z_t + e_t, z_t ~ N(0, I_k), e_t ~ N(0, noise_std^2 I_d);
+    x_t = G diag(scales) z_t + e_t, z_t ~ N(0, I_k), e_t ~ N(0, noise_std^2 I_d)
+    (z_t common to the heads of the sequence and layer when shared_latent);
     with hot_fraction > 0, a seeded Bernoulli share of key positions also gets
     + alpha * sqrt(d) * u (u = hot_direction).  Rows are drawn per 64-token
     chunk, so any window of positions can be regenerated on its own.
@@ -130,7 +135,11 @@ def unit_tokens(w: Workload, b: int, layer: int, head: int, which: int,
     last = (start + count - 1) // chunk if count else first - 1
     for c in range(first, last + 1):
         rng = _rng(w, 1, b, layer, head, which, c)
-        z = rng.standard_normal((chunk, k))
+        if w.shared_latent:
+            # z from a stream without the head; noise and hot keys per head
+            z = _rng(w, 5, b, layer, which, c).standard_normal((chunk, k))
+        else:
+            z = rng.standard_normal((chunk, k))
         x = (z * scales) @ g.T
         if w.noise_std:
             x = x + w.noise_std * rng.standard_normal((chunk, d))
