@@ -99,6 +99,9 @@ def parse():
                          "to every sequence (iskv_append_ragged), attends each at its own length "
                          "(iskv_decode_attn_ragged), and folds the sequences whose ring fills")
     ap.add_argument("--seed", type=int, default=1000)
+    ap.add_argument("--joint-heads", action="store_true",
+                    help="one basis per (sequence, layer) over all KV heads (joint_heads = 1); "
+                         "the heads' inputs mix shared latent factors")
     ap.add_argument("--async-maintenance", action="store_true",
                     help="copy-on-write maintenance on a second stream (iskv_maintain / "
                          "iskv_switch) instead of block update + sync between decode steps")
@@ -119,6 +122,7 @@ def preset(args, cfg_id=None, **over):
             p[k] = v
     p["rank_v"] = (args.rank_v if cfg_id is None else 0) or p["rank"]
     p["prefix"] = args.protected_prefix if cfg_id is None else 0
+    p["joint"] = int(args.joint_heads) if cfg_id is None else 0
     p.update(over)
     p["id"] = cfg_id or args.config
     return p
@@ -169,7 +173,8 @@ class Generator:
     """Per (instance-layer, sequence, KV head, K|V): x_t = G diag(s) z_t + 0.01 e_t
     with G Gaussian (d x k, "gauss") or Haar-orthonormal columns with s_i ~ 1/i
     ("power"); with hot > 0 a Bernoulli share of keys gets + 4 sqrt(d) u, u a unit
-    vector per (layer, KV head), and queries get + 2 u."""
+    vector per (layer, KV head), and queries get + 2 u.  Joint-head presets draw
+    z_t once per (sequence, K|V) for all heads."""
 
     def __init__(self, torch, p, n_layers, seed):
         self.torch, self.p = torch, p
@@ -197,7 +202,11 @@ class Generator:
         """k, v: [batch, n, kv_heads, d] float32."""
         torch, p = self.torch, self.p
         B, H, d, k = p["batch"], p["kv"], 128, p["signal"]
-        z = torch.randn(B, H, 2, n, k, device="cuda", generator=self.g)
+        if p.get("joint"):
+            # the heads of a sequence mix the same latent factors
+            z = torch.randn(B, 1, 2, n, k, device="cuda", generator=self.g).expand(B, H, 2, n, k)
+        else:
+            z = torch.randn(B, H, 2, n, k, device="cuda", generator=self.g)
         x = torch.matmul(z, self.mix[layer])
         if self.noise:
             x = x + self.noise * torch.randn(B, H, 2, n, d, device="cuda", generator=self.g)
@@ -218,18 +227,22 @@ class Generator:
 
 def decode_bytes(p, n_c, n_e):
     """Algorithmic bytes of one decode call of one layer: coefficients of K
-    (rank r) and V (rank r_v), the exact rows of K and V (window ring and
-    protected prefix), the two fp32 bases, the fp32 query and output."""
+    (rank r) and V (rank r_v) -- per KV head, or once per sequence with a
+    joint basis --, the exact rows of K and V (window ring and protected
+    prefix), the two fp32 bases, the fp32 query and output."""
     elem = 2 if p["storage"] == 1 else 4
     rs = p["rank"] + p["rank_v"]
-    per_unit = n_c * rs * elem + n_e * 128 * 2 * elem + 128 * rs * 4
-    return p["batch"] * p["kv"] * per_unit + p["batch"] * p["q"] * 128 * 4 * 2
+    coef = n_c * rs * elem
+    per_unit = n_e * 128 * 2 * elem + 128 * rs * 4 + (0 if p.get("joint") else coef)
+    seq = coef if p.get("joint") else 0
+    return p["batch"] * (p["kv"] * per_unit + seq) + p["batch"] * p["q"] * 128 * 4 * 2
 
 
 def state_bytes(p, n_c, n_e):
     elem = 2 if p["storage"] == 1 else 4
-    return p["layers"] * p["batch"] * p["kv"] * (n_c * (p["rank"] + p["rank_v"]) * elem +
-                                                  n_e * 256 * elem)
+    coef = n_c * (p["rank"] + p["rank_v"]) * elem
+    heads = p["kv"] * n_e * 256 * elem
+    return p["layers"] * p["batch"] * ((coef if p.get("joint") else coef * p["kv"]) + heads)
 
 
 DECODE_SOURCES = ("decode.hip", "device_common.hpp", "iskv_internal.hpp")
@@ -279,6 +292,8 @@ def describe(p):
          f"accumulate; K/V {sig}"
          + ("; 30% hot keys aligned with the queries" if p["hot"] else "")
          + (f"; first {p['prefix']} positions exact" if p["prefix"] else "")
+         + ("; one basis per sequence over the 8 KV heads (joint), heads mixing shared latent "
+            "factors" if p.get("joint") else "")
          + "; block update + sync every 64 tokens")
     return s
 
@@ -305,7 +320,8 @@ def measure(p, steps, warmup, instances, seed, quiet=False):
     per_inst = (warmup + steps + I - 1) // I
     max_tokens = L0 + per_inst + 64 * 3 + 64
     cfg = binding.make_config(p["batch"], nl, p["kv"], p["q"], 128, p["rank"], W, max_tokens,
-                              p["storage"], protected_prefix=P, rank_v=p["rank_v"])
+                              p["storage"], protected_prefix=P, rank_v=p["rank_v"],
+                              joint_heads=p.get("joint", 0))
     cache = binding.IskvCache(cfg)
     stream = torch.cuda.current_stream()
     gen = Generator(torch, p, nl, seed)
@@ -443,7 +459,7 @@ def measure(p, steps, warmup, instances, seed, quiet=False):
     event_ms = (sum(fold_ms) + sum(sync_ms)) / len(events)
     # natural rate: one event per 64 steps of every instance
     ms_per_step = dec_ms / steps + event_ms / (64 * I)
-    units = nl * B * H * 2
+    units = nl * B * (1 if p.get("joint") else H) * 2     # folded (sequence[, head], K|V)
 
     # ---- roofline of the decode kernel: back-to-back decode calls over the
     # layers at their current lengths, one event pair on the decode stream
@@ -641,7 +657,7 @@ def measure_async(p, steps, warmup, instances, seed, quiet=False):
         f1.record(stream)
         torch.cuda.synchronize()
         ev_ms.append(f0.elapsed_time(f1))
-    units = nl * B * H * 2
+    units = nl * B * (1 if p.get("joint") else H) * 2     # folded (sequence[, head], K|V)
     flags = max(cache.status(i).numeric_flags for i in range(nl))
     finite = bool(torch.isfinite(out).all().item())
     res = {
@@ -742,27 +758,39 @@ def cpu_baseline(p, sample_units=2, decode_calls=3):
     from threadpoolctl import threadpool_limits
 
     import workloads
-    from oracle import Unit
+    from oracle import JointUnit, Unit
 
     cores = len(os.sched_getaffinity(0))
     spectrum = "power" if p["spectrum"] == "power" else "gauss"
+    joint = bool(p.get("joint"))
+    heads = p["kv"] if joint else 1          # KV heads per oracle unit
+    if joint:
+        sample_units = 1
     w = workloads.with_(workloads.WORKLOADS[p["id"]], window=p["window"], rank=p["rank"],
-                        context=p["context"], batch=1, kv_heads=1, q_heads=p["q"] // p["kv"],
-                        spectrum=spectrum)
-    g = p["q"] // p["kv"]
+                        context=p["context"], batch=1, kv_heads=heads, q_heads=heads * p["q"] // p["kv"],
+                        spectrum=spectrum, shared_latent=joint)
+    g = heads * p["q"] // p["kv"]
     storage = "bf16" if p["storage"] == 1 else "f32"
     runs = {}
     for threads in (cores, 1):
         with threadpool_limits(limits=threads):
             fold_t, folds, dec_t, t0 = 0.0, 0, 0.0, time.perf_counter()
             for su in range(sample_units):
-                u = Unit(128, p["rank"], p["window"], p["context"] + 64, storage,
-                         r_v=p["rank_v"])
+                if joint:
+                    u = JointUnit(heads, 128, p["rank"], p["window"], p["context"] + 64, storage,
+                                  r_v=p["rank_v"])
+                else:
+                    u = Unit(128, p["rank"], p["window"], p["context"] + 64, storage,
+                             r_v=p["rank_v"])
                 pos = 0
                 while pos < p["context"]:
                     n = min(64, p["context"] - pos)
-                    k = workloads.unit_tokens(w, 0, su, 0, 0, pos, n)
-                    v = workloads.unit_tokens(w, 0, su, 0, 1, pos, n)
+                    if joint:
+                        kk, vv = workloads.tokens(w, 0, pos, n)
+                        k, v = kk[0], vv[0]
+                    else:
+                        k = workloads.unit_tokens(w, 0, su, 0, 0, pos, n)
+                        v = workloads.unit_tokens(w, 0, su, 0, 1, pos, n)
                     for i in range(n):
                         u.append(k[i], v[i])
                         if u.ready:
@@ -778,7 +806,7 @@ def cpu_baseline(p, sample_units=2, decode_calls=3):
                     u.decode(q[:g], u.length - 1, 1.0 / math.sqrt(128))
                 dec_t += (time.perf_counter() - d0) / decode_calls
             build_t = time.perf_counter() - t0
-        n_units = p["layers"] * p["batch"] * p["kv"]
+        n_units = p["layers"] * p["batch"] * p["kv"] // heads
         dec_unit = dec_t / sample_units
         fold_unit = fold_t / max(folds, 1)
         step_s = n_units * (dec_unit + fold_unit / 64.0)
@@ -787,10 +815,11 @@ def cpu_baseline(p, sample_units=2, decode_calls=3):
     best = max(runs, key=lambda t: runs[t]["value"])
     return {
         "value": runs[best]["value"], "unit": "tokens/s", "cores": best, "kind": "oracle",
-        "sample": (f"{sample_units} (sequence, KV head) units (K and V) of the workload built to "
+        "sample": (f"{sample_units} (sequence, {'layer' if joint else 'KV head'}) units (K and V) "
+                   f"of the workload built to "
                    f"{p['context']} tokens by the float64 oracle ({runs[best]['folds']} folds + syncs), "
                    f"then {decode_calls} decode calls of {g} query heads each; one step = "
-                   f"{p['layers'] * p['batch'] * p['kv']} units x (decode + fold+sync / 64); "
+                   f"{p['layers'] * p['batch'] * p['kv'] // heads} units x (decode + fold+sync / 64); "
                    + ("measured" if p["id"] == 1 else "extrapolated linearly from the sample")),
         "cpu_model": cpu_model(),
         "by_threads": {str(t): r for t, r in runs.items()},
@@ -960,7 +989,7 @@ def main():
             "workload": describe(p),
             "config_id": p["id"], "global_batch": p["batch"], "seq_len": p["context"],
             "layers": p["layers"], "rank": p["rank"], "rank_v": p["rank_v"], "window": p["window"],
-            "protected_prefix": p["prefix"], "parallelism": "single GPU",
+            "protected_prefix": p["prefix"], "joint_heads": p["joint"], "parallelism": "single GPU",
             "step_calls": ("per layer iskv_append_decode; when the rings fill, iskv_block_update(-1) "
                            "+ iskv_sync(-1) over every layer of every instance"),
             "timing": ("decode steps timed in segments by HIP events; each fold event (block update "
@@ -1003,6 +1032,10 @@ def main():
                                                                         quiet=True), p5)))
         extras["config5_sweep"] = pts
         extras["config2_prefill_32k_16_layers"] = prefill_compare(preset(args, 2))
+        for cid in (2, 3):
+            pj = preset(args, cid, rank=64, rank_v=64, joint=1)
+            extras[f"config{cid}_joint_heads_r64"] = compact(
+                measure(pj, 128, 16, 0, args.seed + 10 + cid, quiet=True), pj)
         res["extras"] = extras
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(p)
     print(json.dumps(res), flush=True)
