@@ -259,10 +259,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_hash, cfg_id):
+def committed_traffic(kernel_hash, p):
     """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
     counter summary of this workload, if taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_attn_config{cfg_id}_counters.txt")
+    tag = f"_joint_r{p['rank']}" if p.get("joint") else ""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_config{p['id']}{tag}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -968,7 +969,7 @@ def main():
     p = preset(args)
     r = measure(p, args.steps, args.warmup, args.instances, args.seed)
     kh = kernel_source_hash()
-    r["roofline"]["traffic"] = committed_traffic(kh, p["id"])
+    r["roofline"]["traffic"] = committed_traffic(kh, p)
     copy_gbs = stream_bandwidth()
     r["roofline"]["measured_copy_GBs"] = copy_gbs
     r["roofline"]["frac_of_measured_copy"] = r["roofline"]["achieved"] / copy_gbs
