@@ -262,3 +262,94 @@ def test_joint_config_and_state_errors():
     n_e = st.length - st.compressed
     assert st.persistent_bytes == persistent_kv_bytes(st.compressed, n_e, 1, w.kv_heads, w.head_dim,
                                                       w.rank, 2, joint_heads=True)
+
+
+def _joint_full_size(w, n_c, length, q_positions, sample, fold=False):
+    """A random joint state of the workload's full shapes imported into the
+    library; decode (and, with fold=True, one block update + sync first) of
+    every sequence, compared with the joint oracle on the sampled sequences."""
+    import math
+
+    import torch
+    from oracle import JointUnit
+    from rank_decode_attention_iskv_amd import binding
+
+    H, d = w.kv_heads, w.head_dim
+    max_tokens = length + 64
+    cfg = binding.make_config(w.batch, 1, H, w.q_heads, d, w.rank, w.window, max_tokens,
+                              binding.BF16 if w.storage == "bf16" else binding.F32, joint_heads=1)
+    gpu = binding.IskvCache(cfg)
+    states = {}
+
+    def units():
+        for b in range(w.batch):
+            xs = workloads.synthetic_joint(w, b, length, n_c, max_tokens, ring_in_span=fold)
+            if b in sample:
+                states[b] = xs
+            for h in range(H):
+                cols = slice(h * d, (h + 1) * d)
+                yield [dict(basis=x["basis"][cols], S=x["S"], coef=x["coef"], ring=x["ring"][:, cols])
+                       for x in xs]
+    gpu.import_state(0, binding.pack_state(cfg, length, n_c, units()))
+    oras = {}
+    for b in sample:
+        xk, xv = states[b]
+        u = JointUnit(H, d, w.rank, w.window, max_tokens, w.storage)
+        u.load_state(length, n_c, xk["ring"], xv["ring"], xk["basis"], xk["S"], xk["coef"],
+                     xv["basis"], xv["S"], xv["coef"])
+        oras[b] = u
+    if fold:
+        assert gpu.status(0).blocks_ready == 1
+        gpu.block_update(0)
+        gpu.sync(0)
+        for u in oras.values():
+            u.fold()
+            u.sync()
+        length2, n_c2, st = binding.unpack_state(cfg, gpu.export_state(0))
+        for b, u in oras.items():
+            for x, f in enumerate((u.K, u.V)):
+                B = np.concatenate([st[b * H + h][x]["basis"].astype(np.float64) for h in range(H)])
+                assert np.linalg.norm(B.T @ B - np.eye(B.shape[1]), 2) < 1e-5
+                k = _leading(f.S)
+                np.testing.assert_allclose(st[b * H][x]["S"][:k], f.S[:k], rtol=1e-4, atol=1e-5 * f.S[0])
+                H_gpu = st[b * H][x]["coef"][:n_c2].astype(np.float64) @ B.T
+                H_ora = f.C[:n_c2] @ f.B.T
+                err = np.linalg.norm(H_gpu - H_ora) / np.linalg.norm(H_ora)
+                print(f"joint full-size fold: sequence {b} history error {err:.2e}")
+                assert err < 1e-3
+    g = w.q_heads // H
+    errs = []
+    for step, q_pos in enumerate(q_positions):
+        q = q32(workloads.query(w, 0, step))
+        qt = torch.from_numpy(q.astype(np.float32)).cuda()
+        out = torch.empty_like(qt)
+        gpu.decode_attn(0, qt, q_pos, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        for b, u in oras.items():
+            ref = u.decode(q[b], q_pos, 1.0 / math.sqrt(d))
+            errs.append(rel_err_per_head(got[b:b + 1], ref[None]))
+    gpu.destroy()
+    print("joint full-size decode errors", ["%.2e" % e for e in errs])
+    return errs
+
+
+def test_joint_full_size_batch16_16k_rank64():
+    """Batch 16 x 16K, 8 KV / 32 query heads, one basis per sequence over the
+    8 heads at r = 64, window 512, bf16 (the joint bench preset's shapes):
+    decode of all sequences, sequences 0, 7 and 15 against the oracle."""
+    w = workloads.with_(workloads.WORKLOADS[3], shared_latent=True)
+    n_c = 15872
+    errs = _joint_full_size(w, n_c, n_c + w.window + 45, [n_c + w.window + 44], sample=(0, 7, 15))
+    assert max(errs) < ATOL_OUT, errs
+
+
+def test_joint_full_size_gqa_layer_32k_fold_and_sync():
+    """The 32K GQA layer with a joint basis at r = 64 (bf16): one block
+    update + sync at full length, then decode, against the oracle."""
+    w = workloads.with_(workloads.WORKLOADS[2], rank=64, shared_latent=True)
+    n_c = 32448
+    length = n_c + w.window + 64              # ring full: the next fold is ready
+    errs = _joint_full_size(w, n_c, length, [length - 1, length + 5], sample=(0,), fold=True)
+    assert max(errs) < ATOL_OUT, errs

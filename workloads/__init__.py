@@ -227,3 +227,33 @@ def synthetic_state(w: Workload, length: int, n_c: int, max_tokens: int, seed: i
     (b * kv_heads + h)."""
     return [synthetic_unit(w, b, h, length, n_c, max_tokens, seed, rank_v, ring_in_span)
             for b in range(w.batch) for h in range(w.kv_heads)]
+
+
+def synthetic_joint(w: Workload, b: int, length: int, n_c: int, max_tokens: int, seed: int = 7,
+                    rank_v: int = 0, ring_in_span: bool = False):
+    """synthetic_unit for a joint basis over the kv_heads heads of sequence b:
+    per K|V an orthonormal (kv_heads*d x r) basis, singular values, one
+    coefficient row per position for all heads, and ring rows of all heads
+    side by side ((window + 64) x kv_heads*d)."""
+    D, slots = w.kv_heads * w.head_dim, w.window + 64
+    assert n_c % 64 == 0 and w.window <= length - n_c <= w.window + 64
+    xs = []
+    for x in range(2):
+        r = (rank_v or w.rank) if x else w.rank
+        rng = _rng(w, 9002, seed, b, x)             # 9002: joint state stream tag
+        B, _ = np.linalg.qr(rng.standard_normal((D, r)))
+        S = np.sort(rng.uniform(1.0, 50.0, r))[::-1].astype(np.float32)
+        C = np.zeros((max_tokens, r), np.float32)
+        C[:n_c] = rng.standard_normal((n_c, r)).astype(np.float32) * (2.0 / np.sqrt(r))
+        ring = np.zeros((slots, D), np.float32)
+        pos = np.arange(n_c, length)
+        if ring_in_span:
+            z = rng.standard_normal((len(pos), r)) * (2.0 / np.sqrt(r))
+            rows = z @ B.T + 1e-3 * rng.standard_normal((len(pos), D))
+        else:
+            rows = rng.standard_normal((len(pos), D)) * 0.25
+        ring[pos % slots] = rows.astype(np.float32)
+        if w.storage == "bf16":
+            C, ring = _bf16_grid(C), _bf16_grid(ring)
+        xs.append(dict(basis=B.astype(np.float32), S=S, coef=C, ring=ring))
+    return xs
