@@ -83,11 +83,14 @@ __device__ __forceinline__ int opaque_zero() {
 // With BT the tile's four n are strided by N/4, so the lanes of a wave read
 // rows that start in different banks.
 // ---------------------------------------------------------------------------
+// gemm4_part: the same over threads t0 .. t0 + nt - 1 only (thread tid), so
+// that two independent products can share the workgroup.
 template <int M, int N, int K, bool AT, bool BT, typename Out>
-__device__ __forceinline__ void gemm4(const float *A, int lda, const float *B, int ldb, Out out) {
+__device__ __forceinline__ void gemm4_part(const float *A, int lda, const float *B, int ldb, Out out,
+                                           int tid, int nt) {
   static_assert(M % 4 == 0 && N % 4 == 0 && K % 4 == 0, "tile multiples");
   constexpr int TN = N / 4, TILES = (M / 4) * TN;
-  for (int tile = threadIdx.x; tile < TILES; tile += kThreads) {
+  for (int tile = tid; tile < TILES; tile += nt) {
     const int m0 = (tile / TN) * 4, tn = tile % TN;
     int nn[4];
 #pragma unroll
@@ -129,6 +132,61 @@ __device__ __forceinline__ void gemm4(const float *A, int lda, const float *B, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) out(m0 + i, nn[j], acc[i][j]);
   }
+}
+
+template <int M, int N, int K, bool AT, bool BT, typename Out>
+__device__ __forceinline__ void gemm4(const float *A, int lda, const float *B, int ldb, Out out) {
+  gemm4_part<M, N, K, AT, BT>(A, lda, B, ldb, out, (int)threadIdx.x, kThreads);
+}
+
+// ---------------------------------------------------------------------------
+// The same product on the matrix cores (v_mfma_f32_16x16x4_f32: fp32 inputs,
+// fp32 accumulation), 16 x 16 output tiles dealt to waves w0, w0 + nw, ...
+// (this wave is `wave`).  In each group of four MFMAs covering k0 .. k0 + 15,
+// lane (j = lane % 16, g = lane / 16) supplies A(i0 + j, k) and B(k, n0 + j)
+// for k = k0 + 4 g + m in MFMA m: every k once (the sum is order-free), with
+// the lane's four A values contiguous when A is row-major and its four B
+// values contiguous when B is given transposed.  Output rows 4 g .. 4 g + 3,
+// column j of the tile are the lane's accumulator.
+// ---------------------------------------------------------------------------
+template <int M, int N, int K, bool AT, bool BT, typename Out>
+__device__ __forceinline__ void gemm_mfma_part(const float *A, int lda, const float *B, int ldb, Out out,
+                                               int wave, int nw) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "16-wide tiles");
+  constexpr int TN = N / 16, TILES = (M / 16) * TN;
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  for (int tile = wave; tile < TILES; tile += nw) {
+    const int i0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
+    floatx4 acc = zero4();
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const int kb = k0 + 4 * g;
+      float a[4], b[4];
+      if constexpr (!AT) {
+        const float4 v = ld4(A + (i0 + j) * lda + kb);
+        a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = A[(kb + m) * lda + i0 + j];
+      }
+      if constexpr (BT) {
+        const float4 v = ld4(B + (n0 + j) * ldb + kb);
+        b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) b[m] = B[(kb + m) * ldb + n0 + j];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma4(a[m], b[m], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out(i0 + 4 * g + r, n0 + j, acc[r]);
+  }
+}
+
+template <int M, int N, int K, bool AT, bool BT, typename Out>
+__device__ __forceinline__ void gemm_mfma(const float *A, int lda, const float *B, int ldb, Out out) {
+  gemm_mfma_part<M, N, K, AT, BT>(A, lda, B, ldb, out, (int)(threadIdx.x >> 6), kThreads / 64);
 }
 
 // ---------------------------------------------------------------------------

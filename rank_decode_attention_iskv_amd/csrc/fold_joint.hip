@@ -71,6 +71,24 @@ struct JointLayout {
                 "16-byte aligned regions");
 };
 
+// Linv <- L^{-1} (n x n, row strides ldl / ldi) from the factor L and invd
+// that chol_lds left: column j is the forward solve of e_j, so Linv X equals
+// the column-by-column forward solve of X, dropped pivots included (their rows
+// of Linv are 0).  Applied to a head's tile as one product over the whole
+// workgroup instead of one sequential solve per column (or row) per thread.
+template <int n>
+__device__ __forceinline__ void tri_inverse(const float *L, int ldl, const float *invd, float *Linv, int ldi) {
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    float x[n];
+#pragma unroll
+    for (int t = 0; t < n; ++t) x[t] = t == tid ? 1.f : 0.f;
+    fwd_solve<n>(x, L, ldl, invd);
+#pragma unroll
+    for (int t = 0; t < n; ++t) Linv[t * ldi + tid] = x[t];
+  }
+}
+
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel sel, int64_t n_c, int xsel,
                                                               SeqTab tab) {
@@ -133,17 +151,6 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
   auto zero = [&](float *p, int n) {
     for (int i = tid; i < n; i += kThreads) p[i] = 0.f;
   };
-  // x <- L^{-1} x for every column of the 64 x d tile in sX (L, invd in LDS)
-  auto solve_cols = [&](const float *L, int ldl) {
-    if (tid < D) {
-      float x[TB];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) x[t] = sX[t * LA + tid];
-      fwd_solve<TB>(x, L, ldl, invd);
-#pragma unroll
-      for (int t = 0; t < TB; ++t) sX[t * LA + tid] = x[t];
-    }
-  };
 
   // ---------------- phase 1: projection (twice), residual, its Gram ----------
   zero(sP, TB * LB);
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     asq += load_A(h);
     load_slice(basis + (size_t)h * D * R, sB);
     __syncthreads();
-    gemm4<TB, R, D, false, false>(sA, LA, sB, LB, [&](int t, int c, float v) { sP[t * LB + c] += v; });
+    gemm_mfma<TB, R, D, false, false>(sA, LA, sB, LB, [&](int t, int c, float v) { sP[t * LB + c] += v; });
     __syncthreads();
   }
   const float normA2 = block_sum(asq, red);
@@ -163,11 +170,11 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     (void)load_A(h);
     load_slice(basis + (size_t)h * D * R, sB);
     __syncthreads();
-    gemm4<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
+    gemm_mfma<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
       sX[t * LA + f] = sA[t * LA + f] - v;
     });
     __syncthreads();
-    gemm4<TB, R, D, false, false>(sX, LA, sB, LB, [&](int t, int c, float v) { sS1[t * LS + c] += v; });
+    gemm_mfma<TB, R, D, false, false>(sX, LA, sB, LB, [&](int t, int c, float v) { sS1[t * LS + c] += v; });
     __syncthreads();
   }
   for (int i = tid; i < TB * R; i += kThreads) {
@@ -179,16 +186,18 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     (void)load_A(h);
     load_slice(basis + (size_t)h * D * R, sB);
     __syncthreads();
-    gemm4<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
+    gemm_mfma<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
       sX[t * LA + f] = sA[t * LA + f] - v;
     });
     __syncthreads();
     store_cols(h, sX);
-    gemm4<TB, TB, D, false, true>(sX, LA, sX, LA, [&](int a, int b, float v) { sS2[a * LS + b] += v; });
+    gemm_mfma<TB, TB, D, false, true>(sX, LA, sX, LA, [&](int a, int b, float v) { sS2[a * LS + b] += v; });
     __syncthreads();
   }
 
   // ---------------- phase 2: Q by CholeskyQR2, against B once more ----------
+  // (A is not needed until the last pass: its region holds each head's new
+  // Q rows between the product that makes them and their store.)
   {
     float tr = 0.f;
 #pragma unroll 8
@@ -196,28 +205,32 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     const float tau = fmaxf(kGuardAbs * normA2, fminf(kGuard * normA2, kGuardRel * tr));
     chol_lds<TB>(sS2, LS, tau, invd);              // L0 in S2
   }
-  zero(sS1, TB * LS);
+  tri_inverse<TB>(sS2, LS, invd, sS1, LS);         // L0^{-1} in S1
   __syncthreads();
-  for (int h = 0; h < H; ++h) {                    // Q0 = L0^{-1} Res; G1 = Q0 Q0^T, into S1
+  zero(sS2, TB * LS);
+  __syncthreads();
+  for (int h = 0; h < H; ++h) {                    // Q0 = L0^{-1} Res; G1 = Q0 Q0^T, into S2
     load_cols(h, sX);
     __syncthreads();
-    solve_cols(sS2, LS);
+    gemm_mfma<TB, D, TB, false, false>(sS1, LS, sX, LA, [&](int t, int f, float v) { sA[t * LA + f] = v; });
     __syncthreads();
-    store_cols(h, sX);
-    gemm4<TB, TB, D, false, true>(sX, LA, sX, LA, [&](int a, int b, float v) { sS1[a * LS + b] += v; });
+    store_cols(h, sA);
+    gemm_mfma<TB, TB, D, false, true>(sA, LA, sA, LA, [&](int a, int b, float v) { sS2[a * LS + b] += v; });
     __syncthreads();
   }
-  chol_lds<TB>(sS1, LS, 0.25f, invd);              // L1 in S1
+  chol_lds<TB>(sS2, LS, 0.25f, invd);              // L1 in S2
+  tri_inverse<TB>(sS2, LS, invd, sS1, LS);         // L1^{-1} in S1
+  __syncthreads();
   zero(sS2, TB * LS);
   __syncthreads();
   for (int h = 0; h < H; ++h) {                    // Q1 = L1^{-1} Q0; T = Q1 B, into S2
     load_cols(h, sX);
     load_slice(basis + (size_t)h * D * R, sB);
     __syncthreads();
-    solve_cols(sS1, LS);
+    gemm_mfma<TB, D, TB, false, false>(sS1, LS, sX, LA, [&](int t, int f, float v) { sA[t * LA + f] = v; });
     __syncthreads();
-    store_cols(h, sX);
-    gemm4<TB, R, D, false, false>(sX, LA, sB, LB, [&](int t, int c, float v) { sS2[t * LS + c] += v; });
+    store_cols(h, sA);
+    gemm_mfma<TB, R, D, false, false>(sA, LA, sB, LB, [&](int t, int c, float v) { sS2[t * LS + c] += v; });
     __syncthreads();
   }
   zero(sS1, TB * LS);
@@ -227,10 +240,10 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     load_slice(basis + (size_t)h * D * R, sB);
     (void)load_A(h);
     __syncthreads();
-    gemm4<TB, D, R, false, true>(sS2, LS, sB, LB, [&](int t, int f, float v) { sX[t * LA + f] -= v; });
+    gemm_mfma<TB, D, R, false, true>(sS2, LS, sB, LB, [&](int t, int f, float v) { sX[t * LA + f] -= v; });
     __syncthreads();
     store_cols(h, sX);
-    gemm4<TB, TB, D, false, true>(sA, LA, sX, LA, [&](int t, int j, float v) { sS1[t * LS + j] += v; });
+    gemm_mfma<TB, TB, D, false, true>(sA, LA, sX, LA, [&](int t, int j, float v) { sS1[t * LS + j] += v; });
     __syncthreads();
   }
 
@@ -294,68 +307,44 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
   const float tol_null = 64.f * N * FLT_EPSILON * sig0;
   if (!isfinite(sig0) && tid == 0) set_flag(M.sh, 1);
   {
-    constexpr int TK = R / 4, TILES = (D / 4) * TK, TPT = (TILES + kThreads - 1) / kThreads;
+    // On the matrix cores, as gemm_mfma_part: 16 x 16 tiles (16 basis rows f,
+    // 16 new columns k) dealt to the waves; the B operand is row perm[k] of
+    // the core, read along its columns (contiguous), then each column is
+    // scaled by 1/s'_k (0 for a null direction).
+    constexpr int TN = R / 16, TILES = (D / 16) * TN, NW = kThreads / 64;
+    const int lane = tid & 63, wave = tid >> 6, j = lane & 15, g = lane >> 4;
     for (int h = 0; h < H; ++h) {
       load_slice(basis + (size_t)h * D * R, sB);
       load_cols(h, sX);                            // Q_h
       __syncthreads();
-#pragma unroll
-      for (int tt = 0; tt < TPT; ++tt) {
-        const int tile = tid + tt * kThreads;
-        if (tile >= TILES) continue;
-        const int f0 = (tile / TK) * 4, k0 = (tile % TK) * 4;
-        float acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-        const float *zr[4];
-        float zs[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = perm[k0 + j];
-          zr[j] = core + row * LC;
-          zs[j] = sig[row] > tol_null ? 1.f / sig[row] : 0.f;
+      for (int tile = wave; tile < TILES; tile += NW) {
+        const int f0 = (tile / TN) * 16, k0 = (tile % TN) * 16;
+        const int row = perm[k0 + j];
+        const float *zr = core + row * LC;         // this lane's new column k0 + j
+        floatx4 acc = zero4();
+#pragma unroll 2
+        for (int c0 = 0; c0 < R; c0 += 16) {       // B_h (f, c) x V'(c, k)
+          const int cb = c0 + 4 * g;
+          const float4 x = ld4(sB + (f0 + j) * LB + cb);
+          const float4 z = ld4(zr + cb);
+          acc = mfma4(x.x, z.x, acc);
+          acc = mfma4(x.y, z.y, acc);
+          acc = mfma4(x.z, z.z, acc);
+          acc = mfma4(x.w, z.w, acc);
         }
 #pragma unroll 2
-        for (int c0 = 0; c0 < R; c0 += 4) {
-          float xb[4][4], z[4][4];     // xb[f][c], z[k][c]
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 w = ld4(sB + (f0 + i) * LB + c0);
-            xb[i][0] = w.x; xb[i][1] = w.y; xb[i][2] = w.z; xb[i][3] = w.w;
-            const float4 y = ld4(zr[i] + c0);
-            z[i][0] = y.x; z[i][1] = y.y; z[i][2] = y.z; z[i][3] = y.w;
-          }
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xb[i][cc], z[j][cc], acc[i][j]);
+        for (int j0 = 0; j0 < TB; j0 += 16) {      // Q_h^T (f, j) x V'(R + j, k)
+          const int jb = j0 + 4 * g;
+          const float4 z = ld4(zr + R + jb);
+          acc = mfma4(sX[(jb + 0) * LA + f0 + j], z.x, acc);
+          acc = mfma4(sX[(jb + 1) * LA + f0 + j], z.y, acc);
+          acc = mfma4(sX[(jb + 2) * LA + f0 + j], z.z, acc);
+          acc = mfma4(sX[(jb + 3) * LA + f0 + j], z.w, acc);
         }
-#pragma unroll 2
-        for (int j0 = 0; j0 < TB; j0 += 4) {
-          float xq[4][4], z[4][4];     // xq[j][f] = Q[j0 + j][f0 + f], z[k][j]
+        const float zs = sig[row] > tol_null ? 1.f / sig[row] : 0.f;
+        float *dst = gbn + ((size_t)h * D + f0 + 4 * g) * R + k0 + j;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 w = ld4(sX + (j0 + i) * LA + f0);
-            xq[i][0] = w.x; xq[i][1] = w.y; xq[i][2] = w.z; xq[i][3] = w.w;
-            const float4 y = ld4(zr[i] + R + j0);
-            z[i][0] = y.x; z[i][1] = y.y; z[i][2] = y.z; z[i][3] = y.w;
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xq[jj][i], z[j][jj], acc[i][j]);
-        }
-        float *dst = gbn + ((size_t)h * D + f0) * R + k0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st4(dst + (size_t)i * R, make_float4(acc[i][0] * zs[0], acc[i][1] * zs[1], acc[i][2] * zs[2],
-                                               acc[i][3] * zs[3]));
+        for (int r = 0; r < 4; ++r) dst[(size_t)r * R] = acc[r] * zs;
       }
       __syncthreads();             // sB, sX are reloaded for the next head
     }
@@ -420,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
     for (int h = 0; h < H; ++h) {
       load_slice(gbn + (size_t)h * D * R, sX);
       __syncthreads();
-      gemm4<R, R, D, true, false>(sX, LB, sX, LB, [&](int a, int b, float v) { sGb[a * LB + b] += v; });
+      gemm_mfma<R, R, D, true, false>(sX, LB, sX, LB, [&](int a, int b, float v) { sGb[a * LB + b] += v; });
       __syncthreads();
     }
     chol_lds<R>(sGb, LB, 0.25f, invd);
@@ -450,8 +439,15 @@ __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel 
       load_slice(gbn + (size_t)h * D * R, sX);
       (void)load_A(h);
       __syncthreads();
-      gemm4<R, R, D, true, false>(sB, LB, sX, LB, [&](int c, int k, float v) { sM[c * LB + k] += v; });
-      gemm4<TB, R, D, false, false>(sA, LA, sX, LB, [&](int t, int k, float v) { sCb[t * LB + k] += v; });
+      // two independent products, one per half of the workgroup
+      constexpr int NW2 = kThreads / 128;
+      const int wave = tid >> 6;
+      if (wave < NW2)
+        gemm_mfma_part<R, R, D, true, false>(sB, LB, sX, LB, [&](int c, int k, float v) { sM[c * LB + k] += v; },
+                                             wave, NW2);
+      else
+        gemm_mfma_part<TB, R, D, false, false>(sA, LA, sX, LB, [&](int t, int k, float v) { sCb[t * LB + k] += v; },
+                                               wave - NW2, NW2);
       __syncthreads();
     }
     for (int i = tid; i < R * R; i += kThreads) msync[i] = sM[(i / R) * LB + i % R];
