@@ -100,20 +100,20 @@ __device__ __forceinline__ void fold_one(const Model &M, float *lds, const float
     }
   }
   const float normA2 = block_sum(asq, red);     // barriers inside
-  gemm4<TB, R, D, false, false>(sA, LA, Bsrc, ldB,
+  gemm_mfma<TB, R, D, false, false>(sA, LA, Bsrc, ldB,
                                 [&](int t, int c, float v) { sP[t * LB + c] = v; });
   __syncthreads();
   if constexpr (kRes) {
     // Res = A - P B^T
-    gemm4<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
+    gemm_mfma<TB, D, R, false, true>(sP, LB, sB, LB, [&](int t, int f, float v) {
       sQ[t * LA + f] = sA[t * LA + f] - v;
     });
     __syncthreads();
     // second projection: T = Res B (in the G region), Res -= T B^T, P += T
-    gemm4<TB, R, D, false, false>(sQ, LA, sB, LB,
+    gemm_mfma<TB, R, D, false, false>(sQ, LA, sB, LB,
                                   [&](int t, int c, float v) { sG[t * LB + c] = v; });
     __syncthreads();
-    gemm4<TB, D, R, false, true>(sG, LB, sB, LB,
+    gemm_mfma<TB, D, R, false, true>(sG, LB, sB, LB,
                                  [&](int t, int f, float v) { sQ[t * LA + f] -= v; });
     for (int i = tid; i < TB * R; i += kThreads) {
       const int t = i / R, c = i % R;
@@ -127,8 +127,8 @@ __device__ __forceinline__ void fold_one(const Model &M, float *lds, const float
     // drops those that lost their norm.
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
-      gemm4<TB, TB, D, false, true>(sQ, LA, sQ, LA,
-                                    [&](int a, int b, float v) { sG[a * LG + b] = v; });
+      gemm_mfma<TB, TB, D, false, true>(sQ, LA, sQ, LA,
+                                        [&](int a, int b, float v) { sG[a * LG + b] = v; });
       __syncthreads();
       float tau = 0.25f;
       if (pass == 0) {
@@ -149,14 +149,14 @@ __device__ __forceinline__ void fold_one(const Model &M, float *lds, const float
       __syncthreads();
     }
     // re-orthogonalize Q against B
-    gemm4<TB, R, D, false, false>(sQ, LA, sB, LB,
+    gemm_mfma<TB, R, D, false, false>(sQ, LA, sB, LB,
                                   [&](int t, int c, float v) { sG[t * LB + c] = v; });
     __syncthreads();
-    gemm4<TB, D, R, false, true>(sG, LB, sB, LB,
+    gemm_mfma<TB, D, R, false, true>(sG, LB, sB, LB,
                                  [&](int t, int f, float v) { sQ[t * LA + f] -= v; });
     __syncthreads();
     // A Q^T (64 x 64) into the G region
-    gemm4<TB, TB, D, false, true>(sA, LA, sQ, LA,
+    gemm_mfma<TB, TB, D, false, true>(sA, LA, sQ, LA,
                                   [&](int t, int j, float v) { sG[t * LG + j] = v; });
     __syncthreads();
   }
@@ -352,7 +352,7 @@ __device__ __forceinline__ void fold_one(const Model &M, float *lds, const float
   // would otherwise accumulate fold after fold.
   {
     float *sGb = lds + Ly::oA;     // R x LB, over the dead A / core region
-    gemm4<R, R, D, true, false>(sBn, LB, sBn, LB,
+    gemm_mfma<R, R, D, true, false>(sBn, LB, sBn, LB,
                                 [&](int a, int b, float v) { sGb[a * LB + b] = v; });
     __syncthreads();
     chol_lds<R>(sGb, LB, 0.25f, invd);
@@ -368,12 +368,12 @@ __device__ __forceinline__ void fold_one(const Model &M, float *lds, const float
   }
 
   // ---------------- phase 7: M, block coefficients, new basis --------------
-  gemm4<R, R, D, true, false>(Bsrc, ldB, sBn, LB,
+  gemm_mfma<R, R, D, true, false>(Bsrc, ldB, sBn, LB,
                               [&](int c, int k, float v) { msync[c * R + k] = v; });
   // the block again (the core region over A is free now)
   (void)load_A(sA);
   __syncthreads();
-  gemm4<TB, R, D, false, false>(sA, LA, sBn, LB, [&](int t, int k, float v) {
+  gemm_mfma<TB, R, D, false, false>(sA, LA, sBn, LB, [&](int t, int k, float v) {
     Store<T>::store(coef, (size_t)(n_c + t) * R + k, v);
   });
   __syncthreads();                 // M (which reads the old basis) is done

@@ -1,6 +1,6 @@
 // Shared device building blocks of the Brand fold kernels (fold.hip: one
 // workgroup per head, every operand in LDS; fold_joint.hip: one basis over
-// a layer's KV heads, streamed a head at a time): LDS GEMM tiles, blocked
+// a layer's KV heads, streamed a head at a time): LDS products on the matrix cores, blocked
 // Cholesky, triangular solves, Householder QR of the core and the one-sided
 // Jacobi SVD on its rows (internal linkage: each kernel file has its own copy).
 #pragma once
@@ -76,78 +76,19 @@ __device__ __forceinline__ int opaque_zero() {
 }
 
 // ---------------------------------------------------------------------------
-// C(m, n) = sum_k A(m, k) B(k, n) over 16-byte-aligned operands, 4 x 4
-// outputs per thread tile, handed to out(m, n, value).
+// C(m, n) = sum_k A(m, k) B(k, n) over 16-byte-aligned LDS operands on the
+// matrix cores (v_mfma_f32_16x16x4_f32: fp32 inputs, fp32 accumulation),
+// each output handed once to out(m, n, value):
 //   A(m, k) = A[m * lda + k] (AT = false)  or  A[k * lda + m] (AT = true)
 //   B(k, n) = B[k * ldb + n] (BT = false)  or  B[n * ldb + k] (BT = true)
-// With BT the tile's four n are strided by N/4, so the lanes of a wave read
-// rows that start in different banks.
-// ---------------------------------------------------------------------------
-// gemm4_part: the same over threads t0 .. t0 + nt - 1 only (thread tid), so
-// that two independent products can share the workgroup.
-template <int M, int N, int K, bool AT, bool BT, typename Out>
-__device__ __forceinline__ void gemm4_part(const float *A, int lda, const float *B, int ldb, Out out,
-                                           int tid, int nt) {
-  static_assert(M % 4 == 0 && N % 4 == 0 && K % 4 == 0, "tile multiples");
-  constexpr int TN = N / 4, TILES = (M / 4) * TN;
-  for (int tile = tid; tile < TILES; tile += nt) {
-    const int m0 = (tile / TN) * 4, tn = tile % TN;
-    int nn[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) nn[j] = BT ? tn + j * TN : tn * 4 + j;
-    float acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 2
-    for (int k0 = 0; k0 < K; k0 += 4) {
-      float a[4][4], b[4][4];     // a[m][k], b[k][n]
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (!AT) {
-          const float4 v = ld4(A + (m0 + i) * lda + k0);
-          a[i][0] = v.x; a[i][1] = v.y; a[i][2] = v.z; a[i][3] = v.w;
-        } else {
-          const float4 v = ld4(A + (k0 + i) * lda + m0);
-          a[0][i] = v.x; a[1][i] = v.y; a[2][i] = v.z; a[3][i] = v.w;
-        }
-        if constexpr (!BT) {
-          const float4 v = ld4(B + (k0 + i) * ldb + nn[0]);
-          b[i][0] = v.x; b[i][1] = v.y; b[i][2] = v.z; b[i][3] = v.w;
-        } else {
-          const float4 v = ld4(B + nn[i] * ldb + k0);
-          b[0][i] = v.x; b[1][i] = v.y; b[2][i] = v.z; b[3][i] = v.w;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i][kk], b[kk][j], acc[i][j]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out(m0 + i, nn[j], acc[i][j]);
-  }
-}
-
-template <int M, int N, int K, bool AT, bool BT, typename Out>
-__device__ __forceinline__ void gemm4(const float *A, int lda, const float *B, int ldb, Out out) {
-  gemm4_part<M, N, K, AT, BT>(A, lda, B, ldb, out, (int)threadIdx.x, kThreads);
-}
-
-// ---------------------------------------------------------------------------
-// The same product on the matrix cores (v_mfma_f32_16x16x4_f32: fp32 inputs,
-// fp32 accumulation), 16 x 16 output tiles dealt to waves w0, w0 + nw, ...
-// (this wave is `wave`).  In each group of four MFMAs covering k0 .. k0 + 15,
-// lane (j = lane % 16, g = lane / 16) supplies A(i0 + j, k) and B(k, n0 + j)
-// for k = k0 + 4 g + m in MFMA m: every k once (the sum is order-free), with
-// the lane's four A values contiguous when A is row-major and its four B
-// values contiguous when B is given transposed.  Output rows 4 g .. 4 g + 3,
-// column j of the tile are the lane's accumulator.
+// 16 x 16 output tiles are dealt to waves wave, wave + nw, ... .  In each
+// group of four MFMAs covering k0 .. k0 + 15, lane (j = lane % 16,
+// g = lane / 16) supplies A(i0 + j, k) and B(k, n0 + j) for k = k0 + 4 g + m
+// in MFMA m: every k once (the sum is order-free), with the lane's four A
+// values contiguous when A is row-major and its four B values contiguous when
+// B is given transposed.  Output rows 4 g .. 4 g + 3, column j of the tile are
+// the lane's accumulator.  gemm_mfma_part lets two independent products share
+// the workgroup's waves.
 // ---------------------------------------------------------------------------
 template <int M, int N, int K, bool AT, bool BT, typename Out>
 __device__ __forceinline__ void gemm_mfma_part(const float *A, int lda, const float *B, int ldb, Out out,
@@ -366,6 +307,24 @@ __device__ __forceinline__ void fwd_solve(float (&x)[n], const float *L0, int ld
 #pragma unroll
     for (int k = i & ~3; k < i; ++k) s[k & 3] = fmaf(L[i * ldl + k], x[k], s[k & 3]);
     x[i] = (x[i] - ((s[0] + s[1]) + (s[2] + s[3]))) * invd[i];
+  }
+}
+
+// Linv <- L^{-1} (n x n, row strides ldl / ldi) from the factor L and invd
+// that chol_lds left: column j is the forward solve of e_j, so Linv X equals
+// the column-by-column forward solve of X, dropped pivots included (their rows
+// of Linv are 0).  Applied to a head's tile as one product over the whole
+// workgroup instead of one sequential solve per column per thread.
+template <int n>
+__device__ __forceinline__ void tri_inverse(const float *L, int ldl, const float *invd, float *Linv, int ldi) {
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    float x[n];
+#pragma unroll
+    for (int t = 0; t < n; ++t) x[t] = t == tid ? 1.f : 0.f;
+    fwd_solve<n>(x, L, ldl, invd);
+#pragma unroll
+    for (int t = 0; t < n; ++t) Linv[t * ldi + tid] = x[t];
   }
 }
 

@@ -71,24 +71,6 @@ struct JointLayout {
                 "16-byte aligned regions");
 };
 
-// Linv <- L^{-1} (n x n, row strides ldl / ldi) from the factor L and invd
-// that chol_lds left: column j is the forward solve of e_j, so Linv X equals
-// the column-by-column forward solve of X, dropped pivots included (their rows
-// of Linv are 0).  Applied to a head's tile as one product over the whole
-// workgroup instead of one sequential solve per column (or row) per thread.
-template <int n>
-__device__ __forceinline__ void tri_inverse(const float *L, int ldl, const float *invd, float *Linv, int ldi) {
-  const int tid = threadIdx.x;
-  if (tid < n) {
-    float x[n];
-#pragma unroll
-    for (int t = 0; t < n; ++t) x[t] = t == tid ? 1.f : 0.f;
-    fwd_solve<n>(x, L, ldl, invd);
-#pragma unroll
-    for (int t = 0; t < n; ++t) Linv[t * ldi + tid] = x[t];
-  }
-}
-
 template <int R, typename T>
 __global__ __launch_bounds__(kThreads) void joint_fold_kernel(Model M, LayerSel sel, int64_t n_c, int xsel,
                                                               SeqTab tab) {
