@@ -24,10 +24,13 @@
 //           (fp32 storage: fp32 MFMA).  Lane l holds features 16*mb + 4*(l/16)
 //           + i, mb = 0..7, of token l%16: 16 RoPE pairs (f, f + 64), rotated
 //           in registers at the token's position;
-//   scores  S (16 tokens x 16 heads) = K~ Q~^T with both sides split bf16
-//           hi/lo (hi*hi + hi*lo + lo*hi, relative error ~1e-5); lane l gets
-//           head l%16 and tokens 4*(l/16)..+3, the A-operand layout of the
-//           value product; query heads beyond the group are zero;
+//   scores  S (16 tokens x 16 heads) = K~ Q~^T.  bf16 storage: the rotated
+//           key rounded once to fp16 (2^-12 relative, below the bf16 rounding
+//           of the stored coefficients), the query as fp16 hi + lo (two
+//           products); fp32 storage: both sides split bf16 hi/lo (hi*hi +
+//           hi*lo + lo*hi, ~2^-16).  Lane l gets head l%16 and tokens
+//           4*(l/16)..+3, the A-operand layout of the value product; query
+//           heads beyond the group are zero;
 //   softmax running max per head in log2 units, rescaled lazily (only when
 //           the max grows by more than 8, so p <= 2^8);
 //   values  acc (16 heads x r) += P (16 x 16 tokens) C_V (16 tokens x r) with P
@@ -538,8 +541,9 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 
   // ---- query rows rotated at q_pos and scaled by scale*log2(e), via LDS:
   // thread (frequency qi, heads qh0 + NW k) loads (query_issue), then rotates
-  // and stores them, after which the rows are split bf16 hi/lo into the
-  // B-operand layout of the score product (query_finish, one barrier)
+  // and stores them, after which the rows are split hi/lo (fp16 with bf16
+  // storage, bf16 with fp32 storage) into the B-operand layout of the score
+  // product (query_finish, one barrier)
   const int qi = threadIdx.x & 63, qh0 = threadIdx.x >> 6;
   float qx0[QK], qx1[QK];
   float2 qA, qB, qstep;
@@ -574,9 +578,12 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     for (int kb = 0; kb < 4; ++kb) {
       unsigned h[4], lo[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        split2(s_q[n16][score_feature(kb, 2 * j, rho)], s_q[n16][score_feature(kb, 2 * j + 1, rho)],
-               h[j], lo[j]);
+      for (int j = 0; j < 4; ++j) {
+        const float a = s_q[n16][score_feature(kb, 2 * j, rho)];
+        const float bq = s_q[n16][score_feature(kb, 2 * j + 1, rho)];
+        if constexpr (BF) split2_f16(a, bq, h[j], lo[j]);
+        else split2(a, bq, h[j], lo[j]);
+      }
       qhi[kb] = uint4_{h[0], h[1], h[2], h[3]};
       qlo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
     }
@@ -621,6 +628,20 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
         cs_s[mb * 4 + i] = fmaf(s, st.x, c * st.y);
       }
     floatx4 sc[2] = {zero4(), zero4()};          // two chains of dependent MFMAs
+    if constexpr (BF) {
+      // bf16 storage: the rotated key enters once, rounded to fp16 (2^-12
+      // relative; the query as fp16 hi + lo), two products per K-block
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4_ kh = {pack_f16(ka[2 * kb][0], ka[2 * kb][1]), pack_f16(ka[2 * kb][2], ka[2 * kb][3]),
+                           pack_f16(ka[2 * kb + 1][0], ka[2 * kb + 1][1]),
+                           pack_f16(ka[2 * kb + 1][2], ka[2 * kb + 1][3])};
+        floatx4 &a = sc[kb & 1];
+        a = mfma32h(kh, qlo[kb], a);
+        a = mfma32h(kh, qhi[kb], a);
+      }
+      return sc[0] + sc[1];
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       unsigned h[4], lo[4];

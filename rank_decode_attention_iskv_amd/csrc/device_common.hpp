@@ -123,6 +123,22 @@ __device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned 
   lo = __builtin_bit_cast(unsigned, l);
 }
 
+// (a, b) -> packed fp16 (round to nearest even), and the fp16 remainder of
+// each: hi + lo holds a float to ~2^-22 relative.
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((floatx2){a, b}, halfx2));
+}
+__device__ __forceinline__ void split2_f16(float a, float b, unsigned &hi, unsigned &lo) {
+  const halfx2 h = __builtin_convertvector((floatx2){a, b}, halfx2);
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = pack_f16(a - (float)h.x, b - (float)h.y);
+}
+__device__ __forceinline__ floatx4 mfma32h(uint4_ a, uint4_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ floatx4 mfma32(uint4_ a, uint4_ b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
