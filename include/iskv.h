@@ -118,8 +118,8 @@ typedef struct {
                              128-dim heads compress 4-7x [iS-KV explainer,
                              the worked example and Table 1], which needs a
                              basis over several heads.  Requires rank and
-                             rank_v <= 64, num_kv_heads <= 32 and
-                             async_maintenance = 0; iskv_prefill is ESTATE. */
+                             rank_v <= 64 and num_kv_heads <= 32;
+                             iskv_prefill is ESTATE. */
 } iskv_config;
 
 typedef struct {

@@ -72,7 +72,6 @@ bool valid_config(const iskv_config *c) {
     // LDS: r <= 64, and at most 32 heads for its null-completion vectors
     const int rv = c->rank_v ? c->rank_v : c->rank;
     if (c->rank > 64 || rv > 64 || c->num_kv_heads > 32) return false;
-    if (c->async_maintenance) return false;
   }
   return true;
 }

@@ -50,7 +50,7 @@ def test_workspace_bytes_valid_and_monotone():
     dict(protected_prefix=100), dict(protected_prefix=-64), dict(protected_prefix=4160),
     dict(rank_v=48), dict(rank_v=16), dict(rank_v=-32), dict(rank=128, rank_v=256),
     dict(joint_heads=2), dict(joint_heads=1, rank=128), dict(joint_heads=1, rank=64, rank_v=128),
-    dict(joint_heads=1, num_kv_heads=64, num_q_heads=64), dict(joint_heads=1, async_maintenance=1),
+    dict(joint_heads=1, num_kv_heads=64, num_q_heads=64),
 ])
 def test_invalid_configs_rejected(kw):
     assert binding.workspace_bytes(base_cfg(**kw)) == 0

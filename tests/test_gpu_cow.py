@@ -21,12 +21,12 @@ from tests.gpu_util import q32, rel_err_per_head, small
 pytestmark = pytest.mark.gpu
 
 
-def _cache(w, layers, max_tokens, cow, rank_v=0):
+def _cache(w, layers, max_tokens, cow, rank_v=0, joint=False):
     from rank_decode_attention_iskv_amd import binding
     storage = binding.BF16 if w.storage == "bf16" else binding.F32
     cfg = binding.make_config(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim, w.rank,
                               w.window, max_tokens, storage, rank_v=rank_v,
-                              async_maintenance=1 if cow else 0)
+                              async_maintenance=1 if cow else 0, joint_heads=int(joint))
     return cfg, binding.IskvCache(cfg)
 
 
@@ -40,18 +40,20 @@ def _step_tensors(w, layer, pos, step):
             torch.from_numpy(q.astype(np.float32)).cuda())
 
 
-@pytest.mark.parametrize("rank,rank_v", [(32, 0), (16, 32)])
-def test_cow_decode_matches_deferred_oracle(rank, rank_v):
+@pytest.mark.parametrize("rank,rank_v,joint", [(32, 0, False), (16, 32, False), (32, 64, True)])
+def test_cow_decode_matches_deferred_oracle(rank, rank_v, joint):
     """fp32 storage, 2 sequences x 2 KV heads, 2 layers: every decode (fused
-    append + attend) against the oracle folded exactly when the GPU switched."""
+    append + attend) against the oracle folded exactly when the GPU switched
+    (also with one basis per sequence over both heads)."""
     import torch
-    w = small(1, batch=2, kv_heads=2, q_heads=8, window=128, rank=rank)
+    w = small(1, batch=2, kv_heads=2, q_heads=8, window=128, rank=rank, shared_latent=joint)
     layers, tokens = 2, 128 + 64 * 7
-    cfg, gpu = _cache(w, layers, tokens + 64, cow=True, rank_v=rank_v)
+    cfg, gpu = _cache(w, layers, tokens + 64, cow=True, rank_v=rank_v, joint=joint)
     ms = torch.cuda.Stream()
     gpu.set_maintenance_stream(ms)
     ora = Oracle(w.batch, layers, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
-                 tokens + 64, storage=w.storage, rank_v=rank_v or None, slack=64)
+                 tokens + 64, storage=w.storage, rank_v=rank_v or None, slack=64,
+                 joint_heads=joint)
     length = [0] * layers
     worst, in_flight_decodes, switches, held = 0.0, 0, 0, 0
     out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
