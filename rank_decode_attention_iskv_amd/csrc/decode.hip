@@ -19,9 +19,10 @@
 //   stream  the coefficient tiles of K and V are copied HBM -> LDS by direct
 //           DMA loads (no registers), kept several tiles ahead in a per-wave
 //           LDS ring;
-//   keys    K^T (128 x 16) = B_K (128 x r) C_K^T (r x 16): the fp32 basis
-//           enters as bf16 hi + lo (two products), bf16 coefficients exactly
-//           (fp32 storage: fp32 MFMA).  Lane l holds features 16*mb + 4*(l/16)
+//   keys    K^T (128 x 16) = B_K (128 x r) C_K^T (r x 16): bf16 storage, one
+//           fp16 product per 32 coefficients, the basis rounded to fp16
+//           (2^-11 relative) and the stored bf16 coefficients converted to
+//           fp16 exactly; fp32 storage, fp32 MFMA.  Lane l holds features 16*mb + 4*(l/16)
 //           + i, mb = 0..7, of token l%16: 16 RoPE pairs (f, f + 64), rotated
 //           in registers at the token's position;
 //   scores  S (16 tokens x 16 heads) = K~ Q~^T.  bf16 storage: the rotated
@@ -129,6 +130,14 @@ __device__ __forceinline__ int score_feature(int kb, int j, int rho) {
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+#endif
+}
+
+// 16-byte direct load buffer -> LDS: byte offset voff (per lane) + soff
+// (wave-uniform) from the descriptor's base
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, void *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voff, soff, 0, 0);
 #endif
 }
 
@@ -451,20 +460,21 @@ template <int RK, int RV, typename T, int NW> struct Cfg {
   // workgroups load both per wave.
   static_assert(NW == 4 || (NW == 8 && BF && RK <= 64 && RV <= 64), "wave count");
   static constexpr bool kShared = NW == 8;
-  // bf16 r = 64: the low bf16 parts of the key-basis fragments are read from
-  // LDS in the loop instead of registers (which two waves per SIMD lack)
-  static constexpr bool kLoLds = BF && R == 64;
+  // key-basis fragment chunks (16 bytes a lane) per M-block held in
+  // registers: bf16 storage, one fp16 operand per 32 coefficients (16 at
+  // r = 16); fp32 storage, four fp32 values per chunk
+  static constexpr int kFch = BF ? (R >= 32 ? R / 32 : 1) : R / 16;
   // shared prologue data sits in static LDS arrays (fragments, step rows,
   // per-wave base angles): reads of them are then known not to alias the
   // ring DMAs in flight, so the compiler adds no wait for those.  Dynamic
-  // LDS: [low-part fragments (four waves, r = 64) | per-wave rings]
-  static constexpr int kFragBytes = kShared ? 8 * (R / 16) * 1024 : 16;
-  static constexpr int kRingOff = (!kShared && kLoLds) ? 8 * (R / 32) * 1024 : 0;
+  // LDS: the per-wave rings
+  static constexpr int kFragBytes = kShared ? 8 * kFch * 1024 : 16;
+  static constexpr int kRingOff = 0;
   // per wave; wide tiles (r = 128, or r = 64 in float) get a deeper ring.
   // Eight-wave workgroups keep four r <= 32 tiles per wave (eight waves per
   // CU hold enough bytes in flight, and a shorter ring is issued sooner)
   static constexpr int kRingBytes = kShared ? (RK == 64 || RV == 64 ? 12288 : 8192)
-                                    : kLoLds ? 12288 : (kSlot >= 8192 ? 32768 : 16384);
+                                    : (BF && R == 64) ? 12288 : (kSlot >= 8192 ? 32768 : 16384);
   static constexpr int kDepth = kRingBytes / kSlot > 16 ? 16 : kRingBytes / kSlot;
   static_assert(kDepth >= 2, "ring depth");
   static constexpr int kWaves = NW;
@@ -508,7 +518,11 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 
   const Dims &D = M.D;
   const int G = D.group;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // bf16: the wave index in a scalar register (ring and slot addresses, the
+  // LDS-DMA base, become scalar arithmetic); the fp32 kernels keep the plain
+  // form (see the note at the fp32 rotation below)
+  const int wave = BF ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int n16 = lane & 15, rho = lane >> 4;
   // ragged: blockIdx.x = (sequence, split) flattened, blockIdx.y = KV head
   int split_i = blockIdx.x, b_i = (int)blockIdx.y / D.kv_heads;
@@ -623,10 +637,53 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
         const float x0 = ka[mb][i], x1 = ka[mb + 4][i];
         ka[mb][i] = fmaf(x0, c, -x1 * s);
         ka[mb + 4][i] = fmaf(x1, c, x0 * s);
-        const float2 st = s_step[16 * mb + 4 * rho + i];
-        cs_c[mb * 4 + i] = fmaf(c, st.x, -s * st.y);
-        cs_s[mb * 4 + i] = fmaf(s, st.x, c * st.y);
+        if constexpr (!BF) {
+          // fp32 storage keeps the advance inline: with the bf16 forms below
+          // (scalar wave index, buffer-descriptor DMA, batched step reads) the
+          // fp32 r = 64 kernel gave wrong results for the last query head of
+          // each group on joint-basis data, with no cause found in the source
+          const float2 st = s_step[16 * mb + 4 * rho + i];
+          cs_c[mb * 4 + i] = fmaf(c, st.x, -s * st.y);
+          cs_s[mb * 4 + i] = fmaf(s, st.x, c * st.y);
+        }
       }
+    // advance the angle state by 16 positions, after the score products are
+    // issued (they run while the step rotations arrive from LDS)
+    auto advance = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      // the lane's 16 step rotations in one batch of LDS reads (one wait)
+      floatx4 w[8];
+      {
+        const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void *)(
+            reinterpret_cast<const void *>(s_step + 4 * rho));
+        asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
+                     "ds_read_b128 %2, %8 offset:128\n\tds_read_b128 %3, %8 offset:144\n\t"
+                     "ds_read_b128 %4, %8 offset:256\n\tds_read_b128 %5, %8 offset:272\n\t"
+                     "ds_read_b128 %6, %8 offset:384\n\tds_read_b128 %7, %8 offset:400\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
+                       "=&v"(w[6]), "=&v"(w[7])
+                     : "v"(a));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float c = cs_c[mb * 4 + i], s = cs_s[mb * 4 + i];
+          const floatx4 &wv = w[2 * mb + (i >> 1)];
+          const float2 st = (i & 1) ? float2{wv[2], wv[3]} : float2{wv[0], wv[1]};
+          float cc = c, ss = s, t0, t1;
+          // written in place, so the loop-carried state keeps its registers
+          // (the compiler's own form copied all 32 of them every tile)
+          asm("v_mul_f32 %2, %1, %5\n\t"
+              "v_mul_f32 %3, %0, %5\n\t"
+              "v_fma_f32 %0, %0, %4, -%2\n\t"
+              "v_fma_f32 %1, %1, %4, %3"
+              : "+v"(cc), "+v"(ss), "=&v"(t0), "=&v"(t1) : "v"(st.x), "v"(st.y));
+          cs_c[mb * 4 + i] = cc;
+          cs_s[mb * 4 + i] = ss;
+        }
+    };
     floatx4 sc[2] = {zero4(), zero4()};          // two chains of dependent MFMAs
     if constexpr (BF) {
       // bf16 storage: the rotated key enters once, rounded to fp16 (2^-12
@@ -640,6 +697,7 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
         a = mfma32h(kh, qlo[kb], a);
         a = mfma32h(kh, qhi[kb], a);
       }
+      advance();
       return sc[0] + sc[1];
     }
 #pragma unroll
@@ -701,17 +759,25 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     // one tile: kDmaK / kDmaV dwordx4 DMAs per matrix; lane l moves 16 bytes
     // of chunk d*64 + l of the tile (lanes past the tile size idle)
     // tile `src` into ring slot `it` % DEPTH
+    // descriptors over the wave's range: per-lane offsets are constants, the
+    // tile offset is a scalar
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(gk), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(gv), 0, 0x7fffffff, 0x00020000);
     auto issue_from = [&](int it, int src) {
       uint8_t *slot = ring + (it % DEPTH) * C::kSlot;
 #pragma unroll
       for (int d = 0; d < C::kDmaK; ++d) {
         const int off = (d * 64 + lane) * 16;
-        if (off < C::kMatK) dma16(gk + (size_t)src * C::kMatK + off, slot + d * 1024);
+        if (off >= C::kMatK) continue;
+        if constexpr (BF) dma16_buf(rk, off, src * C::kMatK, slot + d * 1024);
+        else dma16(gk + (size_t)src * C::kMatK + off, slot + d * 1024);
       }
 #pragma unroll
       for (int d = 0; d < C::kDmaV; ++d) {
         const int off = (d * 64 + lane) * 16;
-        if (off < C::kMatV) dma16(gv + (size_t)src * C::kMatV + off, slot + C::kMatK + d * 1024);
+        if (off >= C::kMatV) continue;
+        if constexpr (BF) dma16_buf(rv, off, src * C::kMatV, slot + C::kMatK + d * 1024);
+        else dma16(gv + (size_t)src * C::kMatV + off, slot + C::kMatK + d * 1024);
       }
     };
     auto issue = [&](int it) { issue_from(it, it); };
@@ -724,27 +790,18 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     // are older than its query loads, so they have completed before the
     // barrier in query_finish, after which all waves read them.
     const uint8_t *FB = P.frag + (size_t)u * 4 * kHeadDim * R;
-    constexpr int FCH = C::kLoLds ? R / 32 : R / 16;     // register-resident chunks per M-block
-    // LDS address of the low-part chunk (mb, kb) of the key-basis fragments
-    auto lo_chunk = [&](int mb, int kb) -> const uint8_t * {
-      if constexpr (C::kShared) return s_frag + ((mb * (R / 16) + 2 * kb + 1) * 64 + lane) * 16;
-      return s_dyn + ((mb * (R / 32) + kb) * 64 + lane) * 16;
-    };
+    constexpr int FCH = C::kFch;                         // register-resident chunks per M-block
+    // HBM chunk of register chunk ch of M-block mb (bf16 storage: the fp16
+    // operands sit in the even chunks)
+    auto gchunk = [&](int mb, int ch) { return mb * (R / 16) + (BF ? (R >= 32 ? 2 * ch : 0) : ch); };
     if constexpr (C::kShared) {
-      // every fragment chunk (same layout as in HBM) and step rows 0..15
-      constexpr int NCH = 8 * (R / 16);
+      // every used fragment chunk and step rows 0..15
+      constexpr int NCH = 8 * FCH;
       static_assert(NCH % NW == 0, "fragment chunks per wave");
 #pragma unroll
       for (int j = 0; j < NCH / NW; ++j) {
         const int c = wave + NW * j;
-        dma16(FB + ((size_t)c * 64 + lane) * 16, s_frag + c * 1024);
-      }
-    } else if constexpr (C::kLoLds) {
-      // low-part chunks (mb, 2 kb + 1) -> LDS [mb][kb][64 lanes][16 B]; a quarter per wave
-#pragma unroll
-      for (int j = 0; j < 8 * (R / 32) / 4; ++j) {
-        const int c = wave * (8 * (R / 32) / 4) + j, mb = c / (R / 32), kb = c % (R / 32);
-        dma16(FB + ((size_t)(mb * (R / 16) + 2 * kb + 1) * 64 + lane) * 16, s_dyn + c * 1024);
+        dma16(FB + ((size_t)gchunk(c / FCH, c % FCH) * 64 + lane) * 16, s_frag + c * 1024);
       }
     }
     query_issue();
@@ -759,10 +816,8 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int ch = 0; ch < FCH; ++ch) {
-          const int gch = C::kLoLds ? 2 * ch : ch;          // high parts only when the lows are in LDS
-          F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)(mb * (R / 16) + gch) * 64 + lane) * 16);
-        }
+        for (int ch = 0; ch < FCH; ++ch)
+          F[mb][ch] = *reinterpret_cast<const uint4_ *>(FB + ((size_t)gchunk(mb, ch) * 64 + lane) * 16);
       anchor_issue(w_begin + n16);
     }
     wait_vmcnt<0>();
@@ -799,10 +854,8 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-          for (int ch = 0; ch < FCH; ++ch) {
-            const int gch = C::kLoLds ? 2 * ch : ch;
-            F[mb][ch] = *reinterpret_cast<const uint4_ *>(s_frag + ((mb * (R / 16) + gch) * 64 + lane) * 16);
-          }
+          for (int ch = 0; ch < FCH; ++ch)
+            F[mb][ch] = *reinterpret_cast<const uint4_ *>(s_frag + ((mb * FCH + ch) * 64 + lane) * 16);
         const float2 *base = s_base + wave * 64;
         const float2 *st16 = s_st16 + n16;
 #pragma unroll
@@ -841,32 +894,27 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
       // keys: rebuild from the basis fragments and this lane's coefficients
       floatx4 ka[8];
       if constexpr (BF) {
+        // one fp16 product per 32 coefficients: the stored bf16 coefficients
+        // convert exactly, the basis enters rounded to fp16
         const T *row = tk + n16 * R + rho * (R / 4);
         if constexpr (R == 16) {
           const uint2_ bop = *reinterpret_cast<const uint2_ *>(row);
+          const uint2_ bh = {bf16x2_to_f16x2(bop.x), bf16x2_to_f16x2(bop.y)};
 #pragma unroll
-          for (int mb = 0; mb < 8; ++mb) {
-            floatx4 a = mfma16(uint2_{F[mb][0].x, F[mb][0].y}, bop, zero4());
-            ka[mb] = mfma16(uint2_{F[mb][0].z, F[mb][0].w}, bop, a);
-          }
+          for (int mb = 0; mb < 8; ++mb) ka[mb] = mfma16h(uint2_{F[mb][0].x, F[mb][0].y}, bh, zero4());
         } else {
           uint4_ bop[R / 32];
 #pragma unroll
-          for (int kb = 0; kb < R / 32; ++kb) bop[kb] = reinterpret_cast<const uint4_ *>(row)[kb];
+          for (int kb = 0; kb < R / 32; ++kb) {
+            const uint4_ x = reinterpret_cast<const uint4_ *>(row)[kb];
+            bop[kb] = uint4_{bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
+                             bf16x2_to_f16x2(x.w)};
+          }
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb) {
             floatx4 a = zero4();
 #pragma unroll
-            for (int kb = 0; kb < R / 32; ++kb) {
-              if constexpr (C::kLoLds) {
-                const uint4_ lo = *reinterpret_cast<const uint4_ *>(lo_chunk(mb, kb));
-                a = mfma32(F[mb][kb], bop[kb], a);
-                a = mfma32(lo, bop[kb], a);
-              } else {
-                a = mfma32(F[mb][2 * kb], bop[kb], a);
-                a = mfma32(F[mb][2 * kb + 1], bop[kb], a);
-              }
-            }
+            for (int kb = 0; kb < R / 32; ++kb) a = mfma32h(F[mb][kb], bop[kb], a);
             ka[mb] = a;
           }
         }

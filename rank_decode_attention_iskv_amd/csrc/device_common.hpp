@@ -139,6 +139,18 @@ __device__ __forceinline__ floatx4 mfma32h(uint4_ a, uint4_ b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
                                                 __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx4 mfma16h(uint2_ a, uint2_ b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(halfx4, a), __builtin_bit_cast(halfx4, b), c,
+                                               0, 0, 0);
+}
+// two bf16 (low half first) -> two fp16: exact for |x| <= 65504 down to the
+// fp16 normal range (bf16 carries 8 significant bits, fp16 11); larger
+// magnitudes saturate at 65504 (round toward zero)
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned x) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x << 16),
+                                                                 __uint_as_float(x & 0xffff0000u)));
+}
 __device__ __forceinline__ floatx4 mfma32(uint4_ a, uint4_ b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -101,14 +101,14 @@ __global__ void prep_frag_kernel(Model M, LayerSel sel) {
     uint8_t *dst = F + ((size_t)(mb * chunks + ch) * 64 + lane) * 16;
     const float *src = B + (size_t)row * r + rho * per;
     if (D.storage == 1) {
+      // fp16 (round to nearest) operand of the f16 key product: chunk 2 kb
+      // holds coefficients rho * r/4 + 8 kb .. + 7 (r >= 32; r = 16: chunk 0,
+      // coefficients 4 rho .. + 3 in slots 0..3); the other slots are zero
       uint16_t *o = reinterpret_cast<uint16_t *>(dst);
       for (int j = 0; j < 8; ++j) {
-        // coefficient index and part of slot j of this chunk
-        const int c = (r >= 32) ? (ch >> 1) * 8 + j : (j & 3);
-        const int hl = (r >= 32) ? (ch & 1) : (j >> 2);
-        const float x = src[c];
-        const uint16_t hi = f32_to_bf16(x);
-        o[j] = hl == 0 ? hi : f32_to_bf16(x - bf16_to_f32(hi));
+        const bool used = (r >= 32) ? (ch & 1) == 0 : j < 4;
+        const int c = (r >= 32) ? (ch >> 1) * 8 + j : j;
+        o[j] = used ? __builtin_bit_cast(uint16_t, (_Float16)src[c]) : 0;
       }
     } else {
       float *o = reinterpret_cast<float *>(dst);

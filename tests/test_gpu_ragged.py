@@ -185,7 +185,11 @@ def test_ragged_bf16_matches_single_sequence_caches():
                 singles[b].decode_attn(0, qt, q_pos[b], out)
                 torch.cuda.synchronize()
                 ref = out.cpu().numpy().astype(np.float64)
-                assert rel_err_per_head(got[b:b + 1], ref) < 1e-5, (step, b)
+                # different split boundaries give each side its own
+                # reference max, so p = 2^(s - m) is rounded differently
+                # where it is split into bf16 hi + lo for the value product
+                # (~2^-17 relative per weight): agreement to a few 1e-5
+                assert rel_err_per_head(got[b:b + 1], ref) < 5e-5, (step, b)
             checks += 1
     assert checks >= 5 and len(set(r.folds)) > 1 and max(r.folds) >= 4
 
