@@ -493,7 +493,11 @@ template <int RK, int RV, typename T, int NW> struct Cfg {
 // ---------------------------------------------------------------------------
 // The MFMA decode kernel.  grid (splits, units), 64 * kWaves threads.
 // ---------------------------------------------------------------------------
-template <int RK, int RV, typename T, int NW>
+// PK (bf16 storage, 4 query heads per KV head): the score product's B
+// operand carries the fp16 high parts of the 4 query heads in columns 0..3
+// and their low parts in columns 4..7, one product per K-block instead of
+// two; lanes 0..3 of each row then add lanes 4..7
+template <int RK, int RV, typename T, int NW, bool PK>
 __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kOcc)) void decode_mfma_kernel(
     Model M, int layer, const float *__restrict__ q, int64_t q_pos_arg, float *out, int64_t length_arg,
     int64_t n_c_arg, SplitPlan plan_arg, int fused, FusedAppend app, SeqTab tab, SeqPlans sp) {
@@ -588,15 +592,19 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     if (threadIdx.x < 64) s_step[threadIdx.x] = qstep;
     if (lds_only) lds_barrier();
     else __syncthreads();
+    // packed (PK): lanes of columns 4..7 take the low parts of heads 0..3;
+    // columns 8..15 read rows past the group, which are zero
+    const int qrow = PK ? (n16 < 4 ? n16 : n16 - 4) : n16;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       unsigned h[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = s_q[n16][score_feature(kb, 2 * j, rho)];
-        const float bq = s_q[n16][score_feature(kb, 2 * j + 1, rho)];
+        const float a = s_q[qrow][score_feature(kb, 2 * j, rho)];
+        const float bq = s_q[qrow][score_feature(kb, 2 * j + 1, rho)];
         if constexpr (BF) split2_f16(a, bq, h[j], lo[j]);
         else split2(a, bq, h[j], lo[j]);
+        if constexpr (PK) h[j] = n16 < 4 ? h[j] : lo[j];
       }
       qhi[kb] = uint4_{h[0], h[1], h[2], h[3]};
       qlo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
@@ -694,11 +702,18 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
                            pack_f16(ka[2 * kb + 1][0], ka[2 * kb + 1][1]),
                            pack_f16(ka[2 * kb + 1][2], ka[2 * kb + 1][3])};
         floatx4 &a = sc[kb & 1];
-        a = mfma32h(kh, qlo[kb], a);
+        if constexpr (!PK) a = mfma32h(kh, qlo[kb], a);
         a = mfma32h(kh, qhi[kb], a);
       }
       advance();
-      return sc[0] + sc[1];
+      floatx4 st = sc[0] + sc[1];
+      if constexpr (PK) {
+        // head h (lanes h of each row) adds its low-part column h + 4
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st[e] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(st[e]), 0x104, 0xF, 0xF, false));
+      }
+      return st;
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -1273,18 +1288,20 @@ hipError_t launch_mfma(const Model &M, int layer, const float *q, int64_t q_pos,
   const dim3 grid = sp.n ? dim3(sp.off[sp.n], M.D.kv_heads)
                          : dim3(plan_workgroups(plan), M.D.units);
   constexpr int dyn = C::kDynBytes;
-  static bool dattr = false;
+  // the packed score product: bf16 storage with 4 query heads per KV head
+  const bool pk = C::BF && M.D.group == 4;
+  auto kern = pk ? &decode_mfma_kernel<RK, RV, T, NW, C::BF> : &decode_mfma_kernel<RK, RV, T, NW, false>;
+  static bool dattr[2] = {false, false};
   hipError_t e;
-  if (!dattr) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_mfma_kernel<RK, RV, T, NW>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+  if (!dattr[pk]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
     if (e != hipSuccess) return e;
-    dattr = true;
+    dattr[pk] = true;
   }
   // fuse the merge when every workgroup is resident at once
   const int64_t slots = (int64_t)M.D.cus * C::kOcc;
   const int fused = (int64_t)grid.x * grid.y <= slots ? 1 : 0;
-  hipLaunchKernelGGL((decode_mfma_kernel<RK, RV, T, NW>), grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
+  hipLaunchKernelGGL(kern, grid, dim3(C::kThr), dyn, s, M, layer, q, q_pos,
                      out, length, n_c, plan, fused, app, tab, sp);
   e = hipGetLastError();
   if (e != hipSuccess || fused) return e;

@@ -66,6 +66,7 @@ def test_decode_full_size_gqa_layer_32k():
     w = workloads.WORKLOADS[2]
     n_c = 32512
     errs = _decode_vs_oracle(w, n_c, n_c + w.window + 21, [n_c + w.window + 20, n_c + 400])
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
 
 
@@ -75,6 +76,7 @@ def test_decode_full_size_batch16_16k_rank64():
     w = workloads.WORKLOADS[3]
     n_c = 15872
     errs = _decode_vs_oracle(w, n_c, n_c + w.window + 45, [n_c + w.window + 44])
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
 
 
@@ -86,6 +88,7 @@ def test_decode_window_bounds_and_ranks(rank, n_extra):
     n_c = 4096
     length = n_c + w.window + n_extra
     errs = _decode_vs_oracle(w, n_c, length, [length - 1, length + 150])
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
 
 
@@ -99,6 +102,7 @@ def test_decode_many_splits_odd_group(kv_heads, q_heads, batch):
     n_c = 16384
     length = n_c + w.window + 7
     errs = _decode_vs_oracle(w, n_c, length, [length + 3])
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
 
 
@@ -108,6 +112,7 @@ def test_decode_full_size_gqa_layer_32k_value_rank_64():
     w = workloads.WORKLOADS[2]
     n_c = 32512
     errs = _decode_vs_oracle(w, n_c, n_c + w.window + 40, [n_c + w.window + 39, 77], rank_v=64)
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
 
 
@@ -117,4 +122,5 @@ def test_decode_full_size_batch16_16k_rank32_value64():
     w = workloads.with_(workloads.WORKLOADS[3], rank=32)
     n_c = 15872
     errs = _decode_vs_oracle(w, n_c, n_c + w.window + 3, [n_c + w.window + 2], rank_v=64)
+    print(f"decode error on the same state: {max(errs):.2e}")
     assert max(errs) < ATOL_OUT, errs
