@@ -517,6 +517,7 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
   // (the lanes of one read take 16 offsets and 4 frequencies: no bank conflict)
   __shared__ float2 s_st16[C::kShared ? 64 * 17 : 1];
   __shared__ float2 s_base[C::kShared ? NW * 64 : 1];              // per wave: cos, sin of w_begin * theta_f
+  __shared__ float2 s_wbase[C::kShared ? NW * 64 : 1];             // ... of the riding window part's range
   __shared__ int s_prog[NW];                                       // per wave: tile index in the loop
   float (*s_acc)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(s_dyn);
 
@@ -613,6 +614,21 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
 
 
   bool q_ready = false;                                 // query operands built (first part)
+  // this wave's tile range within [r_begin, r_end): an even split, the first
+  // ntiles % NW waves take one tile more (waves w and w + NW/2 share a SIMD,
+  // so every SIMD gets the same count within one)
+  auto wave_tiles = [&](int64_t r_begin, int64_t r_end, int &tile_lo, int &tile_hi) {
+    const int ntiles = (int)((r_end - r_begin + 15) / 16);
+    const int tb = ntiles / NW, tx = ntiles % NW;
+    tile_lo = wave * tb + (wave < tx ? wave : tx);
+    tile_hi = tile_lo + tb + (wave < tx ? 1 : 0);
+  };
+  // range of the window split that rides on compressed split `split`
+  auto ride_range = [&](int64_t &r_begin, int64_t &r_end) {
+    r_begin = n_c + (int64_t)split * plan.win_len;
+    r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
+    if (r_end < r_begin) r_end = r_begin;
+  };
   auto run_part = [&](const int part) {
   // ---- RoPE angle state of the lane's token for its 16 frequencies; the
   // table loads (anchor_issue) and the products (anchor_finish) are apart so
@@ -743,18 +759,15 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     const int64_t pend = length < D.prefix ? length : D.prefix;
     r_begin = (int64_t)xs * plan.pre_len;
     r_end = r_begin + plan.pre_len < pend ? r_begin + plan.pre_len : pend;
+  } else if (cwg) {
+    ride_range(r_begin, r_end);
   } else {
-    const int wi = cwg ? split : xs - plan.n_pre;
-    r_begin = n_c + (int64_t)wi * plan.win_len;
+    r_begin = n_c + (int64_t)(xs - plan.n_pre) * plan.win_len;
     r_end = r_begin + plan.win_len < length ? r_begin + plan.win_len : length;
   }
   if (r_end < r_begin) r_end = r_begin;
-  const int ntiles = (int)((r_end - r_begin + 15) / 16);
-  // even split: the first ntiles % NW waves take one tile more (waves w and
-  // w + NW/2 share a SIMD, so every SIMD gets the same count within one)
-  const int tb = ntiles / NW, tx = ntiles % NW;
-  const int tile_lo = wave * tb + (wave < tx ? wave : tx);
-  const int tile_hi = tile_lo + tb + (wave < tx ? 1 : 0);
+  int tile_lo, tile_hi;
+  wave_tiles(r_begin, r_end, tile_lo, tile_hi);
   const int64_t w_begin = r_begin + 16 * (int64_t)tile_lo;
   const int nt = __builtin_amdgcn_readfirstlane(tile_hi - tile_lo);   // wave-uniform
 
@@ -821,9 +834,18 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     }
     query_issue();
     uint4_ F[8][FCH];
-    float2 bA, bB, stv[2];
+    float2 bA, bB, stv[2], wA, wB;
     if constexpr (C::kShared) {
       rope_load(M.sh, w_begin, lane, bA, bB);       // base angle of the range, frequency = lane
+      if (nparts == 2) {
+        // and of this wave's tiles of the riding window split, so that part
+        // starts without a memory round trip
+        int64_t wb, we;
+        int wlo, whi;
+        ride_range(wb, we);
+        wave_tiles(wb, we, wlo, whi);
+        rope_load(M.sh, wb + 16 * (int64_t)wlo, lane, wA, wB);
+      }
 #pragma unroll
       for (int k = 0; k < 2; ++k)                   // step rows 0..15, entry threadIdx.x + 512 k
         stv[k] = reinterpret_cast<const float2 *>(M.sh.rope_step)[threadIdx.x + 512 * k];
@@ -840,6 +862,10 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
       float c, sn;
       rope_combine(bA, bB, c, sn);
       s_base[wave * 64 + lane] = float2{c, sn};
+      if (nparts == 2) {
+        rope_combine(wA, wB, c, sn);
+        s_wbase[wave * 64 + lane] = float2{c, sn};
+      }
       if (lane == 0) s_prog[wave] = 0;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -1011,32 +1037,46 @@ __global__ __launch_bounds__((Cfg<RK, RV, T, NW>::kThr), (Cfg<RK, RV, T, NW>::kO
     floatx4 wacc[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) wacc[nb] = zero4();
+    // exact rows: the protected prefix (row = position) or the ring (row =
+    // position % slots); V transposed in both, row stride `rows`
+    const int rows = pre ? D.prefix : D.slots;
+    const T *EK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
+    const T *EV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
+    // raw K rows and V columns of a tile, both issued together (one memory
+    // latency per tile instead of a second one for V)
+    using Raw = typename std::conditional<BF, uint2_, floatx4>::type;
+    auto load_raw = [&](int it, Raw (&k)[8], Raw (&v)[8]) {
+      const int64_t t0 = w_begin + 16 * (int64_t)it;
+      const int slot = (int)((t0 + n16) % rows);
+      const int slot0 = (int)(t0 % rows);             // tiles never wrap (16 | slots, 64 | P)
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        k[mb] = *reinterpret_cast<const Raw *>(EK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        v[nb] = *reinterpret_cast<const Raw *>(EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
+    };
+    // the riding part of an eight-wave workgroup takes its base angles from
+    // the prologue (LDS); other exact parts load them here
+    const bool lds_angles = C::kShared && part == 1;
     if (!q_ready) query_issue();
-    if (nt > 0) anchor_issue(w_begin + n16);
+    if (nt > 0 && !lds_angles) anchor_issue(w_begin + n16);
     __builtin_amdgcn_sched_barrier(0);
-    if (nt > 0) anchor_finish();
+    if (nt > 0 && !lds_angles) anchor_finish();
     if (!q_ready) query_finish(false);
     else __syncthreads();               // the fused append's ring rows are visible
+    if (nt > 0 && lds_angles) {
+      const float2 *base = s_wbase + wave * 64;
+      const float2 *st16 = s_st16 + n16;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = 16 * mb + 4 * rho + i;
+          rope_combine(base[f], st16[17 * f], cs_c[mb * 4 + i], cs_s[mb * 4 + i]);
+        }
+    }
     if (nt > 0) {
-      // exact rows: the protected prefix (row = position) or the ring (row =
-      // position % slots); V transposed in both, row stride `rows`
-      const int rows = pre ? D.prefix : D.slots;
-      const T *EK = reinterpret_cast<const T *>(pre ? P.prek : P.ringk) + (size_t)u * rows * kHeadDim;
-      const T *EV = reinterpret_cast<const T *>(pre ? P.prev : P.ringv) + (size_t)u * rows * kHeadDim;
-      // raw K rows and V columns of a tile, both issued at the tile start
-      // (one memory latency per tile instead of a second one for V)
-      using Raw = typename std::conditional<BF, uint2_, floatx4>::type;
-      auto load_raw = [&](int it, Raw (&k)[8], Raw (&v)[8]) {
-        const int64_t t0 = w_begin + 16 * (int64_t)it;
-        const int slot = (int)((t0 + n16) % rows);
-        const int slot0 = (int)(t0 % rows);             // tiles never wrap (16 | slots, 64 | P)
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-          k[mb] = *reinterpret_cast<const Raw *>(EK + (size_t)slot * kHeadDim + 16 * mb + 4 * rho);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-          v[nb] = *reinterpret_cast<const Raw *>(EV + (size_t)(16 * nb + n16) * rows + slot0 + 4 * rho);
-      };
       for (int it = 0; it < nt; ++it) {
         const int64_t t0 = w_begin + 16 * (int64_t)it;
         Raw kc[8], vc[8];
