@@ -173,10 +173,33 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, rho = lane >> 4;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TPW * 16;
-  if (base >= n_old) return;                    // uniform per wave
+  // plain sync at r = 32 and 64: every wave of the workgroup uses the same M,
+  // so the workgroup splits it once into LDS (A-operand order) while its row
+  // loads are in flight; the waves read their operands from there.  (At
+  // r = 16 the per-wave split is cheap and the barrier costs more; r = 128
+  // would need 96 KiB of LDS.)
+  constexpr bool kShareM = !BULK && R >= 32 && R <= 64;
+  constexpr int PAIRS = R >= 32 ? 4 : 2;
+  __shared__ uint4_ s_a[kShareM ? MB * KB * 3 * 64 : 1];
+  if (!kShareM && base >= n_old) return;        // uniform per wave
   if constexpr (BULK) {
     Ms = bulk_matrix(M, bk, blockIdx.z, x, u, R, base);
     if (!Ms) return;
+  }
+  // shared M: each thread's M values are requested before the rows (loads
+  // complete in order, so the split below waits for them alone)
+  constexpr int NIT = kShareM ? MB * KB : 1;    // (MB * KB * 64 * 4) / kThreads slots a thread
+  static_assert(!kShareM || kThreads == 256, "slots per thread");
+  float mv0[NIT], mv1[NIT];
+  if constexpr (kShareM) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int e = threadIdx.x + j * kThreads;
+      const int i = e & 3, ln = (e >> 2) & 63, kb = (e >> 8) % KB, mb = (e >> 8) / KB;
+      const int c = R >= 32 ? kb * 32 + 8 * (ln >> 4) + 2 * i : 4 * (ln >> 4) + 2 * i;
+      mv0[j] = i < PAIRS ? Ms[c * R + mb * 16 + (ln & 15)] : 0.f;
+      mv1[j] = i < PAIRS ? Ms[(c + 1) * R + mb * 16 + (ln & 15)] : 0.f;
+    }
   }
   // every input row of the wave is in registers before any output is written
   uint4_ b[TPW][KB];
@@ -195,22 +218,46 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
       }
     }
   }
+  if constexpr (kShareM) {
+    // slot (mb, kb, lane, i): pair i of the lane's A operand, in its three
+    // parts; slots past PAIRS (r = 16) stay zero
+    unsigned *sa = reinterpret_cast<unsigned *>(s_a);
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int e = threadIdx.x + j * kThreads;
+      const int i = e & 3, ln = (e >> 2) & 63, kb = (e >> 8) % KB, mb = (e >> 8) / KB;
+      unsigned h = 0u, md = 0u, lo = 0u;
+      if (i < PAIRS) split3(mv0[j], mv1[j], h, md, lo);
+      const int q = (mb * KB + kb) * 3 * 64 + ln;
+      sa[(q + 0 * 64) * 4 + i] = h;
+      sa[(q + 1 * 64) * 4 + i] = md;
+      sa[(q + 2 * 64) * 4 + i] = lo;
+    }
+    __syncthreads();
+    if (base >= n_old) return;                  // uniform per wave, after the barrier
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     // A operand: M^T rows mb*16 + n, as high, middle and low bf16 parts
     uint4_ ahi[KB], amid[KB], alo[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      constexpr int PAIRS = R >= 32 ? 4 : 2;
-      unsigned h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+      if constexpr (kShareM) {
+        const int q = (mb * KB + kb) * 3 * 64 + lane;
+        ahi[kb] = s_a[q];
+        amid[kb] = s_a[q + 64];
+        alo[kb] = s_a[q + 128];
+      } else {
+        unsigned h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < PAIRS; ++i) {
-        const int c = R >= 32 ? kb * 32 + 8 * rho + 2 * i : 4 * rho + 2 * i;
-        split3(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], md[i], lo[i]);
+        for (int i = 0; i < PAIRS; ++i) {
+          const int c = R >= 32 ? kb * 32 + 8 * rho + 2 * i : 4 * rho + 2 * i;
+          split3(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], md[i], lo[i]);
+        }
+        ahi[kb] = uint4_{h[0], h[1], h[2], h[3]};
+        amid[kb] = uint4_{md[0], md[1], md[2], md[3]};
+        alo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
       }
-      ahi[kb] = uint4_{h[0], h[1], h[2], h[3]};
-      amid[kb] = uint4_{md[0], md[1], md[2], md[3]};
-      alo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
     }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
