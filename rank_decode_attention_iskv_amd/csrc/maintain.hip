@@ -173,34 +173,39 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, rho = lane >> 4;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * TPW * 16;
-  // plain sync at r = 32 and 64: every wave of the workgroup uses the same M,
-  // so the workgroup splits it once into LDS (A-operand order) while its row
-  // loads are in flight; the waves read their operands from there.  (At
-  // r = 16 the per-wave split is cheap and the barrier costs more; r = 128
-  // would need 96 KiB of LDS.)
-  constexpr bool kShareM = !BULK && R >= 32 && R <= 64;
+  // plain sync at r >= 32: every wave of the workgroup uses the same M, so
+  // the workgroup splits it into LDS in the A-operand order -- at once up to
+  // r = 64, in two halves of the M-blocks at r = 128 (48 KiB of LDS each) --
+  // and the waves read their operands from there.  The first (or only) part
+  // of M is requested before the rows, so its split waits for M alone (loads
+  // complete in order).  At r = 16 each wave splits its own operands (cheap
+  // there; the barrier would cost more).
+  constexpr bool kShareM = !BULK && R >= 32;
   constexpr int PAIRS = R >= 32 ? 4 : 2;
-  __shared__ uint4_ s_a[kShareM ? MB * KB * 3 * 64 : 1];
+  constexpr int MBP = R == 128 ? MB / 2 : MB;    // M-blocks per LDS phase
+  constexpr int NPH = MB / MBP;
+  __shared__ uint4_ s_a[kShareM ? MBP * KB * 3 * 64 : 1];
   if (!kShareM && base >= n_old) return;        // uniform per wave
   if constexpr (BULK) {
     Ms = bulk_matrix(M, bk, blockIdx.z, x, u, R, base);
     if (!Ms) return;
   }
-  // shared M: each thread's M values are requested before the rows (loads
-  // complete in order, so the split below waits for them alone)
-  constexpr int NIT = kShareM ? MB * KB : 1;    // (MB * KB * 64 * 4) / kThreads slots a thread
+  // slot e of a phase: pair i of lane ln's A operand of (local) M-block mbl,
+  // K-block kb; (MBP * KB * 64 * 4) / kThreads slots a thread
+  constexpr int NIT = kShareM ? MBP * KB : 1;
   static_assert(!kShareM || kThreads == 256, "slots per thread");
   float mv0[NIT], mv1[NIT];
-  if constexpr (kShareM) {
+  auto fetch_m = [&](int ph) {
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int e = threadIdx.x + j * kThreads;
-      const int i = e & 3, ln = (e >> 2) & 63, kb = (e >> 8) % KB, mb = (e >> 8) / KB;
-      const int c = R >= 32 ? kb * 32 + 8 * (ln >> 4) + 2 * i : 4 * (ln >> 4) + 2 * i;
-      mv0[j] = i < PAIRS ? Ms[c * R + mb * 16 + (ln & 15)] : 0.f;
-      mv1[j] = i < PAIRS ? Ms[(c + 1) * R + mb * 16 + (ln & 15)] : 0.f;
+      const int i = e & 3, ln = (e >> 2) & 63, kb = (e >> 8) % KB, mb = ph * MBP + (e >> 8) / KB;
+      const int c = kb * 32 + 8 * (ln >> 4) + 2 * i;
+      mv0[j] = Ms[c * R + mb * 16 + (ln & 15)];
+      mv1[j] = Ms[(c + 1) * R + mb * 16 + (ln & 15)];
     }
-  }
+  };
+  if constexpr (kShareM) fetch_m(0);
   // every input row of the wave is in registers before any output is written
   uint4_ b[TPW][KB];
 #pragma unroll
@@ -218,47 +223,9 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
       }
     }
   }
-  if constexpr (kShareM) {
-    // slot (mb, kb, lane, i): pair i of the lane's A operand, in its three
-    // parts; slots past PAIRS (r = 16) stay zero
-    unsigned *sa = reinterpret_cast<unsigned *>(s_a);
-#pragma unroll
-    for (int j = 0; j < NIT; ++j) {
-      const int e = threadIdx.x + j * kThreads;
-      const int i = e & 3, ln = (e >> 2) & 63, kb = (e >> 8) % KB, mb = (e >> 8) / KB;
-      unsigned h = 0u, md = 0u, lo = 0u;
-      if (i < PAIRS) split3(mv0[j], mv1[j], h, md, lo);
-      const int q = (mb * KB + kb) * 3 * 64 + ln;
-      sa[(q + 0 * 64) * 4 + i] = h;
-      sa[(q + 1 * 64) * 4 + i] = md;
-      sa[(q + 2 * 64) * 4 + i] = lo;
-    }
-    __syncthreads();
-    if (base >= n_old) return;                  // uniform per wave, after the barrier
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    // A operand: M^T rows mb*16 + n, as high, middle and low bf16 parts
-    uint4_ ahi[KB], amid[KB], alo[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if constexpr (kShareM) {
-        const int q = (mb * KB + kb) * 3 * 64 + lane;
-        ahi[kb] = s_a[q];
-        amid[kb] = s_a[q + 64];
-        alo[kb] = s_a[q + 128];
-      } else {
-        unsigned h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < PAIRS; ++i) {
-          const int c = R >= 32 ? kb * 32 + 8 * rho + 2 * i : 4 * rho + 2 * i;
-          split3(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], md[i], lo[i]);
-        }
-        ahi[kb] = uint4_{h[0], h[1], h[2], h[3]};
-        amid[kb] = uint4_{md[0], md[1], md[2], md[3]};
-        alo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
-      }
-    }
+  // output column block mb from its A operand: M^T rows mb*16 + n, as high,
+  // middle and low bf16 parts
+  auto column_block = [&](int mb, const uint4_ (&ahi)[KB], const uint4_ (&amid)[KB], const uint4_ (&alo)[KB]) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       floatx4 acc = zero4();
@@ -284,6 +251,61 @@ __global__ __launch_bounds__(kThreads) void sync_mfma_kernel(Model M, LayerSel s
         *reinterpret_cast<uint2_ *>(Co + tok * R + mb * 16 + 4 * rho) =
             uint2_{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
       }
+    }
+  };
+  if constexpr (kShareM) {
+    unsigned *sa = reinterpret_cast<unsigned *>(s_a);
+    const bool active = base < n_old;           // uniform per wave; every wave takes the barriers
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+      if (ph > 0) {
+        __syncthreads();                        // the previous phase's operands are read
+        fetch_m(ph);
+      }
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        const int e = threadIdx.x + j * kThreads;
+        const int i = e & 3, ln = (e >> 2) & 63;
+        unsigned h, md, lo;
+        split3(mv0[j], mv1[j], h, md, lo);
+        const int q = (e >> 8) * 3 * 64 + ln;   // (mbl * KB + kb) * 3 * 64 + ln
+        sa[(q + 0 * 64) * 4 + i] = h;
+        sa[(q + 1 * 64) * 4 + i] = md;
+        sa[(q + 2 * 64) * 4 + i] = lo;
+      }
+      __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int mbl = 0; mbl < MBP; ++mbl) {
+          uint4_ ahi[KB], amid[KB], alo[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int q = (mbl * KB + kb) * 3 * 64 + lane;
+            ahi[kb] = s_a[q];
+            amid[kb] = s_a[q + 64];
+            alo[kb] = s_a[q + 128];
+          }
+          column_block(ph * MBP + mbl, ahi, amid, alo);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      uint4_ ahi[KB], amid[KB], alo[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        unsigned h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) {
+          const int c = R >= 32 ? kb * 32 + 8 * rho + 2 * i : 4 * rho + 2 * i;
+          split3(Ms[c * R + mb * 16 + n], Ms[(c + 1) * R + mb * 16 + n], h[i], md[i], lo[i]);
+        }
+        ahi[kb] = uint4_{h[0], h[1], h[2], h[3]};
+        amid[kb] = uint4_{md[0], md[1], md[2], md[3]};
+        alo[kb] = uint4_{lo[0], lo[1], lo[2], lo[3]};
+      }
+      column_block(mb, ahi, amid, alo);
     }
   }
 }
