@@ -26,10 +26,11 @@
 //           + i, mb = 0..7, of token l%16: 16 RoPE pairs (f, f + 64), rotated
 //           in registers at the token's position;
 //   scores  S (16 tokens x 16 heads) = K~ Q~^T.  bf16 storage: the rotated
-//           key rounded once to fp16 (2^-12 relative, below the bf16 rounding
+//           key rounded once to fp16 (2^-11 relative, below the bf16 rounding
 //           of the stored coefficients), the query as fp16 hi + lo (two
-//           products); fp32 storage: both sides split bf16 hi/lo (hi*hi +
-//           hi*lo + lo*hi, ~2^-16).  Lane l gets head l%16 and tokens
+//           products; with 4 query heads per KV head the low parts ride in
+//           columns 4..7 of one product); fp32 storage: both sides split
+//           bf16 hi/lo (hi*hi + hi*lo + lo*hi, ~2^-16).  Lane l gets head l%16 and tokens
 //           4*(l/16)..+3, the A-operand layout of the value product; query
 //           heads beyond the group are zero;
 //   softmax running max per head in log2 units, rescaled lazily (only when
