@@ -205,7 +205,12 @@ int iskv_discard_sync(iskv_ctx *c, int layer);
  * RoPE.  dev_out: float [batch][num_q_heads][head_dim].  Query head h reads KV
  * head h / (num_q_heads / num_kv_heads).  q_pos must lie in [0, max_tokens + 128)
  * (the range of the RoPE tables built at init), else EINVAL.  ESTATE if the
- * layer is empty. */
+ * layer is empty.  Arithmetic: fp32 accumulation throughout; with bf16
+ * storage the key rebuild multiplies the stored coefficients (converted to
+ * fp16 exactly; a coefficient beyond +-65504 saturates there) by the key
+ * basis rounded to fp16, and the score product takes the rotated key in fp16
+ * against the query as fp16 high + low parts; with fp32 storage both products
+ * carry ~2^-16 relative error or less. */
 int iskv_decode_attn(iskv_ctx *c, int layer, const float *dev_q, int64_t q_pos, float *dev_out);
 
 /* One decode step in one launch: iskv_append of a single token (dev_k, dev_v:
