@@ -52,7 +52,7 @@ paper), abbreviated [iS-KV explainer].
   two factors never interact before decode, so a V factor of rank r_V is the
   same Brand fold and sync at a different r; the default is r_V = r.
 
-Readings taken where the page is silent (each is listed in the design doc):
+Readings taken where the page is silent:
   window of W exact tokens plus up to 63 not yet folded (ring of W+64 rows,
   fold when it is full); basis per KV head, separate for K and V, rank r for
   both unless V is given its own rank r_V (see below);
