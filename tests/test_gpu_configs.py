@@ -159,10 +159,10 @@ def test_config4_all_36_layers_block_update_and_sync():
         assert err < ATOL_OUT, (layer, err)
 
 
-@pytest.mark.parametrize("rank,window", [(16, 128), (64, 1024), (128, 1024)])
+@pytest.mark.parametrize("rank,window", [(r, w) for r in (16, 32, 64, 128) for w in (128, 1024)])
 def test_config5_batch64_8k_decode(rank, window):
-    """Batch 64 x 8,192 tokens, 8 KV / 32 query heads, bf16, at the sweep's
-    corner points; every unit's output is computed on the GPU, twelve sampled
+    """Batch 64 x 8,192 tokens, 8 KV / 32 query heads, bf16, at every point of
+    the sweep (r x window); every unit's output is computed on the GPU, twelve sampled
     (sequence, KV head) units are recomputed by the oracle."""
     w = workloads.with_(workloads.WORKLOADS[5], rank=rank, window=window)
     length = 8192
