@@ -5,8 +5,12 @@
   * 36 layers x 8 KV / 32 query heads, r = 32, window 1,024, bf16: decode at a
     65,536-token context with query positions above 32K (RoPE at 64K), and one
     block update + sync over all 36 layers in one call (576 fold workgroups);
-  * batch 64 x 8K, 8 KV / 32 query heads, (r, window) = (16, 128), (64, 1024),
-    (128, 1024): decode on an imported state, outputs sampled per unit;
+  * batch 64 x 8K, 8 KV / 32 query heads, every (r, window) of the sweep
+    (r in 16, 32, 64, 128; window 128 or 1024): decode on an imported state,
+    outputs sampled per unit;
+  * batch 64, 8 KV heads: one block update + sync over all 512 units (1,024
+    cores, more fold workgroups than the chip holds at once), sampled units
+    against the oracle;
   * the 32K GQA layer: one block update + sync on a full-size state (the sync
     rewrites all 32K old rows);
   * block update + sync on a second stream, checked against the oracle.
@@ -174,6 +178,47 @@ def test_config5_batch64_8k_decode(rank, window):
     err = _sampled_decode_error(w, gpu, length, n_c, max_tokens, [length - 1], units)
     gpu.destroy()
     assert err < ATOL_OUT, err
+
+
+
+@pytest.mark.parametrize("rank,window", [(32, 128), (128, 1024)])
+def test_config5_batch64_fold_and_sync(rank, window):
+    """Batch 64, 8 KV / 32 query heads, bf16, a full ring in every unit: one
+    block update + sync folds 64 x 8 x 2 = 1,024 cores of size (r + 64)^2 in
+    one call; the rebuilt histories and the decode of sampled units are
+    compared with the oracle's fold + sync of the same imported state."""
+    w = workloads.with_(workloads.WORKLOADS[5], rank=rank, window=window)
+    n_c = 1024
+    length = n_c + window + 64
+    max_tokens = length + 64
+    cfg, gpu = _import_synthetic(w, length, n_c, max_tokens, ring_in_span=True)
+    assert gpu.status(0).blocks_ready == 1
+    gpu.block_update(0)
+    gpu.sync(0)
+    from rank_decode_attention_iskv_amd import binding
+    _, n_c2, got = binding.unpack_state(cfg, gpu.export_state(0))
+    assert n_c2 == n_c + 64
+    units = [(0, 0), (1, 3), (13, 5), (31, 1), (47, 4), (63, 7)]
+    g = w.q_heads // w.kv_heads
+    q = q32(workloads.query(w, 0, 0))
+    out = _decode(gpu, q, length - 1)
+    gpu.destroy()
+    worst_hist = worst_out = 0.0
+    for (b, h) in units:
+        u = _oracle_unit(w, workloads.synthetic_unit(w, b, h, length, n_c, max_tokens,
+                                                     ring_in_span=True), length, n_c, max_tokens)
+        u.fold()
+        u.sync()
+        for x, f in enumerate((u.K, u.V)):
+            gu = got[b * w.kv_heads + h][x]
+            Hg = gu["coef"][:n_c2].astype(np.float64) @ gu["basis"].T
+            Ho = f.C[:n_c2] @ f.B.T
+            worst_hist = max(worst_hist, float(np.linalg.norm(Hg - Ho) / np.linalg.norm(Ho)))
+        ref = u.decode(q[b, h * g:(h + 1) * g], length - 1, 1.0 / math.sqrt(w.head_dim))
+        worst_out = max(worst_out, rel_err_per_head(out[b, h * g:(h + 1) * g], ref))
+    print(f"batch-64 fold r={rank} W={window}: history {worst_hist:.2e}, decode {worst_out:.2e}")
+    assert worst_hist < HIST_BF16, worst_hist
+    assert worst_out < ATOL_OUT, worst_out
 
 
 def test_config2_fold_and_sync_at_full_history():
