@@ -11,16 +11,17 @@ against closed forms that do not depend on it.
   * repeated tokens: each 64-token block repeats one key row, so each block
     has rank 1 and the residual Gram has a single non-zero pivot.  Seven
     distinct keys fit in r = 32: the key history comes back exactly.
+  * the shortest caches (1, 2, 15, 16, 17 and 33 tokens, all in the exact
+    window, one partly filled 16-token tile): against the oracle, and at one
+    token against softmax over a single key, which returns that token's value.
 """
-
-import math
 
 import numpy as np
 import pytest
 
 import workloads
 from oracle import Oracle
-from tests.gpu_util import q32, rel_err_per_head, small
+from tests.gpu_util import Pair, q32, rel_err_per_head, small
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +127,23 @@ def test_repeated_token_blocks_keep_the_key_history():
     print(f"repeated-token blocks: key history {hist:.2e}, decode vs oracle {max(errs):.2e}")
     assert hist < 1e-4, hist
     assert max(errs) < ATOL_OUT, errs
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_decode_on_the_shortest_caches(storage):
+    w = small(2, kv_heads=2, q_heads=8, window=128, storage=storage)
+    p = Pair(w, max_tokens=512)
+    errs = {}
+    for L in (1, 2, 15, 16, 17, 33):
+        p.feed(0, L - p.length[0])
+        q = q32(workloads.query(w, 0, L))
+        got = p.decode(0, q, L - 1)
+        errs[L] = rel_err_per_head(got, p.ora.decode_attn(0, q, L - 1))
+        if L == 1 and storage == "f32":
+            _, v0 = workloads.tokens(w, 0, 0, 1)
+            g = w.q_heads // w.kv_heads
+            v0 = v0[:, 0].astype(np.float32).astype(np.float64)       # [batch, kv_heads, d]
+            one = np.repeat(v0, g, axis=1)                           # query head -> its KV head
+            assert rel_err_per_head(got, one) < 1e-6
+    print(f"shortest caches {storage}: " + ", ".join(f"L={L} {e:.1e}" for L, e in errs.items()))
+    assert max(errs.values()) < ATOL_OUT, errs
