@@ -1294,20 +1294,42 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves, int o
   return make_plan_core(D, n_c - D.prefix, n_e, n_p, per_unit < 1 ? 1 : per_unit, waves);
 }
 
-// Ragged batch: the workgroups a batch of the average length would get,
-// shared out in proportion to each sequence's length.
+// Ragged batch: the workgroups a batch of the average length would get, per
+// KV head `budget`, shared out so that the largest share of tokens is as
+// small as the budget allows: the smallest cap c (tokens per workgroup) with
+// sum_b max(1, ceil(L_b / c)) <= budget, sequence b taking ceil(L_b / c).
+// With all lengths equal each sequence takes budget / n, the uniform call's
+// count; with more sequences than the budget every sequence takes one.
 SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ) {
   SeqPlans sp{};
   sp.n = tab.n;
-  int64_t total = 0;
-  for (int b = 0; b < tab.n; ++b) total += tab.len[b];
+  int64_t total = 0, lmax = 1;
+  bool equal = true;
+  for (int b = 0; b < tab.n; ++b) {
+    total += tab.len[b];
+    lmax = std::max<int64_t>(lmax, tab.len[b]);
+    equal = equal && tab.len[b] == tab.len[0];
+  }
   const int64_t target = target_workgroups(D, (total + tab.n - 1) / tab.n, waves, occ);
+  const int64_t budget = target / D.kv_heads;
+  auto shares = [&](int64_t cap) {
+    int64_t s = 0;
+    for (int b = 0; b < tab.n; ++b) s += std::max<int64_t>(1, (tab.len[b] + cap - 1) / cap);
+    return s;
+  };
+  int64_t lo = 1, hi = lmax;                 // shares(lmax) = tab.n, the fewest
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (shares(mid) <= budget) hi = mid;
+    else lo = mid + 1;
+  }
+  const int64_t cap = lo;
   sp.off[0] = 0;
   for (int b = 0; b < tab.n; ++b) {
     const int64_t L = tab.len[b], c = tab.nc[b];
     const int64_t n_e = L > c ? L - c : 0;
     const int64_t n_p = L < D.prefix ? L : D.prefix;
-    const int64_t per_unit = std::max<int64_t>(1, target * L / (total * D.kv_heads));
+    const int64_t per_unit = std::max<int64_t>(1, equal ? budget / tab.n : (L + cap - 1) / cap);
     const SplitPlan p = make_plan_core(D, c - D.prefix, n_e, n_p, per_unit, waves);
     sp.n_comp[b] = (int16_t)p.n_comp;
     sp.n_pre[b] = (int16_t)p.n_pre;
