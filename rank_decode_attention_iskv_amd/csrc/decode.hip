@@ -1300,7 +1300,9 @@ SplitPlan make_plan(const Dims &D, int64_t length, int64_t n_c, int waves, int o
 // sum_b max(1, ceil(L_b / c)) <= budget, sequence b taking ceil(L_b / c).
 // With all lengths equal each sequence takes budget / n, the uniform call's
 // count; with more sequences than the budget every sequence takes one.
-SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ) {
+// *largest (if given) = the most tokens any workgroup of the plan takes.
+SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ,
+                        int64_t *largest = nullptr) {
   SeqPlans sp{};
   sp.n = tab.n;
   int64_t total = 0, lmax = 1;
@@ -1324,12 +1326,14 @@ SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ) {
     else lo = mid + 1;
   }
   const int64_t cap = lo;
+  int64_t most = 0;
   sp.off[0] = 0;
   for (int b = 0; b < tab.n; ++b) {
     const int64_t L = tab.len[b], c = tab.nc[b];
     const int64_t n_e = L > c ? L - c : 0;
     const int64_t n_p = L < D.prefix ? L : D.prefix;
     const int64_t per_unit = std::max<int64_t>(1, equal ? budget / tab.n : (L + cap - 1) / cap);
+    most = std::max(most, (L + per_unit - 1) / per_unit);
     const SplitPlan p = make_plan_core(D, c - D.prefix, n_e, n_p, per_unit, waves);
     sp.n_comp[b] = (int16_t)p.n_comp;
     sp.n_pre[b] = (int16_t)p.n_pre;
@@ -1340,6 +1344,7 @@ SeqPlans make_seq_plans(const Dims &D, const SeqTab &tab, int waves, int occ) {
     sp.win_rides[b] = (uint8_t)p.win_rides;
     sp.off[b + 1] = sp.off[b] + plan_workgroups(p);
   }
+  if (largest) *largest = most;
   return sp;
 }
 
@@ -1400,16 +1405,24 @@ hipError_t launch_rank(const Model &M, int layer, const float *q, int64_t q_pos,
   constexpr int occ4 = Cfg<RK, RV, T, 4>::kOcc;
   constexpr bool has8 = std::is_same<T, bf16_t>::value && RK <= 64 && RV <= 64;
   if (tab.n) {
-    // ragged: one plan per sequence, (sequence, split) flattened into grid.x
+    // ragged: one plan per sequence, (sequence, split) flattened into grid.x;
+    // with lengths that differ, eight waves only if the four-wave plan's
+    // finer shares (twice the workgroups) do not leave each wave fewer
+    // tokens; with equal lengths the uniform call's choice
     const SplitPlan none{};
+    int64_t most4 = 0;
+    const SeqPlans s4 = make_seq_plans(M.D, tab, 4, occ4, &most4);
     if constexpr (has8) {
-      const SeqPlans s8 = make_seq_plans(M.D, tab, 8, 1);
+      int64_t most8 = 0;
+      const SeqPlans s8 = make_seq_plans(M.D, tab, 8, 1, &most8);
+      bool same = true;
+      for (int b = 1; b < tab.n; ++b) same = same && tab.len[b] == tab.len[0];
       if (forced_waves() == 8 ||
-          (forced_waves() != 4 && (int64_t)s8.off[s8.n] * M.D.kv_heads <= M.D.cus))
+          (forced_waves() != 4 && (int64_t)s8.off[s8.n] * M.D.kv_heads <= M.D.cus &&
+           (same || most8 <= 2 * most4)))
         return launch_mfma<RK, RV, T, 8>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab, s8);
     }
-    return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab,
-                                     make_seq_plans(M.D, tab, 4, occ4));
+    return launch_mfma<RK, RV, T, 4>(M, layer, q, q_pos, out, length, n_c, none, s, app, tab, s4);
   }
   const SeqPlans one{};
   if constexpr (has8) {
