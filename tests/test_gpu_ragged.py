@@ -303,3 +303,49 @@ def test_ragged_and_uniform_layers_fold_together():
         np.testing.assert_array_equal(a, b)
     for b in range(w.batch):
         assert caches[0].seq_status(0, b).compressed == caches[1].seq_status(0, b).compressed == n_c[0][b]
+
+
+def test_ragged_widely_unequal_lengths_match_single_sequence_caches():
+    """bf16, G=4, r=32, window 128: 8 sequences held at 192 .. 3,072 tokens.
+    For these lengths the four-wave decode plan leaves each wave fewer tokens
+    than the eight-wave one (280 vs 2 x 128 tokens a workgroup), so the
+    ragged call takes the four-wave form while its eight-wave grid would fit;
+    every sequence's output agrees with a batch-1 cache fed the same stream."""
+    import torch
+    from rank_decode_attention_iskv_amd import binding
+    target = [192, 384, 640, 1024, 1536, 2048, 2560, 3072]
+    w = small(2, batch=len(target), kv_heads=2, q_heads=8, window=128)
+    limit = max(target)
+    r = Ragged(w, limit + 64, oracle=False)
+    singles = []
+    for b in range(w.batch):
+        cfg = binding.make_config(1, 1, w.kv_heads, w.q_heads, w.head_dim, w.rank, w.window,
+                                  limit + 64, binding.BF16)
+        singles.append(binding.IskvCache(cfg))
+    while r.length != target:
+        start = list(r.length)
+        counts = [min(64, r.free(b), target[b] - r.length[b]) for b in range(w.batch)]
+        full = r.step(counts)
+        for b, c in enumerate(counts):
+            if not c:
+                continue
+            k, v = seq_tokens(w, b, start[b], c)
+            ready = singles[b].append(0, torch.from_numpy(k[None]).cuda(), torch.from_numpy(v[None]).cuda())
+            assert ready == (b in full)
+            if ready:
+                singles[b].block_update(0)
+                singles[b].sync(0)
+    q = q32(workloads.query(w, 0, 5))
+    q_pos = [L + 2 for L in r.length]
+    got = r.decode(q, q_pos)
+    errs = []
+    for b in range(w.batch):
+        qt = torch.from_numpy(q[b:b + 1].astype(np.float32)).cuda()
+        out = torch.empty_like(qt)
+        singles[b].decode_attn(0, qt, q_pos[b], out)
+        torch.cuda.synchronize()
+        errs.append(rel_err_per_head(got[b:b + 1], out.cpu().numpy().astype(np.float64)))
+    print(f"widely unequal ragged batch vs batch-1 caches: {max(errs):.2e}")
+    # split boundaries differ between the two sides (see the bound above)
+    assert max(errs) < 5e-5, errs
+    assert min(r.folds) >= 1 and max(r.folds) >= 40
